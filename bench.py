@@ -1,0 +1,281 @@
+#!/usr/bin/env python3
+"""Split-KV decode attention benchmark on one MI355X.
+
+One step is one pass of the whole decode path over the resident batch: the
+host split planner, the partial kernel (per-split online softmax) and the
+combine kernel. The default workload is the 128K-token MHA decode (batch 1,
+32 heads, d = 128, fp16, 1% of key rows scaled by 4). Prints one JSON line.
+
+  value     KV-read GB/s over the whole step = algorithmic KV bytes / step time
+            (K and V read once: sum_b L_b * Hkv * d * 2 * sizeof(fp16))
+  roofline  the partial kernel alone: the same bytes / its mean launch time,
+            measured with HIP events around every launch in the timed region,
+            against the 8 TB/s HBM peak
+  cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
+            workload on this host (a reported baseline, not a target)
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KV-read GB/s and µs/call, decode attention 128K ctx b=1 (fraction of HBM peak)"
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E peak
+O_MAX_ABS, O_REL_RMS, LSE_ABS = 2e-3, 1e-3, 1e-4
+KERNEL_SOURCE = os.path.join(ROOT, "split_kv_flash_decoding_amd", "csrc", "fd_kernels.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(msg: str) -> None:
+    sys.stderr.write(f"[bench] {msg}\n")
+    sys.stderr.flush()
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def kv_bytes(wl) -> int:
+    return wl.total_tokens * wl.num_kv_heads * wl.head_dim * 2 * wl.k.element_size()
+
+
+def measured_traffic(workload: str):
+    """Per-launch HBM bytes of the partial kernel from committed rocprofv3 PMC
+    runs, if they were taken on the current kernel source; else None."""
+    path = os.path.join(PROFILES, f"partial_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def spot_check(fd, wl, out, lse, heads):
+    import numpy as np
+
+    import oracle
+
+    pairs = [(0, h) for h in heads]
+    ref_o, ref_l = oracle.decode_attention(wl.q, wl.k, wl.v, wl.seq_lens, wl.scale, wl.block_table,
+                                           wl.page_size, pairs=pairs)
+    o = out.double().cpu().numpy()
+    ls = lse.double().cpu().numpy()
+    errs = []
+    for b, h in pairs:
+        d = o[b, h] - ref_o[b, h]
+        errs.append((float(np.max(np.abs(d))), float(np.linalg.norm(d) / np.linalg.norm(ref_o[b, h])),
+                     abs(float(ls[b, h] - ref_l[b, h]))))
+    worst = tuple(max(e[i] for e in errs) for i in range(3))
+    ok = worst[0] <= O_MAX_ABS and worst[1] <= O_REL_RMS and worst[2] <= LSE_ABS
+    return ok, worst
+
+
+def cpu_baseline(wl, budget_s: float):
+    """Time the oracle, unchanged, on whole heads of the workload until the
+    budget is spent."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    hq = wl.num_q_heads
+    done = 0
+    t0 = time.perf_counter()
+    for h in range(hq):
+        oracle.decode_attention(wl.q, wl.k, wl.v, wl.seq_lens, wl.scale, wl.block_table, wl.page_size,
+                                pairs=[(b, h) for b in range(wl.batch)])
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    G = wl.group_size
+    kv_heads_read = -(-done // G) if G > 1 else done
+    sample_bytes = wl.total_tokens * kv_heads_read * wl.head_dim * 2 * wl.k.element_size()
+    try:
+        model = next(l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name"))
+    except Exception:
+        model = "unknown"
+    return {
+        "value": sample_bytes / el / 1e9,
+        "unit": "GB/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": f"{done} of {hq} query heads x {wl.total_tokens} tokens (all batch rows), "
+                  f"{el:.1f} s wall; fp64 NumPy oracle; host {model}, "
+                  f"{len(os.sched_getaffinity(0))} cores in affinity mask",
+        "us_per_call_extrapolated": el / done * hq * 1e6,
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=3, help="workload 1..5 (default: 128K MHA)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--check-heads", type=int, default=4, help="query heads spot-checked against the oracle")
+    ap.add_argument("--json-out", default=None)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        sys.stderr.write("bench.py measures one GPU only: this decode path is built and timed on a single "
+                         "MI355X; run it with --gpus 1.\n")
+        return 2
+
+    import torch
+
+    import split_kv_flash_decoding_amd as fd
+    from workloads import make_config
+
+    if not torch.cuda.is_available():
+        sys.stderr.write("bench.py needs a GPU\n")
+        return 2
+    fd.load_library()
+    dev = torch.device("cuda", 0)
+
+    t = time.perf_counter()
+    wl = make_config(args.config)
+    log(f"generated {wl.name} in {time.perf_counter() - t:.1f} s")
+    q, k, v = wl.q.to(dev), wl.k.to(dev), wl.v.to(dev)
+    bt = wl.block_table.to(dev) if wl.paged else None
+    lens_host = wl.lens
+    lens_dev = wl.seq_lens.to(dev)
+    problem = fd.make_problem(batch=wl.batch, num_q_heads=wl.num_q_heads, num_kv_heads=wl.num_kv_heads,
+                              head_dim=wl.head_dim, kv_dtype=wl.dtype, out_dtype=torch.float32, scale=wl.scale,
+                              page_size=wl.page_size, max_pages_per_seq=wl.max_pages_per_seq)
+    plan = fd.fd_plan_splits(problem, lens_host, 0, wl.force_num_splits)
+    ws = torch.empty(-(-plan.workspace_bytes // 4), dtype=torch.float32, device=dev)
+    out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim), dtype=torch.float32, device=dev)
+    lse = torch.empty((wl.batch, wl.num_q_heads), dtype=torch.float32, device=dev)
+    nbytes = kv_bytes(wl)
+    log(f"plan {plan.as_dict()}; KV bytes {nbytes}")
+
+    def step():
+        p = fd.fd_plan_splits(problem, lens_host, 0, wl.force_num_splits)
+        fd.fd_decode_partial(problem, p, q, k, v, bt, lens_dev, ws)
+        fd.fd_combine(problem, p, lens_dev, ws, out, lse)
+
+    step()
+    torch.cuda.synchronize()
+    heads = sorted(set(int(round(i * (wl.num_q_heads - 1) / max(1, args.check_heads - 1)))
+                       for i in range(args.check_heads)))
+    ok, worst = spot_check(fd, wl, out, lse, heads)
+    log(f"spot check heads {heads}: O max-abs {worst[0]:.2e} rel-rms {worst[1]:.2e} LSE {worst[2]:.2e}")
+    if not ok:
+        sys.stderr.write("bench.py: the kernel disagrees with the oracle; refusing to time it\n")
+        return 1
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for i in range(K):
+        p = fd.fd_plan_splits(problem, lens_host, 0, wl.force_num_splits)
+        ev_a[i].record()
+        fd.fd_decode_partial(problem, p, q, k, v, bt, lens_dev, ws)
+        ev_b[i].record()
+        fd.fd_combine(problem, p, lens_dev, ws, out, lse)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = start.elapsed_time(end) / K
+    partial_ms = [a.elapsed_time(b) for a, b in zip(ev_a, ev_b)]
+    partial_mean = statistics.fmean(partial_ms)
+    log(f"{K} steps: {ms_per_step * 1e3:.1f} us/step (events), wall {wall / K * 1e6:.1f} us/step; "
+        f"partial kernel mean {partial_mean * 1e3:.1f} us, median {statistics.median(partial_ms) * 1e3:.1f} us")
+
+    # achievable streaming-read bandwidth on the same buffers, for context
+    sink = torch.empty(fd.PROBE_SINK_FLOATS, dtype=torch.float32, device=dev)
+    for _ in range(3):
+        fd.fd_probe_read(k, sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        fd.fd_probe_read(k, sink)
+        fd.fd_probe_read(v, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    probe_gbps = 2 * reps * k.numel() * k.element_size() / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    log(f"streaming-read probe over K and V: {probe_gbps:.0f} GB/s")
+
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (partial_mean * 1e-3) / 1e9
+    workload = wl.name
+    traffic = measured_traffic(workload)
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_call": round(ms_per_step * 1e3, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if wl.dtype == torch.float16 else "bf16",
+        "data": "synthetic (seeded N(0,1) q/K/V; no dataset involved)",
+        "config": {
+            "workload": workload,
+            "batch": wl.batch, "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads,
+            "head_dim": wl.head_dim, "seq_lens_total": wl.total_tokens, "page_size": wl.page_size,
+            "accumulate": "f32", "out_dtype": "f32",
+            "chunk_tokens": plan.chunk_tokens, "splits": plan.max_splits, "total_splits": plan.total_splits,
+            "kv_bytes_per_call": nbytes,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "partial",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4),
+            "traffic": traffic,
+            "partial_us_mean": round(partial_mean * 1e3, 2),
+            "hbm_read_probe_gbps": round(probe_gbps, 1),
+            "frac_of_probe": round(achieved / probe_gbps, 4),
+        },
+        "parity_spot_check": {"heads": heads, "o_max_abs": worst[0], "o_rel_rms": worst[1], "lse_abs": worst[2]},
+    }
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle for about {args.cpu_budget:.0f} s ...")
+        rec["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    else:
+        rec["cpu_baseline"] = None
+    line = json.dumps(rec)
+    print(line, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(line + "\n")
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

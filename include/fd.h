@@ -1,0 +1,179 @@
+/*
+ * fd.h - split-KV flash decoding for AMD Instinct MI355X (gfx950).
+ *
+ * Decode attention for one query token per sequence over a long KV cache:
+ *     out[b,h,:] = softmax(scale * K_b q[b,h]) V_b,   lse[b,h] = ln sum_t exp(scale * <q[b,h], K_b[t]>)
+ * (the definition in "FlashAttention 全景演进与大模型 Token 生成全链路性能优化实战",
+ * §1.1). The cache of each sequence is cut along the token axis into splits of
+ * `chunk_tokens` consecutive tokens; each split computes a running max m, a
+ * running sum l and an unnormalised partial output O, and a second pass
+ * merges the splits by log-sum-exp rescaling (same page, §2.3 FlashDecoding,
+ * and §1.2 for the merge identity; also "注意力算子、算子融合与 CUDA Graph",
+ * section on decode attention). The merged result is exactly the definition
+ * up to floating-point rounding.
+ *
+ * Layouts (all dense, row-major):
+ *   q            [B, Hq, d]            kv dtype (fp16 or bf16)
+ *   k, v         contiguous: [sum_b L_b, Hkv, d]; sequence b starts at token
+ *                row sum_{b'<b} L_b' (a packed variable-length batch).
+ *                paged (page_size 16): pools [P, 16, Hkv, d]; token t of
+ *                sequence b is at pool[block_table[b, t / 16], t % 16]
+ *                (the 16-token physical blocks and per-request block table of
+ *                the FlashAttention capstone, §4.1).
+ *   block_table  int32 [B, max_pages_per_seq], paged only.
+ *   seq_lens     int32 [B], every L_b >= 1.
+ *   out          [B, Hq, d] in out_dtype;  lse  float32 [B, Hq], natural log.
+ *   Query head h reads KV head h / (Hq / Hkv) (grouped-query attention with
+ *   contiguous groups, capstone §4.2).
+ *
+ * Ownership: the caller allocates every buffer (device memory for q, k, v,
+ * block_table, seq_lens_dev, out, lse and the workspace; host memory for
+ * seq_lens_host and the structs). The library allocates no device memory,
+ * never frees anything and keeps no state except a per-device cache of the
+ * compute-unit count. It reads the inputs and writes only out, lse and the
+ * workspace.
+ *
+ * Streams: `stream` is a hipStream_t passed as void* (NULL = the default
+ * stream). Every call that takes one only enqueues work on it and returns;
+ * results are ready once the stream is synchronised. Calls made on one stream
+ * with one workspace are ordered; using one workspace from two streams at once
+ * races.
+ *
+ * Errors: no C++ exception crosses this interface. Every call returns an
+ * fd_status; on failure fd_last_error_message() (per thread) says why.
+ * Argument checks happen on the host before anything is enqueued, so a call
+ * that returns an error has launched nothing. The device seq_lens must equal
+ * the host seq_lens the plan was made from; the kernels bound every workspace
+ * access by the plan and every paged access by max_pages_per_seq, but they
+ * cannot check device lengths against the caller's contiguous cache size.
+ */
+#ifndef FD_H
+#define FD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fd_status {
+    FD_OK = 0,
+    FD_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad size, inconsistent shapes */
+    FD_ERR_UNSUPPORTED = 2,        /* valid but not built: head_dim, page size, group size */
+    FD_ERR_WORKSPACE_TOO_SMALL = 3,
+    FD_ERR_HIP = 4                 /* the HIP runtime reported an error (launch, device query) */
+} fd_status;
+
+typedef enum fd_dtype {
+    FD_F16 = 0,
+    FD_BF16 = 1,
+    FD_F32 = 2
+} fd_dtype;
+
+/* The problem shape. q, k and v share `kv_dtype`. */
+typedef struct fd_problem {
+    int32_t batch;             /* B >= 1 */
+    int32_t num_q_heads;       /* Hq >= 1 */
+    int32_t num_kv_heads;      /* Hkv >= 1, divides Hq; Hq/Hkv in {1, 2, 4, 8} */
+    int32_t head_dim;          /* d in {64, 128} */
+    int32_t kv_dtype;          /* FD_F16 or FD_BF16 */
+    int32_t out_dtype;         /* FD_F32, FD_F16 or FD_BF16 */
+    float scale;               /* softmax scale; <= 0 selects 1/sqrt(d) */
+    int32_t page_size;         /* 0 = contiguous packed cache, 16 = paged */
+    int32_t max_pages_per_seq; /* paged: columns of block_table; ignored otherwise */
+} fd_problem;
+
+/* How the splits are cut. Holds scalars only: nothing is uploaded per call,
+ * and each kernel derives a sequence's split count ceil(L_b / chunk_tokens)
+ * from the device seq_lens. */
+typedef struct fd_plan {
+    int32_t chunk_tokens;      /* C: tokens per split */
+    int32_t max_splits;        /* S_max = max_b ceil(L_b / C): workspace stride */
+    int32_t total_splits;      /* sum_b ceil(L_b / C) */
+    int32_t num_cus;           /* compute units the plan was sized for */
+    int32_t partial_kernel;    /* which partial kernel runs (0 = vector ALU, 1 = MFMA) */
+    int32_t reserved;
+    int64_t total_tokens;      /* sum_b L_b */
+    uint64_t workspace_bytes;  /* bytes the workspace must hold */
+} fd_plan;
+
+/*
+ * Size the splits for one batch (host only).
+ *
+ * Chooses C so that sum_b ceil(L_b / C) * Hkv work-groups keep every compute
+ * unit busy (FlashAttention capstone §2.3: one head per processor starves a
+ * GPU with few KV heads, so the sequence is cut into chunks), with C at least
+ * 256 tokens (the chunk the same section gives as an example) and a multiple
+ * of 64. `force_num_splits` > 0 instead sets C = ceil(max_b L_b / force) and
+ * accepts any C >= 1. `num_cus` == 0 asks the current HIP device (the only
+ * HIP call here; its count is cached per device). Validates the problem and
+ * every length (1 <= L_b, and L_b <= max_pages_per_seq * 16 when paged).
+ * seq_lens_host: B lengths in host memory. out: receives the plan.
+ * The environment variables FD_NUM_SPLITS (forces splits when the argument
+ * is 0), FD_MIN_CHUNK and FD_WG_PER_CU override the sizing for experiments.
+ */
+fd_status fd_plan_splits(const fd_problem* problem, const int32_t* seq_lens_host,
+                         int32_t num_cus, int32_t force_num_splits, fd_plan* out);
+
+/*
+ * Per-split partials (asynchronous on `stream`).
+ *
+ * For every sequence b, query head h and split s < ceil(L_b / C) writes the
+ * split's running max m_s = max_t scale*<q, k_t>, sum l_s = sum_t
+ * exp(scale*<q,k_t> - m_s) and unnormalised output O_s = sum_t
+ * exp(scale*<q,k_t> - m_s) v_t over the split's tokens t in
+ * [s*C, min((s+1)*C, L_b)) (the per-chunk local softmax of capstone §2.3; the
+ * running-statistics loop of the lpnh.cn memory-wall article, §2.2). Tokens
+ * at or past L_b are never read.
+ *
+ * Workspace layout (float32, all of it written by the kernels, so the caller
+ * never initialises it):
+ *   O  [B, Hq, S_max, d]       at byte offset 0
+ *   ML [B, Hq, S_max, 2]       at byte offset B*Hq*S_max*d*4: (m_s, l_s) pairs,
+ *                              m_s in natural-log units of the scaled score.
+ * Entries of splits a sequence does not have are left untouched.
+ * q, k, v, block_table (NULL when contiguous), seq_lens_dev: device pointers.
+ */
+fd_status fd_decode_partial(const fd_problem* problem, const fd_plan* plan,
+                            const void* q, const void* k, const void* v,
+                            const int32_t* block_table, const int32_t* seq_lens_dev,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Merge the partials (asynchronous on `stream`).
+ *
+ * For every (b, h): M = max_s m_s, w_s = exp(m_s - M), l = sum_s w_s l_s,
+ * out = sum_s w_s O_s / l and lse = M + ln l (the cross-chunk reduce of
+ * capstone §2.3, by the two-block identity of §1.2 applied to every split).
+ * out: device [B, Hq, d] in out_dtype. lse: device float32 [B, Hq], or NULL.
+ */
+fd_status fd_combine(const fd_problem* problem, const fd_plan* plan,
+                     const int32_t* seq_lens_dev, const void* workspace,
+                     size_t workspace_bytes, void* out, float* lse, void* stream);
+
+/*
+ * One call: plan (with num_cus = 0 and no forced split count), partials,
+ * merge. Returns FD_ERR_WORKSPACE_TOO_SMALL, having launched nothing, if
+ * workspace_bytes is below the plan's need; size the workspace with
+ * fd_plan_splits beforehand. seq_lens_host and seq_lens_dev hold the same B
+ * lengths, in host and device memory.
+ */
+fd_status fd_decode_attention(const fd_problem* problem,
+                              const void* q, const void* k, const void* v,
+                              const int32_t* block_table,
+                              const int32_t* seq_lens_host, const int32_t* seq_lens_dev,
+                              void* out, float* lse,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* A static, human-readable name for a status code. */
+const char* fd_status_string(fd_status status);
+
+/* The message of the last failed call on this thread ("" if none). */
+const char* fd_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FD_H */

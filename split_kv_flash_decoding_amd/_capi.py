@@ -1,0 +1,295 @@
+"""ctypes binding of include/fd.h.
+
+Argument marshalling only: every step of decode attention runs in the HIP
+library. PyTorch provides device memory and the stream handle. The library
+must be built (``python -m split_kv_flash_decoding_amd.build``); if it is
+missing, loading raises instead of falling back to anything else.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfd.so")
+
+FD_OK, FD_ERR_INVALID_ARGUMENT, FD_ERR_UNSUPPORTED, FD_ERR_WORKSPACE_TOO_SMALL, FD_ERR_HIP = range(5)
+FD_F16, FD_BF16, FD_F32 = range(3)
+
+# Every function fd.h declares; the CPU tests check the library exports them.
+EXPORTED = (
+    "fd_plan_splits",
+    "fd_decode_partial",
+    "fd_combine",
+    "fd_decode_attention",
+    "fd_status_string",
+    "fd_last_error_message",
+    "fd_probe_read",
+    "fd_probe_copy",
+)
+PROBE_SINK_FLOATS = 4096
+
+
+class FdProblem(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("page_size", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32),
+    ]
+
+
+class FdPlan(ctypes.Structure):
+    _fields_ = [
+        ("chunk_tokens", ctypes.c_int32),
+        ("max_splits", ctypes.c_int32),
+        ("total_splits", ctypes.c_int32),
+        ("num_cus", ctypes.c_int32),
+        ("partial_kernel", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("total_tokens", ctypes.c_int64),
+        ("workspace_bytes", ctypes.c_uint64),
+    ]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+
+
+class FdError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        super().__init__(f"{status_string(status)}: {message}")
+
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libfd.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -m split_kv_flash_decoding_amd.build`")
+    lib = ctypes.CDLL(p)
+    P, Pl = ctypes.POINTER(FdProblem), ctypes.POINTER(FdPlan)
+    vp, i32p, f32p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32), ctypes.c_void_p
+    lib.fd_plan_splits.argtypes = [P, i32p, ctypes.c_int32, ctypes.c_int32, Pl]
+    lib.fd_decode_partial.argtypes = [P, Pl, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.fd_combine.argtypes = [P, Pl, vp, vp, ctypes.c_size_t, vp, f32p, vp]
+    lib.fd_decode_attention.argtypes = [P, vp, vp, vp, vp, i32p, vp, vp, f32p, vp, ctypes.c_size_t, vp]
+    for name in ("fd_plan_splits", "fd_decode_partial", "fd_combine", "fd_decode_attention"):
+        getattr(lib, name).restype = ctypes.c_int
+    lib.fd_status_string.argtypes = [ctypes.c_int]
+    lib.fd_status_string.restype = ctypes.c_char_p
+    lib.fd_last_error_message.argtypes = []
+    lib.fd_last_error_message.restype = ctypes.c_char_p
+    lib.fd_probe_read.argtypes = [vp, ctypes.c_size_t, vp, vp]
+    lib.fd_probe_read.restype = ctypes.c_int
+    lib.fd_probe_copy.argtypes = [vp, vp, ctypes.c_size_t, vp]
+    lib.fd_probe_copy.restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().fd_status_string(status).decode()
+
+
+def _check(status: int) -> None:
+    if status != FD_OK:
+        raise FdError(status, load_library().fd_last_error_message().decode())
+
+
+# ------------------------------------------------------------------ problems
+
+
+def _dtype_code(dt) -> int:
+    import torch
+
+    table = {torch.float16: FD_F16, torch.bfloat16: FD_BF16, torch.float32: FD_F32}
+    if dt not in table:
+        raise ValueError(f"unsupported dtype {dt}")
+    return table[dt]
+
+
+def make_problem(*, batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int, kv_dtype,
+                 out_dtype=None, scale: Optional[float] = None, page_size: int = 0,
+                 max_pages_per_seq: int = 0) -> FdProblem:
+    import torch
+
+    return FdProblem(
+        batch=batch, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
+        kv_dtype=_dtype_code(kv_dtype), out_dtype=_dtype_code(out_dtype or torch.float32),
+        scale=0.0 if scale is None else float(scale), page_size=page_size,
+        max_pages_per_seq=max_pages_per_seq)
+
+
+def _lens_array(seq_lens_host: Sequence[int]):
+    vals = [int(x) for x in (seq_lens_host.tolist() if hasattr(seq_lens_host, "tolist") else seq_lens_host)]
+    return (ctypes.c_int32 * len(vals))(*vals), vals
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check_tensors(problem: FdProblem, q, k, v, block_table, seq_lens_dev, total_tokens: Optional[int]):
+    import torch
+
+    B, hq, hkv, d = problem.batch, problem.num_q_heads, problem.num_kv_heads, problem.head_dim
+    kvdt = {FD_F16: torch.float16, FD_BF16: torch.bfloat16}.get(problem.kv_dtype)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != kvdt:
+            raise ValueError(f"{name} must be a contiguous {kvdt} CUDA tensor")
+    if tuple(q.shape) != (B, hq, d):
+        raise ValueError(f"q has shape {tuple(q.shape)}, expected {(B, hq, d)}")
+    if k.shape != v.shape:
+        raise ValueError("k and v shapes differ")
+    if problem.page_size:
+        if k.dim() != 4 or tuple(k.shape[1:]) != (problem.page_size, hkv, d):
+            raise ValueError(f"paged k must be [P, {problem.page_size}, {hkv}, {d}]")
+        if block_table is None or block_table.dtype != torch.int32 or not block_table.is_cuda \
+                or tuple(block_table.shape) != (B, problem.max_pages_per_seq) or not block_table.is_contiguous():
+            raise ValueError(f"block_table must be a contiguous int32 CUDA tensor [{B}, {problem.max_pages_per_seq}]")
+    else:
+        if k.dim() != 3 or tuple(k.shape[1:]) != (hkv, d):
+            raise ValueError(f"contiguous k must be [rows, {hkv}, {d}]")
+        if total_tokens is not None and k.shape[0] < total_tokens:
+            raise ValueError(f"k holds {k.shape[0]} rows, the lengths need {total_tokens}")
+    if seq_lens_dev.dtype != torch.int32 or not seq_lens_dev.is_cuda or seq_lens_dev.numel() != B:
+        raise ValueError("seq_lens_dev must be an int32 CUDA tensor with one entry per sequence")
+
+
+# ------------------------------------------------------------------ the calls
+
+
+def fd_plan_splits(problem: FdProblem, seq_lens_host, num_cus: int = 0, force_num_splits: int = 0) -> FdPlan:
+    lib = load_library()
+    arr, _ = _lens_array(seq_lens_host)
+    plan = FdPlan()
+    _check(lib.fd_plan_splits(ctypes.byref(problem), arr, num_cus, force_num_splits, ctypes.byref(plan)))
+    return plan
+
+
+def fd_decode_partial(problem: FdProblem, plan: FdPlan, q, k, v, block_table, seq_lens_dev, workspace,
+                      stream=None) -> None:
+    _check_tensors(problem, q, k, v, block_table, seq_lens_dev, plan.total_tokens)
+    _check(load_library().fd_decode_partial(
+        ctypes.byref(problem), ctypes.byref(plan), _ptr(q), _ptr(k), _ptr(v), _ptr(block_table),
+        _ptr(seq_lens_dev), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def fd_combine(problem: FdProblem, plan: FdPlan, seq_lens_dev, workspace, out, lse=None, stream=None) -> None:
+    B, hq, d = problem.batch, problem.num_q_heads, problem.head_dim
+    if tuple(out.shape) != (B, hq, d) or not out.is_contiguous() or _dtype_code(out.dtype) != problem.out_dtype:
+        raise ValueError(f"out must be contiguous [{B}, {hq}, {d}] of the problem's out_dtype")
+    if lse is not None and (tuple(lse.shape) != (B, hq) or not lse.is_contiguous() or _dtype_code(lse.dtype) != FD_F32):
+        raise ValueError(f"lse must be contiguous float32 [{B}, {hq}]")
+    _check(load_library().fd_combine(
+        ctypes.byref(problem), ctypes.byref(plan), _ptr(seq_lens_dev), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def fd_decode_attention(problem: FdProblem, q, k, v, block_table, seq_lens_host, seq_lens_dev, out, lse,
+                        workspace, stream=None) -> None:
+    arr, vals = _lens_array(seq_lens_host)
+    _check_tensors(problem, q, k, v, block_table, seq_lens_dev, sum(vals))
+    B, hq, d = problem.batch, problem.num_q_heads, problem.head_dim
+    if tuple(out.shape) != (B, hq, d) or not out.is_contiguous() or _dtype_code(out.dtype) != problem.out_dtype:
+        raise ValueError(f"out must be contiguous [{B}, {hq}, {d}] of the problem's out_dtype")
+    if lse is not None and (tuple(lse.shape) != (B, hq) or _dtype_code(lse.dtype) != FD_F32):
+        raise ValueError(f"lse must be float32 [{B}, {hq}]")
+    _check(load_library().fd_decode_attention(
+        ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(block_table), arr, _ptr(seq_lens_dev),
+        _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+# --------------------------------------------------------------- convenience
+
+
+@dataclass
+class DecodeResult:
+    out: object
+    lse: object
+    plan: FdPlan
+    workspace: object
+
+
+def workspace_views(problem: FdProblem, plan: FdPlan, workspace):
+    """(O [B,Hq,S,d], m [B,Hq,S], l [B,Hq,S]) float32 views of a workspace."""
+    B, hq, d, S = problem.batch, problem.num_q_heads, problem.head_dim, plan.max_splits
+    n_o = B * hq * S * d
+    flat = workspace.view(-1)[: n_o + B * hq * S * 2]
+    O = flat[:n_o].view(B, hq, S, d)
+    ml = flat[n_o:].view(B, hq, S, 2)
+    return O, ml[..., 0], ml[..., 1]
+
+
+def decode_attention(q, k, v, seq_lens, *, block_table=None, page_size: int = 0, max_pages_per_seq: int = 0,
+                     scale: Optional[float] = None, out_dtype=None, num_splits: int = 0, num_cus: int = 0,
+                     stream=None) -> DecodeResult:
+    """Plan, partials and merge for one batch; allocates out, lse and the
+    workspace with torch on q's device. ``seq_lens`` may be a CPU tensor or list."""
+    import torch
+
+    B, hq, d = q.shape
+    hkv = k.shape[-2]
+    problem = make_problem(batch=B, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, kv_dtype=q.dtype,
+                           out_dtype=out_dtype or torch.float32, scale=scale, page_size=page_size,
+                           max_pages_per_seq=max_pages_per_seq or (block_table.shape[1] if block_table is not None else 0))
+    lens_host = seq_lens.tolist() if hasattr(seq_lens, "tolist") else list(seq_lens)
+    plan = fd_plan_splits(problem, lens_host, num_cus=num_cus, force_num_splits=num_splits)
+    if block_table is not None:
+        # The kernels trust page indices; check the ones they will read (this synchronises).
+        num_pages = k.shape[0]
+        for b, n in enumerate(lens_host):
+            used = block_table[b, : -(-int(n) // page_size)]
+            lo, hi = int(used.min()), int(used.max())
+            if lo < 0 or hi >= num_pages:
+                raise ValueError(f"block_table row {b} names page {lo if lo < 0 else hi} outside [0, {num_pages})")
+    dev = q.device
+    lens_dev = torch.tensor(lens_host, dtype=torch.int32, device=dev)
+    ws = torch.empty(int(math.ceil(plan.workspace_bytes / 4)), dtype=torch.float32, device=dev)
+    out = torch.empty((B, hq, d), dtype=out_dtype or torch.float32, device=dev)
+    lse = torch.empty((B, hq), dtype=torch.float32, device=dev)
+    fd_decode_partial(problem, plan, q, k, v, block_table, lens_dev, ws, stream)
+    fd_combine(problem, plan, lens_dev, ws, out, lse, stream)
+    return DecodeResult(out=out, lse=lse, plan=plan, workspace=ws)
+
+
+# ------------------------------------------------------------------- probes
+
+
+def fd_probe_read(src, sink, stream=None) -> None:
+    """Stream every byte of the CUDA tensor ``src`` once (include/fd_probe.h)."""
+    if not src.is_cuda or not sink.is_cuda or sink.numel() * sink.element_size() < PROBE_SINK_FLOATS * 4:
+        raise ValueError("src and sink must be CUDA tensors; sink holds PROBE_SINK_FLOATS floats")
+    _check(load_library().fd_probe_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(stream)))
+
+
+def fd_probe_copy(dst, src, stream=None) -> None:
+    """Copy the CUDA tensor ``src`` into ``dst`` (same byte size)."""
+    nbytes = src.numel() * src.element_size()
+    if not src.is_cuda or not dst.is_cuda or dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("dst and src must be CUDA tensors of equal byte size")
+    _check(load_library().fd_probe_copy(_ptr(dst), _ptr(src), nbytes, _stream(stream)))

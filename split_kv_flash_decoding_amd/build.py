@@ -1,0 +1,62 @@
+"""Compile the HIP library (libfd.so) for gfx950, in-tree.
+
+Run as ``python -m split_kv_flash_decoding_amd.build``. The library is placed
+next to this file; the binding loads it from there.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_NAME = "libfd.so"
+LIB_PATH = os.path.join(HERE, LIB_NAME)
+
+SOURCES = ["fd_host.cpp", "fd_kernels.hip", "fd_probe.hip"]
+
+# Packed fp32 instructions stay off (the compiler would otherwise form
+# v_pk_* fp32 ops from float code).
+HIP_FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-Wall",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (set HIPCC or install ROCm)")
+
+
+def build(verbose: bool = False, extra_flags=None) -> str:
+    cc = hipcc()
+    tmp = LIB_PATH + ".tmp"
+    cmd = [cc, *HIP_FLAGS, *(extra_flags or []), "-I", INCLUDE, "-I", CSRC, "-shared",
+           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"hipcc failed with status {res.returncode}")
+    noise = "is not a recognized feature for this target"
+    warn = "\n".join(x for x in (res.stdout + res.stderr).splitlines() if noise not in x)
+    if warn.strip() and verbose:
+        sys.stderr.write(warn + "\n")
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

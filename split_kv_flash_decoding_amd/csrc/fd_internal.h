@@ -1,0 +1,37 @@
+// Internal declarations shared by the host planner (fd_host.cpp) and the
+// kernels and launchers (fd_kernels.hip). Not part of the public interface.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "fd.h"
+
+namespace fd {
+
+// Largest grid extent used along y (splits) and z (batch).
+constexpr int32_t kMaxGridYZ = 65535;
+// Token rows a partial-kernel work-group consumes per pass (the planner keeps
+// automatic chunks a multiple of it).
+constexpr int32_t kChunkGranule = 64;
+constexpr int32_t kDefaultMinChunk = 256;
+constexpr int32_t kDefaultWgPerCu = 4;
+constexpr int32_t kPageSize = 16;
+
+// Records `msg` as this thread's last error and returns `st`.
+fd_status fail(fd_status st, const char* fmt, ...);
+void clear_error();
+
+// Checks the problem fields (not the lengths). Resolves the scale.
+fd_status check_problem(const fd_problem* p, float* scale_out);
+// Checks a plan against the problem it is used with.
+fd_status check_plan(const fd_problem* p, const fd_plan* plan);
+
+// Workspace layout: O [B, Hq, S_max, d] then ML [B, Hq, S_max, 2], float32.
+uint64_t workspace_o_bytes(const fd_problem* p, int32_t max_splits);
+uint64_t workspace_bytes(const fd_problem* p, int32_t max_splits);
+
+// Compute units of the current HIP device, cached per device (fd_kernels.hip).
+fd_status query_num_cus(int32_t* out);
+
+}  // namespace fd

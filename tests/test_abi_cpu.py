@@ -1,0 +1,197 @@
+"""The C ABI without a GPU: exports, argument validation and the split planner.
+
+Nothing here launches a kernel. fd_plan_splits with an explicit compute-unit
+count is pure host code; the error paths of the launching calls return before
+any HIP call.
+"""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import split_kv_flash_decoding_amd as fd
+from split_kv_flash_decoding_amd import _capi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+INCLUDE = os.path.join(ROOT, "include")
+
+
+def declared_functions():
+    names = set()
+    for h in sorted(os.listdir(INCLUDE)):
+        if h.endswith(".h"):
+            text = open(os.path.join(INCLUDE, h)).read()
+            names |= set(re.findall(r"^\s*(?:fd_status|const char\*)\s+(fd_\w+)\s*\(", text, re.M))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_function():
+    lib = fd.load_library()
+    names = declared_functions()
+    assert set(names) == set(fd.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_probe_calls_validate_before_launching():
+    lib = fd.load_library()
+    fake = ctypes.c_void_p(0x10000)
+    assert lib.fd_probe_read(None, 16, fake, None) == fd.FD_ERR_INVALID_ARGUMENT
+    assert lib.fd_probe_read(fake, 24, fake, None) == fd.FD_ERR_INVALID_ARGUMENT
+    assert lib.fd_probe_copy(fake, ctypes.c_void_p(0x10010), 64, None) == fd.FD_ERR_INVALID_ARGUMENT  # overlap
+    assert lib.fd_probe_copy(fake, ctypes.c_void_p(0x10008), 16, None) == fd.FD_ERR_INVALID_ARGUMENT  # misaligned
+
+
+def test_status_strings():
+    assert fd.status_string(fd.FD_OK) == "FD_OK"
+    assert fd.status_string(fd.FD_ERR_WORKSPACE_TOO_SMALL) == "FD_ERR_WORKSPACE_TOO_SMALL"
+    assert fd.status_string(99) == "FD_ERR_UNKNOWN"
+
+
+def prob(**kw):
+    import torch
+    base = dict(batch=1, num_q_heads=32, num_kv_heads=32, head_dim=128, kv_dtype=torch.float16)
+    base.update(kw)
+    return fd.make_problem(**base)
+
+
+def ceil_div(a, b):
+    return -(-a // b)
+
+
+@pytest.mark.parametrize("hq,hkv,lens", [
+    (32, 32, [32768]),
+    (32, 32, [131072]),
+    (32, 8, [1024, 16384, 5000, 7777] * 4),
+    (64, 8, [512, 32768, 900, 20000] * 16),
+    (8, 8, [1024]),
+    (8, 2, [1, 2, 3, 300]),
+])
+def test_planner_properties(hq, hkv, lens):
+    p = prob(batch=len(lens), num_q_heads=hq, num_kv_heads=hkv)
+    plan = fd.fd_plan_splits(p, lens, num_cus=256)
+    C = plan.chunk_tokens
+    assert C % 64 == 0 and C >= 256 or C == max(lens)
+    splits = [ceil_div(L, C) for L in lens]
+    assert plan.max_splits == max(splits) and plan.total_splits == sum(splits)
+    assert plan.total_tokens == sum(lens) and plan.num_cus == 256 and plan.partial_kernel in (0, 1)
+    # every split non-empty, splits tile [0, L)
+    for L, S in zip(lens, splits):
+        assert (S - 1) * C < L <= S * C
+    assert plan.workspace_bytes == len(lens) * hq * plan.max_splits * (128 + 2) * 4
+    # enough work-groups to cover the chip when there are enough tokens
+    if sum(lens) * hkv >= 256 * 4 * 256:
+        assert plan.total_splits * hkv >= 256 * 2
+
+
+def test_planner_sizes_long_contexts_to_fill_the_chip():
+    plan = fd.fd_plan_splits(prob(), [131072], num_cus=256)
+    assert plan.chunk_tokens == 4096 and plan.max_splits == 32  # 32 heads x 32 splits = 1024 WGs
+    plan = fd.fd_plan_splits(prob(), [32768], num_cus=256)
+    assert plan.chunk_tokens == 1024 and plan.max_splits == 32
+
+
+def test_forced_split_counts():
+    p = prob(batch=1, num_q_heads=8, num_kv_heads=8, head_dim=64)
+    for S in (1, 2, 3, 4, 7, 16, 64):
+        plan = fd.fd_plan_splits(p, [1024], num_cus=256, force_num_splits=S)
+        assert plan.chunk_tokens == ceil_div(1024, S) and plan.max_splits == ceil_div(1024, plan.chunk_tokens)
+    # the worked example: L = 4 cut in two splits of 2
+    plan = fd.fd_plan_splits(p, [4], num_cus=256, force_num_splits=2)
+    assert (plan.chunk_tokens, plan.max_splits) == (2, 2)
+    # more splits than tokens: one token per split
+    plan = fd.fd_plan_splits(p, [5], num_cus=256, force_num_splits=64)
+    assert (plan.chunk_tokens, plan.max_splits) == (1, 5)
+
+
+def test_env_overrides(monkeypatch):
+    monkeypatch.setenv("FD_NUM_SPLITS", "3")
+    plan = fd.fd_plan_splits(prob(), [3000], num_cus=256)
+    assert plan.chunk_tokens == 1000
+    monkeypatch.delenv("FD_NUM_SPLITS")
+    monkeypatch.setenv("FD_MIN_CHUNK", "2048")
+    plan = fd.fd_plan_splits(prob(), [32768], num_cus=256)
+    assert plan.chunk_tokens == 2048
+
+
+@pytest.mark.parametrize("kw,lens,status", [
+    (dict(num_q_heads=12, num_kv_heads=8), [10], fd.FD_ERR_INVALID_ARGUMENT),
+    (dict(num_q_heads=24, num_kv_heads=8), [10], fd.FD_ERR_UNSUPPORTED),
+    (dict(head_dim=96), [10], fd.FD_ERR_UNSUPPORTED),
+    (dict(page_size=8, max_pages_per_seq=4), [10], fd.FD_ERR_UNSUPPORTED),
+    (dict(page_size=16, max_pages_per_seq=0), [10], fd.FD_ERR_INVALID_ARGUMENT),
+    (dict(page_size=16, max_pages_per_seq=2), [33], fd.FD_ERR_INVALID_ARGUMENT),
+    (dict(), [0], fd.FD_ERR_INVALID_ARGUMENT),
+    (dict(), [-5], fd.FD_ERR_INVALID_ARGUMENT),
+    (dict(batch=0), [], fd.FD_ERR_INVALID_ARGUMENT),
+])
+def test_planner_rejects(kw, lens, status):
+    p = prob(batch=kw.pop("batch", max(1, len(lens))), **kw)
+    with pytest.raises(fd.FdError) as ei:
+        fd.fd_plan_splits(p, lens or [1], num_cus=256)
+    assert ei.value.status == status
+    assert _capi.load_library().fd_last_error_message().decode()
+
+
+def test_fp32_kv_is_unsupported_and_null_args_rejected():
+    lib = fd.load_library()
+    p = prob()
+    p.kv_dtype = fd.FD_F32
+    plan = fd.FdPlan()
+    lens = (ctypes.c_int32 * 1)(16)
+    assert lib.fd_plan_splits(ctypes.byref(p), lens, 256, 0, ctypes.byref(plan)) == fd.FD_ERR_UNSUPPORTED
+    p = prob()
+    assert lib.fd_plan_splits(None, lens, 256, 0, ctypes.byref(plan)) == fd.FD_ERR_INVALID_ARGUMENT
+    assert lib.fd_plan_splits(ctypes.byref(p), None, 256, 0, ctypes.byref(plan)) == fd.FD_ERR_INVALID_ARGUMENT
+    assert lib.fd_plan_splits(ctypes.byref(p), lens, 256, 0, None) == fd.FD_ERR_INVALID_ARGUMENT
+    assert lib.fd_plan_splits(ctypes.byref(p), lens, -1, 0, ctypes.byref(plan)) == fd.FD_ERR_INVALID_ARGUMENT
+
+
+def test_launch_calls_validate_before_launching():
+    """Bad arguments return an error before any HIP call (safe without a GPU)."""
+    lib = fd.load_library()
+    p = prob()
+    plan = fd.fd_plan_splits(p, [4096], num_cus=256)
+    fake = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails validation
+    need = plan.workspace_bytes
+    # null q
+    st = lib.fd_decode_partial(ctypes.byref(p), ctypes.byref(plan), None, fake, fake, None, fake, fake, need, None)
+    assert st == fd.FD_ERR_INVALID_ARGUMENT
+    # workspace too small
+    st = lib.fd_decode_partial(ctypes.byref(p), ctypes.byref(plan), fake, fake, fake, None, fake, fake, need - 4, None)
+    assert st == fd.FD_ERR_WORKSPACE_TOO_SMALL
+    # misaligned k
+    st = lib.fd_decode_partial(ctypes.byref(p), ctypes.byref(plan), fake, ctypes.c_void_p(0x10002), fake, None,
+                               fake, fake, need, None)
+    assert st == fd.FD_ERR_INVALID_ARGUMENT
+    # paged without a table
+    pp = prob(page_size=16, max_pages_per_seq=256)
+    pplan = fd.fd_plan_splits(pp, [4096], num_cus=256)
+    st = lib.fd_decode_partial(ctypes.byref(pp), ctypes.byref(pplan), fake, fake, fake, None, fake, fake,
+                               pplan.workspace_bytes, None)
+    assert st == fd.FD_ERR_INVALID_ARGUMENT
+    # a plan that does not fit the problem
+    bad = fd.FdPlan()
+    bad.chunk_tokens, bad.max_splits, bad.workspace_bytes = 0, 1, need
+    st = lib.fd_decode_partial(ctypes.byref(p), ctypes.byref(bad), fake, fake, fake, None, fake, fake, need, None)
+    assert st == fd.FD_ERR_INVALID_ARGUMENT
+    # combine: null out, small workspace
+    st = lib.fd_combine(ctypes.byref(p), ctypes.byref(plan), fake, fake, need, None, None, None)
+    assert st == fd.FD_ERR_INVALID_ARGUMENT
+    st = lib.fd_combine(ctypes.byref(p), ctypes.byref(plan), fake, fake, need - 1, fake, None, None)
+    assert st == fd.FD_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_one_shot_without_gpu_reports_hip_error():
+    """num_cus = 0 asks the HIP runtime; with no device that is FD_ERR_HIP, not a crash."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    lib = fd.load_library()
+    p = prob()
+    lens = (ctypes.c_int32 * 1)(4096)
+    plan = fd.FdPlan()
+    assert lib.fd_plan_splits(ctypes.byref(p), lens, 0, 0, ctypes.byref(plan)) == fd.FD_ERR_HIP

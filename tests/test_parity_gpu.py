@@ -1,0 +1,239 @@
+"""GPU parity: the HIP path against the fp64 CPU oracle on identical seeded inputs.
+
+Tolerances (fp32 accumulation over fp16/bf16 K/V, fp32 output): on O, max-abs
+<= 2e-3 and relative RMS (||dO||_2 / ||O_ref||_2) <= 1e-3 over the whole
+tensor; on LSE, abs <= 1e-4. Every call goes through the C ABI.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import make_config, make_workload
+from workloads.synth import to_paged
+
+pytestmark = pytest.mark.gpu
+
+O_MAX_ABS = 2e-3
+O_REL_RMS = 1e-3
+LSE_ABS = 1e-4
+
+
+def announce(msg: str) -> None:
+    sys.__stderr__.write(f"[gpu case] {msg}\n")
+    sys.__stderr__.flush()
+
+
+def to_dev(wl):
+    dev = torch.device("cuda", 0)
+    bt = wl.block_table.to(dev) if wl.paged else None
+    return wl.q.to(dev), wl.k.to(dev), wl.v.to(dev), bt
+
+
+def run(fd, wl, num_splits=None, out_dtype=torch.float32, dev_tensors=None):
+    q, k, v, bt = dev_tensors or to_dev(wl)
+    ns = wl.force_num_splits if num_splits is None else num_splits
+    announce(f"{wl.name} B={wl.batch} Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} d={wl.head_dim} "
+             f"{wl.dtype} page={wl.page_size} splits={ns or 'auto'} seed={wl.seed}")
+    res = fd.decode_attention(q, k, v, wl.seq_lens, block_table=bt, page_size=wl.page_size,
+                              max_pages_per_seq=wl.max_pages_per_seq, scale=wl.scale,
+                              out_dtype=out_dtype, num_splits=ns)
+    torch.cuda.synchronize()
+    return res
+
+
+def reference(wl, pairs=None):
+    return oracle.decode_attention(wl.q, wl.k, wl.v, wl.seq_lens, wl.scale, wl.block_table,
+                                   wl.page_size, pairs=pairs)
+
+
+def parity(out, lse, ref_out, ref_lse, o_tol=O_MAX_ABS, what=""):
+    o = out.double().cpu().numpy()
+    ls = lse.double().cpu().numpy()
+    mask = ~np.isnan(ref_lse)
+    d_o = o[mask] - ref_out[mask]
+    max_abs = float(np.max(np.abs(d_o)))
+    rel_rms = float(np.linalg.norm(d_o) / np.linalg.norm(ref_out[mask]))
+    lse_err = float(np.max(np.abs(ls[mask] - ref_lse[mask])))
+    announce(f"  parity {what}: O max-abs {max_abs:.3e} rel-rms {rel_rms:.3e} LSE abs {lse_err:.3e}")
+    assert np.isfinite(o[mask]).all() and np.isfinite(ls[mask]).all()
+    assert max_abs <= o_tol, f"O max-abs {max_abs}"
+    assert rel_rms <= O_REL_RMS, f"O rel-rms {rel_rms}"
+    assert lse_err <= LSE_ABS, f"LSE abs {lse_err}"
+    return max_abs, rel_rms, lse_err
+
+
+# ------------------------------------------------------- the worked example
+
+
+def test_worked_example_on_gpu(fd):
+    """Capstone §1.2 tiny calculator embedded exactly in fp16 at d = 64:
+    q = 8 e0, scale 1/8, K[:, 0] = [2, 4, 3, 5], two splits of two tokens.
+    The split statistics must be the page's (m_A, l_A) = (4, 1.1353...) and
+    (m_B, l_B) = (5, 1.1353...), and LSE = 5 + ln(1.5530...)."""
+    d = 64
+    q = torch.zeros(1, 1, d, dtype=torch.float16)
+    q[0, 0, 0] = 8.0
+    k = torch.zeros(4, 1, d, dtype=torch.float16)
+    k[:, 0, 0] = torch.tensor([2.0, 4.0, 3.0, 5.0])
+    g = torch.Generator().manual_seed(0)
+    v = torch.randn(4, 1, d, generator=g).to(torch.float16)
+    wl = make_workload(batch=1, num_q_heads=1, num_kv_heads=1, head_dim=d, seq_lens=[4], pad_rows=0, seed=0)
+    wl.q, wl.k, wl.v, wl.scale, wl.name = q, k, v, 1 / 8, "worked_example"
+    res = run(fd, wl, num_splits=2)
+    assert (res.plan.chunk_tokens, res.plan.max_splits) == (2, 2)
+    O_s, m_s, l_s = fd.workspace_views(fd.make_problem(batch=1, num_q_heads=1, num_kv_heads=1, head_dim=d,
+                                                       kv_dtype=torch.float16), res.plan, res.workspace)
+    m_s = m_s.double().cpu().numpy()[0, 0]
+    l_s = l_s.double().cpu().numpy()[0, 0]
+    lA = math.exp(-2) + 1.0
+    assert np.allclose(m_s, [4.0, 5.0], rtol=0, atol=2e-6)
+    assert np.allclose(l_s, [lA, lA], rtol=2e-6, atol=0)
+    lse = float(res.lse.cpu()[0, 0])
+    assert abs(lse - (5.0 + math.log(math.exp(-3) + math.exp(-1) + math.exp(-2) + 1.0))) < 2e-6
+    ref_out, ref_lse = reference(wl)
+    parity(res.out, res.lse, ref_out, ref_lse, what="worked example")
+    # the unnormalised split outputs against the oracle's split statistics
+    Oo, mo, lo = oracle.decode_partials(wl.q, wl.k, wl.v, wl.seq_lens, wl.scale, 2)
+    assert np.allclose(O_s.double().cpu().numpy()[0, 0], Oo[0, 0], rtol=1e-5, atol=1e-5)
+
+
+# ------------------------------------------------------------ the five configs
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_config_parity(fd, cfg):
+    wl = make_config(cfg)
+    res = run(fd, wl)
+    ref_out, ref_lse = reference(wl)
+    parity(res.out, res.lse, ref_out, ref_lse, what=f"config {cfg} plan={res.plan.as_dict()}")
+
+
+# ------------------------------------------------------- shapes and splits
+
+
+SHAPES = [
+    # (d, dtype, Hq, Hkv, lens, page)
+    (64, torch.float16, 8, 8, [1024], 0),
+    (64, torch.bfloat16, 8, 2, [1, 17, 300, 2049], 0),
+    (128, torch.float16, 4, 4, [1, 15, 16, 17, 63, 64, 65, 255], 0),
+    (128, torch.bfloat16, 16, 2, [1000, 3001, 77], 0),
+    (128, torch.float16, 8, 1, [4097, 5], 0),
+    (128, torch.bfloat16, 32, 8, [513, 1, 2500], 16),
+    (64, torch.float16, 4, 2, [16, 33, 700], 16),
+    (128, torch.float16, 16, 16, [70000], 0),
+]
+
+
+@pytest.mark.parametrize("shape", range(len(SHAPES)))
+@pytest.mark.parametrize("splits", [0, 1, 2, 3, 7, 64])
+def test_shapes_and_forced_splits(fd, shape, splits):
+    d, dt, hq, hkv, lens, page = SHAPES[shape]
+    wl = make_workload(name=f"shape{shape}", batch=len(lens), num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                       seq_lens=lens, dtype=dt, seed=100 + shape, page_size=page)
+    res = run(fd, wl, num_splits=splits)
+    ref_out, ref_lse = reference(wl)
+    parity(res.out, res.lse, ref_out, ref_lse, what=f"shape {shape} splits {splits}")
+
+
+def test_split_count_invariance(fd):
+    wl = make_workload(name="invariance", batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                       seq_lens=[3000, 1111], dtype=torch.bfloat16, seed=21)
+    ref_out, ref_lse = reference(wl)
+    dev = to_dev(wl)
+    outs = []
+    for S in (1, 2, 3, 4, 7, 16, 64, 0):
+        res = run(fd, wl, num_splits=S, dev_tensors=dev)
+        parity(res.out, res.lse, ref_out, ref_lse, what=f"S={S}")
+        outs.append(res.out.double().cpu().numpy())
+    spread = max(float(np.max(np.abs(a - outs[0]))) for a in outs)
+    assert spread <= O_MAX_ABS
+
+
+def test_split_statistics_match_oracle(fd):
+    wl = make_workload(name="stats", batch=2, num_q_heads=4, num_kv_heads=4, head_dim=128,
+                       seq_lens=[1000, 257], dtype=torch.float16, seed=5)
+    res = run(fd, wl, num_splits=4)
+    C = res.plan.chunk_tokens
+    prob = fd.make_problem(batch=2, num_q_heads=4, num_kv_heads=4, head_dim=128, kv_dtype=torch.float16)
+    O_s, m_s, l_s = (x.double().cpu().numpy() for x in fd.workspace_views(prob, res.plan, res.workspace))
+    Oo, mo, lo = oracle.decode_partials(wl.q, wl.k, wl.v, wl.seq_lens, wl.scale, C)
+    for b, L in enumerate(wl.lens):
+        S = -(-L // C)
+        assert np.allclose(m_s[b, :, :S], mo[b, :, :S], rtol=0, atol=1e-5)
+        assert np.allclose(l_s[b, :, :S], lo[b, :, :S], rtol=1e-5, atol=0)
+        scale = np.abs(Oo[b, :, :S]).max()
+        assert np.max(np.abs(O_s[b, :, :S] - Oo[b, :, :S])) <= 1e-5 * max(1.0, scale) * 8
+
+
+# ------------------------------------------------------- paged and invariants
+
+
+def test_paged_identity_permuted_and_contiguous_agree_bitwise(fd):
+    base = make_workload(name="paged-eq", batch=5, num_q_heads=16, num_kv_heads=2, head_dim=128,
+                         seq_lens=[1, 16, 17, 1500, 4096], dtype=torch.bfloat16, seed=31)
+    res_c = run(fd, base, num_splits=3)
+    outs = []
+    for permute in (False, True):
+        pw = to_paged(base, 16, permute=permute, spare_pages=4)
+        pw.name = f"paged permute={permute}"
+        res = run(fd, pw, num_splits=3)
+        outs.append((res.out.cpu(), res.lse.cpu()))
+    assert res.plan.chunk_tokens == res_c.plan.chunk_tokens
+    for o, l in outs:
+        assert torch.equal(o, res_c.out.cpu()) and torch.equal(l, res_c.lse.cpu())
+
+
+def test_deterministic_across_runs(fd):
+    wl = make_config(4)
+    dev = to_dev(wl)
+    a = run(fd, wl, dev_tensors=dev)
+    b = run(fd, wl, dev_tensors=dev)
+    assert torch.equal(a.out, b.out) and torch.equal(a.lse, b.lse)
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float16, torch.bfloat16])
+def test_low_precision_outputs(fd, out_dtype):
+    wl = make_workload(name="outdtype", batch=2, num_q_heads=8, num_kv_heads=8, head_dim=128,
+                       seq_lens=[5000, 64], dtype=torch.float16, seed=8)
+    res = run(fd, wl, out_dtype=out_dtype)
+    ref_out, ref_lse = reference(wl)
+    o = res.out.double().cpu().numpy()
+    ulp = 2.0 ** -11 if out_dtype == torch.float16 else 2.0 ** -8
+    assert np.all(np.abs(o - ref_out) <= O_MAX_ABS + ulp * np.abs(ref_out))
+    assert np.max(np.abs(res.lse.double().cpu().numpy() - ref_lse)) <= LSE_ABS
+
+
+def test_one_shot_matches_split_api_and_checks_workspace(fd):
+    wl = make_config(2)
+    q, k, v, _ = to_dev(wl)
+    res = run(fd, wl, num_splits=0, dev_tensors=(q, k, v, None))
+    prob = fd.make_problem(batch=1, num_q_heads=32, num_kv_heads=32, head_dim=128, kv_dtype=torch.float16,
+                           scale=wl.scale)
+    out = torch.empty_like(res.out)
+    lse = torch.empty_like(res.lse)
+    lens_dev = wl.seq_lens.cuda()
+    announce("fd_decode_attention one-shot, config 2")
+    fd.fd_decode_attention(prob, q, k, v, None, wl.lens, lens_dev, out, lse, res.workspace)
+    torch.cuda.synchronize()
+    assert torch.equal(out, res.out) and torch.equal(lse, res.lse)
+    small = torch.empty(16, dtype=torch.float32, device="cuda")
+    with pytest.raises(fd.FdError) as ei:
+        fd.fd_decode_attention(prob, q, k, v, None, wl.lens, lens_dev, out, lse, small)
+    assert ei.value.status == fd.FD_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_runs_on_a_side_stream(fd):
+    wl = make_workload(name="stream", batch=3, num_q_heads=8, num_kv_heads=4, head_dim=64,
+                       seq_lens=[100, 2000, 31], dtype=torch.float16, seed=44)
+    q, k, v, _ = to_dev(wl)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        res = fd.decode_attention(q, k, v, wl.seq_lens, scale=wl.scale)
+    s.synchronize()
+    ref_out, ref_lse = reference(wl)
+    parity(res.out, res.lse, ref_out, ref_lse, what="side stream")
