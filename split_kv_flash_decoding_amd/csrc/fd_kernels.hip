@@ -49,6 +49,12 @@ constexpr int kThreads = 64 * kWaves;
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
+// Reinterpret one 32-bit word as two 16-bit floats. The word is taken by value:
+// bit-casting an element of an ext_vector_type in place reads element 0 for
+// every index with this compiler.
+__device__ __forceinline__ half2_t as_half2(uint32_t w) { return __builtin_bit_cast(half2_t, w); }
+__device__ __forceinline__ bf162_t as_bf162(uint32_t w) { return __builtin_bit_cast(bf162_t, w); }
+
 // ---------------------------------------------------------------- element ops
 
 template <int DT> struct Elt;
@@ -59,14 +65,13 @@ template <> struct Elt<FD_F16> {
         float acc = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a[i]),
-                                         __builtin_bit_cast(half2_t, b[i]), acc, false);
+            acc = __builtin_amdgcn_fdot2(as_half2(a[i]), as_half2(b[i]), acc, false);
         return acc;
     }
     static __device__ __forceinline__ void to_f32(u32x4 x, float* f) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            half2_t h = __builtin_bit_cast(half2_t, x[i]);
+            const half2_t h = as_half2(x[i]);
             f[2 * i] = (float)h.x;
             f[2 * i + 1] = (float)h.y;
         }
@@ -78,8 +83,7 @@ template <> struct Elt<FD_BF16> {
         float acc = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, a[i]),
-                                                  __builtin_bit_cast(bf162_t, b[i]), acc, false);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf162(a[i]), as_bf162(b[i]), acc, false);
         return acc;
     }
     static __device__ __forceinline__ void to_f32(u32x4 x, float* f) {
