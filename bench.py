@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 METRIC = "KV-read GB/s and µs/call, decode attention 128K ctx b=1 (fraction of HBM peak)"
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E peak
 O_MAX_ABS, O_REL_RMS, LSE_ABS = 2e-3, 1e-3, 1e-4
-KERNEL_SOURCE = os.path.join(ROOT, "split_kv_flash_decoding_amd", "csrc", "fd_kernels.hip")
+KERNEL_SOURCES = os.path.join(ROOT, "split_kv_flash_decoding_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -41,8 +41,12 @@ def log(msg: str) -> None:
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of every source the library is built from (counters go stale when it changes)."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(KERNEL_SOURCES)):
+        with open(os.path.join(KERNEL_SOURCES, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
 
 
 def kv_bytes(wl) -> int:

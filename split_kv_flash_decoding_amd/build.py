@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libfd.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = ["fd_host.cpp", "fd_kernels.hip", "fd_probe.hip"]
+SOURCES = ["fd_host.cpp", "fd_api.hip", "fd_partial_valu.hip", "fd_partial_mfma.hip", "fd_combine.hip",
+           "fd_probe.hip"]
 
 # Packed fp32 instructions stay off (the compiler would otherwise form
 # v_pk_* fp32 ops from float code).

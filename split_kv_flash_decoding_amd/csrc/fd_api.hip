@@ -1,0 +1,123 @@
+// The C-ABI entry points that launch work (fd_decode_partial, fd_combine,
+// fd_decode_attention) and the compute-unit query the planner uses. Argument
+// checks run on the host before anything is enqueued.
+
+#include "fd_device.h"
+
+namespace fd {
+
+fd_status query_num_cus(int32_t* out) {
+    static int32_t cache[64] = {0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(FD_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev >= 0 && dev < 64 && cache[dev] > 0) {
+        *out = cache[dev];
+        return FD_OK;
+    }
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess || n <= 0)
+        return fail(FD_ERR_HIP, "compute-unit query failed: %s", hipGetErrorString(e));
+    if (dev >= 0 && dev < 64) cache[dev] = n;
+    *out = n;
+    return FD_OK;
+}
+
+}  // namespace fd
+
+using namespace fd;
+
+extern "C" {
+
+fd_status fd_decode_partial(const fd_problem* p, const fd_plan* plan, const void* q, const void* k,
+                            const void* v, const int32_t* block_table, const int32_t* seq_lens_dev,
+                            void* workspace, size_t workspace_bytes_avail, void* stream) {
+    clear_error();
+    float scale = 0.f;
+    fd_status st = check_problem(p, &scale);
+    if (st != FD_OK) return st;
+    st = check_plan(p, plan);
+    if (st != FD_OK) return st;
+    if (!q || !k || !v || !seq_lens_dev || !workspace)
+        return fail(FD_ERR_INVALID_ARGUMENT, "q, k, v, seq_lens_dev and workspace must be non-NULL");
+    if (p->page_size && !block_table)
+        return fail(FD_ERR_INVALID_ARGUMENT, "paged cache needs a block table");
+    if (workspace_bytes_avail < workspace_bytes(p, plan->max_splits))
+        return fail(FD_ERR_WORKSPACE_TOO_SMALL, "workspace holds %zu bytes, the plan needs %llu",
+                    workspace_bytes_avail, (unsigned long long)workspace_bytes(p, plan->max_splits));
+    if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v)) & 15)
+        return fail(FD_ERR_INVALID_ARGUMENT, "q, k and v must be 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(workspace) & 15)
+        return fail(FD_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+
+    fdk::PartialArgs a;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.table = block_table;
+    a.lens = seq_lens_dev;
+    a.ws_o = static_cast<float*>(workspace);
+    a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + workspace_o_bytes(p, plan->max_splits));
+    a.hq = p->num_q_heads;
+    a.hkv = p->num_kv_heads;
+    a.chunk = plan->chunk_tokens;
+    a.s_max = plan->max_splits;
+    a.max_pages = p->page_size ? p->max_pages_per_seq : 0;
+    a.qk_scale_log2 = scale * fdk::kLog2e;
+
+    const int G = p->num_q_heads / p->num_kv_heads;
+    dim3 grid(p->num_kv_heads, plan->max_splits, p->batch);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (plan->partial_kernel == 1) {
+        if (!mfma_applicable(p))
+            return fail(FD_ERR_INVALID_ARGUMENT, "plan selects the MFMA kernel for a problem it does not cover");
+        e = fdk::launch_partial_mfma(G, p->kv_dtype, p->page_size != 0, a, grid, hs);
+    } else {
+        e = fdk::launch_partial_valu(p->head_dim, G, p->kv_dtype, p->page_size != 0, a, grid, hs);
+    }
+    if (e != hipSuccess) return fail(FD_ERR_HIP, "partial kernel launch: %s", hipGetErrorString(e));
+    return FD_OK;
+}
+
+fd_status fd_combine(const fd_problem* p, const fd_plan* plan, const int32_t* seq_lens_dev,
+                     const void* workspace, size_t workspace_bytes_avail, void* out, float* lse,
+                     void* stream) {
+    clear_error();
+    fd_status st = check_problem(p, nullptr);
+    if (st != FD_OK) return st;
+    st = check_plan(p, plan);
+    if (st != FD_OK) return st;
+    if (!seq_lens_dev || !workspace || !out)
+        return fail(FD_ERR_INVALID_ARGUMENT, "seq_lens_dev, workspace and out must be non-NULL");
+    if (workspace_bytes_avail < workspace_bytes(p, plan->max_splits))
+        return fail(FD_ERR_WORKSPACE_TOO_SMALL, "workspace holds %zu bytes, the plan needs %llu",
+                    workspace_bytes_avail, (unsigned long long)workspace_bytes(p, plan->max_splits));
+    const float* ws_o = static_cast<const float*>(workspace);
+    const float* ws_ml =
+        reinterpret_cast<const float*>(static_cast<const char*>(workspace) + workspace_o_bytes(p, plan->max_splits));
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    hipError_t e = fdk::launch_combine(p->head_dim, p->out_dtype, ws_o, ws_ml, seq_lens_dev, out, lse, p->batch,
+                                       p->num_q_heads, plan->chunk_tokens, plan->max_splits, hs);
+    if (e != hipSuccess) return fail(FD_ERR_HIP, "combine kernel launch: %s", hipGetErrorString(e));
+    return FD_OK;
+}
+
+fd_status fd_decode_attention(const fd_problem* p, const void* q, const void* k, const void* v,
+                              const int32_t* block_table, const int32_t* seq_lens_host,
+                              const int32_t* seq_lens_dev, void* out, float* lse, void* workspace,
+                              size_t workspace_bytes_avail, void* stream) {
+    fd_plan plan;
+    fd_status st = fd_plan_splits(p, seq_lens_host, 0, 0, &plan);
+    if (st != FD_OK) return st;
+    if (!out) return fail(FD_ERR_INVALID_ARGUMENT, "out must be non-NULL");
+    if (workspace_bytes_avail < plan.workspace_bytes)
+        return fail(FD_ERR_WORKSPACE_TOO_SMALL, "workspace holds %zu bytes, the plan needs %llu",
+                    workspace_bytes_avail, (unsigned long long)plan.workspace_bytes);
+    st = fd_decode_partial(p, &plan, q, k, v, block_table, seq_lens_dev, workspace, workspace_bytes_avail, stream);
+    if (st != FD_OK) return st;
+    return fd_combine(p, &plan, seq_lens_dev, workspace, workspace_bytes_avail, out, lse, stream);
+}
+
+}  // extern "C"

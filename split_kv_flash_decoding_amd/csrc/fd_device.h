@@ -1,0 +1,143 @@
+// Device-side helpers shared by the decode kernels (gfx950 / CDNA4), and the
+// launcher interface between the kernel files and the C-ABI entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "fd_internal.h"
+
+namespace fdk {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Compile-time tuning knobs of the partial kernel (defaults are the measured
+// best on MI355X): 16-byte loads of K (and of V) per wave stage, waves per
+// work-group, and whether K/V loads carry the non-temporal hint.
+#ifndef FD_PARTIAL_UNROLL
+#define FD_PARTIAL_UNROLL 4
+#endif
+#ifndef FD_PARTIAL_WAVES
+#define FD_PARTIAL_WAVES 4
+#endif
+#ifndef FD_PARTIAL_NT
+#define FD_PARTIAL_NT 1
+#endif
+
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr int kWaves = FD_PARTIAL_WAVES;  // waves per partial work-group
+constexpr int kThreads = 64 * kWaves;
+constexpr int kUnroll = FD_PARTIAL_UNROLL;
+
+__device__ __forceinline__ u32x4 load16(const uint16_t* p) {
+#if FD_PARTIAL_NT
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#else
+    return *reinterpret_cast<const u32x4*>(p);
+#endif
+}
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+// Reinterpret one 32-bit word as two 16-bit floats. The word is taken by value:
+// bit-casting an element of an ext_vector_type in place reads element 0 for
+// every index with this compiler.
+__device__ __forceinline__ half2_t as_half2(uint32_t w) { return __builtin_bit_cast(half2_t, w); }
+__device__ __forceinline__ bf162_t as_bf162(uint32_t w) { return __builtin_bit_cast(bf162_t, w); }
+
+// ---------------------------------------------------------------- element ops
+
+template <int DT> struct Elt;
+
+template <> struct Elt<FD_F16> {
+    // sum_i a[i] * b[i] over 8 fp16 pairs, accumulated in fp32
+    static __device__ __forceinline__ float dot8(u32x4 a, u32x4 b) {
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            acc = __builtin_amdgcn_fdot2(as_half2(a[i]), as_half2(b[i]), acc, false);
+        return acc;
+    }
+    static __device__ __forceinline__ void to_f32(u32x4 x, float* f) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const half2_t h = as_half2(x[i]);
+            f[2 * i] = (float)h.x;
+            f[2 * i + 1] = (float)h.y;
+        }
+    }
+};
+
+template <> struct Elt<FD_BF16> {
+    static __device__ __forceinline__ float dot8(u32x4 a, u32x4 b) {
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf162(a[i]), as_bf162(b[i]), acc, false);
+        return acc;
+    }
+    static __device__ __forceinline__ void to_f32(u32x4 x, float* f) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = __uint_as_float(x[i] << 16);
+            f[2 * i + 1] = __uint_as_float(x[i] & 0xffff0000u);
+        }
+    }
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each aligned group of LPR lanes (LPR in {8, 16}); every lane of the
+// group receives the sum.
+template <int LPR>
+__device__ __forceinline__ float row_sum(float x) {
+    x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
+    x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
+    x += dpp_mov<0x141>(x);  // row_half_mirror: the other quad of the 8
+    if constexpr (LPR == 16) x += dpp_mov<0x140>(x);  // row_mirror: the other 8 of the 16
+    return x;
+}
+
+// Merge running statistics (m, l, o) with another set, all in log2 units.
+template <int N>
+__device__ __forceinline__ void merge_stats(float& m, float& l, float* o, float m2, float l2,
+                                            const float* o2) {
+    const float mn = fmaxf(m, m2);
+    const float mu = (mn == neg_inf()) ? 0.f : mn;
+    const float a = __builtin_amdgcn_exp2f(m - mu);
+    const float b = __builtin_amdgcn_exp2f(m2 - mu);
+    l = l * a + l2 * b;
+#pragma unroll
+    for (int e = 0; e < N; ++e) o[e] = o[e] * a + o2[e] * b;
+    m = mn;
+}
+
+// Arguments every partial kernel takes.
+struct PartialArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const int32_t* table;
+    const int32_t* lens;
+    float* ws_o;
+    float* ws_ml;
+    int hq, hkv, chunk, s_max, max_pages;
+    float qk_scale_log2;
+};
+
+// Launchers (each defined in the file that holds its kernel). They enqueue on
+// `st` and return hipGetLastError().
+hipError_t launch_partial_valu(int D, int G, int dt, bool paged, const PartialArgs& a, dim3 grid,
+                               hipStream_t st);
+hipError_t launch_partial_mfma(int G, int dt, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st);
+hipError_t launch_combine(int D, int out_dt, const float* ws_o, const float* ws_ml, const int32_t* lens,
+                          void* out, float* lse, int B, int hq, int chunk, int s_max, hipStream_t st);
+
+}  // namespace fdk

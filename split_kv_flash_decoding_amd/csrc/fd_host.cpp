@@ -1,6 +1,6 @@
 // Host-side validation, split planning and error reporting for fd.h.
 // Pure C++: the only HIP call reachable from here is the compute-unit query,
-// which lives in fd_kernels.hip and runs only when the caller passes
+// which lives in fd_api.hip and runs only when the caller passes
 // num_cus = 0.
 
 #include <math.h>
@@ -78,6 +78,11 @@ uint64_t workspace_o_bytes(const fd_problem* p, int32_t max_splits) {
 uint64_t workspace_bytes(const fd_problem* p, int32_t max_splits) {
     return workspace_o_bytes(p, max_splits) +
            (uint64_t)p->batch * p->num_q_heads * max_splits * 2 * sizeof(float);
+}
+
+bool mfma_applicable(const fd_problem* p) {
+    const int32_t G = p->num_q_heads / p->num_kv_heads;
+    return p->head_dim == 128 && (G == 2 || G == 4 || G == 8);
 }
 
 fd_status check_plan(const fd_problem* p, const fd_plan* plan) {
@@ -169,14 +174,23 @@ fd_status fd_plan_splits(const fd_problem* p, const int32_t* lens, int32_t num_c
     plan.max_splits = (int32_t)smax;
     plan.total_splits = (int32_t)std::min<int64_t>(nsplit, INT32_MAX);
     plan.num_cus = num_cus;
-    plan.partial_kernel = 0;
+    // Query heads per KV head decide the partial kernel: one query per K/V row
+    // leaves nothing for a matrix instruction to share; a group of four or
+    // more forms a contraction worth an MFMA. FD_PARTIAL_KERNEL=0/1 overrides.
+    const int32_t G = p->num_q_heads / p->num_kv_heads;
+    int32_t kernel = (mfma_applicable(p) && G >= 4) ? 1 : 0;
+    const int32_t forced = env_int("FD_PARTIAL_KERNEL", -1);
+    if (forced == 0) kernel = 0;
+    if (forced == 1 && mfma_applicable(p)) kernel = 1;
+    plan.partial_kernel = kernel;
     plan.total_tokens = total;
     plan.workspace_bytes = workspace_bytes(p, plan.max_splits);
     *out = plan;
     if (getenv("FD_LOG"))
-        fprintf(stderr, "[fd] plan: B=%d Hq=%d Hkv=%d d=%d tokens=%lld chunk=%d S_max=%d splits=%d cus=%d ws=%llu\n",
+        fprintf(stderr, "[fd] plan: B=%d Hq=%d Hkv=%d d=%d tokens=%lld chunk=%d S_max=%d splits=%d cus=%d kernel=%d ws=%llu\n",
                 p->batch, p->num_q_heads, p->num_kv_heads, p->head_dim, (long long)total, plan.chunk_tokens,
-                plan.max_splits, plan.total_splits, plan.num_cus, (unsigned long long)plan.workspace_bytes);
+                plan.max_splits, plan.total_splits, plan.num_cus, plan.partial_kernel,
+                (unsigned long long)plan.workspace_bytes);
     return FD_OK;
 }
 

@@ -15,7 +15,7 @@ constexpr int32_t kMaxGridYZ = 65535;
 // automatic chunks a multiple of it).
 constexpr int32_t kChunkGranule = 64;
 constexpr int32_t kDefaultMinChunk = 256;
-constexpr int32_t kDefaultWgPerCu = 4;
+constexpr int32_t kDefaultWgPerCu = 2;  // measured best for long uniform contexts on MI355X
 constexpr int32_t kPageSize = 16;
 
 // Records `msg` as this thread's last error and returns `st`.
@@ -31,7 +31,11 @@ fd_status check_plan(const fd_problem* p, const fd_plan* plan);
 uint64_t workspace_o_bytes(const fd_problem* p, int32_t max_splits);
 uint64_t workspace_bytes(const fd_problem* p, int32_t max_splits);
 
-// Compute units of the current HIP device, cached per device (fd_kernels.hip).
+// Compute units of the current HIP device, cached per device (fd_api.hip).
 fd_status query_num_cus(int32_t* out);
+
+// Whether the matrix-core partial kernel covers this problem: d = 128 and a
+// group of 2, 4 or 8 query heads per KV head.
+bool mfma_applicable(const fd_problem* p);
 
 }  // namespace fd

@@ -1,0 +1,309 @@
+// Partial kernel, matrix-core form for grouped-query attention (G query heads
+// per KV head, 2 <= G <= 16), d = 128, fp16/bf16 K/V, contiguous or paged.
+//
+// With G query heads sharing one KV head, each K row meets G queries and each
+// V row is weighted by G probabilities: both products are small dense
+// contractions ("FlashAttention 全景演进与大模型 Token 生成全链路性能优化实战",
+// §4.2 on grouped-query attention; §2.3 for the split-KV decomposition), so
+// they run on MFMA instead of the vector ALU, which would spend ~G times the
+// instructions of the MHA kernel per byte read.
+//
+// One work-group of four wave64s per (sequence, KV head, split); each wave
+// takes 16-token tiles of the split in turn (a tile is one page of a paged
+// cache). Per tile, with lane l in group g = l/16 at column c = l%16:
+//   * scores: S^T[16 tokens x 16 heads] = K_tile [16 x 128] . Q^T [128 x 16]
+//     as four v_mfma_f32_16x16x32 (the A operand is the K row of token c,
+//     8 dims per lane, loaded straight from HBM with 16-byte non-temporal
+//     loads; Q^T is a register-resident B operand, zero past head G-1). The
+//     result leaves lane l holding tokens 4g..4g+3 of head c;
+//   * online softmax per head, log2 domain: the tile max is reduced over the
+//     four lanes of a head (two shuffles); each lane keeps the head's running
+//     max and a partial running sum over its own tokens (summed at the end);
+//   * probabilities in fp32 are split into a high and a low 16-bit part
+//     (p = hi + lo exactly to ~2^-17), so the 16-bit matrix product loses
+//     nothing the tolerance would see;
+//   * O^T [128 x 16 heads] += V^T [128 x 16 tokens] . P^T [16 tokens x 16]
+//     as eight 16x16x16 MFMAs per part. P^T is exactly the layout the score
+//     MFMA produced; V^T comes from the V tile staged in LDS (row-major,
+//     padded rows) and read back transposed with ds_read_b64_tr_b16, so
+//     every lane's output column is its own head and the per-head rescale
+//     needs no cross-lane traffic;
+//   * the next tile's K and V loads are issued before the current tile is
+//     computed (register double buffer).
+// At the end the four waves merge through LDS by the two-block identity
+// (same page, §1.2) and the split's (O, m, l) go to the workspace.
+
+#include "fd_device.h"
+
+namespace fdk {
+
+namespace {
+
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kD = 128;
+constexpr int kTile = 16;                  // tokens per tile (one 16-token page)
+constexpr int kMW = 4;                     // waves per work-group
+constexpr int kPitch = kD + 16;            // LDS row pitch of a V tile, elements (288 B)
+
+template <int DT> struct Mfma;
+
+template <> struct Mfma<FD_F16> {
+    typedef f16x8_t v8;
+    typedef f16x4_t v4;
+    static __device__ __forceinline__ f32x4_t qk(u32x4 a, u32x4 b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8, a), __builtin_bit_cast(v8, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4_t pv(i16x4_t a, v4 b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(v4, a), b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ void split(const float* p, v4& hi, v4& lo) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const _Float16 h = (_Float16)p[e];
+            hi[e] = h;
+            lo[e] = (_Float16)(p[e] - (float)h);
+        }
+    }
+};
+
+template <> struct Mfma<FD_BF16> {
+    typedef bf16x8_t v8;
+    typedef bf16x4_t v4;
+    static __device__ __forceinline__ f32x4_t qk(u32x4 a, u32x4 b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8, a), __builtin_bit_cast(v8, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4_t pv(i16x4_t a, v4 b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4, a), b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ void split(const float* p, v4& hi, v4& lo) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const __bf16 h = (__bf16)p[e];
+            hi[e] = h;
+            lo[e] = (__bf16)(p[e] - (float)h);
+        }
+    }
+};
+
+__device__ __forceinline__ i16x4_t lds_read_transposed(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4_t*)(const_cast<uint16_t*>(p)));
+}
+
+}  // namespace
+
+template <int G, int DT, bool PAGED>
+__global__ __launch_bounds__(64 * kMW) void partial_mfma(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens, float* __restrict__ ws_o,
+    float* __restrict__ ws_ml, int hq, int hkv, int chunk, int s_max, int max_pages, float qk_scale_log2) {
+    using M = Mfma<DT>;
+    __shared__ __attribute__((aligned(16))) uint16_t sv[kMW][kTile * kPitch];
+    __shared__ float sm_o[kMW][G][kD];
+    __shared__ float sm_m[kMW][G];
+    __shared__ float sm_l[kMW][G];
+
+    const int g = blockIdx.x;
+    const int s = blockIdx.y;
+    const int b = blockIdx.z;
+    int L = seq_lens[b];
+    if constexpr (PAGED) L = min(L, max_pages * 16);
+    if (L <= 0) return;
+    const int nsplit = (L + chunk - 1) / chunk;
+    if (s >= nsplit || s >= s_max) return;
+    const int t0 = s * chunk;
+    const int t1 = min(t0 + chunk, L);
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int grp = lane >> 4;  // 0..3
+    const int col = lane & 15;  // head (scores, output) / token (K operand) / d-slice (V load)
+
+    int64_t row0 = 0;
+    if constexpr (!PAGED) {
+        int64_t acc = 0;
+        for (int i = lane; i < b; i += 64) acc += seq_lens[i];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+        row0 = acc;
+    }
+    const int32_t* table = PAGED ? block_table + (int64_t)b * max_pages : nullptr;
+    const int64_t row_stride = (int64_t)hkv * kD;
+    const uint16_t* kbase = k + (int64_t)g * kD;
+    const uint16_t* vbase = v + (int64_t)g * kD;
+
+    // Q^T as the B operand of the score MFMAs: lane l holds, for d-block j,
+    // q[head col][32 j + 8 grp .. +8]; heads past G-1 are zero.
+    u32x4 qb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (col < G) {
+            qb[j] = *reinterpret_cast<const u32x4*>(q + ((int64_t)b * hq + g * G + col) * kD + 32 * j + 8 * grp);
+        } else {
+            qb[j] = u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+
+    float m_run = neg_inf();  // running max of head `col` (log2 units)
+    float l_run = 0.f;        // running sum over this lane's tokens of head `col`
+    f32x4_t acc[8];
+#pragma unroll
+    for (int jd = 0; jd < 8; ++jd) acc[jd] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const int ntiles = (t1 - t0 + kTile - 1) / kTile;
+    uint16_t* my_sv = sv[wave];
+
+    auto row_of = [&](int t) -> int64_t {
+        if constexpr (PAGED) {
+            return (int64_t)table[t >> 4] * 16 + (t & 15);
+        } else {
+            return row0 + t;
+        }
+    };
+
+    // K: lane loads token (tile start + col), dims 32 j + 8 grp .. +8 for j = 0..3.
+    // V: lane loads token (tile start + 4 i + grp), dims 8 col .. +8 for i = 0..3.
+    auto load = [&](int tile, u32x4* kr, u32x4* vr) {
+        const int tt = t0 + tile * kTile;
+        const int64_t krow = row_of(min(tt + col, t1 - 1)) * row_stride;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kr[j] = load16(kbase + krow + 32 * j + 8 * grp);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t vrow = row_of(min(tt + 4 * i + grp, t1 - 1)) * row_stride;
+            vr[i] = load16(vbase + vrow + 8 * col);
+        }
+    };
+
+    auto compute = [&](int tile, const u32x4* kr, const u32x4* vr) {
+        const int tt = t0 + tile * kTile;
+        // Stage the V tile: row 4 i + grp, dims 8 col .. +8.
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<u32x4*>(my_sv + (4 * i + grp) * kPitch + 8 * col) = vr[i];
+
+        f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sc = M::qk(kr[j], qb[j], sc);
+
+        float p[4];
+        float mx = neg_inf();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p[i] = (tt + 4 * grp + i < t1) ? sc[i] * qk_scale_log2 : neg_inf();
+            mx = fmaxf(mx, p[i]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mn = fmaxf(m_run, mx);
+        const float mu = (mn == neg_inf()) ? 0.f : mn;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - mu);
+        float ps = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p[i] = __builtin_amdgcn_exp2f(p[i] - mu);
+            ps += p[i];
+        }
+        l_run = l_run * alpha + ps;
+        m_run = mn;
+        typename M::v4 phi, plo;
+        M::split(p, phi, plo);
+
+        // V^T blocks of 16 dims: lane 16 g' + 4 e + j reads row 4 g' + e,
+        // dims 16 jd + 4 j .. +4; the transposing read hands lane 16 g' + i
+        // the dims-i column of rows 4 g' .. 4 g' + 3.
+        const uint16_t* rd = my_sv + (4 * grp + ((lane >> 2) & 3)) * kPitch + 4 * (lane & 3);
+#pragma unroll
+        for (int jd = 0; jd < 8; ++jd) {
+            const i16x4_t vt = lds_read_transposed(rd + 16 * jd);
+            f32x4_t a = acc[jd] * alpha;
+            a = M::pv(vt, phi, a);
+            acc[jd] = M::pv(vt, plo, a);
+        }
+    };
+
+    u32x4 ka[4], va[4], kb[4], vb[4];
+    int tile = wave;
+    if (tile < ntiles) load(tile, ka, va);
+    while (tile < ntiles) {
+        int nxt = tile + kMW;
+        if (nxt < ntiles) load(nxt, kb, vb);
+        compute(tile, ka, va);
+        tile = nxt;
+        if (tile >= ntiles) break;
+        nxt = tile + kMW;
+        if (nxt < ntiles) load(nxt, ka, va);
+        compute(tile, kb, vb);
+        tile = nxt;
+    }
+
+    // Each head's sum is spread over the four lanes that hold it.
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+
+    // Lane (grp, col) holds O[head col][16 jd + 4 grp + i].
+    if (col < G) {
+#pragma unroll
+        for (int jd = 0; jd < 8; ++jd)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sm_o[wave][col][16 * jd + 4 * grp + i] = acc[jd][i];
+        if (grp == 0) {
+            sm_m[wave][col] = m_run;
+            sm_l[wave][col] = l_run;
+        }
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < G * kD; idx += 64 * kMW) {
+        const int j = idx / kD;
+        const int d = idx % kD;
+        float Mx = sm_m[0][j];
+#pragma unroll
+        for (int w = 1; w < kMW; ++w) Mx = fmaxf(Mx, sm_m[w][j]);
+        const float mu = (Mx == neg_inf()) ? 0.f : Mx;
+        float o = 0.f, lsum = 0.f;
+#pragma unroll
+        for (int w = 0; w < kMW; ++w) {
+            const float a = __builtin_amdgcn_exp2f(sm_m[w][j] - mu);
+            o += a * sm_o[w][j][d];
+            lsum += a * sm_l[w][j];
+        }
+        const int64_t slot = ((int64_t)b * hq + g * G + j) * s_max + s;
+        ws_o[slot * kD + d] = o;
+        if (d == 0) {
+            ws_ml[slot * 2] = Mx * kLn2;
+            ws_ml[slot * 2 + 1] = lsum;
+        }
+    }
+}
+
+template <int G, int DT>
+hipError_t launch_g(bool paged, const PartialArgs& a, dim3 grid, hipStream_t st) {
+    if (paged)
+        hipLaunchKernelGGL((partial_mfma<G, DT, true>), grid, dim3(64 * kMW), 0, st, a.q, a.k, a.v, a.table, a.lens,
+                           a.ws_o, a.ws_ml, a.hq, a.hkv, a.chunk, a.s_max, a.max_pages, a.qk_scale_log2);
+    else
+        hipLaunchKernelGGL((partial_mfma<G, DT, false>), grid, dim3(64 * kMW), 0, st, a.q, a.k, a.v, a.table,
+                           a.lens, a.ws_o, a.ws_ml, a.hq, a.hkv, a.chunk, a.s_max, a.max_pages, a.qk_scale_log2);
+    return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_dt(int G, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st) {
+    switch (G) {
+        case 2: return launch_g<2, DT>(paged, a, grid, st);
+        case 4: return launch_g<4, DT>(paged, a, grid, st);
+        default: return launch_g<8, DT>(paged, a, grid, st);
+    }
+}
+
+hipError_t launch_partial_mfma(int G, int dt, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st) {
+    return dt == FD_F16 ? launch_dt<FD_F16>(G, paged, a, grid, st) : launch_dt<FD_BF16>(G, paged, a, grid, st);
+}
+
+}  // namespace fdk

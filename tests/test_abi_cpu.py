@@ -84,14 +84,14 @@ def test_planner_properties(hq, hkv, lens):
     assert plan.workspace_bytes == len(lens) * hq * plan.max_splits * (128 + 2) * 4
     # enough work-groups to cover the chip when there are enough tokens
     if sum(lens) * hkv >= 256 * 4 * 256:
-        assert plan.total_splits * hkv >= 256 * 2
+        assert plan.total_splits * hkv >= 256
 
 
 def test_planner_sizes_long_contexts_to_fill_the_chip():
     plan = fd.fd_plan_splits(prob(), [131072], num_cus=256)
-    assert plan.chunk_tokens == 4096 and plan.max_splits == 32  # 32 heads x 32 splits = 1024 WGs
+    assert plan.chunk_tokens == 8192 and plan.max_splits == 16  # 32 heads x 16 splits = 2 WGs per CU
     plan = fd.fd_plan_splits(prob(), [32768], num_cus=256)
-    assert plan.chunk_tokens == 1024 and plan.max_splits == 32
+    assert plan.chunk_tokens == 2048 and plan.max_splits == 16
 
 
 def test_forced_split_counts():
@@ -195,3 +195,16 @@ def test_one_shot_without_gpu_reports_hip_error():
     lens = (ctypes.c_int32 * 1)(4096)
     plan = fd.FdPlan()
     assert lib.fd_plan_splits(ctypes.byref(p), lens, 0, 0, ctypes.byref(plan)) == fd.FD_ERR_HIP
+
+
+@pytest.mark.parametrize("hq,hkv,d,expect", [
+    (32, 32, 128, 0), (32, 8, 128, 1), (64, 8, 128, 1), (16, 8, 128, 0), (32, 8, 64, 0), (8, 8, 64, 0)])
+def test_planner_picks_the_partial_kernel(hq, hkv, d, expect, monkeypatch):
+    monkeypatch.delenv("FD_PARTIAL_KERNEL", raising=False)
+    plan = fd.fd_plan_splits(prob(num_q_heads=hq, num_kv_heads=hkv, head_dim=d), [5000], num_cus=256)
+    assert plan.partial_kernel == expect
+    monkeypatch.setenv("FD_PARTIAL_KERNEL", "0")
+    assert fd.fd_plan_splits(prob(num_q_heads=hq, num_kv_heads=hkv, head_dim=d), [5000], num_cus=256).partial_kernel == 0
+    monkeypatch.setenv("FD_PARTIAL_KERNEL", "1")
+    forced = fd.fd_plan_splits(prob(num_q_heads=hq, num_kv_heads=hkv, head_dim=d), [5000], num_cus=256).partial_kernel
+    assert forced == (1 if d == 128 and hq // hkv in (2, 4, 8) else 0)

@@ -237,3 +237,46 @@ def test_runs_on_a_side_stream(fd):
     s.synchronize()
     ref_out, ref_lse = reference(wl)
     parity(res.out, res.lse, ref_out, ref_lse, what="side stream")
+
+
+GQA_CASES = [
+    # (dtype, Hq, Hkv, lens, page)
+    (torch.bfloat16, 32, 8, [1, 15, 16, 17, 100, 3000], 0),  # G = 4, ragged tails
+    (torch.float16, 16, 2, [777, 4096], 0),                 # G = 8
+    (torch.bfloat16, 4, 2, [33, 1024], 16),                 # G = 2, paged
+    (torch.bfloat16, 64, 8, [5000, 31, 700], 16),           # G = 8, paged
+    (torch.float16, 8, 2, [1, 2, 3, 64, 65], 16),           # G = 4, paged, tiny
+]
+
+
+@pytest.mark.parametrize("kernel", [0, 1])
+@pytest.mark.parametrize("case", range(len(GQA_CASES)))
+@pytest.mark.parametrize("splits", [0, 3])
+def test_gqa_partial_kernels_agree_with_oracle(fd, monkeypatch, kernel, case, splits):
+    """The vector-ALU (0) and MFMA (1) partial kernels on the same GQA inputs."""
+    dt, hq, hkv, lens, page = GQA_CASES[case]
+    monkeypatch.setenv("FD_PARTIAL_KERNEL", str(kernel))
+    wl = make_workload(name=f"gqa{case}-k{kernel}", batch=len(lens), num_q_heads=hq, num_kv_heads=hkv,
+                       head_dim=128, seq_lens=lens, dtype=dt, seed=300 + case, page_size=page)
+    res = run(fd, wl, num_splits=splits)
+    assert res.plan.partial_kernel == kernel
+    ref_out, ref_lse = reference(wl)
+    parity(res.out, res.lse, ref_out, ref_lse, what=f"gqa case {case} kernel {kernel} splits {splits}")
+
+
+def test_mfma_split_statistics_match_oracle(fd, monkeypatch):
+    monkeypatch.setenv("FD_PARTIAL_KERNEL", "1")
+    wl = make_workload(name="stats-mfma", batch=2, num_q_heads=16, num_kv_heads=2, head_dim=128,
+                       seq_lens=[1000, 257], dtype=torch.bfloat16, seed=6)
+    res = run(fd, wl, num_splits=4)
+    assert res.plan.partial_kernel == 1
+    C = res.plan.chunk_tokens
+    prob = fd.make_problem(batch=2, num_q_heads=16, num_kv_heads=2, head_dim=128, kv_dtype=torch.bfloat16)
+    O_s, m_s, l_s = (x.double().cpu().numpy() for x in fd.workspace_views(prob, res.plan, res.workspace))
+    Oo, mo, lo = oracle.decode_partials(wl.q, wl.k, wl.v, wl.seq_lens, wl.scale, C)
+    for b, L in enumerate(wl.lens):
+        S = -(-L // C)
+        assert np.allclose(m_s[b, :, :S], mo[b, :, :S], rtol=0, atol=1e-5)
+        assert np.allclose(l_s[b, :, :S], lo[b, :, :S], rtol=1e-5, atol=0)
+        scale = np.abs(Oo[b, :, :S]).max()
+        assert np.max(np.abs(O_s[b, :, :S] - Oo[b, :, :S])) <= 1e-5 * max(1.0, scale) * 8
