@@ -22,7 +22,9 @@ SOURCES = ["fd_host.cpp", "fd_api.hip", "fd_partial_valu.hip", "fd_partial_mfma.
            "fd_probe.hip"]
 
 # Packed fp32 instructions stay off (the compiler would otherwise form
-# v_pk_* fp32 ops from float code).
+# v_pk_* fp32 ops from float code). MFMA accumulators live in ordinary VGPRs:
+# with the default AGPR form the allocator copied the 32 accumulator registers
+# out and back around every tile of the GQA kernel (68 extra moves per tile).
 HIP_FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
@@ -30,6 +32,7 @@ HIP_FLAGS = [
     "-fPIC",
     "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

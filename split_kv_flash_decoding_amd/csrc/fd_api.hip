@@ -59,6 +59,7 @@ fd_status fd_decode_partial(const fd_problem* p, const fd_plan* plan, const void
     a.lens = seq_lens_dev;
     a.ws_o = static_cast<float*>(workspace);
     a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + workspace_o_bytes(p, plan->max_splits));
+    a.batch = p->batch;
     a.hq = p->num_q_heads;
     a.hkv = p->num_kv_heads;
     a.chunk = plan->chunk_tokens;
@@ -67,7 +68,12 @@ fd_status fd_decode_partial(const fd_problem* p, const fd_plan* plan, const void
     a.qk_scale_log2 = scale * fdk::kLog2e;
 
     const int G = p->num_q_heads / p->num_kv_heads;
-    dim3 grid(p->num_kv_heads, plan->max_splits, p->batch);
+    // One work-group per (split, KV head) of the work list (see locate_unit).
+    const int64_t units = (int64_t)plan->total_splits * p->num_kv_heads;
+    if (plan->total_splits < 1 || units > INT32_MAX)
+        return fail(FD_ERR_INVALID_ARGUMENT, "plan has %d splits (x %d KV heads)", plan->total_splits,
+                    p->num_kv_heads);
+    dim3 grid((uint32_t)units);
     hipStream_t hs = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (plan->partial_kernel == 1) {

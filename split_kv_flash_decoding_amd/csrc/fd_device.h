@@ -41,6 +41,22 @@ __device__ __forceinline__ u32x4 load16(const uint16_t* p) {
 #endif
 }
 
+// Cache policy of streaming buffer loads: the non-temporal bit (every K/V byte
+// is read once).
+constexpr int kBufferLoadPolicy = FD_PARTIAL_NT ? 2 : 0;
+// Third descriptor word of a raw (unformatted, stride 0) buffer on CDNA.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
+// A raw buffer over [base, base + bytes): 16-byte loads at offsets at or past
+// `bytes` return zeros instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufferRsrcWord3);
+}
+
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int byte_offset) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, kBufferLoadPolicy));
+}
+
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
 // Reinterpret one 32-bit word as two 16-bit floats. The word is taken by value:
@@ -119,6 +135,78 @@ __device__ __forceinline__ void merge_stats(float& m, float& l, float* o, float 
     m = mn;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave (all lanes active).
+__device__ __forceinline__ int64_t wave_incl_scan(int64_t x) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int64_t y = __shfl_up(x, d);
+        if (lane >= d) x += y;
+    }
+    return x;
+}
+
+// One work-group's share of a partial kernel: KV head g of split s of
+// sequence b, tokens [t0, t1); row0 is the sequence's first row in a packed
+// contiguous cache.
+struct WorkUnit {
+    int b, g, s, t0, t1;
+    int64_t row0;
+};
+
+// The partial kernels' work list, one work-group per entry: entry u is KV
+// head u % hkv of work item u / hkv. Items 0..F-1 are the splits that hold a
+// full chunk of tokens, in (sequence, split) order; items F.. are the shorter
+// last splits, one per sequence whose length is not a multiple of the chunk,
+// in sequence order. The hardware dispatches work-groups in index order, so
+// every full-size unit starts before any short one (longest-first list
+// scheduling), and the grid holds no empty work-groups. Each wave computes
+// the lookup by itself from the device lengths (two wave-wide passes over
+// seq_lens). Returns false for an entry past the end of the list.
+__device__ inline bool locate_unit(int u, const int32_t* __restrict__ seq_lens, int B, int hkv, int chunk,
+                                   int len_cap, WorkUnit& out) {
+    const int lane = threadIdx.x & 63;
+    const int g = u % hkv;
+    const int64_t w = u / hkv;
+    int64_t F = 0;
+    for (int base = 0; base < B; base += 64) {
+        const int i = base + lane;
+        const int L = i < B ? max(0, min(seq_lens[i], len_cap)) : 0;
+        int64_t f = L / chunk;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) f += __shfl_xor(f, off);
+        F += f;
+    }
+    const bool full = w < F;
+    const int64_t target = full ? w : w - F;
+    int64_t acc = 0, racc = 0;
+    for (int base = 0; base < B; base += 64) {
+        const int i = base + lane;
+        const int L = i < B ? max(0, min(seq_lens[i], len_cap)) : 0;
+        const int cnt = full ? L / chunk : (L % chunk != 0 ? 1 : 0);
+        const int64_t incl = wave_incl_scan(cnt);
+        const int64_t lincl = wave_incl_scan(L);
+        const int64_t total = __shfl(incl, 63);
+        if (target < acc + total) {
+            const unsigned long long mask = __ballot(acc + incl > target);
+            const int j = __builtin_ctzll(mask);
+            const int64_t incl_j = __shfl(incl, j);
+            const int cnt_j = __shfl(cnt, j);
+            const int L_j = __shfl(L, j);
+            out.b = base + j;
+            out.g = g;
+            out.s = full ? (int)(target - (acc + incl_j - cnt_j)) : L_j / chunk;
+            out.t0 = out.s * chunk;
+            out.t1 = min(out.t0 + chunk, L_j);
+            out.row0 = racc + __shfl(lincl, j) - L_j;
+            return true;
+        }
+        acc += total;
+        racc += __shfl(lincl, 63);
+    }
+    return false;
+}
+
 // Arguments every partial kernel takes.
 struct PartialArgs {
     const uint16_t* q;
@@ -128,7 +216,7 @@ struct PartialArgs {
     const int32_t* lens;
     float* ws_o;
     float* ws_ml;
-    int hq, hkv, chunk, s_max, max_pages;
+    int batch, hq, hkv, chunk, s_max, max_pages;
     float qk_scale_log2;
 };
 

@@ -11,14 +11,24 @@
 // One work-group of four wave64s per (sequence, KV head, split); each wave
 // takes 16-token tiles of the split in turn (a tile is one page of a paged
 // cache). Per tile, with lane l in group g = l/16 at column c = l%16:
+//   * K and V tiles are read from HBM the same way: each 16-byte load
+//     instruction covers four whole 256-byte token rows (loading K straight
+//     into the MFMA operand layout instead, 16 rows x 64 bytes per
+//     instruction, measured 5.3 TB/s against 6.5-7.1 TB/s for whole rows);
+//     both tiles are staged in LDS (rows padded to 288 bytes, so the column
+//     reads below are bank-conflict free);
 //   * scores: S^T[16 tokens x 16 heads] = K_tile [16 x 128] . Q^T [128 x 16]
-//     as four v_mfma_f32_16x16x32 (the A operand is the K row of token c,
-//     8 dims per lane, loaded straight from HBM with 16-byte non-temporal
-//     loads; Q^T is a register-resident B operand, zero past head G-1). The
-//     result leaves lane l holding tokens 4g..4g+3 of head c;
+//     as four v_mfma_f32_16x16x32 (the A operand, K row c with 8 dims per
+//     lane, is read back from LDS; Q^T is a register-resident B operand, zero
+//     past head G-1). The result leaves lane l holding tokens 4g..4g+3 of
+//     head c;
 //   * online softmax per head, log2 domain: the tile max is reduced over the
-//     four lanes of a head (two shuffles); each lane keeps the head's running
-//     max and a partial running sum over its own tokens (summed at the end);
+//     four lanes of a head (two shuffles); each lane keeps a partial running
+//     sum over its own tokens (summed at the end). The exponentials use a
+//     reference max that only moves when a tile's max exceeds it by more than
+//     8 (a wave-uniform branch), so probabilities stay <= 2^8 and the
+//     accumulators are rescaled rarely instead of every tile; one final
+//     rescale moves (O, l) to the split's true max, which the workspace holds;
 //   * probabilities in fp32 are split into a high and a low 16-bit part
 //     (p = hi + lo exactly to ~2^-17), so the 16-bit matrix product loses
 //     nothing the tolerance would see;
@@ -28,8 +38,16 @@
 //     padded rows) and read back transposed with ds_read_b64_tr_b16, so
 //     every lane's output column is its own head and the per-head rescale
 //     needs no cross-lane traffic;
-//   * the next tile's K and V loads are issued before the current tile is
-//     computed (register double buffer).
+//   * K/V loads are buffer loads from a per-tile scalar base with fixed
+//     per-lane offsets (no per-load address arithmetic); the descriptor's
+//     size ends at the split's last row, so rows past it read as zeros;
+//   * the next tile's K and V loads are in flight while the current tile is
+//     computed (a register ring, two deep by default; FD_MFMA_DEPTH=3 keeps
+//     two tiles in flight at the cost of 32 more registers);
+//   * paged caches whose splits start on a page boundary look pages up once
+//     per 64 tiles: lane i of a wave holds the page of its i-th next tile and
+//     each tile reads its page with readlane, so no K/V load waits on a table
+//     load.
 // At the end the four waves merge through LDS by the two-block identity
 // (same page, §1.2) and the split's (O, m, l) go to the workspace.
 
@@ -98,41 +116,33 @@ __device__ __forceinline__ i16x4_t lds_read_transposed(const uint16_t* p) {
 
 }  // namespace
 
-template <int G, int DT, bool PAGED>
+// PAGE_MODE: 0 contiguous cache; 1 paged, any split alignment (a table
+// lookup per token); 2 paged, splits start on page boundaries.
+template <int G, int DT, int PAGE_MODE>
 __global__ __launch_bounds__(64 * kMW) void partial_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens, float* __restrict__ ws_o,
-    float* __restrict__ ws_ml, int hq, int hkv, int chunk, int s_max, int max_pages, float qk_scale_log2) {
+    float* __restrict__ ws_ml, int batch, int hq, int hkv, int chunk, int s_max, int max_pages,
+    float qk_scale_log2) {
     using M = Mfma<DT>;
+    constexpr bool PAGED = PAGE_MODE != 0;
+    __shared__ __attribute__((aligned(16))) uint16_t sk[kMW][kTile * kPitch];
     __shared__ __attribute__((aligned(16))) uint16_t sv[kMW][kTile * kPitch];
     __shared__ float sm_o[kMW][G][kD];
     __shared__ float sm_m[kMW][G];
     __shared__ float sm_l[kMW][G];
 
-    const int g = blockIdx.x;
-    const int s = blockIdx.y;
-    const int b = blockIdx.z;
-    int L = seq_lens[b];
-    if constexpr (PAGED) L = min(L, max_pages * 16);
-    if (L <= 0) return;
-    const int nsplit = (L + chunk - 1) / chunk;
-    if (s >= nsplit || s >= s_max) return;
-    const int t0 = s * chunk;
-    const int t1 = min(t0 + chunk, L);
+    WorkUnit wu;
+    if (!locate_unit(blockIdx.x, seq_lens, batch, hkv, chunk, PAGED ? max_pages * 16 : INT32_MAX, wu)) return;
+    if (wu.s >= s_max) return;
+    const int g = wu.g, s = wu.s, b = wu.b, t0 = wu.t0, t1 = wu.t1;
+    const int64_t row0 = wu.row0;
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int grp = lane >> 4;  // 0..3
     const int col = lane & 15;  // head (scores, output) / token (K operand) / d-slice (V load)
 
-    int64_t row0 = 0;
-    if constexpr (!PAGED) {
-        int64_t acc = 0;
-        for (int i = lane; i < b; i += 64) acc += seq_lens[i];
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-        row0 = acc;
-    }
     const int32_t* table = PAGED ? block_table + (int64_t)b * max_pages : nullptr;
     const int64_t row_stride = (int64_t)hkv * kD;
     const uint16_t* kbase = k + (int64_t)g * kD;
@@ -150,14 +160,23 @@ __global__ __launch_bounds__(64 * kMW) void partial_mfma(
         }
     }
 
-    float m_run = neg_inf();  // running max of head `col` (log2 units)
-    float l_run = 0.f;        // running sum over this lane's tokens of head `col`
+    float m_ref = neg_inf();   // reference max of head `col` for the exponentials (log2 units)
+    float m_use = 0.f;         // m_ref, or 0 while it is still -inf
+    float m_true = neg_inf();  // running max of head `col`
+    float l_run = 0.f;         // running sum (relative to m_ref) over this lane's tokens of head `col`
     f32x4_t acc[8];
 #pragma unroll
     for (int jd = 0; jd < 8; ++jd) acc[jd] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     const int ntiles = (t1 - t0 + kTile - 1) / kTile;
+    uint16_t* my_sk = sk[wave];
     uint16_t* my_sv = sv[wave];
+    const int row_bytes = hkv * kD * 2;
+    // Byte offsets of this lane's K and V loads inside a tile (row r of the
+    // tile is at r * row_bytes): rows 4 i + grp, dims 8 col .. +8.
+    int voff_v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) voff_v[i] = (4 * i + grp) * row_bytes + 16 * col;
 
     auto row_of = [&](int t) -> int64_t {
         if constexpr (PAGED) {
@@ -167,30 +186,58 @@ __global__ __launch_bounds__(64 * kMW) void partial_mfma(
         }
     };
 
-    // K: lane loads token (tile start + col), dims 32 j + 8 grp .. +8 for j = 0..3.
-    // V: lane loads token (tile start + 4 i + grp), dims 8 col .. +8 for i = 0..3.
+    // Tile-aligned pages: lane i holds the page of this wave's tile 64 blk + i.
+    int pg = 0, pg_blk = -1;
+    auto tile_page = [&](int tile) -> int64_t {
+        const int kk = (tile - wave) / kMW;
+        const int blk = kk >> 6;
+        if (blk != pg_blk) {
+            const int tidx = wave + kMW * (64 * blk + lane);
+            pg = tidx < ntiles ? table[(t0 >> 4) + tidx] : 0;
+            pg_blk = blk;
+        }
+        return (int64_t)__builtin_amdgcn_readlane(pg, kk & 63) * 16;
+    };
+
     auto load = [&](int tile, u32x4* kr, u32x4* vr) {
         const int tt = t0 + tile * kTile;
-        const int64_t krow = row_of(min(tt + col, t1 - 1)) * row_stride;
+        if constexpr (PAGE_MODE == 1) {
+            // Pages may start mid-tile: one table lookup per row, clamped to the split.
 #pragma unroll
-        for (int j = 0; j < 4; ++j) kr[j] = load16(kbase + krow + 32 * j + 8 * grp);
+            for (int i = 0; i < 4; ++i) {
+                const int64_t row = row_of(min(tt + 4 * i + grp, t1 - 1)) * row_stride;
+                kr[i] = load16(kbase + row + 8 * col);
+                vr[i] = load16(vbase + row + 8 * col);
+            }
+        } else {
+            const int64_t first = (PAGE_MODE == 2) ? tile_page(tile) : row0 + tt;
+            const int bytes = min(kTile, t1 - tt) * row_bytes;
+            const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + first * row_stride, bytes);
+            const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + first * row_stride, bytes);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t vrow = row_of(min(tt + 4 * i + grp, t1 - 1)) * row_stride;
-            vr[i] = load16(vbase + vrow + 8 * col);
+            for (int i = 0; i < 4; ++i) {
+                kr[i] = buffer_load16(rk, voff_v[i]);
+                vr[i] = buffer_load16(rv, voff_v[i]);
+            }
         }
     };
 
     auto compute = [&](int tile, const u32x4* kr, const u32x4* vr) {
         const int tt = t0 + tile * kTile;
-        // Stage the V tile: row 4 i + grp, dims 8 col .. +8.
+        // Stage the K and V tiles: row 4 i + grp, dims 8 col .. +8.
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i) {
+            *reinterpret_cast<u32x4*>(my_sk + (4 * i + grp) * kPitch + 8 * col) = kr[i];
             *reinterpret_cast<u32x4*>(my_sv + (4 * i + grp) * kPitch + 8 * col) = vr[i];
+        }
 
+        // A operand of d-block j: K row col, dims 32 j + 8 grp .. +8.
         f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sc = M::qk(kr[j], qb[j], sc);
+        for (int j = 0; j < 4; ++j) {
+            const u32x4 ka = *reinterpret_cast<const u32x4*>(my_sk + col * kPitch + 32 * j + 8 * grp);
+            sc = M::qk(ka, qb[j], sc);
+        }
 
         float p[4];
         float mx = neg_inf();
@@ -201,17 +248,25 @@ __global__ __launch_bounds__(64 * kMW) void partial_mfma(
         }
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mn = fmaxf(m_run, mx);
-        const float mu = (mn == neg_inf()) ? 0.f : mn;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - mu);
+        m_true = fmaxf(m_true, mx);
+        // Move the reference only when some head's scores outgrow it by 2^8.
+        if (__ballot(mx > m_ref + 8.f)) {
+            const float mn = fmaxf(m_ref, mx);
+            const float mu = (mn == neg_inf()) ? 0.f : mn;
+            const float alpha = __builtin_amdgcn_exp2f(m_ref - mu);  // 0 on the first tile
+            l_run *= alpha;
+#pragma unroll
+            for (int jd = 0; jd < 8; ++jd) acc[jd] = acc[jd] * alpha;
+            m_ref = mn;
+            m_use = mu;
+        }
         float ps = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            p[i] = __builtin_amdgcn_exp2f(p[i] - mu);
+            p[i] = __builtin_amdgcn_exp2f(p[i] - m_use);
             ps += p[i];
         }
-        l_run = l_run * alpha + ps;
-        m_run = mn;
+        l_run += ps;
         typename M::v4 phi, plo;
         M::split(p, phi, plo);
 
@@ -222,30 +277,61 @@ __global__ __launch_bounds__(64 * kMW) void partial_mfma(
 #pragma unroll
         for (int jd = 0; jd < 8; ++jd) {
             const i16x4_t vt = lds_read_transposed(rd + 16 * jd);
-            f32x4_t a = acc[jd] * alpha;
-            a = M::pv(vt, phi, a);
-            acc[jd] = M::pv(vt, plo, a);
+            acc[jd] = M::pv(vt, plo, M::pv(vt, phi, acc[jd]));
         }
     };
 
+#ifndef FD_MFMA_DEPTH
+#define FD_MFMA_DEPTH 2
+#endif
+#if FD_MFMA_DEPTH == 3
+    // Three-deep ring: tiles tile+kMW and tile+2*kMW are in flight while
+    // `tile` is computed.
+    u32x4 ka[4], va[4], kb[4], vb[4], kc[4], vc[4];
+    int tile = wave;
+    if (tile < ntiles) load(tile, ka, va);
+    if (tile + kMW < ntiles) load(tile + kMW, kb, vb);
+    while (tile < ntiles) {
+        if (tile + 2 * kMW < ntiles) load(tile + 2 * kMW, kc, vc);
+        compute(tile, ka, va);
+        tile += kMW;
+        if (tile >= ntiles) break;
+        if (tile + 2 * kMW < ntiles) load(tile + 2 * kMW, ka, va);
+        compute(tile, kb, vb);
+        tile += kMW;
+        if (tile >= ntiles) break;
+        if (tile + 2 * kMW < ntiles) load(tile + 2 * kMW, kb, vb);
+        compute(tile, kc, vc);
+        tile += kMW;
+    }
+#else
+    // Two-deep ring: tile+kMW is in flight while `tile` is computed.
     u32x4 ka[4], va[4], kb[4], vb[4];
     int tile = wave;
     if (tile < ntiles) load(tile, ka, va);
     while (tile < ntiles) {
-        int nxt = tile + kMW;
-        if (nxt < ntiles) load(nxt, kb, vb);
+        if (tile + kMW < ntiles) load(tile + kMW, kb, vb);
         compute(tile, ka, va);
-        tile = nxt;
+        tile += kMW;
         if (tile >= ntiles) break;
-        nxt = tile + kMW;
-        if (nxt < ntiles) load(nxt, ka, va);
+        if (tile + kMW < ntiles) load(tile + kMW, ka, va);
         compute(tile, kb, vb);
-        tile = nxt;
+        tile += kMW;
     }
+#endif
 
     // Each head's sum is spread over the four lanes that hold it.
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
+    // Express (O, l) relative to the true max (a factor in [2^-8, 1]).
+    {
+        const float mu = (m_true == neg_inf()) ? 0.f : m_true;
+        const float alpha = (m_ref == neg_inf()) ? 0.f : __builtin_amdgcn_exp2f(m_ref - mu);
+        l_run *= alpha;
+#pragma unroll
+        for (int jd = 0; jd < 8; ++jd) acc[jd] = acc[jd] * alpha;
+    }
+    const float m_run = m_true;
 
     // Lane (grp, col) holds O[head col][16 jd + 4 grp + i].
     if (col < G) {
@@ -282,15 +368,17 @@ __global__ __launch_bounds__(64 * kMW) void partial_mfma(
     }
 }
 
+template <int G, int DT, int MODE>
+hipError_t launch_mode(const PartialArgs& a, dim3 grid, hipStream_t st) {
+    hipLaunchKernelGGL((partial_mfma<G, DT, MODE>), grid, dim3(64 * kMW), 0, st, a.q, a.k, a.v, a.table, a.lens,
+                       a.ws_o, a.ws_ml, a.batch, a.hq, a.hkv, a.chunk, a.s_max, a.max_pages, a.qk_scale_log2);
+    return hipGetLastError();
+}
+
 template <int G, int DT>
 hipError_t launch_g(bool paged, const PartialArgs& a, dim3 grid, hipStream_t st) {
-    if (paged)
-        hipLaunchKernelGGL((partial_mfma<G, DT, true>), grid, dim3(64 * kMW), 0, st, a.q, a.k, a.v, a.table, a.lens,
-                           a.ws_o, a.ws_ml, a.hq, a.hkv, a.chunk, a.s_max, a.max_pages, a.qk_scale_log2);
-    else
-        hipLaunchKernelGGL((partial_mfma<G, DT, false>), grid, dim3(64 * kMW), 0, st, a.q, a.k, a.v, a.table,
-                           a.lens, a.ws_o, a.ws_ml, a.hq, a.hkv, a.chunk, a.s_max, a.max_pages, a.qk_scale_log2);
-    return hipGetLastError();
+    if (!paged) return launch_mode<G, DT, 0>(a, grid, st);
+    return (a.chunk % 16 == 0) ? launch_mode<G, DT, 2>(a, grid, st) : launch_mode<G, DT, 1>(a, grid, st);
 }
 
 template <int DT>

@@ -10,7 +10,8 @@
 // article; rows and waves merge by the two-block identity of the capstone's
 // §1.2 formal proof).
 //
-// One work-group of kWaves wave64s per (sequence, KV head, split):
+// One work-group of kWaves wave64s per (sequence, KV head, split), taken from
+// the longest-first work list (locate_unit):
 //   * a token row of one KV head is d fp16/bf16 values = d/8 lanes x 16 bytes,
 //     so one wave-wide 16-byte load covers 64/(d/8) consecutive tokens
 //     (4 at d = 128, 8 at d = 64); each wave streams U such loads of K and U
@@ -39,7 +40,7 @@ template <int D, int G, int DT, bool PAGED>
 __global__ __launch_bounds__(kThreads) void partial_valu(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
-    float* __restrict__ ws_o, float* __restrict__ ws_ml, int hq, int hkv, int chunk, int s_max,
+    float* __restrict__ ws_o, float* __restrict__ ws_ml, int batch, int hq, int hkv, int chunk, int s_max,
     int max_pages, float qk_scale_log2) {
     constexpr int LPR = D / 8;       // lanes per token row
     constexpr int RPW = 64 / LPR;    // token rows per wave-wide load
@@ -47,31 +48,17 @@ __global__ __launch_bounds__(kThreads) void partial_valu(
     constexpr int TPW = U * RPW;     // tokens per wave stage
     using E = Elt<DT>;
 
-    const int g = blockIdx.x;
-    const int s = blockIdx.y;
-    const int b = blockIdx.z;
-    int L = seq_lens[b];
-    if constexpr (PAGED) L = min(L, max_pages * 16);  // never index past the table row
-    if (L <= 0) return;
-    const int nsplit = (L + chunk - 1) / chunk;
-    if (s >= nsplit || s >= s_max) return;
-    const int t0 = s * chunk;
-    const int t1 = min(t0 + chunk, L);
+    WorkUnit wu;
+    if (!locate_unit(blockIdx.x, seq_lens, batch, hkv, chunk, PAGED ? max_pages * 16 : INT32_MAX, wu)) return;
+    if (wu.s >= s_max) return;
+    const int g = wu.g, s = wu.s, b = wu.b, t0 = wu.t0, t1 = wu.t1;
+    const int64_t row0 = wu.row0;
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int r = lane / LPR;
     const int c = lane % LPR;
 
-    // First token row of this sequence in a packed contiguous cache.
-    int64_t row0 = 0;
-    if constexpr (!PAGED) {
-        int64_t acc = 0;
-        for (int i = lane; i < b; i += 64) acc += seq_lens[i];
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-        row0 = acc;
-    }
     const int32_t* table = PAGED ? block_table + (int64_t)b * max_pages : nullptr;
     const int64_t head_off = (int64_t)g * D + c * 8;
 
@@ -229,7 +216,7 @@ __global__ __launch_bounds__(kThreads) void partial_valu(
 template <int D, int G, int DT, bool PAGED>
 hipError_t launch_partial(const PartialArgs& a, dim3 grid, hipStream_t st) {
     hipLaunchKernelGGL((partial_valu<D, G, DT, PAGED>), grid, dim3(kThreads), 0, st, a.q, a.k, a.v,
-                       a.table, a.lens, a.ws_o, a.ws_ml, a.hq, a.hkv, a.chunk, a.s_max, a.max_pages,
+                       a.table, a.lens, a.ws_o, a.ws_ml, a.batch, a.hq, a.hkv, a.chunk, a.s_max, a.max_pages,
                        a.qk_scale_log2);
     return hipGetLastError();
 }

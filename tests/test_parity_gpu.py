@@ -280,3 +280,19 @@ def test_mfma_split_statistics_match_oracle(fd, monkeypatch):
         assert np.allclose(l_s[b, :, :S], lo[b, :, :S], rtol=1e-5, atol=0)
         scale = np.abs(Oo[b, :, :S]).max()
         assert np.max(np.abs(O_s[b, :, :S] - Oo[b, :, :S])) <= 1e-5 * max(1.0, scale) * 8
+
+
+@pytest.mark.parametrize("kernel", [0, 1])
+@pytest.mark.parametrize("page", [0, 16])
+def test_large_batch_work_list(fd, monkeypatch, kernel, page):
+    """More than 64 sequences: the work-list lookup scans the lengths in
+    several 64-lane blocks; full and short splits interleave across blocks."""
+    monkeypatch.setenv("FD_PARTIAL_KERNEL", str(kernel))
+    g = np.random.default_rng(77)
+    lens = [int(x) for x in g.integers(1, 700, size=150)] + [64, 128, 1]
+    wl = make_workload(name=f"bigbatch-k{kernel}-p{page}", batch=len(lens), num_q_heads=8, num_kv_heads=2,
+                       head_dim=128, seq_lens=lens, dtype=torch.bfloat16, seed=78, page_size=page)
+    for splits in (0, 5):
+        res = run(fd, wl, num_splits=splits)
+        ref_out, ref_lse = reference(wl)
+        parity(res.out, res.lse, ref_out, ref_lse, what=f"B={len(lens)} kernel {kernel} page {page} splits {splits}")
