@@ -101,17 +101,22 @@ typedef struct fd_plan {
 /*
  * Size the splits for one batch (host only).
  *
- * Chooses C so that sum_b ceil(L_b / C) * Hkv work-groups keep every compute
- * unit busy (FlashAttention capstone §2.3: one head per processor starves a
- * GPU with few KV heads, so the sequence is cut into chunks), with C at least
- * 256 tokens (the chunk the same section gives as an example) and a multiple
- * of 64. `force_num_splits` > 0 instead sets C = ceil(max_b L_b / force) and
- * accepts any C >= 1. `num_cus` == 0 asks the current HIP device (the only
- * HIP call here; its count is cached per device). Validates the problem and
- * every length (1 <= L_b, and L_b <= max_pages_per_seq * 16 when paged).
+ * One head per processor starves a GPU with few KV heads, so each sequence is
+ * cut into chunks (FlashAttention capstone §2.3, which gives 256 tokens as an
+ * example chunk). The planner tries chunks that make about num_cus * k
+ * work-groups (sequence, KV head, split) for k = 1, 2, 3, 4, 6, 8, ... and
+ * keeps the largest one whose full-size splits alone give every compute unit
+ * two work-groups while at most a tenth of the tokens fall in shorter last
+ * splits; chunks are multiples of 64 and at least 256 tokens (1024 for the
+ * kernel whose work-groups cover several heads).
+ * `force_num_splits` > 0 instead sets C = ceil(max_b L_b / force) and accepts
+ * any C >= 1. `num_cus` == 0 asks the current HIP device (the only HIP call
+ * here; its count is cached per device). Validates the problem and every
+ * length (1 <= L_b, and L_b <= max_pages_per_seq * 16 when paged).
  * seq_lens_host: B lengths in host memory. out: receives the plan.
  * The environment variables FD_NUM_SPLITS (forces splits when the argument
- * is 0), FD_MIN_CHUNK and FD_WG_PER_CU override the sizing for experiments.
+ * is 0), FD_MIN_CHUNK, FD_WG_PER_CU (fixes k) and FD_PARTIAL_KERNEL (0 or 1)
+ * override these choices for experiments.
  */
 fd_status fd_plan_splits(const fd_problem* problem, const int32_t* seq_lens_host,
                          int32_t num_cus, int32_t force_num_splits, fd_plan* out);

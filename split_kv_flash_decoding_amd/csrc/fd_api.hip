@@ -67,21 +67,20 @@ fd_status fd_decode_partial(const fd_problem* p, const fd_plan* plan, const void
     a.max_pages = p->page_size ? p->max_pages_per_seq : 0;
     a.qk_scale_log2 = scale * fdk::kLog2e;
 
-    const int G = p->num_q_heads / p->num_kv_heads;
-    // One work-group per (split, KV head) of the work list (see locate_unit).
-    const int64_t units = (int64_t)plan->total_splits * p->num_kv_heads;
+    // One work-group per (split, KV head group) of the work list (see locate_unit).
+    const int32_t groups = p->num_kv_heads / heads_per_workgroup(p, plan->partial_kernel);
+    const int64_t units = (int64_t)plan->total_splits * groups;
     if (plan->total_splits < 1 || units > INT32_MAX)
-        return fail(FD_ERR_INVALID_ARGUMENT, "plan has %d splits (x %d KV heads)", plan->total_splits,
-                    p->num_kv_heads);
+        return fail(FD_ERR_INVALID_ARGUMENT, "plan has %d splits (x %d head groups)", plan->total_splits, groups);
     dim3 grid((uint32_t)units);
     hipStream_t hs = static_cast<hipStream_t>(stream);
+    const int G = p->num_q_heads / p->num_kv_heads;
+    const bool paged = p->page_size != 0;
     hipError_t e;
-    if (plan->partial_kernel == 1) {
-        if (!mfma_applicable(p))
-            return fail(FD_ERR_INVALID_ARGUMENT, "plan selects the MFMA kernel for a problem it does not cover");
-        e = fdk::launch_partial_mfma(G, p->kv_dtype, p->page_size != 0, a, grid, hs);
-    } else {
-        e = fdk::launch_partial_valu(p->head_dim, G, p->kv_dtype, p->page_size != 0, a, grid, hs);
+    switch (plan->partial_kernel) {
+        case kPartialMfma: e = fdk::launch_partial_mfma(G, p->kv_dtype, paged, a, grid, hs); break;
+        case kPartialHeadRows: e = fdk::launch_partial_valu_heads(p->head_dim, G, p->kv_dtype, paged, a, grid, hs); break;
+        default: e = fdk::launch_partial_valu(p->head_dim, G, p->kv_dtype, paged, a, grid, hs); break;
     }
     if (e != hipSuccess) return fail(FD_ERR_HIP, "partial kernel launch: %s", hipGetErrorString(e));
     return FD_OK;

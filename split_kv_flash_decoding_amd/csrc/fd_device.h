@@ -224,6 +224,8 @@ struct PartialArgs {
 // `st` and return hipGetLastError().
 hipError_t launch_partial_valu(int D, int G, int dt, bool paged, const PartialArgs& a, dim3 grid,
                                hipStream_t st);
+hipError_t launch_partial_valu_heads(int D, int G, int dt, bool paged, const PartialArgs& a, dim3 grid,
+                                     hipStream_t st);
 hipError_t launch_partial_mfma(int G, int dt, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st);
 hipError_t launch_combine(int D, int out_dt, const float* ws_o, const float* ws_ml, const int32_t* lens,
                           void* out, float* lse, int B, int hq, int chunk, int s_max, hipStream_t st);

@@ -85,6 +85,15 @@ bool mfma_applicable(const fd_problem* p) {
     return p->head_dim == 128 && (G == 2 || G == 4 || G == 8);
 }
 
+bool head_rows_applicable(const fd_problem* p) {
+    const int32_t G = p->num_q_heads / p->num_kv_heads;
+    return G <= 2 && p->num_kv_heads % rows_per_load(p) == 0;
+}
+
+int32_t heads_per_workgroup(const fd_problem* p, int32_t kernel) {
+    return kernel == kPartialHeadRows ? rows_per_load(p) : 1;
+}
+
 fd_status check_plan(const fd_problem* p, const fd_plan* plan) {
     if (!plan) return fail(FD_ERR_INVALID_ARGUMENT, "plan is NULL");
     if (plan->chunk_tokens < 1 || plan->max_splits < 1 || plan->max_splits > kMaxGridYZ)
@@ -92,8 +101,11 @@ fd_status check_plan(const fd_problem* p, const fd_plan* plan) {
                     plan->chunk_tokens, plan->max_splits);
     if (plan->workspace_bytes < workspace_bytes(p, plan->max_splits))
         return fail(FD_ERR_INVALID_ARGUMENT, "plan does not belong to this problem (workspace_bytes)");
-    if (plan->partial_kernel != 0 && plan->partial_kernel != 1)
-        return fail(FD_ERR_INVALID_ARGUMENT, "plan names unknown partial kernel %d", plan->partial_kernel);
+    if ((plan->partial_kernel == kPartialMfma && !mfma_applicable(p)) ||
+        (plan->partial_kernel == kPartialHeadRows && !head_rows_applicable(p)) ||
+        plan->partial_kernel < kPartialTokenRows || plan->partial_kernel > kPartialHeadRows)
+        return fail(FD_ERR_INVALID_ARGUMENT, "plan names partial kernel %d, which does not cover this problem",
+                    plan->partial_kernel);
     return FD_OK;
 }
 
@@ -146,19 +158,65 @@ fd_status fd_plan_splits(const fd_problem* p, const int32_t* lens, int32_t num_c
         if (st != FD_OK) return st;
     }
 
+    // Query heads per KV head decide the partial kernel: a group of four or
+    // more forms a contraction worth an MFMA; one or two queries per K/V row
+    // leave a matrix instruction mostly idle, and the vector kernel reads
+    // whole multi-head rows when Hkv allows. FD_PARTIAL_KERNEL=0/1/2 overrides
+    // (when the forced kernel covers the problem).
+    const int32_t G = p->num_q_heads / p->num_kv_heads;
+    int32_t kernel = kPartialTokenRows;
+    if (mfma_applicable(p) && G >= 4)
+        kernel = kPartialMfma;
+    else if (head_rows_applicable(p))
+        kernel = kPartialHeadRows;
+    const int32_t forced = env_int("FD_PARTIAL_KERNEL", -1);
+    if (forced == kPartialTokenRows) kernel = kPartialTokenRows;
+    if (forced == kPartialMfma && mfma_applicable(p)) kernel = kPartialMfma;
+    if (forced == kPartialHeadRows && head_rows_applicable(p)) kernel = kPartialHeadRows;
+    const int64_t wg_heads = p->num_kv_heads / heads_per_workgroup(p, kernel);
+
     if (force_num_splits == 0) force_num_splits = env_int("FD_NUM_SPLITS", 0);
     int64_t chunk;
     if (force_num_splits > 0) {
         chunk = ceil_div(lmax, force_num_splits);
     } else {
-        const int64_t min_chunk = std::max<int32_t>(1, env_int("FD_MIN_CHUNK", kDefaultMinChunk));
-        const int64_t wg_per_cu = std::max<int32_t>(1, env_int("FD_WG_PER_CU", kDefaultWgPerCu));
-        const int64_t target = (int64_t)num_cus * wg_per_cu;
-        // Work-groups are (sequence, KV head, split); pick the chunk that makes
-        // about `target` of them, never below the minimum chunk.
-        chunk = ceil_div(total * p->num_kv_heads, std::max<int64_t>(1, target));
-        chunk = std::max(chunk, min_chunk);
-        chunk = ceil_div(chunk, kChunkGranule) * kChunkGranule;
+        // Head-rows work-groups cover several heads and slow down below ~1024
+        // tokens per split (measured: 32K tokens at 512-token chunks ran 23%
+        // slower than at 1024).
+        const int64_t min_chunk = std::max<int32_t>(
+            1, env_int("FD_MIN_CHUNK", kernel == kPartialHeadRows ? kHeadRowsMinChunk : kDefaultMinChunk));
+        // Work-groups are (sequence, KV head, split). A chunk that makes about
+        // num_cus * k of them, never below the minimum chunk, a multiple of 64.
+        auto chunk_for = [&](int64_t k) {
+            int64_t c = ceil_div(total * wg_heads, std::max<int64_t>(1, (int64_t)num_cus * k));
+            c = std::max(c, min_chunk);
+            return ceil_div(c, kChunkGranule) * kChunkGranule;
+        };
+        const int32_t wg_per_cu = env_int("FD_WG_PER_CU", 0);
+        if (wg_per_cu > 0) {
+            chunk = chunk_for(wg_per_cu);
+        } else {
+            // The largest chunk (fewest, longest work-groups) such that the
+            // full-size splits alone give every compute unit two work-groups
+            // and at most a tenth of the tokens sit in shorter last splits.
+            // Measured on MI355X: uniform long contexts run best with ~2
+            // work-groups per CU; mixed lengths need smaller chunks so the
+            // longest-first work list can even out the tail.
+            static const int32_t kSteps[] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32};
+            chunk = chunk_for(kSteps[9]);
+            for (int32_t k : kSteps) {
+                const int64_t c = std::min<int64_t>(chunk_for(k), lmax);
+                int64_t full = 0, rest = 0;
+                for (int32_t b = 0; b < p->batch; ++b) {
+                    full += lens[b] / c;
+                    rest += lens[b] % c;
+                }
+                if (full * wg_heads >= 2 * (int64_t)num_cus && rest * 10 <= total) {
+                    chunk = c;
+                    break;
+                }
+            }
+        }
     }
     chunk = std::min<int64_t>(std::max<int64_t>(chunk, 1), std::max<int32_t>(lmax, 1));
     int64_t smax = ceil_div(lmax, chunk);
@@ -174,14 +232,6 @@ fd_status fd_plan_splits(const fd_problem* p, const int32_t* lens, int32_t num_c
     plan.max_splits = (int32_t)smax;
     plan.total_splits = (int32_t)std::min<int64_t>(nsplit, INT32_MAX);
     plan.num_cus = num_cus;
-    // Query heads per KV head decide the partial kernel: one query per K/V row
-    // leaves nothing for a matrix instruction to share; a group of four or
-    // more forms a contraction worth an MFMA. FD_PARTIAL_KERNEL=0/1 overrides.
-    const int32_t G = p->num_q_heads / p->num_kv_heads;
-    int32_t kernel = (mfma_applicable(p) && G >= 4) ? 1 : 0;
-    const int32_t forced = env_int("FD_PARTIAL_KERNEL", -1);
-    if (forced == 0) kernel = 0;
-    if (forced == 1 && mfma_applicable(p)) kernel = 1;
     plan.partial_kernel = kernel;
     plan.total_tokens = total;
     plan.workspace_bytes = workspace_bytes(p, plan.max_splits);

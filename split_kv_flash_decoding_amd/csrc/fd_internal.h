@@ -15,7 +15,7 @@ constexpr int32_t kMaxGridYZ = 65535;
 // automatic chunks a multiple of it).
 constexpr int32_t kChunkGranule = 64;
 constexpr int32_t kDefaultMinChunk = 256;
-constexpr int32_t kDefaultWgPerCu = 2;  // measured best for long uniform contexts on MI355X
+constexpr int32_t kHeadRowsMinChunk = 1024;
 constexpr int32_t kPageSize = 16;
 
 // Records `msg` as this thread's last error and returns `st`.
@@ -34,8 +34,23 @@ uint64_t workspace_bytes(const fd_problem* p, int32_t max_splits);
 // Compute units of the current HIP device, cached per device (fd_api.hip).
 fd_status query_num_cus(int32_t* out);
 
+// Partial kernels a plan can select.
+enum PartialKernel : int32_t {
+    kPartialTokenRows = 0,  // vector ALU, lane rows are tokens of one KV head
+    kPartialMfma = 1,       // matrix cores, grouped-query heads
+    kPartialHeadRows = 2,   // vector ALU, lane rows are consecutive KV heads
+};
+
+// Token rows (head rows) one 16-byte wave-wide load covers: 64 / (d / 8).
+inline int32_t rows_per_load(const fd_problem* p) { return 64 / (p->head_dim / 8); }
+
 // Whether the matrix-core partial kernel covers this problem: d = 128 and a
 // group of 2, 4 or 8 query heads per KV head.
 bool mfma_applicable(const fd_problem* p);
+// Whether the head-rows kernel covers it: G <= 2 and Hkv a multiple of the
+// rows one load covers.
+bool head_rows_applicable(const fd_problem* p);
+// KV heads one work-group of `kernel` handles.
+int32_t heads_per_workgroup(const fd_problem* p, int32_t kernel);
 
 }  // namespace fd

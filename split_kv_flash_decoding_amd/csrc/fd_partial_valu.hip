@@ -211,6 +211,192 @@ __global__ __launch_bounds__(kThreads) void partial_valu(
     }
 }
 
+// ------------------------------------------------- partial kernel, head rows
+
+// The same online softmax with the roles of the lane rows swapped: row r of a
+// wave holds KV head g0 + r (RPW consecutive heads per work-group), so one
+// 16-byte load instruction covers one token of RPW heads, RPW * 2d bytes in a
+// row of the token-major cache (1 KB at d = 128). Whole contiguous kilobytes
+// per instruction stream from HBM faster than RPW separate 2d-byte rows
+// (a read-only probe of the two patterns measured ~7.0 against ~6.5 TB/s on
+// MI355X). Rows never mix heads, so only the waves merge at the end.
+// Requires Hkv % RPW == 0. PAGE_MODE: 0 contiguous, 1 paged (a table lookup
+// per token), 2 paged with page-aligned splits and U dividing 16 (page
+// indices fetched 64 at a time and read with readlane).
+template <int D, int G, int DT, int PAGE_MODE>
+__global__ __launch_bounds__(kThreads) void partial_valu_heads(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
+    float* __restrict__ ws_o, float* __restrict__ ws_ml, int batch, int hq, int hkv, int chunk, int s_max,
+    int max_pages, float qk_scale_log2) {
+    constexpr int LPR = D / 8;     // lanes per head row
+    constexpr int RPW = 64 / LPR;  // heads per work-group
+    constexpr int U = kUnroll;     // tokens per wave stage
+    constexpr bool PAGED = PAGE_MODE != 0;
+    using E = Elt<DT>;
+
+    WorkUnit wu;
+    if (!locate_unit(blockIdx.x, seq_lens, batch, hkv / RPW, chunk, PAGED ? max_pages * 16 : INT32_MAX, wu)) return;
+    if (wu.s >= s_max) return;
+    const int s = wu.s, b = wu.b, t0 = wu.t0, t1 = wu.t1;
+    const int64_t row0 = wu.row0;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = lane / LPR;
+    const int c = lane % LPR;
+    const int g = wu.g * RPW + r;  // this row's KV head
+
+    const int32_t* table = PAGED ? block_table + (int64_t)b * max_pages : nullptr;
+    const int64_t row_stride = (int64_t)hkv * D;
+    const uint16_t* kl = k + (int64_t)g * D + c * 8;
+    const uint16_t* vl = v + (int64_t)g * D + c * 8;
+
+    u32x4 qv[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+        qv[j] = *reinterpret_cast<const u32x4*>(q + ((int64_t)b * hq + g * G + j) * D + c * 8);
+
+    float m[G], l[G], o[G][8];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        m[j] = neg_inf();
+        l[j] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
+    }
+
+    const int nstages = (t1 - t0 + U - 1) / U;
+
+    // Page-aligned splits: lane i holds the page of this wave's stage 64 blk + i.
+    int pg = 0, pg_blk = -1;
+    auto stage_page_row = [&](int stage) -> int64_t {
+        const int kk = (stage - wave) / kWaves;
+        const int blk = kk >> 6;
+        if (blk != pg_blk) {
+            const int st = wave + kWaves * (64 * blk + lane);
+            pg = st < nstages ? table[(t0 + st * U) >> 4] : 0;
+            pg_blk = blk;
+        }
+        return (int64_t)__builtin_amdgcn_readlane(pg, kk & 63) * 16;
+    };
+
+    auto load = [&](int stage, u32x4* kb, u32x4* vb) {
+        const int ts = t0 + stage * U;
+        int64_t prow = 0;
+        if constexpr (PAGE_MODE == 2) prow = stage_page_row(stage);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int t = min(ts + u, t1 - 1);  // tokens past the split re-read its last one; masked below
+            int64_t row;
+            if constexpr (PAGE_MODE == 2) {
+                row = prow + (t & 15);
+            } else if constexpr (PAGE_MODE == 1) {
+                row = (int64_t)table[t >> 4] * 16 + (t & 15);
+            } else {
+                row = row0 + t;
+            }
+            kb[u] = load16(kl + row * row_stride);
+            vb[u] = load16(vl + row * row_stride);
+        }
+    };
+
+    auto compute = [&](int stage, const u32x4* kb, const u32x4* vb) {
+        const int ts = t0 + stage * U;
+        float sc[U][G];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool valid = ts + u < t1;
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                const float dot = row_sum<LPR>(E::dot8(qv[j], kb[u]));
+                sc[u][j] = valid ? dot * qk_scale_log2 : neg_inf();
+            }
+        }
+        float vf[U][8];
+#pragma unroll
+        for (int u = 0; u < U; ++u) E::to_f32(vb[u], vf[u]);
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            float mx = sc[0][j];
+#pragma unroll
+            for (int u = 1; u < U; ++u) mx = fmaxf(mx, sc[u][j]);
+            const float mn = fmaxf(m[j], mx);
+            const float mu = (mn == neg_inf()) ? 0.f : mn;
+            const float alpha = __builtin_amdgcn_exp2f(m[j] - mu);
+            float p[U];
+            float ps = 0.f;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                p[u] = __builtin_amdgcn_exp2f(sc[u][j] - mu);
+                ps += p[u];
+            }
+            l[j] = l[j] * alpha + ps;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float acc = o[j][e] * alpha;
+#pragma unroll
+                for (int u = 0; u < U; ++u) acc = fmaf(p[u], vf[u][e], acc);
+                o[j][e] = acc;
+            }
+            m[j] = mn;
+        }
+    };
+
+    u32x4 ka[U], va[U], kb2[U], vb2[U];
+    int stage = wave;
+    if (stage < nstages) load(stage, ka, va);
+    while (stage < nstages) {
+        int nxt = stage + kWaves;
+        if (nxt < nstages) load(nxt, kb2, vb2);
+        compute(stage, ka, va);
+        stage = nxt;
+        if (stage >= nstages) break;
+        nxt = stage + kWaves;
+        if (nxt < nstages) load(nxt, ka, va);
+        compute(stage, kb2, vb2);
+        stage = nxt;
+    }
+
+    // Merge the waves through LDS (every lane of a row holds the same m, l).
+    __shared__ float sm_o[kWaves][RPW][G][D];
+    __shared__ float sm_m[kWaves][RPW][G];
+    __shared__ float sm_l[kWaves][RPW][G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sm_o[wave][r][j][c * 8 + e] = o[j][e];
+        if (c == 0) {
+            sm_m[wave][r][j] = m[j];
+            sm_l[wave][r][j] = l[j];
+        }
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < RPW * G * D; idx += kThreads) {
+        const int rr = idx / (G * D);
+        const int j = (idx / D) % G;
+        const int col = idx % D;
+        float M = sm_m[0][rr][j];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm_m[w][rr][j]);
+        const float mu = (M == neg_inf()) ? 0.f : M;
+        float acc = 0.f, lsum = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float a = __builtin_amdgcn_exp2f(sm_m[w][rr][j] - mu);
+            acc += a * sm_o[w][rr][j][col];
+            lsum += a * sm_l[w][rr][j];
+        }
+        const int h = (wu.g * RPW + rr) * G + j;
+        const int64_t slot = ((int64_t)b * hq + h) * s_max + s;
+        ws_o[slot * D + col] = acc;
+        if (col == 0) {
+            ws_ml[slot * 2] = M * kLn2;
+            ws_ml[slot * 2 + 1] = lsum;
+        }
+    }
+}
+
 // ------------------------------------------------------------------ dispatch
 
 template <int D, int G, int DT, bool PAGED>
@@ -245,6 +431,33 @@ hipError_t pick_group(int G, int dt, bool paged, const PartialArgs& a, dim3 grid
 hipError_t launch_partial_valu(int D, int G, int dt, bool paged, const PartialArgs& a, dim3 grid,
                                hipStream_t st) {
     return D == 64 ? pick_group<64>(G, dt, paged, a, grid, st) : pick_group<128>(G, dt, paged, a, grid, st);
+}
+
+template <int D, int G, int DT, int MODE>
+hipError_t launch_heads_mode(const PartialArgs& a, dim3 grid, hipStream_t st) {
+    hipLaunchKernelGGL((partial_valu_heads<D, G, DT, MODE>), grid, dim3(kThreads), 0, st, a.q, a.k, a.v, a.table,
+                       a.lens, a.ws_o, a.ws_ml, a.batch, a.hq, a.hkv, a.chunk, a.s_max, a.max_pages,
+                       a.qk_scale_log2);
+    return hipGetLastError();
+}
+
+template <int D, int G, int DT>
+hipError_t launch_heads_dt(bool paged, const PartialArgs& a, dim3 grid, hipStream_t st) {
+    if (!paged) return launch_heads_mode<D, G, DT, 0>(a, grid, st);
+    const bool aligned = (a.chunk % 16 == 0) && (16 % kUnroll == 0);
+    return aligned ? launch_heads_mode<D, G, DT, 2>(a, grid, st) : launch_heads_mode<D, G, DT, 1>(a, grid, st);
+}
+
+template <int D, int G>
+hipError_t launch_heads_g(int dt, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st) {
+    return dt == FD_F16 ? launch_heads_dt<D, G, FD_F16>(paged, a, grid, st)
+                        : launch_heads_dt<D, G, FD_BF16>(paged, a, grid, st);
+}
+
+hipError_t launch_partial_valu_heads(int D, int G, int dt, bool paged, const PartialArgs& a, dim3 grid,
+                                     hipStream_t st) {
+    if (D == 64) return G == 1 ? launch_heads_g<64, 1>(dt, paged, a, grid, st) : launch_heads_g<64, 2>(dt, paged, a, grid, st);
+    return G == 1 ? launch_heads_g<128, 1>(dt, paged, a, grid, st) : launch_heads_g<128, 2>(dt, paged, a, grid, st);
 }
 
 }  // namespace fdk

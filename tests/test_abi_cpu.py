@@ -77,7 +77,7 @@ def test_planner_properties(hq, hkv, lens):
     assert C % 64 == 0 and C >= 256 or C == max(lens)
     splits = [ceil_div(L, C) for L in lens]
     assert plan.max_splits == max(splits) and plan.total_splits == sum(splits)
-    assert plan.total_tokens == sum(lens) and plan.num_cus == 256 and plan.partial_kernel in (0, 1)
+    assert plan.total_tokens == sum(lens) and plan.num_cus == 256 and plan.partial_kernel in (0, 1, 2)
     # every split non-empty, splits tile [0, L)
     for L, S in zip(lens, splits):
         assert (S - 1) * C < L <= S * C
@@ -87,11 +87,18 @@ def test_planner_properties(hq, hkv, lens):
         assert plan.total_splits * hkv >= 256
 
 
-def test_planner_sizes_long_contexts_to_fill_the_chip():
+def test_planner_sizes_long_contexts_to_fill_the_chip(monkeypatch):
+    monkeypatch.delenv("FD_PARTIAL_KERNEL", raising=False)
+    # head-rows kernel: a work-group covers 4 of the 32 heads
     plan = fd.fd_plan_splits(prob(), [131072], num_cus=256)
-    assert plan.chunk_tokens == 8192 and plan.max_splits == 16  # 32 heads x 16 splits = 2 WGs per CU
+    assert plan.partial_kernel == 2
+    assert plan.chunk_tokens == 2048 and plan.max_splits == 64  # 8 head groups x 64 splits = 2 WGs per CU
     plan = fd.fd_plan_splits(prob(), [32768], num_cus=256)
-    assert plan.chunk_tokens == 2048 and plan.max_splits == 16
+    assert plan.chunk_tokens == 1024 and plan.max_splits == 32  # the head-rows floor
+    # one KV head per work-group
+    monkeypatch.setenv("FD_PARTIAL_KERNEL", "0")
+    plan = fd.fd_plan_splits(prob(), [131072], num_cus=256)
+    assert plan.chunk_tokens == 8192 and plan.max_splits == 16  # 32 heads x 16 splits
 
 
 def test_forced_split_counts():
@@ -198,13 +205,17 @@ def test_one_shot_without_gpu_reports_hip_error():
 
 
 @pytest.mark.parametrize("hq,hkv,d,expect", [
-    (32, 32, 128, 0), (32, 8, 128, 1), (64, 8, 128, 1), (16, 8, 128, 0), (32, 8, 64, 0), (8, 8, 64, 0)])
+    (32, 32, 128, 2), (32, 8, 128, 1), (64, 8, 128, 1), (16, 8, 128, 2), (32, 8, 64, 0), (8, 8, 64, 2),
+    (4, 4, 64, 0), (6, 6, 128, 0), (4, 2, 128, 0)])
 def test_planner_picks_the_partial_kernel(hq, hkv, d, expect, monkeypatch):
     monkeypatch.delenv("FD_PARTIAL_KERNEL", raising=False)
-    plan = fd.fd_plan_splits(prob(num_q_heads=hq, num_kv_heads=hkv, head_dim=d), [5000], num_cus=256)
-    assert plan.partial_kernel == expect
+    mk = lambda: fd.fd_plan_splits(prob(num_q_heads=hq, num_kv_heads=hkv, head_dim=d), [5000], num_cus=256)
+    assert mk().partial_kernel == expect
     monkeypatch.setenv("FD_PARTIAL_KERNEL", "0")
-    assert fd.fd_plan_splits(prob(num_q_heads=hq, num_kv_heads=hkv, head_dim=d), [5000], num_cus=256).partial_kernel == 0
+    assert mk().partial_kernel == 0
+    G = hq // hkv
     monkeypatch.setenv("FD_PARTIAL_KERNEL", "1")
-    forced = fd.fd_plan_splits(prob(num_q_heads=hq, num_kv_heads=hkv, head_dim=d), [5000], num_cus=256).partial_kernel
-    assert forced == (1 if d == 128 and hq // hkv in (2, 4, 8) else 0)
+    assert mk().partial_kernel == (1 if d == 128 and G in (2, 4, 8) else expect)
+    monkeypatch.setenv("FD_PARTIAL_KERNEL", "2")
+    rows = 64 // (d // 8)
+    assert mk().partial_kernel == (2 if G <= 2 and hkv % rows == 0 else expect)

@@ -296,3 +296,29 @@ def test_large_batch_work_list(fd, monkeypatch, kernel, page):
         res = run(fd, wl, num_splits=splits)
         ref_out, ref_lse = reference(wl)
         parity(res.out, res.lse, ref_out, ref_lse, what=f"B={len(lens)} kernel {kernel} page {page} splits {splits}")
+
+
+MHA_CASES = [
+    # (d, dtype, Hq, Hkv, lens, page) -- Hkv a multiple of the rows one load covers
+    (128, torch.float16, 8, 8, [1, 15, 16, 17, 2000], 0),
+    (128, torch.bfloat16, 16, 8, [700, 3001], 0),       # G = 2
+    (64, torch.float16, 16, 16, [5, 999, 4096], 0),     # d = 64: 8 heads per load
+    (128, torch.float16, 32, 32, [1500, 33], 16),       # paged
+    (64, torch.bfloat16, 8, 8, [17, 260], 16),          # paged, d = 64
+]
+
+
+@pytest.mark.parametrize("kernel", [0, 2])
+@pytest.mark.parametrize("case", range(len(MHA_CASES)))
+@pytest.mark.parametrize("splits", [0, 3, 7])
+def test_token_rows_and_head_rows_kernels_agree_with_oracle(fd, monkeypatch, kernel, case, splits):
+    """The two vector-ALU partial kernels on the same inputs; forced split
+    counts make paged splits start mid-page (per-token page lookups)."""
+    d, dt, hq, hkv, lens, page = MHA_CASES[case]
+    monkeypatch.setenv("FD_PARTIAL_KERNEL", str(kernel))
+    wl = make_workload(name=f"mha{case}-k{kernel}", batch=len(lens), num_q_heads=hq, num_kv_heads=hkv,
+                       head_dim=d, seq_lens=lens, dtype=dt, seed=400 + case, page_size=page)
+    res = run(fd, wl, num_splits=splits)
+    assert res.plan.partial_kernel == kernel
+    ref_out, ref_lse = reference(wl)
+    parity(res.out, res.lse, ref_out, ref_lse, what=f"mha case {case} kernel {kernel} splits {splits}")
