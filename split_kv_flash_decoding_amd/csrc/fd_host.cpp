@@ -173,52 +173,67 @@ fd_status fd_plan_splits(const fd_problem* p, const int32_t* lens, int32_t num_c
     if (forced == kPartialTokenRows) kernel = kPartialTokenRows;
     if (forced == kPartialMfma && mfma_applicable(p)) kernel = kPartialMfma;
     if (forced == kPartialHeadRows && head_rows_applicable(p)) kernel = kPartialHeadRows;
-    const int64_t wg_heads = p->num_kv_heads / heads_per_workgroup(p, kernel);
-
     if (force_num_splits == 0) force_num_splits = env_int("FD_NUM_SPLITS", 0);
-    int64_t chunk;
-    if (force_num_splits > 0) {
-        chunk = ceil_div(lmax, force_num_splits);
-    } else {
-        // Head-rows work-groups cover several heads and slow down below ~1024
-        // tokens per split (measured: 32K tokens at 512-token chunks ran 23%
-        // slower than at 1024).
-        const int64_t min_chunk = std::max<int32_t>(
-            1, env_int("FD_MIN_CHUNK", kernel == kPartialHeadRows ? kHeadRowsMinChunk : kDefaultMinChunk));
-        // Work-groups are (sequence, KV head, split). A chunk that makes about
-        // num_cus * k of them, never below the minimum chunk, a multiple of 64.
-        auto chunk_for = [&](int64_t k) {
-            int64_t c = ceil_div(total * wg_heads, std::max<int64_t>(1, (int64_t)num_cus * k));
-            c = std::max(c, min_chunk);
-            return ceil_div(c, kChunkGranule) * kChunkGranule;
-        };
-        const int32_t wg_per_cu = env_int("FD_WG_PER_CU", 0);
-        if (wg_per_cu > 0) {
-            chunk = chunk_for(wg_per_cu);
+
+    auto choose_chunk = [&](int32_t kern) -> int64_t {
+        const int64_t wg_heads = p->num_kv_heads / heads_per_workgroup(p, kern);
+        int64_t c;
+        if (force_num_splits > 0) {
+            c = ceil_div(lmax, force_num_splits);
         } else {
-            // The largest chunk (fewest, longest work-groups) such that the
-            // full-size splits alone give every compute unit two work-groups
-            // and at most a tenth of the tokens sit in shorter last splits.
-            // Measured on MI355X: uniform long contexts run best with ~2
-            // work-groups per CU; mixed lengths need smaller chunks so the
-            // longest-first work list can even out the tail.
-            static const int32_t kSteps[] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32};
-            chunk = chunk_for(kSteps[9]);
-            for (int32_t k : kSteps) {
-                const int64_t c = std::min<int64_t>(chunk_for(k), lmax);
-                int64_t full = 0, rest = 0;
-                for (int32_t b = 0; b < p->batch; ++b) {
-                    full += lens[b] / c;
-                    rest += lens[b] % c;
-                }
-                if (full * wg_heads >= 2 * (int64_t)num_cus && rest * 10 <= total) {
-                    chunk = c;
-                    break;
+            // Head-rows work-groups cover several heads and slow down below
+            // ~1024 tokens per split (measured: 32K tokens at 512-token chunks
+            // ran 23% slower than at 1024).
+            const int64_t min_chunk = std::max<int32_t>(
+                1, env_int("FD_MIN_CHUNK", kern == kPartialHeadRows ? kHeadRowsMinChunk : kDefaultMinChunk));
+            // Work-groups are (sequence, KV head group, split). A chunk that
+            // makes about num_cus * k of them, never below the minimum chunk, a
+            // multiple of 64.
+            auto chunk_for = [&](int64_t k) {
+                int64_t cc = ceil_div(total * wg_heads, std::max<int64_t>(1, (int64_t)num_cus * k));
+                cc = std::max(cc, min_chunk);
+                return ceil_div(cc, kChunkGranule) * kChunkGranule;
+            };
+            const int32_t wg_per_cu = env_int("FD_WG_PER_CU", 0);
+            if (wg_per_cu > 0) {
+                c = chunk_for(wg_per_cu);
+            } else {
+                // The largest chunk (fewest, longest work-groups) such that the
+                // full-size splits alone give every compute unit two
+                // work-groups and at most an eighth of the tokens sit in
+                // shorter last splits. Measured on MI355X: uniform long
+                // contexts run best with ~2 work-groups per CU; mixed lengths
+                // need smaller chunks so the longest-first work list can even
+                // out the tail.
+                static const int32_t kSteps[] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32};
+                c = chunk_for(kSteps[9]);
+                for (int32_t k : kSteps) {
+                    const int64_t cc = std::min<int64_t>(chunk_for(k), lmax);
+                    int64_t full = 0, rest = 0;
+                    for (int32_t b = 0; b < p->batch; ++b) {
+                        full += lens[b] / cc;
+                        rest += lens[b] % cc;
+                    }
+                    if (full * wg_heads >= 2 * (int64_t)num_cus && rest * 8 <= total) {
+                        c = cc;
+                        break;
+                    }
                 }
             }
         }
+        return std::min<int64_t>(std::max<int64_t>(c, 1), std::max<int32_t>(lmax, 1));
+    };
+    int64_t chunk = choose_chunk(kernel);
+    if (kernel == kPartialHeadRows && forced != kPartialHeadRows) {
+        // Too few multi-head work-groups to occupy the chip (short or forced
+        // few splits): one KV head per work-group gives Hkv/4 to Hkv/8 times more.
+        int64_t nsplit = 0;
+        for (int32_t b = 0; b < p->batch; ++b) nsplit += ceil_div(lens[b], chunk);
+        if (nsplit * (p->num_kv_heads / heads_per_workgroup(p, kernel)) < num_cus) {
+            kernel = kPartialTokenRows;
+            chunk = choose_chunk(kernel);
+        }
     }
-    chunk = std::min<int64_t>(std::max<int64_t>(chunk, 1), std::max<int32_t>(lmax, 1));
     int64_t smax = ceil_div(lmax, chunk);
     if (smax > kMaxGridYZ)
         return fail(FD_ERR_UNSUPPORTED, "%lld splits exceed the grid limit %d", (long long)smax,

@@ -209,7 +209,7 @@ def test_one_shot_without_gpu_reports_hip_error():
     (4, 4, 64, 0), (6, 6, 128, 0), (4, 2, 128, 0)])
 def test_planner_picks_the_partial_kernel(hq, hkv, d, expect, monkeypatch):
     monkeypatch.delenv("FD_PARTIAL_KERNEL", raising=False)
-    mk = lambda: fd.fd_plan_splits(prob(num_q_heads=hq, num_kv_heads=hkv, head_dim=d), [5000], num_cus=256)
+    mk = lambda: fd.fd_plan_splits(prob(num_q_heads=hq, num_kv_heads=hkv, head_dim=d), [500000], num_cus=256)
     assert mk().partial_kernel == expect
     monkeypatch.setenv("FD_PARTIAL_KERNEL", "0")
     assert mk().partial_kernel == 0
@@ -219,3 +219,15 @@ def test_planner_picks_the_partial_kernel(hq, hkv, d, expect, monkeypatch):
     monkeypatch.setenv("FD_PARTIAL_KERNEL", "2")
     rows = 64 // (d // 8)
     assert mk().partial_kernel == (2 if G <= 2 and hkv % rows == 0 else expect)
+
+
+def test_head_rows_fall_back_when_work_groups_are_few(monkeypatch):
+    """Multi-head work-groups that would leave most compute units idle (short
+    context, or a forced small split count) give way to one KV head each."""
+    monkeypatch.delenv("FD_PARTIAL_KERNEL", raising=False)
+    p = prob(num_q_heads=8, num_kv_heads=8, head_dim=64)
+    assert fd.fd_plan_splits(p, [1024], num_cus=256, force_num_splits=4).partial_kernel == 0
+    assert fd.fd_plan_splits(p, [3000], num_cus=256).partial_kernel == 0
+    assert fd.fd_plan_splits(p, [2_000_000], num_cus=256).partial_kernel == 2
+    monkeypatch.setenv("FD_PARTIAL_KERNEL", "2")  # an explicit request is kept
+    assert fd.fd_plan_splits(p, [1024], num_cus=256, force_num_splits=4).partial_kernel == 2
