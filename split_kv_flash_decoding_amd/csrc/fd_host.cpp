@@ -200,11 +200,11 @@ fd_status fd_plan_splits(const fd_problem* p, const int32_t* lens, int32_t num_c
             } else {
                 // The largest chunk (fewest, longest work-groups) such that the
                 // full-size splits alone give every compute unit two
-                // work-groups and at most an eighth of the tokens sit in
-                // shorter last splits. Measured on MI355X: uniform long
-                // contexts run best with ~2 work-groups per CU; mixed lengths
-                // need smaller chunks so the longest-first work list can even
-                // out the tail.
+                // work-groups (three when shorter last splits exist) and at most
+                // an eighth of the tokens sit in shorter last splits. Measured on
+                // MI355X: uniform long contexts run best with ~2 work-groups per
+                // CU; mixed lengths need smaller chunks so the longest-first work
+                // list can even out the tail.
                 static const int32_t kSteps[] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32};
                 c = chunk_for(kSteps[9]);
                 for (int32_t k : kSteps) {
@@ -214,7 +214,8 @@ fd_status fd_plan_splits(const fd_problem* p, const int32_t* lens, int32_t num_c
                         full += lens[b] / cc;
                         rest += lens[b] % cc;
                     }
-                    if (full * wg_heads >= 2 * (int64_t)num_cus && rest * 8 <= total) {
+                    const int64_t need = (rest == 0 ? 2 : 3) * (int64_t)num_cus;
+                    if (full * wg_heads >= need && rest * 8 <= total) {
                         c = cc;
                         break;
                     }
