@@ -1,6 +1,8 @@
 // Combine kernel: merges the per-split statistics of every (sequence, query
-// head) into the output and its log-sum-exp. One wave per (b, h): the wave
-// finds M = max_s m_s, then accumulates w_s = exp(m_s - M) times l_s and O_s;
+// head) into the output and its log-sum-exp. One work-group of four waves per
+// (b, h): M = max_s m_s over all splits, then each wave accumulates
+// w_s = exp(m_s - M) times l_s and O_s over every fourth split (eight splits'
+// loads in flight; the kernel is latency-bound) and the waves add up in LDS;
 // out = sum_s w_s O_s / sum_s w_s l_s, lse = M + ln(sum_s w_s l_s). This is
 // the cross-chunk reduce of FlashDecoding ("FlashAttention 全景演进与大模型
 // Token 生成全链路性能优化实战", §2.3), with every split rescaled by the
@@ -21,36 +23,54 @@ template <> __device__ __forceinline__ void store_out<FD_BF16>(void* out, int64_
     reinterpret_cast<__bf16*>(out)[i] = (__bf16)x;
 }
 
+constexpr int kCombineWaves = 4;
+
 template <int D, int OUT>
-__global__ __launch_bounds__(64) void combine(const float* __restrict__ ws_o,
-                                              const float* __restrict__ ws_ml,
-                                              const int32_t* __restrict__ seq_lens, void* __restrict__ out,
-                                              float* __restrict__ lse, int hq, int chunk, int s_max) {
+__global__ __launch_bounds__(64 * kCombineWaves) void combine(const float* __restrict__ ws_o,
+                                                              const float* __restrict__ ws_ml,
+                                                              const int32_t* __restrict__ seq_lens,
+                                                              void* __restrict__ out, float* __restrict__ lse, int hq,
+                                                              int chunk, int s_max) {
     constexpr int PER = D / 64;  // output columns per lane
     const int h = blockIdx.x;
     const int b = blockIdx.y;
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
     const int L = seq_lens[b];
     const int S = L > 0 ? min((L + chunk - 1) / chunk, s_max) : 0;
     const int64_t base = ((int64_t)b * hq + h) * s_max;
     const int64_t orow = ((int64_t)b * hq + h) * D;
     if (S == 0) {
+        if (wave == 0) {
 #pragma unroll
-        for (int e = 0; e < PER; ++e) store_out<OUT>(out, orow + lane * PER + e, 0.f);
-        if (lse && lane == 0) lse[(int64_t)b * hq + h] = neg_inf();
+            for (int e = 0; e < PER; ++e) store_out<OUT>(out, orow + lane * PER + e, 0.f);
+            if (lse && lane == 0) lse[(int64_t)b * hq + h] = neg_inf();
+        }
         return;
     }
+    __shared__ float red_m[kCombineWaves];
+    __shared__ float red_l[kCombineWaves];
+    __shared__ float red_o[kCombineWaves][D];
+
+    // M = max_s m_s over the whole block.
     float M = neg_inf();
-    for (int i = lane; i < S; i += 64) M = fmaxf(M, ws_ml[(base + i) * 2]);
+    for (int i = tid; i < S; i += 64 * kCombineWaves) M = fmaxf(M, ws_ml[(base + i) * 2]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    if (lane == 0) red_m[wave] = M;
+    __syncthreads();
+    M = red_m[0];
+#pragma unroll
+    for (int w = 1; w < kCombineWaves; ++w) M = fmaxf(M, red_m[w]);
 
+    // Wave w takes splits w, w + 4, ...; loads of eight splits in flight.
     float acc[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) acc[e] = 0.f;
     float lsum = 0.f;
-#pragma unroll 4
-    for (int i = 0; i < S; ++i) {
+#pragma unroll 8
+    for (int i = wave; i < S; i += kCombineWaves) {
         const float ms = ws_ml[(base + i) * 2];
         const float ls = ws_ml[(base + i) * 2 + 1];
         const float w = __builtin_amdgcn_exp2f((ms - M) * kLog2e);
@@ -58,10 +78,24 @@ __global__ __launch_bounds__(64) void combine(const float* __restrict__ ws_o,
 #pragma unroll
         for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, ws_o[(base + i) * D + lane * PER + e], acc[e]);
     }
-    const float inv = 1.0f / lsum;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) store_out<OUT>(out, orow + lane * PER + e, acc[e] * inv);
-    if (lse && lane == 0) lse[(int64_t)b * hq + h] = M + __builtin_amdgcn_logf(lsum) * kLn2;
+    for (int e = 0; e < PER; ++e) red_o[wave][lane * PER + e] = acc[e];
+    if (lane == 0) red_l[wave] = lsum;
+    __syncthreads();
+    if (wave == 0) {
+        float l = red_l[0];
+#pragma unroll
+        for (int w = 1; w < kCombineWaves; ++w) l += red_l[w];
+        const float inv = 1.0f / l;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            float o = red_o[0][lane * PER + e];
+#pragma unroll
+            for (int w = 1; w < kCombineWaves; ++w) o += red_o[w][lane * PER + e];
+            store_out<OUT>(out, orow + lane * PER + e, o * inv);
+        }
+        if (lse && lane == 0) lse[(int64_t)b * hq + h] = M + __builtin_amdgcn_logf(l) * kLn2;
+    }
 }
 
 template <int D>
@@ -70,13 +104,13 @@ hipError_t launch_combine_d(int out_dt, const float* ws_o, const float* ws_ml, c
     dim3 grid(hq, B);
     switch (out_dt) {
         case FD_F32:
-            hipLaunchKernelGGL((combine<D, FD_F32>), grid, dim3(64), 0, st, ws_o, ws_ml, lens, out, lse, hq, chunk, s_max);
+            hipLaunchKernelGGL((combine<D, FD_F32>), grid, dim3(64 * kCombineWaves), 0, st, ws_o, ws_ml, lens, out, lse, hq, chunk, s_max);
             break;
         case FD_F16:
-            hipLaunchKernelGGL((combine<D, FD_F16>), grid, dim3(64), 0, st, ws_o, ws_ml, lens, out, lse, hq, chunk, s_max);
+            hipLaunchKernelGGL((combine<D, FD_F16>), grid, dim3(64 * kCombineWaves), 0, st, ws_o, ws_ml, lens, out, lse, hq, chunk, s_max);
             break;
         default:
-            hipLaunchKernelGGL((combine<D, FD_BF16>), grid, dim3(64), 0, st, ws_o, ws_ml, lens, out, lse, hq, chunk, s_max);
+            hipLaunchKernelGGL((combine<D, FD_BF16>), grid, dim3(64 * kCombineWaves), 0, st, ws_o, ws_ml, lens, out, lse, hq, chunk, s_max);
             break;
     }
     return hipGetLastError();
