@@ -78,6 +78,18 @@ def cpu_baseline(wl, budget_s: float, out, lse):
         blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         blas_threads = 1
+    if wl.q_len > 1:
+        t0 = time.perf_counter()
+        ref_o, ref_l = oracle.decode_attention_multi(wl.q, wl.k, wl.v, wl.seq_lens, wl.scale, wl.block_table,
+                                                     wl.page_size)
+        el = time.perf_counter() - t0
+        d = out.double().cpu().numpy() - ref_o
+        return {"value": kv_bytes(wl) / el / 1e9, "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
+                "sample": f"the whole workload ({wl.q_len} query tokens per sequence), {el:.1f} s wall",
+                "parity_of_sampled_heads": {
+                    "o_max_abs": float(np.max(np.abs(d))),
+                    "o_rel_rms": float(np.linalg.norm(d) / np.linalg.norm(ref_o)),
+                    "lse_abs": float(np.max(np.abs(lse.double().cpu().numpy() - ref_l)))}}
     hq = wl.num_q_heads
     done = 0
     ref_o = ref_l = None
@@ -122,6 +134,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=3, help="workload 1..5 (default: 128K MHA)")
+    ap.add_argument("--q-len", type=int, default=1, help="query tokens per sequence (speculative verification)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--json-out", default=None)
@@ -145,7 +158,7 @@ def main() -> int:
     dev = torch.device("cuda", 0)
 
     t = time.perf_counter()
-    wl = make_config(args.config)
+    wl = make_config(args.config, q_len=args.q_len)
     log(f"generated {wl.name} in {time.perf_counter() - t:.1f} s")
     q, k, v = wl.q.to(dev), wl.k.to(dev), wl.v.to(dev)
     bt = wl.block_table.to(dev) if wl.paged else None
@@ -153,11 +166,11 @@ def main() -> int:
     lens_dev = wl.seq_lens.to(dev)
     problem = fd.make_problem(batch=wl.batch, num_q_heads=wl.num_q_heads, num_kv_heads=wl.num_kv_heads,
                               head_dim=wl.head_dim, kv_dtype=wl.dtype, out_dtype=torch.float32, scale=wl.scale,
-                              page_size=wl.page_size, max_pages_per_seq=wl.max_pages_per_seq)
+                              page_size=wl.page_size, max_pages_per_seq=wl.max_pages_per_seq, q_len=wl.q_len)
     plan = fd.fd_plan_splits(problem, lens_host, 0, wl.force_num_splits)
     ws = torch.empty(-(-plan.workspace_bytes // 4), dtype=torch.float32, device=dev)
-    out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim), dtype=torch.float32, device=dev)
-    lse = torch.empty((wl.batch, wl.num_q_heads), dtype=torch.float32, device=dev)
+    out = torch.empty(tuple(wl.q.shape), dtype=torch.float32, device=dev)
+    lse = torch.empty(tuple(wl.q.shape[:-1]), dtype=torch.float32, device=dev)
     nbytes = kv_bytes(wl)
     log(f"plan {plan.as_dict()}; KV bytes {nbytes}")
 
@@ -245,7 +258,8 @@ def main() -> int:
         "config": {
             "workload": workload,
             "batch": wl.batch, "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads,
-            "head_dim": wl.head_dim, "seq_lens_total": wl.total_tokens, "page_size": wl.page_size,
+            "head_dim": wl.head_dim, "q_len": wl.q_len, "seq_lens_total": wl.total_tokens,
+            "page_size": wl.page_size,
             "accumulate": "f32", "out_dtype": "f32",
             "chunk_tokens": plan.chunk_tokens, "splits": plan.max_splits, "total_splits": plan.total_splits,
             "kv_bytes_per_call": nbytes,

@@ -13,7 +13,7 @@
  * up to floating-point rounding.
  *
  * Layouts (all dense, row-major):
- *   q            [B, Hq, d]            kv dtype (fp16 or bf16)
+ *   q            [B, Hq, d] (q_len = 1) or [B, q_len, Hq, d], kv dtype
  *   k, v         contiguous: [sum_b L_b, Hkv, d]; sequence b starts at token
  *                row sum_{b'<b} L_b' (a packed variable-length batch).
  *                paged (page_size 16): pools [P, 16, Hkv, d]; token t of
@@ -22,9 +22,13 @@
  *                the FlashAttention capstone, §4.1).
  *   block_table  int32 [B, max_pages_per_seq], paged only.
  *   seq_lens     int32 [B], every L_b >= 1.
- *   out          [B, Hq, d] in out_dtype;  lse  float32 [B, Hq], natural log.
+ *   out          [B, q_len, Hq, d] in out_dtype;  lse  float32 [B, q_len, Hq],
+ *                natural log (q_len = 1: [B, Hq, d] and [B, Hq]).
  *   Query head h reads KV head h / (Hq / Hkv) (grouped-query attention with
  *   contiguous groups, capstone §4.2).
+ *   Several query tokens per sequence (q_len > 1, the verification pass of
+ *   speculative decoding, capstone §4.5) are the last q_len tokens of the
+ *   cache: query i of sequence b attends to tokens 0 .. L_b - q_len + i.
  *
  * Ownership: the caller allocates every buffer (device memory for q, k, v,
  * block_table, seq_lens_dev, out, lse and the workspace; host memory for
@@ -82,6 +86,8 @@ typedef struct fd_problem {
     float scale;               /* softmax scale; <= 0 selects 1/sqrt(d) */
     int32_t page_size;         /* 0 = contiguous packed cache, 16 = paged */
     int32_t max_pages_per_seq; /* paged: columns of block_table; ignored otherwise */
+    int32_t q_len;             /* query tokens per sequence, 0 or 1 = one; q_len > 1 needs d = 128
+                                  and q_len * Hq/Hkv <= 16, and every L_b >= q_len */
 } fd_problem;
 
 /* How the splits are cut. Holds scalars only: nothing is uploaded per call,
@@ -126,19 +132,20 @@ fd_status fd_plan_splits(const fd_problem* problem, const int32_t* seq_lens_host
 /*
  * Per-split partials (asynchronous on `stream`).
  *
- * For every sequence b, query head h and split s < ceil(L_b / C) writes the
- * split's running max m_s = max_t scale*<q, k_t>, sum l_s = sum_t
- * exp(scale*<q,k_t> - m_s) and unnormalised output O_s = sum_t
- * exp(scale*<q,k_t> - m_s) v_t over the split's tokens t in
- * [s*C, min((s+1)*C, L_b)) (the per-chunk local softmax of capstone §2.3; the
- * running-statistics loop of the lpnh.cn memory-wall article, §2.2). Tokens
- * at or past L_b are never read.
+ * For every sequence b, query row r (= i * Hq + h for query token i and head
+ * h) and split s < ceil(L_b / C) writes the split's running max
+ * m_s = max_t scale*<q, k_t>, sum l_s = sum_t exp(scale*<q,k_t> - m_s) and
+ * unnormalised output O_s = sum_t exp(scale*<q,k_t> - m_s) v_t over the
+ * split's tokens t in [s*C, min((s+1)*C, L_b)) that the query may see (the
+ * per-chunk local softmax of capstone §2.3; the running-statistics loop of
+ * the lpnh.cn memory-wall article, §2.2). A split holding no such token gets
+ * m_s = -inf, l_s = 0, O_s = 0. Tokens at or past L_b are never read.
  *
  * Workspace layout (float32, all of it written by the kernels, so the caller
  * never initialises it):
- *   O  [B, Hq, S_max, d]       at byte offset 0
- *   ML [B, Hq, S_max, 2]       at byte offset B*Hq*S_max*d*4: (m_s, l_s) pairs,
- *                              m_s in natural-log units of the scaled score.
+ *   O  [B, q_len*Hq, S_max, d]     at byte offset 0
+ *   ML [B, q_len*Hq, S_max, 2]     after O: (m_s, l_s) pairs, m_s in
+ *                                  natural-log units of the scaled score.
  * Entries of splits a sequence does not have are left untouched.
  * q, k, v, block_table (NULL when contiguous), seq_lens_dev: device pointers.
  */
@@ -150,10 +157,11 @@ fd_status fd_decode_partial(const fd_problem* problem, const fd_plan* plan,
 /*
  * Merge the partials (asynchronous on `stream`).
  *
- * For every (b, h): M = max_s m_s, w_s = exp(m_s - M), l = sum_s w_s l_s,
- * out = sum_s w_s O_s / l and lse = M + ln l (the cross-chunk reduce of
- * capstone §2.3, by the two-block identity of §1.2 applied to every split).
- * out: device [B, Hq, d] in out_dtype. lse: device float32 [B, Hq], or NULL.
+ * For every (b, query row): M = max_s m_s, w_s = exp(m_s - M),
+ * l = sum_s w_s l_s, out = sum_s w_s O_s / l and lse = M + ln l (the
+ * cross-chunk reduce of capstone §2.3, by the two-block identity of §1.2
+ * applied to every split). out: device [B, q_len, Hq, d] in out_dtype.
+ * lse: device float32 [B, q_len, Hq], or NULL.
  */
 fd_status fd_combine(const fd_problem* problem, const fd_plan* plan,
                      const int32_t* seq_lens_dev, const void* workspace,

@@ -18,6 +18,7 @@ from .attention import (  # noqa: F401
     attention_row,
     block_stats,
     decode_attention,
+    decode_attention_multi,
     decode_partials,
     logical_kv,
     merge_partials,

@@ -21,6 +21,12 @@ Sources, by page title and section:
     before each new tile is added, and a single division at the end.
 
 Readings where the pages leave a step open:
+  * several query tokens per sequence (the verification pass of speculative
+    decoding, FlashAttention capstone §4.5: the target model scores K draft
+    tokens appended to the input in one pass) are the last q_len positions
+    of the cache; query i attends to tokens 0 .. L - q_len + i (causal);
+  * a split that holds no token a query may see has statistics m = -inf,
+    l = 0, O = 0 (the max and sum over an empty set);
   * merging finished partials rescales both sides: O = sum_s e^{m_s-M} O_s,
     l = sum_s e^{m_s-M} l_s (the capstone's two-block identity applied to
     every split);
@@ -247,13 +253,50 @@ def decode_attention(q, k, v, seq_lens, scale: float, block_table=None, page_siz
     return out, lse
 
 
+def decode_attention_multi(q, k, v, seq_lens, scale: float, block_table=None, page_size: int = 0):
+    """Several query tokens per sequence: q [B, q_len, Hq, d] -> out
+    [B, q_len, Hq, d], lse [B, q_len, Hq] (fp64).
+
+    Query i of sequence b is the token at position L_b - q_len + i and
+    attends to tokens 0 .. L_b - q_len + i (causal among the new tokens;
+    FlashAttention capstone §4.5). Each query is ``attention_row`` over its
+    visible prefix.
+    """
+    qf = as_f64(q)
+    B, ql, hq, d = qf.shape
+    hkv = k.shape[-2]
+    G = hq // hkv
+    lens = _lens(seq_lens)
+    out = np.full((B, ql, hq, d), np.nan)
+    lse = np.full((B, ql, hq), np.nan)
+    for b in range(B):
+        if lens[b] < ql:
+            raise ValueError("every sequence must hold its q_len new tokens")
+        for g in range(hkv):
+            K, V = logical_kv(k, v, seq_lens, b, g, block_table, page_size)
+            for i in range(ql):
+                n = lens[b] - ql + i + 1
+                for h in range(g * G, (g + 1) * G):
+                    o, ls, _, _ = attention_row(qf[b, i, h], K[:n], V[:n], scale)
+                    out[b, i, h] = o
+                    lse[b, i, h] = ls
+    return out, lse
+
+
 def decode_partials(q, k, v, seq_lens, scale: float, chunk: int, block_table=None,
                     page_size: int = 0, max_splits: Optional[int] = None,
                     pairs: Optional[Sequence[Tuple[int, int]]] = None):
     """Per-split statistics for every (b, h): O [B, Hq, S, d] (unnormalised),
     m [B, Hq, S] and l [B, Hq, S], S = max_b ceil(L_b / chunk). Splits a
-    sequence does not have are NaN."""
+    sequence does not have are NaN.
+
+    With several queries per sequence (q [B, q_len, Hq, d]) the row index is
+    i * Hq + h and each query sees its causal prefix; a split past that
+    prefix has m = -inf, l = 0, O = 0."""
     qf = as_f64(q)
+    if qf.ndim == 4:
+        B, ql, hq, d = qf.shape
+        return _decode_partials_multi(qf, k, v, seq_lens, scale, chunk, block_table, page_size, max_splits)
     B, hq, d = qf.shape
     hkv = k.shape[-2]
     G = hq // hkv
@@ -270,4 +313,28 @@ def decode_partials(q, k, v, seq_lens, scale: float, chunk: int, block_table=Non
         for si, (lo, hi) in enumerate(split_bounds(lens[b], chunk)):
             for h in heads:
                 O[b, h, si], m[b, h, si], l[b, h, si] = _split_partial(qf[b, h], K[lo:hi], V[lo:hi], scale)
+    return O, m, l
+
+
+def _decode_partials_multi(qf, k, v, seq_lens, scale, chunk, block_table, page_size, max_splits):
+    B, ql, hq, d = qf.shape
+    hkv = k.shape[-2]
+    G = hq // hkv
+    lens = _lens(seq_lens)
+    S = max((L + chunk - 1) // chunk for L in lens) if max_splits is None else max_splits
+    O = np.full((B, ql * hq, S, d), np.nan)
+    m = np.full((B, ql * hq, S), np.nan)
+    l = np.full((B, ql * hq, S), np.nan)
+    for b in range(B):
+        for g in range(hkv):
+            K, V = logical_kv(k, v, seq_lens, b, g, block_table, page_size)
+            for si, (lo, hi) in enumerate(split_bounds(lens[b], chunk)):
+                for i in range(ql):
+                    top = min(hi, lens[b] - ql + i + 1)
+                    for h in range(g * G, (g + 1) * G):
+                        r = i * hq + h
+                        if top <= lo:
+                            O[b, r, si], m[b, r, si], l[b, r, si] = 0.0, -math.inf, 0.0
+                        else:
+                            O[b, r, si], m[b, r, si], l[b, r, si] = _split_partial(qf[b, i, h], K[lo:top], V[lo:top], scale)
     return O, m, l

@@ -45,7 +45,13 @@ class FdProblem(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("page_size", ctypes.c_int32),
         ("max_pages_per_seq", ctypes.c_int32),
+        ("q_len", ctypes.c_int32),
     ]
+
+    @property
+    def rows(self) -> int:
+        """Query rows per sequence: q_len * Hq."""
+        return max(1, self.q_len) * self.num_q_heads
 
 
 class FdPlan(ctypes.Structure):
@@ -126,14 +132,19 @@ def _dtype_code(dt) -> int:
 
 def make_problem(*, batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int, kv_dtype,
                  out_dtype=None, scale: Optional[float] = None, page_size: int = 0,
-                 max_pages_per_seq: int = 0) -> FdProblem:
+                 max_pages_per_seq: int = 0, q_len: int = 1) -> FdProblem:
     import torch
 
     return FdProblem(
         batch=batch, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
         kv_dtype=_dtype_code(kv_dtype), out_dtype=_dtype_code(out_dtype or torch.float32),
         scale=0.0 if scale is None else float(scale), page_size=page_size,
-        max_pages_per_seq=max_pages_per_seq)
+        max_pages_per_seq=max_pages_per_seq, q_len=q_len)
+
+
+def _q_shape(problem: FdProblem, d: int):
+    B, hq = problem.batch, problem.num_q_heads
+    return (B, hq, d) if problem.q_len <= 1 else (B, problem.q_len, hq, d)
 
 
 def _lens_array(seq_lens_host: Sequence[int]):
@@ -161,8 +172,8 @@ def _check_tensors(problem: FdProblem, q, k, v, block_table, seq_lens_dev, total
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not t.is_cuda or not t.is_contiguous() or t.dtype != kvdt:
             raise ValueError(f"{name} must be a contiguous {kvdt} CUDA tensor")
-    if tuple(q.shape) != (B, hq, d):
-        raise ValueError(f"q has shape {tuple(q.shape)}, expected {(B, hq, d)}")
+    if tuple(q.shape) != _q_shape(problem, d):
+        raise ValueError(f"q has shape {tuple(q.shape)}, expected {_q_shape(problem, d)}")
     if k.shape != v.shape:
         raise ValueError("k and v shapes differ")
     if problem.page_size:
@@ -199,12 +210,18 @@ def fd_decode_partial(problem: FdProblem, plan: FdPlan, q, k, v, block_table, se
         _ptr(seq_lens_dev), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
+def _check_out(problem: FdProblem, out, lse) -> None:
+    oshape = _q_shape(problem, problem.head_dim)
+    if tuple(out.shape) != oshape or not out.is_contiguous() or _dtype_code(out.dtype) != problem.out_dtype \
+            or not out.is_cuda:
+        raise ValueError(f"out must be a contiguous CUDA tensor {list(oshape)} of the problem's out_dtype")
+    if lse is not None and (tuple(lse.shape) != oshape[:-1] or not lse.is_contiguous()
+                            or _dtype_code(lse.dtype) != FD_F32 or not lse.is_cuda):
+        raise ValueError(f"lse must be a contiguous float32 CUDA tensor {list(oshape[:-1])}")
+
+
 def fd_combine(problem: FdProblem, plan: FdPlan, seq_lens_dev, workspace, out, lse=None, stream=None) -> None:
-    B, hq, d = problem.batch, problem.num_q_heads, problem.head_dim
-    if tuple(out.shape) != (B, hq, d) or not out.is_contiguous() or _dtype_code(out.dtype) != problem.out_dtype:
-        raise ValueError(f"out must be contiguous [{B}, {hq}, {d}] of the problem's out_dtype")
-    if lse is not None and (tuple(lse.shape) != (B, hq) or not lse.is_contiguous() or _dtype_code(lse.dtype) != FD_F32):
-        raise ValueError(f"lse must be contiguous float32 [{B}, {hq}]")
+    _check_out(problem, out, lse)
     _check(load_library().fd_combine(
         ctypes.byref(problem), ctypes.byref(plan), _ptr(seq_lens_dev), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(stream)))
@@ -214,11 +231,7 @@ def fd_decode_attention(problem: FdProblem, q, k, v, block_table, seq_lens_host,
                         workspace, stream=None) -> None:
     arr, vals = _lens_array(seq_lens_host)
     _check_tensors(problem, q, k, v, block_table, seq_lens_dev, sum(vals))
-    B, hq, d = problem.batch, problem.num_q_heads, problem.head_dim
-    if tuple(out.shape) != (B, hq, d) or not out.is_contiguous() or _dtype_code(out.dtype) != problem.out_dtype:
-        raise ValueError(f"out must be contiguous [{B}, {hq}, {d}] of the problem's out_dtype")
-    if lse is not None and (tuple(lse.shape) != (B, hq) or _dtype_code(lse.dtype) != FD_F32):
-        raise ValueError(f"lse must be float32 [{B}, {hq}]")
+    _check_out(problem, out, lse)
     _check(load_library().fd_decode_attention(
         ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(block_table), arr, _ptr(seq_lens_dev),
         _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
@@ -236,8 +249,9 @@ class DecodeResult:
 
 
 def workspace_views(problem: FdProblem, plan: FdPlan, workspace):
-    """(O [B,Hq,S,d], m [B,Hq,S], l [B,Hq,S]) float32 views of a workspace."""
-    B, hq, d, S = problem.batch, problem.num_q_heads, problem.head_dim, plan.max_splits
+    """(O [B,R,S,d], m [B,R,S], l [B,R,S]) float32 views of a workspace, R =
+    q_len * Hq query rows (row i * Hq + h for query token i, head h)."""
+    B, hq, d, S = problem.batch, problem.rows, problem.head_dim, plan.max_splits
     n_o = B * hq * S * d
     flat = workspace.view(-1)[: n_o + B * hq * S * 2]
     O = flat[:n_o].view(B, hq, S, d)
@@ -249,14 +263,20 @@ def decode_attention(q, k, v, seq_lens, *, block_table=None, page_size: int = 0,
                      scale: Optional[float] = None, out_dtype=None, num_splits: int = 0, num_cus: int = 0,
                      stream=None) -> DecodeResult:
     """Plan, partials and merge for one batch; allocates out, lse and the
-    workspace with torch on q's device. ``seq_lens`` may be a CPU tensor or list."""
+    workspace with torch on q's device. ``seq_lens`` may be a CPU tensor or
+    list. q is [B, Hq, d], or [B, q_len, Hq, d] for several query tokens per
+    sequence (the last q_len tokens of each cache, causal among themselves)."""
     import torch
 
-    B, hq, d = q.shape
+    if q.dim() == 4:
+        B, q_len, hq, d = q.shape
+    else:
+        (B, hq, d), q_len = q.shape, 1
     hkv = k.shape[-2]
     problem = make_problem(batch=B, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, kv_dtype=q.dtype,
                            out_dtype=out_dtype or torch.float32, scale=scale, page_size=page_size,
-                           max_pages_per_seq=max_pages_per_seq or (block_table.shape[1] if block_table is not None else 0))
+                           max_pages_per_seq=max_pages_per_seq or (block_table.shape[1] if block_table is not None else 0),
+                           q_len=q_len)
     lens_host = seq_lens.tolist() if hasattr(seq_lens, "tolist") else list(seq_lens)
     plan = fd_plan_splits(problem, lens_host, num_cus=num_cus, force_num_splits=num_splits)
     if block_table is not None:
@@ -270,8 +290,9 @@ def decode_attention(q, k, v, seq_lens, *, block_table=None, page_size: int = 0,
     dev = q.device
     lens_dev = torch.tensor(lens_host, dtype=torch.int32, device=dev)
     ws = torch.empty(int(math.ceil(plan.workspace_bytes / 4)), dtype=torch.float32, device=dev)
-    out = torch.empty((B, hq, d), dtype=out_dtype or torch.float32, device=dev)
-    lse = torch.empty((B, hq), dtype=torch.float32, device=dev)
+    oshape = _q_shape(problem, d)
+    out = torch.empty(oshape, dtype=out_dtype or torch.float32, device=dev)
+    lse = torch.empty(oshape[:-1], dtype=torch.float32, device=dev)
     fd_decode_partial(problem, plan, q, k, v, block_table, lens_dev, ws, stream)
     fd_combine(problem, plan, lens_dev, ws, out, lse, stream)
     return DecodeResult(out=out, lse=lse, plan=plan, workspace=ws)

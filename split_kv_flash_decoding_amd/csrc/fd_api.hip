@@ -65,6 +65,7 @@ fd_status fd_decode_partial(const fd_problem* p, const fd_plan* plan, const void
     a.chunk = plan->chunk_tokens;
     a.s_max = plan->max_splits;
     a.max_pages = p->page_size ? p->max_pages_per_seq : 0;
+    a.q_len = problem_q_len(p);
     a.qk_scale_log2 = scale * fdk::kLog2e;
 
     // One work-group per (split, KV head group) of the work list (see locate_unit).
@@ -103,8 +104,9 @@ fd_status fd_combine(const fd_problem* p, const fd_plan* plan, const int32_t* se
     const float* ws_ml =
         reinterpret_cast<const float*>(static_cast<const char*>(workspace) + workspace_o_bytes(p, plan->max_splits));
     hipStream_t hs = static_cast<hipStream_t>(stream);
+    // The combine treats the q_len * Hq query rows of a sequence alike.
     hipError_t e = fdk::launch_combine(p->head_dim, p->out_dtype, ws_o, ws_ml, seq_lens_dev, out, lse, p->batch,
-                                       p->num_q_heads, plan->chunk_tokens, plan->max_splits, hs);
+                                       problem_q_len(p) * p->num_q_heads, plan->chunk_tokens, plan->max_splits, hs);
     if (e != hipSuccess) return fail(FD_ERR_HIP, "combine kernel launch: %s", hipGetErrorString(e));
     return FD_OK;
 }

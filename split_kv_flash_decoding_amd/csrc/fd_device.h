@@ -150,7 +150,7 @@ __device__ __forceinline__ int64_t wave_incl_scan(int64_t x) {
 // sequence b, tokens [t0, t1); row0 is the sequence's first row in a packed
 // contiguous cache.
 struct WorkUnit {
-    int b, g, s, t0, t1;
+    int b, g, s, t0, t1, L;
     int64_t row0;
 };
 
@@ -198,6 +198,7 @@ __device__ inline bool locate_unit(int u, const int32_t* __restrict__ seq_lens, 
             out.s = full ? (int)(target - (acc + incl_j - cnt_j)) : L_j / chunk;
             out.t0 = out.s * chunk;
             out.t1 = min(out.t0 + chunk, L_j);
+            out.L = L_j;
             out.row0 = racc + __shfl(lincl, j) - L_j;
             return true;
         }
@@ -216,7 +217,7 @@ struct PartialArgs {
     const int32_t* lens;
     float* ws_o;
     float* ws_ml;
-    int batch, hq, hkv, chunk, s_max, max_pages;
+    int batch, hq, hkv, chunk, s_max, max_pages, q_len;
     float qk_scale_log2;
 };
 

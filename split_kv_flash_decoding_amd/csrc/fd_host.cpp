@@ -67,27 +67,32 @@ fd_status check_problem(const fd_problem* p, float* scale_out) {
         return fail(FD_ERR_INVALID_ARGUMENT, "paged cache needs max_pages_per_seq >= 1");
     if (!(p->scale == p->scale) || isinf(p->scale))
         return fail(FD_ERR_INVALID_ARGUMENT, "scale is not finite");
+    if (p->q_len < 0) return fail(FD_ERR_INVALID_ARGUMENT, "q_len %d < 0", p->q_len);
+    if (problem_q_len(p) > 1 && (p->head_dim != 128 || problem_q_len(p) * G > kMaxQueryRows))
+        return fail(FD_ERR_UNSUPPORTED, "q_len %d with %d query heads per KV head and d=%d not built "
+                    "(several query tokens need d = 128 and q_len * Hq/Hkv <= %d)",
+                    p->q_len, G, p->head_dim, kMaxQueryRows);
     if (scale_out) *scale_out = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->head_dim);
     return FD_OK;
 }
 
 uint64_t workspace_o_bytes(const fd_problem* p, int32_t max_splits) {
-    return (uint64_t)p->batch * p->num_q_heads * max_splits * p->head_dim * sizeof(float);
+    return (uint64_t)p->batch * problem_q_len(p) * p->num_q_heads * max_splits * p->head_dim * sizeof(float);
 }
 
 uint64_t workspace_bytes(const fd_problem* p, int32_t max_splits) {
     return workspace_o_bytes(p, max_splits) +
-           (uint64_t)p->batch * p->num_q_heads * max_splits * 2 * sizeof(float);
+           (uint64_t)p->batch * problem_q_len(p) * p->num_q_heads * max_splits * 2 * sizeof(float);
 }
 
 bool mfma_applicable(const fd_problem* p) {
-    const int32_t G = p->num_q_heads / p->num_kv_heads;
-    return p->head_dim == 128 && (G == 2 || G == 4 || G == 8);
+    const int32_t rows = problem_q_len(p) * (p->num_q_heads / p->num_kv_heads);
+    return p->head_dim == 128 && rows >= 2 && rows <= kMaxQueryRows;
 }
 
 bool head_rows_applicable(const fd_problem* p) {
     const int32_t G = p->num_q_heads / p->num_kv_heads;
-    return G <= 2 && p->num_kv_heads % rows_per_load(p) == 0;
+    return problem_q_len(p) == 1 && G <= 2 && p->num_kv_heads % rows_per_load(p) == 0;
 }
 
 int32_t heads_per_workgroup(const fd_problem* p, int32_t kernel) {
@@ -101,7 +106,8 @@ fd_status check_plan(const fd_problem* p, const fd_plan* plan) {
                     plan->chunk_tokens, plan->max_splits);
     if (plan->workspace_bytes < workspace_bytes(p, plan->max_splits))
         return fail(FD_ERR_INVALID_ARGUMENT, "plan does not belong to this problem (workspace_bytes)");
-    if ((plan->partial_kernel == kPartialMfma && !mfma_applicable(p)) ||
+    if ((plan->partial_kernel != kPartialMfma && problem_q_len(p) > 1) ||
+        (plan->partial_kernel == kPartialMfma && !mfma_applicable(p)) ||
         (plan->partial_kernel == kPartialHeadRows && !head_rows_applicable(p)) ||
         plan->partial_kernel < kPartialTokenRows || plan->partial_kernel > kPartialHeadRows)
         return fail(FD_ERR_INVALID_ARGUMENT, "plan names partial kernel %d, which does not cover this problem",
@@ -149,6 +155,9 @@ fd_status fd_plan_splits(const fd_problem* p, const int32_t* lens, int32_t num_c
         if (lens[b] > cap)
             return fail(FD_ERR_INVALID_ARGUMENT, "seq_lens[%d] = %d exceeds the block table (%lld tokens)",
                         b, lens[b], (long long)cap);
+        if (lens[b] < problem_q_len(p))
+            return fail(FD_ERR_INVALID_ARGUMENT, "seq_lens[%d] = %d is shorter than its %d query tokens", b,
+                        lens[b], problem_q_len(p));
         total += lens[b];
         lmax = std::max(lmax, lens[b]);
     }
@@ -165,12 +174,12 @@ fd_status fd_plan_splits(const fd_problem* p, const int32_t* lens, int32_t num_c
     // (when the forced kernel covers the problem).
     const int32_t G = p->num_q_heads / p->num_kv_heads;
     int32_t kernel = kPartialTokenRows;
-    if (mfma_applicable(p) && G >= 4)
+    if (mfma_applicable(p) && (G >= 4 || problem_q_len(p) > 1))
         kernel = kPartialMfma;
     else if (head_rows_applicable(p))
         kernel = kPartialHeadRows;
     const int32_t forced = env_int("FD_PARTIAL_KERNEL", -1);
-    if (forced == kPartialTokenRows) kernel = kPartialTokenRows;
+    if (forced == kPartialTokenRows && problem_q_len(p) == 1) kernel = kPartialTokenRows;
     if (forced == kPartialMfma && mfma_applicable(p)) kernel = kPartialMfma;
     if (forced == kPartialHeadRows && head_rows_applicable(p)) kernel = kPartialHeadRows;
     if (force_num_splits == 0) force_num_splits = env_int("FD_NUM_SPLITS", 0);

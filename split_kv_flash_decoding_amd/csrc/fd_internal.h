@@ -41,14 +41,19 @@ enum PartialKernel : int32_t {
     kPartialHeadRows = 2,   // vector ALU, lane rows are consecutive KV heads
 };
 
+// Query tokens per sequence (a q_len of 0 means one).
+inline int32_t problem_q_len(const fd_problem* p) { return p->q_len > 1 ? p->q_len : 1; }
+// Largest q_len * Hq/Hkv the matrix-core kernel handles (one 16-column MFMA tile).
+constexpr int32_t kMaxQueryRows = 16;
+
 // Token rows (head rows) one 16-byte wave-wide load covers: 64 / (d / 8).
 inline int32_t rows_per_load(const fd_problem* p) { return 64 / (p->head_dim / 8); }
 
-// Whether the matrix-core partial kernel covers this problem: d = 128 and a
-// group of 2, 4 or 8 query heads per KV head.
+// Whether the matrix-core partial kernel covers this problem: d = 128 and
+// 2 <= q_len * Hq/Hkv <= 16 query rows per KV head.
 bool mfma_applicable(const fd_problem* p);
-// Whether the head-rows kernel covers it: G <= 2 and Hkv a multiple of the
-// rows one load covers.
+// Whether the head-rows kernel covers it: one query token, G <= 2 and Hkv a
+// multiple of the rows one load covers.
 bool head_rows_applicable(const fd_problem* p);
 // KV heads one work-group of `kernel` handles.
 int32_t heads_per_workgroup(const fd_problem* p, int32_t kernel);

@@ -1,5 +1,6 @@
-// Partial kernel, matrix-core form for grouped-query attention (G query heads
-// per KV head, 2 <= G <= 16), d = 128, fp16/bf16 K/V, contiguous or paged.
+// Partial kernel, matrix-core form: every K/V row serves nq = q_len * G query
+// rows (G query heads per KV head, q_len query tokens per sequence),
+// 2 <= nq <= 16; d = 128, fp16/bf16 K/V, contiguous or paged.
 //
 // With G query heads sharing one KV head, each K row meets G queries and each
 // V row is weighted by G probabilities: both products are small dense
@@ -48,6 +49,11 @@
 //     per 64 tiles: lane i of a wave holds the page of its i-th next tile and
 //     each tile reads its page with readlane, so no K/V load waits on a table
 //     load.
+// Several query tokens per sequence (capstone §4.5, speculative decoding's
+// verification pass) add query rows: row n = i * G + j is head j of the group
+// for query token i, which sees tokens up to L - q_len + i, so each lane
+// masks its column with its own causal limit; a row that sees nothing of a
+// split leaves (m, l, O) = (-inf, 0, 0).
 // At the end the four waves merge through LDS by the two-block identity
 // (same page, §1.2) and the split's (O, m, l) go to the workspace.
 
@@ -116,21 +122,23 @@ __device__ __forceinline__ i16x4_t lds_read_transposed(const uint16_t* p) {
 
 }  // namespace
 
-// PAGE_MODE: 0 contiguous cache; 1 paged, any split alignment (a table
-// lookup per token); 2 paged, splits start on page boundaries.
-template <int G, int DT, int PAGE_MODE>
+// NQ: query rows per KV head rounded up to a power of two (2..16); the rows
+// nq..NQ-1 and 16-NQ..15 of the MFMA tile are idle. PAGE_MODE: 0 contiguous
+// cache; 1 paged, any split alignment (a table lookup per token); 2 paged,
+// splits start on page boundaries.
+template <int NQ, int DT, int PAGE_MODE>
 __global__ __launch_bounds__(64 * kMW) void partial_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens, float* __restrict__ ws_o,
-    float* __restrict__ ws_ml, int batch, int hq, int hkv, int chunk, int s_max, int max_pages,
+    float* __restrict__ ws_ml, int batch, int hq, int hkv, int chunk, int s_max, int max_pages, int q_len,
     float qk_scale_log2) {
     using M = Mfma<DT>;
     constexpr bool PAGED = PAGE_MODE != 0;
     __shared__ __attribute__((aligned(16))) uint16_t sk[kMW][kTile * kPitch];
     __shared__ __attribute__((aligned(16))) uint16_t sv[kMW][kTile * kPitch];
-    __shared__ float sm_o[kMW][G][kD];
-    __shared__ float sm_m[kMW][G];
-    __shared__ float sm_l[kMW][G];
+    __shared__ float sm_o[kMW][NQ][kD];
+    __shared__ float sm_m[kMW][NQ];
+    __shared__ float sm_l[kMW][NQ];
 
     WorkUnit wu;
     if (!locate_unit(blockIdx.x, seq_lens, batch, hkv, chunk, PAGED ? max_pages * 16 : INT32_MAX, wu)) return;
@@ -141,7 +149,15 @@ __global__ __launch_bounds__(64 * kMW) void partial_mfma(
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int grp = lane >> 4;  // 0..3
-    const int col = lane & 15;  // head (scores, output) / token (K operand) / d-slice (V load)
+    const int col = lane & 15;  // query row (scores, output) / token (K operand) / d-slice (V load)
+
+    // Query row `col`: head qj of the group for query token qi; it may see
+    // tokens below `lim` (its causal limit, inside this split).
+    const int G = hq / hkv;
+    const int nq = q_len * G;
+    const int qi = col / G;
+    const int qj = col - qi * G;
+    const int lim = min(t1, wu.L - q_len + qi + 1);
 
     const int32_t* table = PAGED ? block_table + (int64_t)b * max_pages : nullptr;
     const int64_t row_stride = (int64_t)hkv * kD;
@@ -149,12 +165,13 @@ __global__ __launch_bounds__(64 * kMW) void partial_mfma(
     const uint16_t* vbase = v + (int64_t)g * kD;
 
     // Q^T as the B operand of the score MFMAs: lane l holds, for d-block j,
-    // q[head col][32 j + 8 grp .. +8]; heads past G-1 are zero.
+    // dims 32 j + 8 grp .. +8 of query row col; rows past nq-1 are zero.
+    const int64_t qrow = ((int64_t)b * q_len + qi) * hq + g * G + qj;
     u32x4 qb[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        if (col < G) {
-            qb[j] = *reinterpret_cast<const u32x4*>(q + ((int64_t)b * hq + g * G + col) * kD + 32 * j + 8 * grp);
+        if (col < nq) {
+            qb[j] = *reinterpret_cast<const u32x4*>(q + qrow * kD + 32 * j + 8 * grp);
         } else {
             qb[j] = u32x4{0u, 0u, 0u, 0u};
         }
@@ -243,7 +260,7 @@ __global__ __launch_bounds__(64 * kMW) void partial_mfma(
         float mx = neg_inf();
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            p[i] = (tt + 4 * grp + i < t1) ? sc[i] * qk_scale_log2 : neg_inf();
+            p[i] = (tt + 4 * grp + i < lim) ? sc[i] * qk_scale_log2 : neg_inf();
             mx = fmaxf(mx, p[i]);
         }
         mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -333,8 +350,8 @@ __global__ __launch_bounds__(64 * kMW) void partial_mfma(
     }
     const float m_run = m_true;
 
-    // Lane (grp, col) holds O[head col][16 jd + 4 grp + i].
-    if (col < G) {
+    // Lane (grp, col) holds O[row col][16 jd + 4 grp + i].
+    if (col < nq) {
 #pragma unroll
         for (int jd = 0; jd < 8; ++jd)
 #pragma unroll
@@ -345,21 +362,23 @@ __global__ __launch_bounds__(64 * kMW) void partial_mfma(
         }
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < G * kD; idx += 64 * kMW) {
-        const int j = idx / kD;
+    for (int idx = threadIdx.x; idx < nq * kD; idx += 64 * kMW) {
+        const int n = idx / kD;
         const int d = idx % kD;
-        float Mx = sm_m[0][j];
+        float Mx = sm_m[0][n];
 #pragma unroll
-        for (int w = 1; w < kMW; ++w) Mx = fmaxf(Mx, sm_m[w][j]);
+        for (int w = 1; w < kMW; ++w) Mx = fmaxf(Mx, sm_m[w][n]);
         const float mu = (Mx == neg_inf()) ? 0.f : Mx;
         float o = 0.f, lsum = 0.f;
 #pragma unroll
         for (int w = 0; w < kMW; ++w) {
-            const float a = __builtin_amdgcn_exp2f(sm_m[w][j] - mu);
-            o += a * sm_o[w][j][d];
-            lsum += a * sm_l[w][j];
+            const float a = __builtin_amdgcn_exp2f(sm_m[w][n] - mu);
+            o += a * sm_o[w][n][d];
+            lsum += a * sm_l[w][n];
         }
-        const int64_t slot = ((int64_t)b * hq + g * G + j) * s_max + s;
+        const int ni = n / G;
+        const int64_t row = ((int64_t)b * q_len + ni) * hq + g * G + (n - ni * G);
+        const int64_t slot = row * s_max + s;
         ws_o[slot * kD + d] = o;
         if (d == 0) {
             ws_ml[slot * 2] = Mx * kLn2;
@@ -368,30 +387,31 @@ __global__ __launch_bounds__(64 * kMW) void partial_mfma(
     }
 }
 
-template <int G, int DT, int MODE>
+template <int NQ, int DT, int MODE>
 hipError_t launch_mode(const PartialArgs& a, dim3 grid, hipStream_t st) {
-    hipLaunchKernelGGL((partial_mfma<G, DT, MODE>), grid, dim3(64 * kMW), 0, st, a.q, a.k, a.v, a.table, a.lens,
-                       a.ws_o, a.ws_ml, a.batch, a.hq, a.hkv, a.chunk, a.s_max, a.max_pages, a.qk_scale_log2);
+    hipLaunchKernelGGL((partial_mfma<NQ, DT, MODE>), grid, dim3(64 * kMW), 0, st, a.q, a.k, a.v, a.table, a.lens,
+                       a.ws_o, a.ws_ml, a.batch, a.hq, a.hkv, a.chunk, a.s_max, a.max_pages, a.q_len,
+                       a.qk_scale_log2);
     return hipGetLastError();
 }
 
-template <int G, int DT>
-hipError_t launch_g(bool paged, const PartialArgs& a, dim3 grid, hipStream_t st) {
-    if (!paged) return launch_mode<G, DT, 0>(a, grid, st);
-    return (a.chunk % 16 == 0) ? launch_mode<G, DT, 2>(a, grid, st) : launch_mode<G, DT, 1>(a, grid, st);
+template <int NQ, int DT>
+hipError_t launch_nq(bool paged, const PartialArgs& a, dim3 grid, hipStream_t st) {
+    if (!paged) return launch_mode<NQ, DT, 0>(a, grid, st);
+    return (a.chunk % 16 == 0) ? launch_mode<NQ, DT, 2>(a, grid, st) : launch_mode<NQ, DT, 1>(a, grid, st);
 }
 
 template <int DT>
-hipError_t launch_dt(int G, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st) {
-    switch (G) {
-        case 2: return launch_g<2, DT>(paged, a, grid, st);
-        case 4: return launch_g<4, DT>(paged, a, grid, st);
-        default: return launch_g<8, DT>(paged, a, grid, st);
-    }
+hipError_t launch_dt(int nq, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st) {
+    if (nq <= 2) return launch_nq<2, DT>(paged, a, grid, st);
+    if (nq <= 4) return launch_nq<4, DT>(paged, a, grid, st);
+    if (nq <= 8) return launch_nq<8, DT>(paged, a, grid, st);
+    return launch_nq<16, DT>(paged, a, grid, st);
 }
 
 hipError_t launch_partial_mfma(int G, int dt, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st) {
-    return dt == FD_F16 ? launch_dt<FD_F16>(G, paged, a, grid, st) : launch_dt<FD_BF16>(G, paged, a, grid, st);
+    const int nq = G * a.q_len;
+    return dt == FD_F16 ? launch_dt<FD_F16>(nq, paged, a, grid, st) : launch_dt<FD_BF16>(nq, paged, a, grid, st);
 }
 
 }  // namespace fdk

@@ -231,3 +231,23 @@ def test_head_rows_fall_back_when_work_groups_are_few(monkeypatch):
     assert fd.fd_plan_splits(p, [2_000_000], num_cus=256).partial_kernel == 2
     monkeypatch.setenv("FD_PARTIAL_KERNEL", "2")  # an explicit request is kept
     assert fd.fd_plan_splits(p, [1024], num_cus=256, force_num_splits=4).partial_kernel == 2
+
+
+def test_multi_query_problems():
+    """q_len > 1 runs on the matrix-core kernel: d = 128 and q_len * G <= 16."""
+    plan = fd.fd_plan_splits(prob(num_q_heads=32, num_kv_heads=32, q_len=4), [131072], num_cus=256)
+    assert plan.partial_kernel == 1
+    base = fd.fd_plan_splits(prob(num_q_heads=32, num_kv_heads=32, q_len=1), [131072], num_cus=256,
+                             force_num_splits=plan.max_splits)
+    assert plan.workspace_bytes == 4 * base.workspace_bytes
+    assert fd.fd_plan_splits(prob(num_q_heads=64, num_kv_heads=8, q_len=2), [1000], num_cus=256).partial_kernel == 1
+    for kw, lens, status in [
+        (dict(head_dim=64, q_len=2), [100], fd.FD_ERR_UNSUPPORTED),
+        (dict(num_q_heads=64, num_kv_heads=8, q_len=4), [100], fd.FD_ERR_UNSUPPORTED),  # 32 rows
+        (dict(q_len=17), [100], fd.FD_ERR_UNSUPPORTED),
+        (dict(q_len=-1), [100], fd.FD_ERR_INVALID_ARGUMENT),
+        (dict(q_len=4), [3], fd.FD_ERR_INVALID_ARGUMENT),  # shorter than its query tokens
+    ]:
+        with pytest.raises(fd.FdError) as ei:
+            fd.fd_plan_splits(prob(**kw), lens, num_cus=256)
+        assert ei.value.status == status, kw

@@ -304,3 +304,64 @@ def test_large_scores_stay_finite():
     assert np.allclose(o, w @ V, rtol=1e-12, atol=1e-14)
     o2, lse2, _, _ = A.online_softmax_row(q, K, V, 1.0, 7)
     assert np.allclose(o2, o, rtol=1e-12, atol=1e-14) and abs(lse2 - lse) < 1e-9
+
+
+
+# ------------------------------------------------------- several query tokens
+
+
+def test_multi_query_with_one_query_is_single_query_decode():
+    wl = _wl(seq_lens=[5, 40, 17])
+    out, lse = A.decode_attention(wl.q, wl.k, wl.v, wl.seq_lens, wl.scale)
+    o2, l2 = A.decode_attention_multi(wl.q[:, None], wl.k, wl.v, wl.seq_lens, wl.scale)
+    assert np.array_equal(o2[:, 0], out) and np.array_equal(l2[:, 0], lse)
+
+
+@pytest.mark.parametrize("q_len", [2, 4, 7])
+def test_multi_query_matches_torch_causal_masked_softmax(q_len):
+    """Query i sees tokens 0 .. L - q_len + i: checked against torch's softmax
+    over the full row with -inf past each query's limit (an independent
+    library and a different way to express the mask)."""
+    wl = make_workload(batch=3, num_q_heads=8, num_kv_heads=2, head_dim=64, seq_lens=[q_len, 50, 130],
+                       dtype=torch.bfloat16, seed=q_len, q_len=q_len)
+    out, lse = A.decode_attention_multi(wl.q, wl.k, wl.v, wl.seq_lens, wl.scale)
+    G = wl.group_size
+    start = 0
+    for b, L in enumerate(wl.lens):
+        K = wl.k[start:start + L].double()
+        V = wl.v[start:start + L].double()
+        for i in range(q_len):
+            for h in range(wl.num_q_heads):
+                logits = (K[:, h // G] @ wl.q[b, i, h].double()) * wl.scale
+                logits[L - q_len + i + 1:] = -float("inf")
+                o = torch.softmax(logits, 0) @ V[:, h // G]
+                assert np.allclose(out[b, i, h], o.numpy(), rtol=1e-12, atol=1e-14)
+                assert abs(lse[b, i, h] - float(torch.logsumexp(logits, 0))) < 1e-12
+        start += L
+
+
+def test_multi_query_split_statistics_merge_to_the_result():
+    wl = make_workload(batch=2, num_q_heads=4, num_kv_heads=2, head_dim=32, seq_lens=[9, 70],
+                       dtype=torch.float16, seed=3, q_len=4)
+    out, lse = A.decode_attention_multi(wl.q, wl.k, wl.v, wl.seq_lens, wl.scale)
+    for chunk in (1, 3, 8, 70):
+        O, m, l = A.decode_partials(wl.q, wl.k, wl.v, wl.seq_lens, wl.scale, chunk)
+        for b, L in enumerate(wl.lens):
+            S = -(-L // chunk)
+            for i in range(4):
+                for h in range(4):
+                    r = i * 4 + h
+                    # splits past a query's causal limit hold the empty statistics
+                    for si in range(S):
+                        if si * chunk > L - 4 + i:
+                            assert m[b, r, si] == -np.inf and l[b, r, si] == 0 and not O[b, r, si].any()
+                    ms = m[b, r, :S]
+                    keep = ms > -np.inf
+                    o, ls = A.merge_partials(O[b, r, :S][keep], ms[keep], l[b, r, :S][keep])
+                    assert np.allclose(o, out[b, i, h], rtol=1e-12, atol=1e-14) and abs(ls - lse[b, i, h]) < 1e-12
+
+
+def test_multi_query_rejects_short_caches():
+    wl = make_workload(batch=1, num_q_heads=2, num_kv_heads=2, head_dim=16, seq_lens=[3], seed=1, q_len=4)
+    with pytest.raises(ValueError):
+        A.decode_attention_multi(wl.q, wl.k, wl.v, wl.seq_lens, wl.scale)

@@ -118,7 +118,26 @@ def _split_bounds_drops_tail(L, chunk):
     return [(s, s + chunk) for s in range(0, L - chunk + 1, chunk)] or [(0, L)]
 
 
+def _multi_causal_off_by_one(q, k, v, seq_lens, scale, block_table=None, page_size=0):
+    qf = A.as_f64(q)
+    B, ql, hq, d = qf.shape
+    hkv = k.shape[-2]
+    G = hq // hkv
+    lens = A._lens(seq_lens)
+    out = np.full((B, ql, hq, d), np.nan)
+    lse = np.full((B, ql, hq), np.nan)
+    for b in range(B):
+        for g in range(hkv):
+            K, V = A.logical_kv(k, v, seq_lens, b, g, block_table, page_size)
+            for i in range(ql):
+                n = max(1, lens[b] - ql + i)
+                for h in range(g * G, (g + 1) * G):
+                    out[b, i, h], lse[b, i, h], _, _ = A.attention_row(qf[b, i, h], K[:n], V[:n], scale)
+    return out, lse
+
+
 MUTANTS = [
+    ("decode_attention_multi", _multi_causal_off_by_one, [lambda: P.test_multi_query_matches_torch_causal_masked_softmax(4)]),
     ("merge_two", _merge_two_flipped_sign,
      [P.test_worked_example_printed_values, lambda: P.test_every_split_merges_to_the_full_row(17)]),
     ("merge_partials", _merge_partials_unweighted_l,

@@ -322,3 +322,49 @@ def test_token_rows_and_head_rows_kernels_agree_with_oracle(fd, monkeypatch, ker
     assert res.plan.partial_kernel == kernel
     ref_out, ref_lse = reference(wl)
     parity(res.out, res.lse, ref_out, ref_lse, what=f"mha case {case} kernel {kernel} splits {splits}")
+
+
+# ------------------------------------------------- several query tokens (n1)
+
+
+MQ_CASES = [
+    # (dtype, Hq, Hkv, q_len, lens, page)
+    (torch.float16, 8, 8, 4, [4, 17, 1000], 0),       # MHA, 4 draft tokens
+    (torch.bfloat16, 32, 8, 4, [600, 4096], 0),       # G = 4: 16 query rows
+    (torch.bfloat16, 64, 8, 2, [100, 3000], 16),      # G = 8, paged
+    (torch.float16, 4, 2, 8, [8, 9, 777], 16),        # G = 2, 8 tokens, paged
+    (torch.float16, 16, 16, 16, [16, 2048], 0),       # MHA, 16 tokens
+    (torch.bfloat16, 8, 8, 3, [5, 300], 0),           # 3 rows padded to 4
+]
+
+
+@pytest.mark.parametrize("case", range(len(MQ_CASES)))
+@pytest.mark.parametrize("splits", [0, 3, 64])
+def test_multi_query_decode_matches_oracle(fd, case, splits):
+    dt, hq, hkv, ql, lens, page = MQ_CASES[case]
+    wl = make_workload(name=f"mq{case}", batch=len(lens), num_q_heads=hq, num_kv_heads=hkv, head_dim=128,
+                       seq_lens=lens, dtype=dt, seed=500 + case, page_size=page, q_len=ql)
+    res = run(fd, wl, num_splits=splits)
+    assert res.plan.partial_kernel == 1 and tuple(res.out.shape) == (len(lens), ql, hq, 128)
+    ref_out, ref_lse = oracle.decode_attention_multi(wl.q, wl.k, wl.v, wl.seq_lens, wl.scale, wl.block_table,
+                                                     wl.page_size)
+    parity(res.out, res.lse, ref_out, ref_lse, what=f"multi-query case {case} splits {splits}")
+
+
+def test_multi_query_split_statistics_include_empty_splits(fd):
+    """Splits past a query's causal limit hold (m, l, O) = (-inf, 0, 0)."""
+    ql = 8
+    wl = make_workload(name="mq-stats", batch=2, num_q_heads=4, num_kv_heads=2, head_dim=128, seq_lens=[64, 30],
+                       dtype=torch.bfloat16, seed=9, q_len=ql)
+    res = run(fd, wl, num_splits=32)  # chunk 2: the last splits lie past the early queries' limits
+    C = res.plan.chunk_tokens
+    prob = fd.make_problem(batch=2, num_q_heads=4, num_kv_heads=2, head_dim=128, kv_dtype=torch.bfloat16, q_len=ql)
+    O_s, m_s, l_s = (x.double().cpu().numpy() for x in fd.workspace_views(prob, res.plan, res.workspace))
+    Oo, mo, lo = oracle.decode_partials(wl.q, wl.k, wl.v, wl.seq_lens, wl.scale, C)
+    for b, L in enumerate(wl.lens):
+        S = -(-L // C)
+        assert np.array_equal(np.isinf(m_s[b, :, :S]), np.isinf(mo[b, :, :S]))
+        fin = np.isfinite(mo[b, :, :S])
+        assert np.allclose(m_s[b, :, :S][fin], mo[b, :, :S][fin], rtol=0, atol=1e-5)
+        assert np.allclose(l_s[b, :, :S], lo[b, :, :S], rtol=1e-5, atol=0)
+        assert np.allclose(O_s[b, :, :S], Oo[b, :, :S], rtol=1e-5, atol=1e-5)

@@ -50,7 +50,7 @@ class Workload:
     """One decode-attention problem: a query token per sequence and its KV cache.
 
     Layouts (all row-major, contiguous):
-      q            [B, Hq, d]
+      q            [B, Hq, d], or [B, q_len, Hq, d] with several query tokens
       k, v         contiguous: [sum(L_b) + pad_rows, Hkv, d]; sequence b
                    occupies rows [start_b, start_b + L_b), start_b the sum of
                    the lengths before it; the pad rows hold NaN.
@@ -78,6 +78,10 @@ class Workload:
     pad_rows: int = 0
     seed: int = 0
     meta: dict = field(default_factory=dict)
+
+    @property
+    def q_len(self) -> int:
+        return 1 if self.q.dim() == 3 else int(self.q.shape[1])
 
     @property
     def group_size(self) -> int:
@@ -189,10 +193,13 @@ def make_workload(
     spare_pages: int = 8,
     permute_pages: bool = True,
     max_pages_per_seq: Optional[int] = None,
+    q_len: int = 1,
 ) -> Workload:
     """Draw one workload. ``seq_lens`` is a list of lengths, or a tuple
     ``("uniform", lo, hi)`` (integers, both ends included) or
-    ``("loguniform", lo, hi)`` (rounded, clamped to [lo, hi])."""
+    ``("loguniform", lo, hi)`` (rounded, clamped to [lo, hi]). With
+    ``q_len`` > 1, q is [B, q_len, Hq, d]: the queries of the last q_len
+    tokens of each cache."""
     if num_q_heads % num_kv_heads:
         raise ValueError("num_q_heads must be a multiple of num_kv_heads")
     root = np.random.SeedSequence(seed)
@@ -201,7 +208,8 @@ def make_workload(
     lens = _draw_lengths(seq_lens, batch, ss_len)
     total = int(sum(lens))
 
-    q = torch.empty((batch, num_q_heads, head_dim), dtype=dtype)
+    q_shape = (batch, num_q_heads, head_dim) if q_len == 1 else (batch, q_len, num_q_heads, head_dim)
+    q = torch.empty(q_shape, dtype=dtype)
     _normal_into(q, ss_q)
     k = torch.empty((total + pad_rows, num_kv_heads, head_dim), dtype=dtype)
     v = torch.empty((total + pad_rows, num_kv_heads, head_dim), dtype=dtype)
@@ -280,10 +288,19 @@ def to_paged(wl: Workload, page_size: int, ss_page=None, *, spare_pages: int = 8
     )
 
 
-def make_config(i: int, seed: Optional[int] = None) -> Workload:
+def make_config(i: int, seed: Optional[int] = None, q_len: int = 1) -> Workload:
     """The five decode workloads, numbered 1..5 (tiny MHA, 32K MHA, 128K MHA
-    with key spikes, GQA varlen, paged GQA). Seeds default to 1000 + i."""
+    with key spikes, GQA varlen, paged GQA). Seeds default to 1000 + i. With
+    q_len > 1 each sequence carries that many query tokens (its last q_len
+    cache positions); the name gets a ``_q<q_len>`` suffix."""
     s = 1000 + i if seed is None else seed
+    if q_len > 1:
+        wl = make_config(i, seed, 1)
+        q = torch.empty((wl.batch, q_len, wl.num_q_heads, wl.head_dim), dtype=wl.dtype)
+        _normal_into(q, np.random.SeedSequence([s, q_len]))
+        wl.q = q
+        wl.name = f"{wl.name}_q{q_len}"
+        return wl
     name = CONFIG_NAMES[i]
     if i == 1:
         return make_workload(name=name, batch=1, num_q_heads=8, num_kv_heads=8, head_dim=64,
