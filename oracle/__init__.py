@@ -26,3 +26,4 @@ from .attention import (  # noqa: F401
     online_softmax_row,
     split_bounds,
 )
+from .fp8 import decode_e4m3, e4m3_value  # noqa: F401

@@ -34,7 +34,9 @@ Readings where the pages leave a step open:
   * query head h reads KV head h // (Hq / Hkv) (contiguous groups);
   * tokens at or past a sequence's length never contribute (masking, not
     padding with copies of the last token);
-  * a zero-length sequence has no defined output and is rejected.
+  * a zero-length sequence has no defined output and is rejected;
+  * an FP8 cache holds OCP E4M3 codes; the value attention sees is the code's
+    value times a per-KV-head scale, one for K and one for V (``oracle.fp8``).
 
 Arithmetic is float64 throughout; inputs (fp16/bf16 tensors or arrays) are
 converted exactly. Library primitives used as steps: matrix-vector products,
@@ -48,6 +50,8 @@ from typing import Iterable, List, Optional, Sequence, Tuple
 
 import numpy as np
 
+from .fp8 import decode_e4m3, is_fp8
+
 try:  # torch is only used to read bf16 tensors exactly
     import torch
 except Exception:  # pragma: no cover
@@ -58,7 +62,10 @@ except Exception:  # pragma: no cover
 
 
 def as_f64(x) -> np.ndarray:
-    """Exact conversion of an fp16/bf16/fp32 array or CPU tensor to float64."""
+    """Exact conversion of an fp16/bf16/fp32 array or CPU tensor to float64;
+    E4M3 code tensors are decoded by the format's definition."""
+    if is_fp8(x):
+        return decode_e4m3(x)
     if torch is not None and isinstance(x, torch.Tensor):
         return x.detach().to("cpu").to(torch.float64).numpy()
     return np.asarray(x, dtype=np.float64)
@@ -70,12 +77,15 @@ def _lens(seq_lens) -> List[int]:
     return [int(t) for t in seq_lens]
 
 
-def logical_kv(k, v, seq_lens, b: int, g: int, block_table=None, page_size: int = 0):
+def logical_kv(k, v, seq_lens, b: int, g: int, block_table=None, page_size: int = 0,
+               k_scale=None, v_scale=None):
     """Rows 0..L_b-1 of KV head ``g`` of sequence ``b``, as float64 [L_b, d].
 
     Contiguous caches pack the sequences one after another along the token
     axis. Paged caches find token t in physical block ``block_table[b, t //
     page_size]`` at slot ``t % page_size`` (FlashAttention capstone, §4.1).
+    ``k_scale`` / ``v_scale`` (one value per KV head, or None for 1) multiply
+    the rows of head ``g``.
     """
     lens = _lens(seq_lens)
     L = lens[b]
@@ -94,7 +104,12 @@ def logical_kv(k, v, seq_lens, b: int, g: int, block_table=None, page_size: int 
         start = sum(lens[:b])
         kr = k[start:start + L, g, :]
         vr = v[start:start + L, g, :]
-    return as_f64(kr), as_f64(vr)
+    K, V = as_f64(kr), as_f64(vr)
+    if k_scale is not None:
+        K = K * float(as_f64(k_scale)[g])
+    if v_scale is not None:
+        V = V * float(as_f64(v_scale)[g])
+    return K, V
 
 
 # ------------------------------------------------------- the plain definition
@@ -227,13 +242,14 @@ def _pairs(batch: int, hq: int, pairs: Optional[Iterable[Tuple[int, int]]]):
 
 
 def decode_attention(q, k, v, seq_lens, scale: float, block_table=None, page_size: int = 0,
-                     pairs: Optional[Sequence[Tuple[int, int]]] = None):
+                     pairs: Optional[Sequence[Tuple[int, int]]] = None, k_scale=None, v_scale=None):
     """Exact decode attention for a batch: out [B, Hq, d] and lse [B, Hq] (fp64).
 
     For each sequence b and query head h, with KV head g = h // (Hq / Hkv)
     (FlashAttention capstone §4.2, contiguous groups), ``attention_row`` over
     the sequence's logical rows. ``pairs`` restricts the work to some (b, h);
-    entries not computed are NaN.
+    entries not computed are NaN. ``k_scale`` / ``v_scale``: per-KV-head
+    dequantisation scales (see ``logical_kv``).
     """
     qf = as_f64(q)
     B, hq, d = qf.shape
@@ -245,7 +261,7 @@ def decode_attention(q, k, v, seq_lens, scale: float, block_table=None, page_siz
     for b, h in _pairs(B, hq, pairs):
         todo.setdefault((b, h // G), []).append(h)
     for (b, g), heads in sorted(todo.items()):
-        K, V = logical_kv(k, v, seq_lens, b, g, block_table, page_size)
+        K, V = logical_kv(k, v, seq_lens, b, g, block_table, page_size, k_scale, v_scale)
         for h in heads:
             o, ls, _, _ = attention_row(qf[b, h], K, V, scale)
             out[b, h] = o
@@ -253,7 +269,8 @@ def decode_attention(q, k, v, seq_lens, scale: float, block_table=None, page_siz
     return out, lse
 
 
-def decode_attention_multi(q, k, v, seq_lens, scale: float, block_table=None, page_size: int = 0):
+def decode_attention_multi(q, k, v, seq_lens, scale: float, block_table=None, page_size: int = 0,
+                           k_scale=None, v_scale=None):
     """Several query tokens per sequence: q [B, q_len, Hq, d] -> out
     [B, q_len, Hq, d], lse [B, q_len, Hq] (fp64).
 
@@ -273,7 +290,7 @@ def decode_attention_multi(q, k, v, seq_lens, scale: float, block_table=None, pa
         if lens[b] < ql:
             raise ValueError("every sequence must hold its q_len new tokens")
         for g in range(hkv):
-            K, V = logical_kv(k, v, seq_lens, b, g, block_table, page_size)
+            K, V = logical_kv(k, v, seq_lens, b, g, block_table, page_size, k_scale, v_scale)
             for i in range(ql):
                 n = lens[b] - ql + i + 1
                 for h in range(g * G, (g + 1) * G):
@@ -285,7 +302,7 @@ def decode_attention_multi(q, k, v, seq_lens, scale: float, block_table=None, pa
 
 def decode_partials(q, k, v, seq_lens, scale: float, chunk: int, block_table=None,
                     page_size: int = 0, max_splits: Optional[int] = None,
-                    pairs: Optional[Sequence[Tuple[int, int]]] = None):
+                    pairs: Optional[Sequence[Tuple[int, int]]] = None, k_scale=None, v_scale=None):
     """Per-split statistics for every (b, h): O [B, Hq, S, d] (unnormalised),
     m [B, Hq, S] and l [B, Hq, S], S = max_b ceil(L_b / chunk). Splits a
     sequence does not have are NaN.
@@ -296,7 +313,8 @@ def decode_partials(q, k, v, seq_lens, scale: float, chunk: int, block_table=Non
     qf = as_f64(q)
     if qf.ndim == 4:
         B, ql, hq, d = qf.shape
-        return _decode_partials_multi(qf, k, v, seq_lens, scale, chunk, block_table, page_size, max_splits)
+        return _decode_partials_multi(qf, k, v, seq_lens, scale, chunk, block_table, page_size, max_splits,
+                                      k_scale, v_scale)
     B, hq, d = qf.shape
     hkv = k.shape[-2]
     G = hq // hkv
@@ -309,14 +327,15 @@ def decode_partials(q, k, v, seq_lens, scale: float, chunk: int, block_table=Non
     for b, h in _pairs(B, hq, pairs):
         todo.setdefault((b, h // G), []).append(h)
     for (b, g), heads in sorted(todo.items()):
-        K, V = logical_kv(k, v, seq_lens, b, g, block_table, page_size)
+        K, V = logical_kv(k, v, seq_lens, b, g, block_table, page_size, k_scale, v_scale)
         for si, (lo, hi) in enumerate(split_bounds(lens[b], chunk)):
             for h in heads:
                 O[b, h, si], m[b, h, si], l[b, h, si] = _split_partial(qf[b, h], K[lo:hi], V[lo:hi], scale)
     return O, m, l
 
 
-def _decode_partials_multi(qf, k, v, seq_lens, scale, chunk, block_table, page_size, max_splits):
+def _decode_partials_multi(qf, k, v, seq_lens, scale, chunk, block_table, page_size, max_splits,
+                           k_scale=None, v_scale=None):
     B, ql, hq, d = qf.shape
     hkv = k.shape[-2]
     G = hq // hkv
@@ -327,7 +346,7 @@ def _decode_partials_multi(qf, k, v, seq_lens, scale, chunk, block_table, page_s
     l = np.full((B, ql * hq, S), np.nan)
     for b in range(B):
         for g in range(hkv):
-            K, V = logical_kv(k, v, seq_lens, b, g, block_table, page_size)
+            K, V = logical_kv(k, v, seq_lens, b, g, block_table, page_size, k_scale, v_scale)
             for si, (lo, hi) in enumerate(split_bounds(lens[b], chunk)):
                 for i in range(ql):
                     top = min(hi, lens[b] - ql + i + 1)

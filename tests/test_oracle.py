@@ -365,3 +365,74 @@ def test_multi_query_rejects_short_caches():
     wl = make_workload(batch=1, num_q_heads=2, num_kv_heads=2, head_dim=16, seq_lens=[3], seed=1, q_len=4)
     with pytest.raises(ValueError):
         A.decode_attention_multi(wl.q, wl.k, wl.v, wl.seq_lens, wl.scale)
+
+
+# ------------------------------------------------------------ FP8 KV cache
+
+import oracle.fp8 as F  # noqa: E402
+
+
+def test_e4m3_codes_match_torch_float8_e4m3fn():
+    """Every one of the 256 codes against torch's float8_e4m3fn -> float64
+    cast (an independent implementation of the OCP E4M3 format)."""
+    codes = torch.arange(256, dtype=torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    mine = np.array([F.e4m3_value(c) for c in range(256)])
+    assert np.array_equal(mine, ref, equal_nan=True)
+    fin = ~np.isnan(ref)
+    assert np.array_equal(np.signbit(mine[fin]), np.signbit(ref[fin]))  # -0 included
+    assert np.array_equal(F.decode_e4m3(codes), ref, equal_nan=True)
+    assert np.array_equal(A.as_f64(codes.view(torch.float8_e4m3fn)), ref, equal_nan=True)
+
+
+def test_e4m3_format_closed_forms():
+    """Values the format's definition fixes: signed zeros, the smallest and
+    largest subnormals (2^-9, 7 * 2^-9), the smallest normal (2^-6), 1, 1.5,
+    -2, the largest finite magnitude 448, NaN only at S.1111.111, and the
+    positive codes in increasing order."""
+    v = F.e4m3_value
+    assert v(0x00) == 0.0 and v(0x80) == 0.0 and math.copysign(1.0, v(0x80)) == -1.0
+    assert v(0x01) == 2.0 ** -9 and v(0x07) == 7 * 2.0 ** -9 and v(0x08) == 2.0 ** -6
+    assert v(0x38) == 1.0 and v(0x3C) == 1.5 and v(0xC0) == -2.0
+    assert v(0x7E) == 448.0 and v(0xFE) == -448.0
+    assert [c for c in range(256) if math.isnan(v(c))] == [0x7F, 0xFF]
+    pos = [v(c) for c in range(0x7F)]
+    assert all(a < b for a, b in zip(pos, pos[1:]))
+
+
+def _fp8_wl(**kw):
+    from workloads import quantize_kv_fp8
+    return quantize_kv_fp8(_wl(**kw))
+
+
+def test_fp8_cache_with_unit_scales_equals_the_same_values_in_fp16():
+    """Every E4M3 value is exact in fp16, so an FP8 cache read with scales of
+    1 gives the fp16 cache of the same values (torch's cast) bit for bit."""
+    wl = _fp8_wl()
+    k16, v16 = wl.k.to(torch.float16), wl.v.to(torch.float16)
+    a = A.decode_attention(wl.q, wl.k, wl.v, wl.seq_lens, wl.scale)
+    b = A.decode_attention(wl.q, k16, v16, wl.seq_lens, wl.scale)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    assert np.isfinite(a[0]).all()
+
+
+def test_fp8_scales_apply_per_kv_head():
+    """A K scale c on KV head g acts as a softmax scale c times larger for
+    the query heads of group g only; a V scale c on head g multiplies their
+    outputs by c and leaves their lse alone (powers of two: exact)."""
+    wl = _fp8_wl()
+    G = wl.group_size
+    base = A.decode_attention(wl.q, wl.k, wl.v, wl.seq_lens, wl.scale)
+    half = A.decode_attention(wl.q, wl.k, wl.v, wl.seq_lens, wl.scale * 0.5)
+    o, lse = A.decode_attention(wl.q, wl.k, wl.v, wl.seq_lens, wl.scale,
+                                k_scale=torch.tensor([1.0, 0.5]), v_scale=torch.tensor([1.0, 4.0]))
+    assert np.array_equal(o[:, :G], base[0][:, :G]) and np.array_equal(lse[:, :G], base[1][:, :G])
+    assert np.array_equal(o[:, G:], 4.0 * half[0][:, G:]) and np.array_equal(lse[:, G:], half[1][:, G:])
+    # the same through the split statistics
+    O, m, l = A.decode_partials(wl.q, wl.k, wl.v, wl.seq_lens, wl.scale, 8,
+                                k_scale=torch.tensor([1.0, 0.5]), v_scale=torch.tensor([1.0, 4.0]))
+    for b, L in enumerate(wl.lens):
+        S = (L + 7) // 8
+        for h in range(wl.num_q_heads):
+            ob, lb = A.merge_partials(O[b, h, :S], m[b, h, :S], l[b, h, :S])
+            assert np.allclose(ob, o[b, h], rtol=1e-12, atol=1e-13) and abs(lb - lse[b, h]) < 1e-12

@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 
 import oracle.attention as A
+import oracle.fp8 as F
 import tests.test_oracle as P
 
 
@@ -102,7 +103,7 @@ def _decode_head_mod_mapping(q, k, v, seq_lens, scale, block_table=None, page_si
 _orig_logical = A.logical_kv
 
 
-def _logical_kv_slot_reversed(k, v, seq_lens, b, g, block_table=None, page_size=0):
+def _logical_kv_slot_reversed(k, v, seq_lens, b, g, block_table=None, page_size=0, k_scale=None, v_scale=None):
     if not page_size:
         return _orig_logical(k, v, seq_lens, b, g, block_table, page_size)
     L = A._lens(seq_lens)[b]
@@ -136,7 +137,27 @@ def _multi_causal_off_by_one(q, k, v, seq_lens, scale, block_table=None, page_si
     return out, lse
 
 
+def _e4m3_bias_8(code):
+    code = int(code) & 0xFF
+    sign = -1.0 if code & 0x80 else 1.0
+    e, mnt = (code >> 3) & 0xF, code & 0x7
+    if e == 0xF and mnt == 0x7:
+        return math.nan
+    if e == 0:
+        return sign * (mnt / 8.0) * 2.0 ** (1 - 8)
+    return sign * (1.0 + mnt / 8.0) * 2.0 ** (e - 8)
+
+
+_logical_kv_orig = A.logical_kv
+
+
+def _logical_kv_scales_swapped(k, v, seq_lens, b, g, block_table=None, page_size=0, k_scale=None, v_scale=None):
+    return _logical_kv_orig(k, v, seq_lens, b, g, block_table, page_size, v_scale, k_scale)
+
+
 MUTANTS = [
+    ("fp8:e4m3_value", _e4m3_bias_8, [P.test_e4m3_codes_match_torch_float8_e4m3fn, P.test_e4m3_format_closed_forms]),
+    ("logical_kv", _logical_kv_scales_swapped, [P.test_fp8_scales_apply_per_kv_head]),
     ("decode_attention_multi", _multi_causal_off_by_one, [lambda: P.test_multi_query_matches_torch_causal_masked_softmax(4)]),
     ("merge_two", _merge_two_flipped_sign,
      [P.test_worked_example_printed_values, lambda: P.test_every_split_merges_to_the_full_row(17)]),
@@ -158,7 +179,10 @@ MUTANTS = [
 @pytest.mark.parametrize("idx", range(len(MUTANTS)), ids=[f"{m[0]}:{m[1].__name__}" for m in MUTANTS])
 def test_mutant_is_caught(monkeypatch, idx):
     name, fn, pins = MUTANTS[idx]
-    monkeypatch.setattr(A, name, fn)
+    mod = A
+    if name.startswith("fp8:"):
+        mod, name = F, name[4:]
+    monkeypatch.setattr(mod, name, fn)
     caught = 0
     for pin in pins:
         try:

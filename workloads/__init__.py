@@ -7,6 +7,7 @@ sharing any computation.
 """
 
 from .synth import (  # noqa: F401
+    quantize_kv_fp8,
     CONFIG_NAMES,
     Workload,
     make_config,

@@ -12,6 +12,10 @@ Every random draw comes from ``numpy.random.default_rng`` under a
 fixed-size chunks, each with its own child seed, so the result does not depend
 on how many threads generate it.
 
+FP8 caches (``quantize_kv_fp8``) store each K/V element as an OCP E4M3 code of
+the drawn value divided by a per-KV-head scale (the head's largest magnitude
+over 448, the format's largest finite value), rounded by torch's cast.
+
 Nothing here computes attention: the module draws numbers and places them in
 the cache layouts. Slots that no valid token occupies are filled with NaN so
 that any read past a sequence's end shows up in the output.
@@ -58,6 +62,9 @@ class Workload:
       seq_lens     int32 [B]
       block_table  int32 [B, max_pages_per_seq] (paged only); entries past a
                    sequence's last page point at a NaN-filled spare page.
+      k_scale, v_scale  float32 [Hkv] for an FP8 cache (element value =
+                   scale[g] * code value), else None.
+    ``dtype`` is q's dtype; ``kv_dtype`` the cache's.
     """
 
     name: str
@@ -78,6 +85,12 @@ class Workload:
     pad_rows: int = 0
     seed: int = 0
     meta: dict = field(default_factory=dict)
+    k_scale: Optional[torch.Tensor] = None
+    v_scale: Optional[torch.Tensor] = None
+
+    @property
+    def kv_dtype(self) -> torch.dtype:
+        return self.k.dtype
 
     @property
     def q_len(self) -> int:
@@ -284,16 +297,69 @@ def to_paged(wl: Workload, page_size: int, ss_page=None, *, spare_pages: int = 8
         scale=wl.scale, page_size=page_size, q=wl.q, k=kp, v=vp,
         seq_lens=wl.seq_lens, block_table=torch.from_numpy(table),
         max_pages_per_seq=mp, force_num_splits=wl.force_num_splits, pad_rows=0,
-        seed=wl.seed, meta=meta,
+        seed=wl.seed, meta=meta, k_scale=wl.k_scale, v_scale=wl.v_scale,
     )
 
 
-def make_config(i: int, seed: Optional[int] = None, q_len: int = 1) -> Workload:
+_FP8_MAX = 448.0  # largest finite E4M3 magnitude
+
+
+def _fp8_codes(x: torch.Tensor, scale: torch.Tensor) -> torch.Tensor:
+    """E4M3 codes of x / scale (per KV head, the second-to-last axis), cast
+    in token chunks to bound host memory. NaN stays NaN (code 0x7F)."""
+    out = torch.empty(x.shape, dtype=torch.float8_e4m3fn)
+    step = max(1, _CHUNK // max(1, x[0].numel()))
+    shape = (1,) * (x.dim() - 2) + (scale.numel(), 1)
+    inv = (1.0 / scale.float()).view(shape)
+    for lo in range(0, x.shape[0], step):
+        out[lo:lo + step] = (x[lo:lo + step].float() * inv).to(torch.float8_e4m3fn)
+    return out
+
+
+def _head_amax(x: torch.Tensor) -> torch.Tensor:
+    """Largest finite magnitude per KV head (the second-to-last axis)."""
+    hkv = x.shape[-2]
+    flat = x.reshape(-1, hkv, x.shape[-1])
+    amax = torch.zeros(hkv, dtype=torch.float32)
+    step = max(1, _CHUNK // max(1, flat[0].numel()))
+    for lo in range(0, flat.shape[0], step):
+        blk = flat[lo:lo + step].float().abs()
+        blk = torch.nan_to_num(blk, nan=0.0)
+        amax = torch.maximum(amax, blk.amax(dim=(0, 2)))
+    return amax
+
+
+def quantize_kv_fp8(wl: Workload) -> Workload:
+    """The same workload with an FP8 (OCP E4M3) cache: per KV head, scale =
+    amax / 448 and code = e4m3(x / scale), separately for K and V. q stays in
+    its 16-bit type. Poisoned (NaN) slots stay NaN."""
+    def quant(x):
+        amax = _head_amax(x)
+        scale = torch.where(amax > 0, amax / _FP8_MAX, torch.ones_like(amax)).to(torch.float32)
+        return _fp8_codes(x, scale), scale
+
+    kq, ks = quant(wl.k)
+    vq, vs = quant(wl.v)
+    meta = dict(wl.meta)
+    return Workload(
+        name=wl.name + "_fp8", batch=wl.batch, num_q_heads=wl.num_q_heads,
+        num_kv_heads=wl.num_kv_heads, head_dim=wl.head_dim, dtype=wl.dtype,
+        scale=wl.scale, page_size=wl.page_size, q=wl.q, k=kq, v=vq,
+        seq_lens=wl.seq_lens, block_table=wl.block_table, max_pages_per_seq=wl.max_pages_per_seq,
+        force_num_splits=wl.force_num_splits, pad_rows=wl.pad_rows, seed=wl.seed, meta=meta,
+        k_scale=ks, v_scale=vs,
+    )
+
+
+def make_config(i: int, seed: Optional[int] = None, q_len: int = 1, kv_fp8: bool = False) -> Workload:
     """The five decode workloads, numbered 1..5 (tiny MHA, 32K MHA, 128K MHA
     with key spikes, GQA varlen, paged GQA). Seeds default to 1000 + i. With
     q_len > 1 each sequence carries that many query tokens (its last q_len
-    cache positions); the name gets a ``_q<q_len>`` suffix."""
+    cache positions); the name gets a ``_q<q_len>`` suffix. ``kv_fp8`` stores
+    the cache as E4M3 codes with per-head scales (``quantize_kv_fp8``)."""
     s = 1000 + i if seed is None else seed
+    if kv_fp8:
+        return quantize_kv_fp8(make_config(i, seed, q_len))
     if q_len > 1:
         wl = make_config(i, seed, 1)
         q = torch.empty((wl.batch, q_len, wl.num_q_heads, wl.head_dim), dtype=wl.dtype)
