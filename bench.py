@@ -81,7 +81,7 @@ def cpu_baseline(wl, budget_s: float, out, lse):
     if wl.q_len > 1:
         t0 = time.perf_counter()
         ref_o, ref_l = oracle.decode_attention_multi(wl.q, wl.k, wl.v, wl.seq_lens, wl.scale, wl.block_table,
-                                                     wl.page_size)
+                                                     wl.page_size, k_scale=wl.k_scale, v_scale=wl.v_scale)
         el = time.perf_counter() - t0
         d = out.double().cpu().numpy() - ref_o
         return {"value": kv_bytes(wl) / el / 1e9, "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
@@ -96,7 +96,8 @@ def cpu_baseline(wl, budget_s: float, out, lse):
     t0 = time.perf_counter()
     for h in range(hq):
         o, l = oracle.decode_attention(wl.q, wl.k, wl.v, wl.seq_lens, wl.scale, wl.block_table, wl.page_size,
-                                       pairs=[(b, h) for b in range(wl.batch)])
+                                       pairs=[(b, h) for b in range(wl.batch)], k_scale=wl.k_scale,
+                                       v_scale=wl.v_scale)
         ref_o = o if ref_o is None else np.where(np.isnan(o), ref_o, o)
         ref_l = l if ref_l is None else np.where(np.isnan(l), ref_l, l)
         done += 1
@@ -135,6 +136,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=3, help="workload 1..5 (default: 128K MHA)")
     ap.add_argument("--q-len", type=int, default=1, help="query tokens per sequence (speculative verification)")
+    ap.add_argument("--kv-fp8", action="store_true", help="FP8 (E4M3) cache with per-KV-head scales")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--json-out", default=None)
@@ -158,15 +160,18 @@ def main() -> int:
     dev = torch.device("cuda", 0)
 
     t = time.perf_counter()
-    wl = make_config(args.config, q_len=args.q_len)
+    wl = make_config(args.config, q_len=args.q_len, kv_fp8=args.kv_fp8)
     log(f"generated {wl.name} in {time.perf_counter() - t:.1f} s")
     q, k, v = wl.q.to(dev), wl.k.to(dev), wl.v.to(dev)
     bt = wl.block_table.to(dev) if wl.paged else None
     lens_host = wl.lens
     lens_dev = wl.seq_lens.to(dev)
+    ks = wl.k_scale.to(dev) if wl.k_scale is not None else None
+    vs = wl.v_scale.to(dev) if wl.v_scale is not None else None
     problem = fd.make_problem(batch=wl.batch, num_q_heads=wl.num_q_heads, num_kv_heads=wl.num_kv_heads,
-                              head_dim=wl.head_dim, kv_dtype=wl.dtype, out_dtype=torch.float32, scale=wl.scale,
-                              page_size=wl.page_size, max_pages_per_seq=wl.max_pages_per_seq, q_len=wl.q_len)
+                              head_dim=wl.head_dim, kv_dtype=wl.kv_dtype, q_dtype=wl.dtype, out_dtype=torch.float32,
+                              scale=wl.scale, page_size=wl.page_size, max_pages_per_seq=wl.max_pages_per_seq,
+                              q_len=wl.q_len)
     plan = fd.fd_plan_splits(problem, lens_host, 0, wl.force_num_splits)
     ws = torch.empty(-(-plan.workspace_bytes // 4), dtype=torch.float32, device=dev)
     out = torch.empty(tuple(wl.q.shape), dtype=torch.float32, device=dev)
@@ -176,7 +181,7 @@ def main() -> int:
 
     def step():
         p = fd.fd_plan_splits(problem, lens_host, 0, wl.force_num_splits)
-        fd.fd_decode_partial(problem, p, q, k, v, bt, lens_dev, ws)
+        fd.fd_decode_partial(problem, p, q, k, v, bt, lens_dev, ws, None, ks, vs)
         fd.fd_combine(problem, p, lens_dev, ws, out, lse)
 
     step()
@@ -196,7 +201,7 @@ def main() -> int:
     for i in range(K):
         p = fd.fd_plan_splits(problem, lens_host, 0, wl.force_num_splits)
         ev_a[i].record()
-        fd.fd_decode_partial(problem, p, q, k, v, bt, lens_dev, ws)
+        fd.fd_decode_partial(problem, p, q, k, v, bt, lens_dev, ws, None, ks, vs)
         ev_b[i].record()
         fd.fd_combine(problem, p, lens_dev, ws, out, lse)
     end.record()
@@ -253,7 +258,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16" if wl.dtype == torch.float16 else "bf16",
+        "dtype": {torch.float16: "f16", torch.bfloat16: "bf16", torch.float8_e4m3fn: "fp8_e4m3"}[wl.kv_dtype],
         "data": "synthetic (seeded N(0,1) q/K/V; no dataset involved)",
         "config": {
             "workload": workload,

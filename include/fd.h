@@ -13,7 +13,8 @@
  * up to floating-point rounding.
  *
  * Layouts (all dense, row-major):
- *   q            [B, Hq, d] (q_len = 1) or [B, q_len, Hq, d], kv dtype
+ *   q            [B, Hq, d] (q_len = 1) or [B, q_len, Hq, d], in kv_dtype
+ *                (q_dtype for an FP8 cache)
  *   k, v         contiguous: [sum_b L_b, Hkv, d]; sequence b starts at token
  *                row sum_{b'<b} L_b' (a packed variable-length batch).
  *                paged (page_size 16): pools [P, 16, Hkv, d]; token t of
@@ -29,6 +30,12 @@
  *   Several query tokens per sequence (q_len > 1, the verification pass of
  *   speculative decoding, capstone §4.5) are the last q_len tokens of the
  *   cache: query i of sequence b attends to tokens 0 .. L_b - q_len + i.
+ *   An FP8 cache (kv_dtype FD_FP8_E4M3; FP8 attention with fp32 accumulation
+ *   and scaling factors is capstone §2.2's FA-3 paragraph) holds OCP E4M3
+ *   codes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+ *   infinities, NaN at S.1111.111, largest finite 448); element (t, g, i)
+ *   stands for k_scale[g] * e4m3(k[t, g, i]) (v likewise with v_scale), one
+ *   float32 scale per KV head, passed to the *_scaled calls.
  *
  * Ownership: the caller allocates every buffer (device memory for q, k, v,
  * block_table, seq_lens_dev, out, lse and the workspace; host memory for
@@ -72,22 +79,25 @@ typedef enum fd_status {
 typedef enum fd_dtype {
     FD_F16 = 0,
     FD_BF16 = 1,
-    FD_F32 = 2
+    FD_F32 = 2,
+    FD_FP8_E4M3 = 3            /* OCP E4M3 codes, KV cache only */
 } fd_dtype;
 
-/* The problem shape. q, k and v share `kv_dtype`. */
+/* The problem shape. q, k and v share `kv_dtype`, except that q of an FP8
+ * cache is in `q_dtype`. */
 typedef struct fd_problem {
     int32_t batch;             /* B >= 1 */
     int32_t num_q_heads;       /* Hq >= 1 */
     int32_t num_kv_heads;      /* Hkv >= 1, divides Hq; Hq/Hkv in {1, 2, 4, 8} */
     int32_t head_dim;          /* d in {64, 128} */
-    int32_t kv_dtype;          /* FD_F16 or FD_BF16 */
+    int32_t kv_dtype;          /* FD_F16, FD_BF16 or FD_FP8_E4M3 */
     int32_t out_dtype;         /* FD_F32, FD_F16 or FD_BF16 */
     float scale;               /* softmax scale; <= 0 selects 1/sqrt(d) */
     int32_t page_size;         /* 0 = contiguous packed cache, 16 = paged */
     int32_t max_pages_per_seq; /* paged: columns of block_table; ignored otherwise */
     int32_t q_len;             /* query tokens per sequence, 0 or 1 = one; q_len > 1 needs d = 128
                                   and q_len * Hq/Hkv <= 16, and every L_b >= q_len */
+    int32_t q_dtype;           /* FP8 cache: q's type, FD_F16 or FD_BF16; ignored otherwise */
 } fd_problem;
 
 /* How the splits are cut. Holds scalars only: nothing is uploaded per call,
@@ -98,7 +108,8 @@ typedef struct fd_plan {
     int32_t max_splits;        /* S_max = max_b ceil(L_b / C): workspace stride */
     int32_t total_splits;      /* sum_b ceil(L_b / C) */
     int32_t num_cus;           /* compute units the plan was sized for */
-    int32_t partial_kernel;    /* which partial kernel runs (0 = vector ALU, 1 = MFMA) */
+    int32_t partial_kernel;    /* which partial kernel runs (0 = vector ALU token rows, 1 = MFMA,
+                                  2 = vector ALU head rows) */
     int32_t reserved;
     int64_t total_tokens;      /* sum_b L_b */
     uint64_t workspace_bytes;  /* bytes the workspace must hold */
@@ -123,7 +134,7 @@ typedef struct fd_plan {
  * length (1 <= L_b, and L_b <= max_pages_per_seq * 16 when paged).
  * seq_lens_host: B lengths in host memory. out: receives the plan.
  * The environment variables FD_NUM_SPLITS (forces splits when the argument
- * is 0), FD_MIN_CHUNK, FD_WG_PER_CU (fixes k) and FD_PARTIAL_KERNEL (0 or 1)
+ * is 0), FD_MIN_CHUNK, FD_WG_PER_CU (fixes k) and FD_PARTIAL_KERNEL (0, 1 or 2)
  * override these choices for experiments.
  */
 fd_status fd_plan_splits(const fd_problem* problem, const int32_t* seq_lens_host,
@@ -148,11 +159,27 @@ fd_status fd_plan_splits(const fd_problem* problem, const int32_t* seq_lens_host
  *                                  natural-log units of the scaled score.
  * Entries of splits a sequence does not have are left untouched.
  * q, k, v, block_table (NULL when contiguous), seq_lens_dev: device pointers.
+ * q, k and v must be 16-byte aligned. An FP8 cache takes fd_decode_partial_scaled.
  */
 fd_status fd_decode_partial(const fd_problem* problem, const fd_plan* plan,
                             const void* q, const void* k, const void* v,
                             const int32_t* block_table, const int32_t* seq_lens_dev,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fd_decode_partial with per-KV-head dequantisation scales: the cache element
+ * (t, g, i) stands for k_scale[g] * k[t, g, i] (and v_scale[g] * v[t, g, i]).
+ * k_scale, v_scale: device float32 [Hkv], finite; NULL means all ones. The
+ * kernels fold k_scale[g] into the score scale and v_scale[g] into the
+ * split's O_s, so m_s, l_s and O_s are those of the dequantised cache.
+ * Required for kv_dtype FD_FP8_E4M3 (NULL scales are then allowed and mean
+ * the codes' own values); accepted for 16-bit caches too.
+ */
+fd_status fd_decode_partial_scaled(const fd_problem* problem, const fd_plan* plan,
+                                   const void* q, const void* k, const void* v,
+                                   const float* k_scale, const float* v_scale,
+                                   const int32_t* block_table, const int32_t* seq_lens_dev,
+                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Merge the partials (asynchronous on `stream`).
@@ -180,6 +207,15 @@ fd_status fd_decode_attention(const fd_problem* problem,
                               const int32_t* seq_lens_host, const int32_t* seq_lens_dev,
                               void* out, float* lse,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* fd_decode_attention with the per-KV-head scales of fd_decode_partial_scaled. */
+fd_status fd_decode_attention_scaled(const fd_problem* problem,
+                                     const void* q, const void* k, const void* v,
+                                     const float* k_scale, const float* v_scale,
+                                     const int32_t* block_table,
+                                     const int32_t* seq_lens_host, const int32_t* seq_lens_dev,
+                                     void* out, float* lse,
+                                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* A static, human-readable name for a status code. */
 const char* fd_status_string(fd_status status);

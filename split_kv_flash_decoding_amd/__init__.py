@@ -16,6 +16,7 @@ from ._capi import (  # noqa: F401
     FD_ERR_WORKSPACE_TOO_SMALL,
     FD_F16,
     FD_F32,
+    FD_FP8_E4M3,
     FD_OK,
     LIB_PATH,
     PROBE_SINK_FLOATS,

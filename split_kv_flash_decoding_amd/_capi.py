@@ -18,14 +18,16 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfd.so")
 
 FD_OK, FD_ERR_INVALID_ARGUMENT, FD_ERR_UNSUPPORTED, FD_ERR_WORKSPACE_TOO_SMALL, FD_ERR_HIP = range(5)
-FD_F16, FD_BF16, FD_F32 = range(3)
+FD_F16, FD_BF16, FD_F32, FD_FP8_E4M3 = range(4)
 
 # Every function fd.h declares; the CPU tests check the library exports them.
 EXPORTED = (
     "fd_plan_splits",
     "fd_decode_partial",
+    "fd_decode_partial_scaled",
     "fd_combine",
     "fd_decode_attention",
+    "fd_decode_attention_scaled",
     "fd_status_string",
     "fd_last_error_message",
     "fd_probe_read",
@@ -46,6 +48,7 @@ class FdProblem(ctypes.Structure):
         ("page_size", ctypes.c_int32),
         ("max_pages_per_seq", ctypes.c_int32),
         ("q_len", ctypes.c_int32),
+        ("q_dtype", ctypes.c_int32),
     ]
 
     @property
@@ -94,7 +97,11 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.fd_decode_partial.argtypes = [P, Pl, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.fd_combine.argtypes = [P, Pl, vp, vp, ctypes.c_size_t, vp, f32p, vp]
     lib.fd_decode_attention.argtypes = [P, vp, vp, vp, vp, i32p, vp, vp, f32p, vp, ctypes.c_size_t, vp]
-    for name in ("fd_plan_splits", "fd_decode_partial", "fd_combine", "fd_decode_attention"):
+    lib.fd_decode_partial_scaled.argtypes = [P, Pl, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.fd_decode_attention_scaled.argtypes = [P, vp, vp, vp, vp, vp, vp, i32p, vp, vp, f32p, vp,
+                                               ctypes.c_size_t, vp]
+    for name in ("fd_plan_splits", "fd_decode_partial", "fd_combine", "fd_decode_attention",
+                 "fd_decode_partial_scaled", "fd_decode_attention_scaled"):
         getattr(lib, name).restype = ctypes.c_int
     lib.fd_status_string.argtypes = [ctypes.c_int]
     lib.fd_status_string.restype = ctypes.c_char_p
@@ -124,7 +131,8 @@ def _check(status: int) -> None:
 def _dtype_code(dt) -> int:
     import torch
 
-    table = {torch.float16: FD_F16, torch.bfloat16: FD_BF16, torch.float32: FD_F32}
+    table = {torch.float16: FD_F16, torch.bfloat16: FD_BF16, torch.float32: FD_F32,
+             torch.float8_e4m3fn: FD_FP8_E4M3}
     if dt not in table:
         raise ValueError(f"unsupported dtype {dt}")
     return table[dt]
@@ -132,14 +140,18 @@ def _dtype_code(dt) -> int:
 
 def make_problem(*, batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int, kv_dtype,
                  out_dtype=None, scale: Optional[float] = None, page_size: int = 0,
-                 max_pages_per_seq: int = 0, q_len: int = 1) -> FdProblem:
+                 max_pages_per_seq: int = 0, q_len: int = 1, q_dtype=None) -> FdProblem:
+    """``kv_dtype``: the cache's torch dtype (float16, bfloat16 or
+    float8_e4m3fn); ``q_dtype``: q's dtype for an FP8 cache (default
+    float16)."""
     import torch
 
     return FdProblem(
         batch=batch, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
         kv_dtype=_dtype_code(kv_dtype), out_dtype=_dtype_code(out_dtype or torch.float32),
         scale=0.0 if scale is None else float(scale), page_size=page_size,
-        max_pages_per_seq=max_pages_per_seq, q_len=q_len)
+        max_pages_per_seq=max_pages_per_seq, q_len=q_len,
+        q_dtype=_dtype_code(q_dtype or torch.float16) if kv_dtype == torch.float8_e4m3fn else 0)
 
 
 def _q_shape(problem: FdProblem, d: int):
@@ -168,10 +180,12 @@ def _check_tensors(problem: FdProblem, q, k, v, block_table, seq_lens_dev, total
     import torch
 
     B, hq, hkv, d = problem.batch, problem.num_q_heads, problem.num_kv_heads, problem.head_dim
-    kvdt = {FD_F16: torch.float16, FD_BF16: torch.bfloat16}.get(problem.kv_dtype)
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if not t.is_cuda or not t.is_contiguous() or t.dtype != kvdt:
-            raise ValueError(f"{name} must be a contiguous {kvdt} CUDA tensor")
+    types = {FD_F16: torch.float16, FD_BF16: torch.bfloat16, FD_FP8_E4M3: torch.float8_e4m3fn}
+    kvdt = types.get(problem.kv_dtype)
+    qdt = types.get(problem.q_dtype if problem.kv_dtype == FD_FP8_E4M3 else problem.kv_dtype)
+    for name, t, dt in (("q", q, qdt), ("k", k, kvdt), ("v", v, kvdt)):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != dt:
+            raise ValueError(f"{name} must be a contiguous {dt} CUDA tensor")
     if tuple(q.shape) != _q_shape(problem, d):
         raise ValueError(f"q has shape {tuple(q.shape)}, expected {_q_shape(problem, d)}")
     if k.shape != v.shape:
@@ -202,10 +216,29 @@ def fd_plan_splits(problem: FdProblem, seq_lens_host, num_cus: int = 0, force_nu
     return plan
 
 
+def _check_scales(problem: FdProblem, k_scale, v_scale) -> None:
+    import torch
+
+    for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+        if t is not None and (not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous()
+                              or t.numel() != problem.num_kv_heads):
+            raise ValueError(f"{name} must be a contiguous float32 CUDA tensor with one entry per KV head")
+
+
 def fd_decode_partial(problem: FdProblem, plan: FdPlan, q, k, v, block_table, seq_lens_dev, workspace,
-                      stream=None) -> None:
+                      stream=None, k_scale=None, v_scale=None) -> None:
+    """fd_decode_partial, or fd_decode_partial_scaled when the cache is FP8 or
+    scales are given."""
     _check_tensors(problem, q, k, v, block_table, seq_lens_dev, plan.total_tokens)
-    _check(load_library().fd_decode_partial(
+    lib = load_library()
+    if problem.kv_dtype == FD_FP8_E4M3 or k_scale is not None or v_scale is not None:
+        _check_scales(problem, k_scale, v_scale)
+        _check(lib.fd_decode_partial_scaled(
+            ctypes.byref(problem), ctypes.byref(plan), _ptr(q), _ptr(k), _ptr(v), _ptr(k_scale), _ptr(v_scale),
+            _ptr(block_table), _ptr(seq_lens_dev), _ptr(workspace), workspace.numel() * workspace.element_size(),
+            _stream(stream)))
+        return
+    _check(lib.fd_decode_partial(
         ctypes.byref(problem), ctypes.byref(plan), _ptr(q), _ptr(k), _ptr(v), _ptr(block_table),
         _ptr(seq_lens_dev), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
 
@@ -228,11 +261,21 @@ def fd_combine(problem: FdProblem, plan: FdPlan, seq_lens_dev, workspace, out, l
 
 
 def fd_decode_attention(problem: FdProblem, q, k, v, block_table, seq_lens_host, seq_lens_dev, out, lse,
-                        workspace, stream=None) -> None:
+                        workspace, stream=None, k_scale=None, v_scale=None) -> None:
+    """fd_decode_attention, or fd_decode_attention_scaled when the cache is
+    FP8 or scales are given."""
     arr, vals = _lens_array(seq_lens_host)
     _check_tensors(problem, q, k, v, block_table, seq_lens_dev, sum(vals))
     _check_out(problem, out, lse)
-    _check(load_library().fd_decode_attention(
+    lib = load_library()
+    if problem.kv_dtype == FD_FP8_E4M3 or k_scale is not None or v_scale is not None:
+        _check_scales(problem, k_scale, v_scale)
+        _check(lib.fd_decode_attention_scaled(
+            ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
+            arr, _ptr(seq_lens_dev), _ptr(out), _ptr(lse), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream)))
+        return
+    _check(lib.fd_decode_attention(
         ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(block_table), arr, _ptr(seq_lens_dev),
         _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
 
@@ -261,11 +304,13 @@ def workspace_views(problem: FdProblem, plan: FdPlan, workspace):
 
 def decode_attention(q, k, v, seq_lens, *, block_table=None, page_size: int = 0, max_pages_per_seq: int = 0,
                      scale: Optional[float] = None, out_dtype=None, num_splits: int = 0, num_cus: int = 0,
-                     stream=None) -> DecodeResult:
+                     stream=None, k_scale=None, v_scale=None) -> DecodeResult:
     """Plan, partials and merge for one batch; allocates out, lse and the
     workspace with torch on q's device. ``seq_lens`` may be a CPU tensor or
     list. q is [B, Hq, d], or [B, q_len, Hq, d] for several query tokens per
-    sequence (the last q_len tokens of each cache, causal among themselves)."""
+    sequence (the last q_len tokens of each cache, causal among themselves).
+    k and v may be float8_e4m3fn codes with per-KV-head ``k_scale`` /
+    ``v_scale`` (float32 CUDA tensors [Hkv])."""
     import torch
 
     if q.dim() == 4:
@@ -273,7 +318,7 @@ def decode_attention(q, k, v, seq_lens, *, block_table=None, page_size: int = 0,
     else:
         (B, hq, d), q_len = q.shape, 1
     hkv = k.shape[-2]
-    problem = make_problem(batch=B, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, kv_dtype=q.dtype,
+    problem = make_problem(batch=B, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, kv_dtype=k.dtype, q_dtype=q.dtype,
                            out_dtype=out_dtype or torch.float32, scale=scale, page_size=page_size,
                            max_pages_per_seq=max_pages_per_seq or (block_table.shape[1] if block_table is not None else 0),
                            q_len=q_len)
@@ -293,7 +338,7 @@ def decode_attention(q, k, v, seq_lens, *, block_table=None, page_size: int = 0,
     oshape = _q_shape(problem, d)
     out = torch.empty(oshape, dtype=out_dtype or torch.float32, device=dev)
     lse = torch.empty(oshape[:-1], dtype=torch.float32, device=dev)
-    fd_decode_partial(problem, plan, q, k, v, block_table, lens_dev, ws, stream)
+    fd_decode_partial(problem, plan, q, k, v, block_table, lens_dev, ws, stream, k_scale, v_scale)
     fd_combine(problem, plan, lens_dev, ws, out, lse, stream)
     return DecodeResult(out=out, lse=lse, plan=plan, workspace=ws)
 

@@ -10,6 +10,8 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -28,7 +30,7 @@ SOURCES = ["fd_host.cpp", "fd_api.hip", "fd_partial_valu.hip", "fd_partial_mfma.
 HIP_FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
-    "-std=c++17",
+    "-std=c++20",
     "-fPIC",
     "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -43,11 +45,7 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (set HIPCC or install ROCm)")
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
-    cc = hipcc()
-    tmp = LIB_PATH + ".tmp"
-    cmd = [cc, *HIP_FLAGS, *(extra_flags or []), "-I", INCLUDE, "-I", CSRC, "-shared",
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -58,7 +56,25 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     warn = "\n".join(x for x in (res.stdout + res.stderr).splitlines() if noise not in x)
     if warn.strip() and verbose:
         sys.stderr.write(warn + "\n")
-    os.replace(tmp, LIB_PATH)
+
+
+def build(verbose: bool = False, extra_flags=None) -> str:
+    """Compile every source to an object (in parallel), link libfd.so, and
+    replace the library atomically."""
+    cc = hipcc()
+    objdir = tempfile.mkdtemp(prefix="fd_build_")
+    try:
+        objs = [os.path.join(objdir, s + ".o") for s in SOURCES]
+        cmds = [[cc, *HIP_FLAGS, *(extra_flags or []), "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, s),
+                 "-o", o] for s, o in zip(SOURCES, objs)]
+        with ThreadPoolExecutor(max(1, min(len(cmds), os.cpu_count() or 1))) as ex:
+            for f in [ex.submit(_run, c, verbose) for c in cmds]:
+                f.result()
+        tmp = LIB_PATH + ".tmp"
+        _run([cc, "--offload-arch=gfx950", "-shared", *objs, "-o", tmp], verbose)
+        os.replace(tmp, LIB_PATH)
+    finally:
+        shutil.rmtree(objdir, ignore_errors=True)
     return LIB_PATH
 
 

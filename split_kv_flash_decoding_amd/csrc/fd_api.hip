@@ -1,6 +1,6 @@
-// The C-ABI entry points that launch work (fd_decode_partial, fd_combine,
-// fd_decode_attention) and the compute-unit query the planner uses. Argument
-// checks run on the host before anything is enqueued.
+// The C-ABI entry points that launch work (fd_decode_partial[_scaled],
+// fd_combine, fd_decode_attention[_scaled]) and the compute-unit query the
+// planner uses. Argument checks run on the host before anything is enqueued.
 
 #include "fd_device.h"
 
@@ -24,16 +24,11 @@ fd_status query_num_cus(int32_t* out) {
     return FD_OK;
 }
 
-}  // namespace fd
+namespace {
 
-using namespace fd;
-
-extern "C" {
-
-fd_status fd_decode_partial(const fd_problem* p, const fd_plan* plan, const void* q, const void* k,
-                            const void* v, const int32_t* block_table, const int32_t* seq_lens_dev,
-                            void* workspace, size_t workspace_bytes_avail, void* stream) {
-    clear_error();
+fd_status decode_partial(const fd_problem* p, const fd_plan* plan, const void* q, const void* k, const void* v,
+                         const float* k_scale, const float* v_scale, const int32_t* block_table,
+                         const int32_t* seq_lens_dev, void* workspace, size_t workspace_bytes_avail, void* stream) {
     float scale = 0.f;
     fd_status st = check_problem(p, &scale);
     if (st != FD_OK) return st;
@@ -50,11 +45,17 @@ fd_status fd_decode_partial(const fd_problem* p, const fd_plan* plan, const void
         return fail(FD_ERR_INVALID_ARGUMENT, "q, k and v must be 16-byte aligned");
     if (reinterpret_cast<uintptr_t>(workspace) & 15)
         return fail(FD_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(k_scale) | reinterpret_cast<uintptr_t>(v_scale)) & 3)
+        return fail(FD_ERR_INVALID_ARGUMENT, "k_scale and v_scale must be 4-byte aligned");
 
     fdk::PartialArgs a;
     a.q = static_cast<const uint16_t*>(q);
-    a.k = static_cast<const uint16_t*>(k);
-    a.v = static_cast<const uint16_t*>(v);
+    a.k = k;
+    a.v = v;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.kv_dt = p->kv_dtype;
+    a.q_dt = q_dtype_of(p);
     a.table = block_table;
     a.lens = seq_lens_dev;
     a.ws_o = static_cast<float*>(workspace);
@@ -79,12 +80,45 @@ fd_status fd_decode_partial(const fd_problem* p, const fd_plan* plan, const void
     const bool paged = p->page_size != 0;
     hipError_t e;
     switch (plan->partial_kernel) {
-        case kPartialMfma: e = fdk::launch_partial_mfma(G, p->kv_dtype, paged, a, grid, hs); break;
-        case kPartialHeadRows: e = fdk::launch_partial_valu_heads(p->head_dim, G, p->kv_dtype, paged, a, grid, hs); break;
-        default: e = fdk::launch_partial_valu(p->head_dim, G, p->kv_dtype, paged, a, grid, hs); break;
+        case kPartialMfma: e = fdk::launch_partial_mfma(G, paged, a, grid, hs); break;
+        case kPartialHeadRows: e = fdk::launch_partial_valu_heads(p->head_dim, G, paged, a, grid, hs); break;
+        default: e = fdk::launch_partial_valu(p->head_dim, G, paged, a, grid, hs); break;
     }
     if (e != hipSuccess) return fail(FD_ERR_HIP, "partial kernel launch: %s", hipGetErrorString(e));
     return FD_OK;
+}
+
+fd_status reject_fp8(const fd_problem* p, const char* call) {
+    if (p && p->kv_dtype == FD_FP8_E4M3)
+        return fail(FD_ERR_INVALID_ARGUMENT, "an fp8 cache needs its scales: call %s_scaled", call);
+    return FD_OK;
+}
+
+}  // namespace
+
+}  // namespace fd
+
+using namespace fd;
+
+extern "C" {
+
+fd_status fd_decode_partial(const fd_problem* p, const fd_plan* plan, const void* q, const void* k,
+                            const void* v, const int32_t* block_table, const int32_t* seq_lens_dev,
+                            void* workspace, size_t workspace_bytes_avail, void* stream) {
+    clear_error();
+    fd_status st = reject_fp8(p, "fd_decode_partial");
+    if (st != FD_OK) return st;
+    return decode_partial(p, plan, q, k, v, nullptr, nullptr, block_table, seq_lens_dev, workspace,
+                          workspace_bytes_avail, stream);
+}
+
+fd_status fd_decode_partial_scaled(const fd_problem* p, const fd_plan* plan, const void* q, const void* k,
+                                   const void* v, const float* k_scale, const float* v_scale,
+                                   const int32_t* block_table, const int32_t* seq_lens_dev, void* workspace,
+                                   size_t workspace_bytes_avail, void* stream) {
+    clear_error();
+    return decode_partial(p, plan, q, k, v, k_scale, v_scale, block_table, seq_lens_dev, workspace,
+                          workspace_bytes_avail, stream);
 }
 
 fd_status fd_combine(const fd_problem* p, const fd_plan* plan, const int32_t* seq_lens_dev,
@@ -111,10 +145,10 @@ fd_status fd_combine(const fd_problem* p, const fd_plan* plan, const int32_t* se
     return FD_OK;
 }
 
-fd_status fd_decode_attention(const fd_problem* p, const void* q, const void* k, const void* v,
-                              const int32_t* block_table, const int32_t* seq_lens_host,
-                              const int32_t* seq_lens_dev, void* out, float* lse, void* workspace,
-                              size_t workspace_bytes_avail, void* stream) {
+fd_status fd_decode_attention_scaled(const fd_problem* p, const void* q, const void* k, const void* v,
+                                     const float* k_scale, const float* v_scale, const int32_t* block_table,
+                                     const int32_t* seq_lens_host, const int32_t* seq_lens_dev, void* out,
+                                     float* lse, void* workspace, size_t workspace_bytes_avail, void* stream) {
     fd_plan plan;
     fd_status st = fd_plan_splits(p, seq_lens_host, 0, 0, &plan);
     if (st != FD_OK) return st;
@@ -122,9 +156,21 @@ fd_status fd_decode_attention(const fd_problem* p, const void* q, const void* k,
     if (workspace_bytes_avail < plan.workspace_bytes)
         return fail(FD_ERR_WORKSPACE_TOO_SMALL, "workspace holds %zu bytes, the plan needs %llu",
                     workspace_bytes_avail, (unsigned long long)plan.workspace_bytes);
-    st = fd_decode_partial(p, &plan, q, k, v, block_table, seq_lens_dev, workspace, workspace_bytes_avail, stream);
+    st = fd_decode_partial_scaled(p, &plan, q, k, v, k_scale, v_scale, block_table, seq_lens_dev, workspace,
+                                  workspace_bytes_avail, stream);
     if (st != FD_OK) return st;
     return fd_combine(p, &plan, seq_lens_dev, workspace, workspace_bytes_avail, out, lse, stream);
+}
+
+fd_status fd_decode_attention(const fd_problem* p, const void* q, const void* k, const void* v,
+                              const int32_t* block_table, const int32_t* seq_lens_host,
+                              const int32_t* seq_lens_dev, void* out, float* lse, void* workspace,
+                              size_t workspace_bytes_avail, void* stream) {
+    clear_error();
+    fd_status st = reject_fp8(p, "fd_decode_attention");
+    if (st != FD_OK) return st;
+    return fd_decode_attention_scaled(p, q, k, v, nullptr, nullptr, block_table, seq_lens_host, seq_lens_dev, out,
+                                      lse, workspace, workspace_bytes_avail, stream);
 }
 
 }  // extern "C"

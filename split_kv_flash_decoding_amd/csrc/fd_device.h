@@ -33,7 +33,7 @@ constexpr int kWaves = FD_PARTIAL_WAVES;  // waves per partial work-group
 constexpr int kThreads = 64 * kWaves;
 constexpr int kUnroll = FD_PARTIAL_UNROLL;
 
-__device__ __forceinline__ u32x4 load16(const uint16_t* p) {
+__device__ __forceinline__ u32x4 load16(const void* p) {
 #if FD_PARTIAL_NT
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 #else
@@ -105,17 +105,74 @@ template <> struct Elt<FD_BF16> {
     }
 };
 
+// One 16-byte load of the cache, by cache element type KT and query type QT:
+// how many elements it holds, their dot product with this lane's query slice
+// (kQWords 16-byte words of QT) accumulated in fp32, and their fp32 values.
+template <int KT, int QT> struct KvLoad;
+
+template <int DT> struct KvLoad<DT, DT> {
+    static constexpr int kElems = 8;
+    static constexpr int kQWords = 1;
+    static __device__ __forceinline__ float dot(const u32x4* q, u32x4 k) { return Elt<DT>::dot8(q[0], k); }
+    static __device__ __forceinline__ void to_f32(u32x4 x, float* f) { Elt<DT>::to_f32(x, f); }
+};
+
+// OCP E4M3 codes (16 per load). Two codes at a time widen exactly to a
+// 16-bit pair (v_cvt_scalef32_pk_{f16,bf16}_fp8 with a unit scale) for the
+// packed dot product, or to two floats (v_cvt_pk_f32_fp8); on gfx950 both
+// decode every E4M3 code exactly (checked over all 256 codes on MI355X).
+// Word i of a load holds codes 4i .. 4i+3, lowest byte first.
+template <int QT> struct KvLoad<FD_FP8_E4M3, QT> {
+    static constexpr int kElems = 16;
+    static constexpr int kQWords = 2;
+    static __device__ __forceinline__ float dot(const u32x4* q, u32x4 k) {
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t w = k[i];
+            const uint32_t q0 = q[i >> 1][2 * (i & 1)];
+            const uint32_t q1 = q[i >> 1][2 * (i & 1) + 1];
+            if constexpr (QT == FD_F16) {
+                acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.f, false), as_half2(q0),
+                                             acc, false);
+                acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.f, true), as_half2(q1),
+                                             acc, false);
+            } else {
+                acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, false),
+                                                      as_bf162(q0), acc, false);
+                acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, true),
+                                                      as_bf162(q1), acc, false);
+            }
+        }
+        return acc;
+    }
+    static __device__ __forceinline__ void to_f32(u32x4 x, float* f) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t w = x[i];
+            const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+            const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+            f[4 * i] = lo[0];
+            f[4 * i + 1] = lo[1];
+            f[4 * i + 2] = hi[0];
+            f[4 * i + 3] = hi[1];
+        }
+    }
+};
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
-// Sum over each aligned group of LPR lanes (LPR in {8, 16}); every lane of the
-// group receives the sum.
+// Sum over each aligned group of LPR lanes (LPR in {4, 8, 16}); every lane of
+// the group receives the sum.
 template <int LPR>
 __device__ __forceinline__ float row_sum(float x) {
+    static_assert(LPR == 4 || LPR == 8 || LPR == 16, "row width");
     x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
     x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
+    if constexpr (LPR == 4) return x;
     x += dpp_mov<0x141>(x);  // row_half_mirror: the other quad of the 8
     if constexpr (LPR == 16) x += dpp_mov<0x140>(x);  // row_mirror: the other 8 of the 16
     return x;
@@ -208,26 +265,31 @@ __device__ inline bool locate_unit(int u, const int32_t* __restrict__ seq_lens, 
     return false;
 }
 
-// Arguments every partial kernel takes.
+// Arguments every partial kernel takes. q is 16-bit (q_dt); k and v hold
+// kv_dt elements; k_scale / v_scale are per-KV-head factors or NULL (1).
 struct PartialArgs {
     const uint16_t* q;
-    const uint16_t* k;
-    const uint16_t* v;
+    const void* k;
+    const void* v;
+    const float* k_scale;
+    const float* v_scale;
     const int32_t* table;
     const int32_t* lens;
     float* ws_o;
     float* ws_ml;
     int batch, hq, hkv, chunk, s_max, max_pages, q_len;
     float qk_scale_log2;
+    int kv_dt, q_dt;
 };
+
+// Scale of KV head g (1 when no scales are given).
+__device__ __forceinline__ float head_scale(const float* __restrict__ sc, int g) { return sc ? sc[g] : 1.f; }
 
 // Launchers (each defined in the file that holds its kernel). They enqueue on
 // `st` and return hipGetLastError().
-hipError_t launch_partial_valu(int D, int G, int dt, bool paged, const PartialArgs& a, dim3 grid,
-                               hipStream_t st);
-hipError_t launch_partial_valu_heads(int D, int G, int dt, bool paged, const PartialArgs& a, dim3 grid,
-                                     hipStream_t st);
-hipError_t launch_partial_mfma(int G, int dt, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st);
+hipError_t launch_partial_valu(int D, int G, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st);
+hipError_t launch_partial_valu_heads(int D, int G, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st);
+hipError_t launch_partial_mfma(int G, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st);
 hipError_t launch_combine(int D, int out_dt, const float* ws_o, const float* ws_ml, const int32_t* lens,
                           void* out, float* lse, int B, int hq, int chunk, int s_max, hipStream_t st);
 

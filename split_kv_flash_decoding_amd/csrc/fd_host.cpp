@@ -55,9 +55,11 @@ fd_status check_problem(const fd_problem* p, float* scale_out) {
         return fail(FD_ERR_UNSUPPORTED, "group size Hq/Hkv=%d not built (1, 2, 4, 8)", G);
     if (p->head_dim != 64 && p->head_dim != 128)
         return fail(FD_ERR_UNSUPPORTED, "head_dim %d not built (64, 128)", p->head_dim);
-    if (p->kv_dtype != FD_F16 && p->kv_dtype != FD_BF16)
+    if (p->kv_dtype != FD_F16 && p->kv_dtype != FD_BF16 && p->kv_dtype != FD_FP8_E4M3)
         return fail(p->kv_dtype == FD_F32 ? FD_ERR_UNSUPPORTED : FD_ERR_INVALID_ARGUMENT,
-                    "kv_dtype %d: fp16 or bf16 only", p->kv_dtype);
+                    "kv_dtype %d: fp16, bf16 or fp8 e4m3 only", p->kv_dtype);
+    if (p->kv_dtype == FD_FP8_E4M3 && p->q_dtype != FD_F16 && p->q_dtype != FD_BF16)
+        return fail(FD_ERR_INVALID_ARGUMENT, "q_dtype %d: an fp8 cache takes fp16 or bf16 queries", p->q_dtype);
     if (p->out_dtype != FD_F16 && p->out_dtype != FD_BF16 && p->out_dtype != FD_F32)
         return fail(FD_ERR_INVALID_ARGUMENT, "out_dtype %d unknown", p->out_dtype);
     if (p->page_size != 0 && p->page_size != kPageSize)

@@ -46,8 +46,14 @@ inline int32_t problem_q_len(const fd_problem* p) { return p->q_len > 1 ? p->q_l
 // Largest q_len * Hq/Hkv the matrix-core kernel handles (one 16-column MFMA tile).
 constexpr int32_t kMaxQueryRows = 16;
 
-// Token rows (head rows) one 16-byte wave-wide load covers: 64 / (d / 8).
-inline int32_t rows_per_load(const fd_problem* p) { return 64 / (p->head_dim / 8); }
+// Bytes of one cache element (2 for fp16/bf16, 1 for E4M3).
+inline int32_t kv_elem_bytes(const fd_problem* p) { return p->kv_dtype == FD_FP8_E4M3 ? 1 : 2; }
+// q's element type: the cache's, or q_dtype for an FP8 cache.
+inline int32_t q_dtype_of(const fd_problem* p) { return p->kv_dtype == FD_FP8_E4M3 ? p->q_dtype : p->kv_dtype; }
+
+// Token rows (head rows) one 16-byte wave-wide load covers: 64 lanes over
+// d * bytes / 16 lanes per row.
+inline int32_t rows_per_load(const fd_problem* p) { return 64 / (p->head_dim * kv_elem_bytes(p) / 16); }
 
 // Whether the matrix-core partial kernel covers this problem: d = 128 and
 // 2 <= q_len * Hq/Hkv <= 16 query rows per KV head.

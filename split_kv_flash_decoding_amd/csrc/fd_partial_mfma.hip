@@ -1,6 +1,7 @@
 // Partial kernel, matrix-core form: every K/V row serves nq = q_len * G query
 // rows (G query heads per KV head, q_len query tokens per sequence),
-// 2 <= nq <= 16; d = 128, fp16/bf16 K/V, contiguous or paged.
+// 2 <= nq <= 16; d = 128, fp16/bf16 K/V or FP8 (E4M3) K/V with per-head
+// scales, contiguous or paged.
 //
 // With G query heads sharing one KV head, each K row meets G queries and each
 // V row is weighted by G probabilities: both products are small dense
@@ -39,6 +40,11 @@
 //     padded rows) and read back transposed with ds_read_b64_tr_b16, so
 //     every lane's output column is its own head and the per-head rescale
 //     needs no cross-lane traffic;
+//   * an FP8 cache has 128-byte rows: one load instruction covers eight
+//     rows, and the codes are widened exactly to the query's 16-bit type on
+//     their way into LDS, so the matrix products are those of a 16-bit cache;
+//     the K scale of the head joins the score scale and its V scale the
+//     split's output;
 //   * K/V loads are buffer loads from a per-tile scalar base with fixed
 //     per-lane offsets (no per-load address arithmetic); the descriptor's
 //     size ends at the split's last row, so rows past it read as zeros;
@@ -126,14 +132,32 @@ __device__ __forceinline__ i16x4_t lds_read_transposed(const uint16_t* p) {
 // nq..NQ-1 and 16-NQ..15 of the MFMA tile are idle. PAGE_MODE: 0 contiguous
 // cache; 1 paged, any split alignment (a table lookup per token); 2 paged,
 // splits start on page boundaries.
-template <int NQ, int DT, int PAGE_MODE>
-__global__ __launch_bounds__(64 * kMW) void partial_mfma(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens, float* __restrict__ ws_o,
-    float* __restrict__ ws_ml, int batch, int hq, int hkv, int chunk, int s_max, int max_pages, int q_len,
-    float qk_scale_log2) {
-    using M = Mfma<DT>;
+// Two codes of an E4M3 word (the low or high half) widened to a 16-bit pair.
+template <int QT, bool HIGH>
+__device__ __forceinline__ uint32_t widen_fp8_pair(uint32_t w) {
+    if constexpr (QT == FD_F16)
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.f, HIGH));
+    else
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, HIGH));
+}
+
+// NQ: as above. KT: cache element type (QT, or FP8 E4M3); QT: q's 16-bit
+// type, which the matrix products use.
+template <int NQ, int KT, int QT, int PAGE_MODE>
+__global__ __launch_bounds__(64 * kMW) void partial_mfma(const PartialArgs a) {
+    using M = Mfma<QT>;
     constexpr bool PAGED = PAGE_MODE != 0;
+    constexpr bool FP8 = KT == FD_FP8_E4M3;
+    constexpr int EB = FP8 ? 1 : 2;   // bytes per cache element
+    constexpr int RPI = FP8 ? 8 : 4;  // token rows per wave-wide 16-byte load
+    constexpr int KL = kTile / RPI;   // loads of K (and of V) per tile
+    const uint16_t* __restrict__ q = a.q;
+    const int32_t* __restrict__ block_table = a.table;
+    const int32_t* __restrict__ seq_lens = a.lens;
+    float* __restrict__ ws_o = a.ws_o;
+    float* __restrict__ ws_ml = a.ws_ml;
+    const int batch = a.batch, hq = a.hq, hkv = a.hkv, chunk = a.chunk, s_max = a.s_max, max_pages = a.max_pages;
+    const int q_len = a.q_len;
     __shared__ __attribute__((aligned(16))) uint16_t sk[kMW][kTile * kPitch];
     __shared__ __attribute__((aligned(16))) uint16_t sv[kMW][kTile * kPitch];
     __shared__ float sm_o[kMW][NQ][kD];
@@ -160,9 +184,10 @@ __global__ __launch_bounds__(64 * kMW) void partial_mfma(
     const int lim = min(t1, wu.L - q_len + qi + 1);
 
     const int32_t* table = PAGED ? block_table + (int64_t)b * max_pages : nullptr;
-    const int64_t row_stride = (int64_t)hkv * kD;
-    const uint16_t* kbase = k + (int64_t)g * kD;
-    const uint16_t* vbase = v + (int64_t)g * kD;
+    const int row_bytes = hkv * kD * EB;
+    const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + (int64_t)g * kD * EB;
+    const uint8_t* vbase = static_cast<const uint8_t*>(a.v) + (int64_t)g * kD * EB;
+    const float qk_scale_log2 = a.qk_scale_log2 * head_scale(a.k_scale, g);
 
     // Q^T as the B operand of the score MFMAs: lane l holds, for d-block j,
     // dims 32 j + 8 grp .. +8 of query row col; rows past nq-1 are zero.
@@ -188,12 +213,13 @@ __global__ __launch_bounds__(64 * kMW) void partial_mfma(
     const int ntiles = (t1 - t0 + kTile - 1) / kTile;
     uint16_t* my_sk = sk[wave];
     uint16_t* my_sv = sv[wave];
-    const int row_bytes = hkv * kD * 2;
-    // Byte offsets of this lane's K and V loads inside a tile (row r of the
-    // tile is at r * row_bytes): rows 4 i + grp, dims 8 col .. +8.
-    int voff_v[4];
+    // This lane's part of a tile load: row RPI i + lrow, bytes 16 lcol .. +16
+    // (dims 8 lcol .. +8 of a 16-bit row, 16 lcol .. +16 of an FP8 row).
+    const int lrow = lane / (64 / RPI);
+    const int lcol = lane % (64 / RPI);
+    int voff_v[KL];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) voff_v[i] = (4 * i + grp) * row_bytes + 16 * col;
+    for (int i = 0; i < KL; ++i) voff_v[i] = (RPI * i + lrow) * row_bytes + 16 * lcol;
 
     auto row_of = [&](int t) -> int64_t {
         if constexpr (PAGED) {
@@ -221,18 +247,18 @@ __global__ __launch_bounds__(64 * kMW) void partial_mfma(
         if constexpr (PAGE_MODE == 1) {
             // Pages may start mid-tile: one table lookup per row, clamped to the split.
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t row = row_of(min(tt + 4 * i + grp, t1 - 1)) * row_stride;
-                kr[i] = load16(kbase + row + 8 * col);
-                vr[i] = load16(vbase + row + 8 * col);
+            for (int i = 0; i < KL; ++i) {
+                const int64_t row = row_of(min(tt + RPI * i + lrow, t1 - 1)) * row_bytes;
+                kr[i] = load16(kbase + row + 16 * lcol);
+                vr[i] = load16(vbase + row + 16 * lcol);
             }
         } else {
             const int64_t first = (PAGE_MODE == 2) ? tile_page(tile) : row0 + tt;
             const int bytes = min(kTile, t1 - tt) * row_bytes;
-            const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + first * row_stride, bytes);
-            const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + first * row_stride, bytes);
+            const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + first * row_bytes, bytes);
+            const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + first * row_bytes, bytes);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < KL; ++i) {
                 kr[i] = buffer_load16(rk, voff_v[i]);
                 vr[i] = buffer_load16(rv, voff_v[i]);
             }
@@ -241,11 +267,33 @@ __global__ __launch_bounds__(64 * kMW) void partial_mfma(
 
     auto compute = [&](int tile, const u32x4* kr, const u32x4* vr) {
         const int tt = t0 + tile * kTile;
-        // Stage the K and V tiles: row 4 i + grp, dims 8 col .. +8.
+        // Stage the K and V tiles as 16-bit rows: row RPI i + lrow.
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            *reinterpret_cast<u32x4*>(my_sk + (4 * i + grp) * kPitch + 8 * col) = kr[i];
-            *reinterpret_cast<u32x4*>(my_sv + (4 * i + grp) * kPitch + 8 * col) = vr[i];
+        for (int i = 0; i < KL; ++i) {
+            if constexpr (FP8) {
+                // codes 4 w .. 4 w + 3 sit in word w; dims 16 lcol .. +16
+                u32x4 klo, khi, vlo, vhi;
+#pragma unroll
+                for (int w = 0; w < 2; ++w) {
+                    klo[2 * w] = widen_fp8_pair<QT, false>(kr[i][w]);
+                    klo[2 * w + 1] = widen_fp8_pair<QT, true>(kr[i][w]);
+                    khi[2 * w] = widen_fp8_pair<QT, false>(kr[i][w + 2]);
+                    khi[2 * w + 1] = widen_fp8_pair<QT, true>(kr[i][w + 2]);
+                    vlo[2 * w] = widen_fp8_pair<QT, false>(vr[i][w]);
+                    vlo[2 * w + 1] = widen_fp8_pair<QT, true>(vr[i][w]);
+                    vhi[2 * w] = widen_fp8_pair<QT, false>(vr[i][w + 2]);
+                    vhi[2 * w + 1] = widen_fp8_pair<QT, true>(vr[i][w + 2]);
+                }
+                uint16_t* dk = my_sk + (RPI * i + lrow) * kPitch + 16 * lcol;
+                uint16_t* dv = my_sv + (RPI * i + lrow) * kPitch + 16 * lcol;
+                *reinterpret_cast<u32x4*>(dk) = klo;
+                *reinterpret_cast<u32x4*>(dk + 8) = khi;
+                *reinterpret_cast<u32x4*>(dv) = vlo;
+                *reinterpret_cast<u32x4*>(dv + 8) = vhi;
+            } else {
+                *reinterpret_cast<u32x4*>(my_sk + (RPI * i + lrow) * kPitch + 8 * lcol) = kr[i];
+                *reinterpret_cast<u32x4*>(my_sv + (RPI * i + lrow) * kPitch + 8 * lcol) = vr[i];
+            }
         }
 
         // A operand of d-block j: K row col, dims 32 j + 8 grp .. +8.
@@ -304,7 +352,7 @@ __global__ __launch_bounds__(64 * kMW) void partial_mfma(
 #if FD_MFMA_DEPTH == 3
     // Three-deep ring: tiles tile+kMW and tile+2*kMW are in flight while
     // `tile` is computed.
-    u32x4 ka[4], va[4], kb[4], vb[4], kc[4], vc[4];
+    u32x4 ka[KL], va[KL], kb[KL], vb[KL], kc[KL], vc[KL];
     int tile = wave;
     if (tile < ntiles) load(tile, ka, va);
     if (tile + kMW < ntiles) load(tile + kMW, kb, vb);
@@ -323,7 +371,7 @@ __global__ __launch_bounds__(64 * kMW) void partial_mfma(
     }
 #else
     // Two-deep ring: tile+kMW is in flight while `tile` is computed.
-    u32x4 ka[4], va[4], kb[4], vb[4];
+    u32x4 ka[KL], va[KL], kb[KL], vb[KL];
     int tile = wave;
     if (tile < ntiles) load(tile, ka, va);
     while (tile < ntiles) {
@@ -362,6 +410,7 @@ __global__ __launch_bounds__(64 * kMW) void partial_mfma(
         }
     }
     __syncthreads();
+    const float v_sc = head_scale(a.v_scale, g);
     for (int idx = threadIdx.x; idx < nq * kD; idx += 64 * kMW) {
         const int n = idx / kD;
         const int d = idx % kD;
@@ -379,7 +428,7 @@ __global__ __launch_bounds__(64 * kMW) void partial_mfma(
         const int ni = n / G;
         const int64_t row = ((int64_t)b * q_len + ni) * hq + g * G + (n - ni * G);
         const int64_t slot = row * s_max + s;
-        ws_o[slot * kD + d] = o;
+        ws_o[slot * kD + d] = o * v_sc;
         if (d == 0) {
             ws_ml[slot * 2] = Mx * kLn2;
             ws_ml[slot * 2 + 1] = lsum;
@@ -387,31 +436,33 @@ __global__ __launch_bounds__(64 * kMW) void partial_mfma(
     }
 }
 
-template <int NQ, int DT, int MODE>
-hipError_t launch_mode(const PartialArgs& a, dim3 grid, hipStream_t st) {
-    hipLaunchKernelGGL((partial_mfma<NQ, DT, MODE>), grid, dim3(64 * kMW), 0, st, a.q, a.k, a.v, a.table, a.lens,
-                       a.ws_o, a.ws_ml, a.batch, a.hq, a.hkv, a.chunk, a.s_max, a.max_pages, a.q_len,
-                       a.qk_scale_log2);
+template <int NQ, int KT, int QT>
+hipError_t launch_nq(bool paged, const PartialArgs& a, dim3 grid, hipStream_t st) {
+    // Paged splits that start on page boundaries read their page indices 64 at a time.
+    if (!paged)
+        hipLaunchKernelGGL((partial_mfma<NQ, KT, QT, 0>), grid, dim3(64 * kMW), 0, st, a);
+    else if (a.chunk % 16 == 0)
+        hipLaunchKernelGGL((partial_mfma<NQ, KT, QT, 2>), grid, dim3(64 * kMW), 0, st, a);
+    else
+        hipLaunchKernelGGL((partial_mfma<NQ, KT, QT, 1>), grid, dim3(64 * kMW), 0, st, a);
     return hipGetLastError();
 }
 
-template <int NQ, int DT>
-hipError_t launch_nq(bool paged, const PartialArgs& a, dim3 grid, hipStream_t st) {
-    if (!paged) return launch_mode<NQ, DT, 0>(a, grid, st);
-    return (a.chunk % 16 == 0) ? launch_mode<NQ, DT, 2>(a, grid, st) : launch_mode<NQ, DT, 1>(a, grid, st);
+template <int KT, int QT>
+hipError_t launch_types(int nq, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st) {
+    if (nq <= 2) return launch_nq<2, KT, QT>(paged, a, grid, st);
+    if (nq <= 4) return launch_nq<4, KT, QT>(paged, a, grid, st);
+    if (nq <= 8) return launch_nq<8, KT, QT>(paged, a, grid, st);
+    return launch_nq<16, KT, QT>(paged, a, grid, st);
 }
 
-template <int DT>
-hipError_t launch_dt(int nq, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st) {
-    if (nq <= 2) return launch_nq<2, DT>(paged, a, grid, st);
-    if (nq <= 4) return launch_nq<4, DT>(paged, a, grid, st);
-    if (nq <= 8) return launch_nq<8, DT>(paged, a, grid, st);
-    return launch_nq<16, DT>(paged, a, grid, st);
-}
-
-hipError_t launch_partial_mfma(int G, int dt, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st) {
+hipError_t launch_partial_mfma(int G, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st) {
     const int nq = G * a.q_len;
-    return dt == FD_F16 ? launch_dt<FD_F16>(nq, paged, a, grid, st) : launch_dt<FD_BF16>(nq, paged, a, grid, st);
+    if (a.kv_dt == FD_FP8_E4M3)
+        return a.q_dt == FD_F16 ? launch_types<FD_FP8_E4M3, FD_F16>(nq, paged, a, grid, st)
+                                : launch_types<FD_FP8_E4M3, FD_BF16>(nq, paged, a, grid, st);
+    return a.kv_dt == FD_F16 ? launch_types<FD_F16, FD_F16>(nq, paged, a, grid, st)
+                             : launch_types<FD_BF16, FD_BF16>(nq, paged, a, grid, st);
 }
 
 }  // namespace fdk

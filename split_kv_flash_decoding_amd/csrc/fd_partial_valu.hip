@@ -1,6 +1,6 @@
 // Partial kernel, vector-ALU form: per-split online softmax for any group
-// size G (query heads per KV head), d in {64, 128}, fp16/bf16 K/V, contiguous
-// or paged cache.
+// size G (query heads per KV head), d in {64, 128}, fp16/bf16 or FP8 (E4M3)
+// K/V with per-head scales, contiguous or paged cache.
 //
 // The method: a single query token per sequence attends over a long KV cache
 // that is cut along the token axis into splits; every split computes its local
@@ -12,9 +12,11 @@
 //
 // One work-group of kWaves wave64s per (sequence, KV head, split), taken from
 // the longest-first work list (locate_unit):
-//   * a token row of one KV head is d fp16/bf16 values = d/8 lanes x 16 bytes,
-//     so one wave-wide 16-byte load covers 64/(d/8) consecutive tokens
-//     (4 at d = 128, 8 at d = 64); each wave streams U such loads of K and U
+//   * a token row of one KV head is d fp16/bf16 values = d/8 lanes x 16 bytes
+//     (d/16 lanes for FP8), so one wave-wide 16-byte load covers 64/(d/8)
+//     consecutive tokens (4 at d = 128, 8 at d = 64; twice that for FP8,
+//     whose codes widen exactly to the query's 16-bit type before the dot
+//     product and to fp32 before the P.V update); each wave streams U such loads of K and U
 //     of V per stage and issues the next stage's loads before it computes on
 //     the current one (double buffering in registers: the data is used once,
 //     so it never needs a trip through LDS); the loads carry the non-temporal
@@ -36,17 +38,24 @@
 
 namespace fdk {
 
-template <int D, int G, int DT, bool PAGED>
-__global__ __launch_bounds__(kThreads) void partial_valu(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
-    float* __restrict__ ws_o, float* __restrict__ ws_ml, int batch, int hq, int hkv, int chunk, int s_max,
-    int max_pages, float qk_scale_log2) {
-    constexpr int LPR = D / 8;       // lanes per token row
+template <int D, int G, int KT, int QT, bool PAGED>
+__global__ __launch_bounds__(kThreads) void partial_valu(const PartialArgs a) {
+    using KV = KvLoad<KT, QT>;
+    constexpr int EPL = KV::kElems;  // elements per 16-byte load
+    constexpr int EB = 16 / EPL;     // bytes per element
+    constexpr int LPR = D / EPL;     // lanes per token row
     constexpr int RPW = 64 / LPR;    // token rows per wave-wide load
     constexpr int U = kUnroll;       // loads of K (and of V) per stage
     constexpr int TPW = U * RPW;     // tokens per wave stage
-    using E = Elt<DT>;
+    constexpr int QW = KV::kQWords;
+    const uint16_t* __restrict__ q = a.q;
+    const uint8_t* __restrict__ k = static_cast<const uint8_t*>(a.k);
+    const uint8_t* __restrict__ v = static_cast<const uint8_t*>(a.v);
+    const int32_t* __restrict__ block_table = a.table;
+    const int32_t* __restrict__ seq_lens = a.lens;
+    float* __restrict__ ws_o = a.ws_o;
+    float* __restrict__ ws_ml = a.ws_ml;
+    const int batch = a.batch, hq = a.hq, hkv = a.hkv, chunk = a.chunk, s_max = a.s_max, max_pages = a.max_pages;
 
     WorkUnit wu;
     if (!locate_unit(blockIdx.x, seq_lens, batch, hkv, chunk, PAGED ? max_pages * 16 : INT32_MAX, wu)) return;
@@ -60,7 +69,8 @@ __global__ __launch_bounds__(kThreads) void partial_valu(
     const int c = lane % LPR;
 
     const int32_t* table = PAGED ? block_table + (int64_t)b * max_pages : nullptr;
-    const int64_t head_off = (int64_t)g * D + c * 8;
+    const int64_t head_off = (int64_t)g * D * EB + c * 16;  // bytes
+    const float qk_scale_log2 = a.qk_scale_log2 * head_scale(a.k_scale, g);
 
     auto row_offset = [&](int t) -> int64_t {
         int64_t row;
@@ -69,22 +79,24 @@ __global__ __launch_bounds__(kThreads) void partial_valu(
         } else {
             row = row0 + t;
         }
-        return row * hkv * D + head_off;
+        return row * hkv * D * EB + head_off;
     };
 
     // This lane's slice of the G query heads of KV head g.
-    u32x4 qv[G];
+    u32x4 qv[G][QW];
 #pragma unroll
     for (int j = 0; j < G; ++j)
-        qv[j] = *reinterpret_cast<const u32x4*>(q + ((int64_t)b * hq + g * G + j) * D + c * 8);
+#pragma unroll
+        for (int w = 0; w < QW; ++w)
+            qv[j][w] = *reinterpret_cast<const u32x4*>(q + ((int64_t)b * hq + g * G + j) * D + c * EPL + 8 * w);
 
-    float m[G], l[G], o[G][8];
+    float m[G], l[G], o[G][EPL];
 #pragma unroll
     for (int j = 0; j < G; ++j) {
         m[j] = neg_inf();
         l[j] = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
+        for (int e = 0; e < EPL; ++e) o[j][e] = 0.f;
     }
 
     const int ntok = t1 - t0;
@@ -108,13 +120,13 @@ __global__ __launch_bounds__(kThreads) void partial_valu(
             const bool valid = (t0 + tile * TPW + u * RPW + r) < t1;
 #pragma unroll
             for (int j = 0; j < G; ++j) {
-                const float dot = row_sum<LPR>(E::dot8(qv[j], kb[u]));
+                const float dot = row_sum<LPR>(KV::dot(qv[j], kb[u]));
                 sc[u][j] = valid ? dot * qk_scale_log2 : neg_inf();
             }
         }
-        float vf[U][8];
+        float vf[U][EPL];
 #pragma unroll
-        for (int u = 0; u < U; ++u) E::to_f32(vb[u], vf[u]);
+        for (int u = 0; u < U; ++u) KV::to_f32(vb[u], vf[u]);
 #pragma unroll
         for (int j = 0; j < G; ++j) {
             float mx = sc[0][j];
@@ -132,7 +144,7 @@ __global__ __launch_bounds__(kThreads) void partial_valu(
             }
             l[j] = l[j] * alpha + ps;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
+            for (int e = 0; e < EPL; ++e) {
                 float acc = o[j][e] * alpha;
 #pragma unroll
                 for (int u = 0; u < U; ++u) acc = fmaf(p[u], vf[u][e], acc);
@@ -162,12 +174,12 @@ __global__ __launch_bounds__(kThreads) void partial_valu(
     for (int off = LPR; off < 64; off <<= 1) {
 #pragma unroll
         for (int j = 0; j < G; ++j) {
-            float o2[8];
+            float o2[EPL];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o2[e] = __shfl_xor(o[j][e], off);
+            for (int e = 0; e < EPL; ++e) o2[e] = __shfl_xor(o[j][e], off);
             const float m2 = __shfl_xor(m[j], off);
             const float l2 = __shfl_xor(l[j], off);
-            merge_stats<8>(m[j], l[j], o[j], m2, l2, o2);
+            merge_stats<EPL>(m[j], l[j], o[j], m2, l2, o2);
         }
     }
 
@@ -179,7 +191,7 @@ __global__ __launch_bounds__(kThreads) void partial_valu(
 #pragma unroll
         for (int j = 0; j < G; ++j) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sm_o[wave][j][c * 8 + e] = o[j][e];
+            for (int e = 0; e < EPL; ++e) sm_o[wave][j][c * EPL + e] = o[j][e];
             if (c == 0) {
                 sm_m[wave][j] = m[j];
                 sm_l[wave][j] = l[j];
@@ -187,6 +199,7 @@ __global__ __launch_bounds__(kThreads) void partial_valu(
         }
     }
     __syncthreads();
+    const float v_sc = head_scale(a.v_scale, g);
     for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
         const int j = idx / D;
         const int col = idx % D;
@@ -203,7 +216,7 @@ __global__ __launch_bounds__(kThreads) void partial_valu(
         }
         const int h = g * G + j;
         const int64_t slot = ((int64_t)b * hq + h) * s_max + s;
-        ws_o[slot * D + col] = acc;
+        ws_o[slot * D + col] = acc * v_sc;
         if (col == 0) {
             ws_ml[slot * 2] = M * kLn2;
             ws_ml[slot * 2 + 1] = lsum;
@@ -223,17 +236,22 @@ __global__ __launch_bounds__(kThreads) void partial_valu(
 // Requires Hkv % RPW == 0. PAGE_MODE: 0 contiguous, 1 paged (a table lookup
 // per token), 2 paged with page-aligned splits and U dividing 16 (page
 // indices fetched 64 at a time and read with readlane).
-template <int D, int G, int DT, int PAGE_MODE>
-__global__ __launch_bounds__(kThreads) void partial_valu_heads(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
-    float* __restrict__ ws_o, float* __restrict__ ws_ml, int batch, int hq, int hkv, int chunk, int s_max,
-    int max_pages, float qk_scale_log2) {
-    constexpr int LPR = D / 8;     // lanes per head row
-    constexpr int RPW = 64 / LPR;  // heads per work-group
-    constexpr int U = kUnroll;     // tokens per wave stage
+template <int D, int G, int KT, int QT, int PAGE_MODE>
+__global__ __launch_bounds__(kThreads) void partial_valu_heads(const PartialArgs a) {
+    using KV = KvLoad<KT, QT>;
+    constexpr int EPL = KV::kElems;  // elements per 16-byte load
+    constexpr int EB = 16 / EPL;     // bytes per element
+    constexpr int LPR = D / EPL;     // lanes per head row
+    constexpr int RPW = 64 / LPR;    // heads per work-group
+    constexpr int U = kUnroll;       // tokens per wave stage
+    constexpr int QW = KV::kQWords;
     constexpr bool PAGED = PAGE_MODE != 0;
-    using E = Elt<DT>;
+    const uint16_t* __restrict__ q = a.q;
+    const int32_t* __restrict__ block_table = a.table;
+    const int32_t* __restrict__ seq_lens = a.lens;
+    float* __restrict__ ws_o = a.ws_o;
+    float* __restrict__ ws_ml = a.ws_ml;
+    const int batch = a.batch, hq = a.hq, hkv = a.hkv, chunk = a.chunk, s_max = a.s_max, max_pages = a.max_pages;
 
     WorkUnit wu;
     if (!locate_unit(blockIdx.x, seq_lens, batch, hkv / RPW, chunk, PAGED ? max_pages * 16 : INT32_MAX, wu)) return;
@@ -248,22 +266,25 @@ __global__ __launch_bounds__(kThreads) void partial_valu_heads(
     const int g = wu.g * RPW + r;  // this row's KV head
 
     const int32_t* table = PAGED ? block_table + (int64_t)b * max_pages : nullptr;
-    const int64_t row_stride = (int64_t)hkv * D;
-    const uint16_t* kl = k + (int64_t)g * D + c * 8;
-    const uint16_t* vl = v + (int64_t)g * D + c * 8;
+    const int64_t row_stride = (int64_t)hkv * D * EB;  // bytes
+    const uint8_t* kl = static_cast<const uint8_t*>(a.k) + (int64_t)g * D * EB + c * 16;
+    const uint8_t* vl = static_cast<const uint8_t*>(a.v) + (int64_t)g * D * EB + c * 16;
+    const float qk_scale_log2 = a.qk_scale_log2 * head_scale(a.k_scale, g);
 
-    u32x4 qv[G];
+    u32x4 qv[G][QW];
 #pragma unroll
     for (int j = 0; j < G; ++j)
-        qv[j] = *reinterpret_cast<const u32x4*>(q + ((int64_t)b * hq + g * G + j) * D + c * 8);
+#pragma unroll
+        for (int w = 0; w < QW; ++w)
+            qv[j][w] = *reinterpret_cast<const u32x4*>(q + ((int64_t)b * hq + g * G + j) * D + c * EPL + 8 * w);
 
-    float m[G], l[G], o[G][8];
+    float m[G], l[G], o[G][EPL];
 #pragma unroll
     for (int j = 0; j < G; ++j) {
         m[j] = neg_inf();
         l[j] = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
+        for (int e = 0; e < EPL; ++e) o[j][e] = 0.f;
     }
 
     const int nstages = (t1 - t0 + U - 1) / U;
@@ -309,13 +330,13 @@ __global__ __launch_bounds__(kThreads) void partial_valu_heads(
             const bool valid = ts + u < t1;
 #pragma unroll
             for (int j = 0; j < G; ++j) {
-                const float dot = row_sum<LPR>(E::dot8(qv[j], kb[u]));
+                const float dot = row_sum<LPR>(KV::dot(qv[j], kb[u]));
                 sc[u][j] = valid ? dot * qk_scale_log2 : neg_inf();
             }
         }
-        float vf[U][8];
+        float vf[U][EPL];
 #pragma unroll
-        for (int u = 0; u < U; ++u) E::to_f32(vb[u], vf[u]);
+        for (int u = 0; u < U; ++u) KV::to_f32(vb[u], vf[u]);
 #pragma unroll
         for (int j = 0; j < G; ++j) {
             float mx = sc[0][j];
@@ -333,7 +354,7 @@ __global__ __launch_bounds__(kThreads) void partial_valu_heads(
             }
             l[j] = l[j] * alpha + ps;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
+            for (int e = 0; e < EPL; ++e) {
                 float acc = o[j][e] * alpha;
 #pragma unroll
                 for (int u = 0; u < U; ++u) acc = fmaf(p[u], vf[u][e], acc);
@@ -365,7 +386,7 @@ __global__ __launch_bounds__(kThreads) void partial_valu_heads(
 #pragma unroll
     for (int j = 0; j < G; ++j) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sm_o[wave][r][j][c * 8 + e] = o[j][e];
+        for (int e = 0; e < EPL; ++e) sm_o[wave][r][j][c * EPL + e] = o[j][e];
         if (c == 0) {
             sm_m[wave][r][j] = m[j];
             sm_l[wave][r][j] = l[j];
@@ -389,7 +410,7 @@ __global__ __launch_bounds__(kThreads) void partial_valu_heads(
         }
         const int h = (wu.g * RPW + rr) * G + j;
         const int64_t slot = ((int64_t)b * hq + h) * s_max + s;
-        ws_o[slot * D + col] = acc;
+        ws_o[slot * D + col] = acc * head_scale(a.v_scale, wu.g * RPW + rr);
         if (col == 0) {
             ws_ml[slot * 2] = M * kLn2;
             ws_ml[slot * 2 + 1] = lsum;
@@ -399,65 +420,58 @@ __global__ __launch_bounds__(kThreads) void partial_valu_heads(
 
 // ------------------------------------------------------------------ dispatch
 
-template <int D, int G, int DT, bool PAGED>
-hipError_t launch_partial(const PartialArgs& a, dim3 grid, hipStream_t st) {
-    hipLaunchKernelGGL((partial_valu<D, G, DT, PAGED>), grid, dim3(kThreads), 0, st, a.q, a.k, a.v,
-                       a.table, a.lens, a.ws_o, a.ws_ml, a.batch, a.hq, a.hkv, a.chunk, a.s_max, a.max_pages,
-                       a.qk_scale_log2);
-    return hipGetLastError();
-}
-
-template <int D, int G, int DT>
-hipError_t pick_paged(bool paged, const PartialArgs& a, dim3 grid, hipStream_t st) {
-    return paged ? launch_partial<D, G, DT, true>(a, grid, st) : launch_partial<D, G, DT, false>(a, grid, st);
+// Calls f.template operator()<KT, QT>() for the problem's cache and query types.
+template <typename F>
+hipError_t with_types(const PartialArgs& a, F&& f) {
+    if (a.kv_dt == FD_FP8_E4M3)
+        return a.q_dt == FD_F16 ? f.template operator()<FD_FP8_E4M3, FD_F16>()
+                                : f.template operator()<FD_FP8_E4M3, FD_BF16>();
+    return a.kv_dt == FD_F16 ? f.template operator()<FD_F16, FD_F16>() : f.template operator()<FD_BF16, FD_BF16>();
 }
 
 template <int D, int G>
-hipError_t pick_dtype(int dt, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st) {
-    return dt == FD_F16 ? pick_paged<D, G, FD_F16>(paged, a, grid, st)
-                        : pick_paged<D, G, FD_BF16>(paged, a, grid, st);
+hipError_t launch_tokens_g(bool paged, const PartialArgs& a, dim3 grid, hipStream_t st) {
+    return with_types(a, [&]<int KT, int QT>() {
+        if (paged)
+            hipLaunchKernelGGL((partial_valu<D, G, KT, QT, true>), grid, dim3(kThreads), 0, st, a);
+        else
+            hipLaunchKernelGGL((partial_valu<D, G, KT, QT, false>), grid, dim3(kThreads), 0, st, a);
+        return hipGetLastError();
+    });
 }
 
 template <int D>
-hipError_t pick_group(int G, int dt, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st) {
+hipError_t launch_tokens_d(int G, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st) {
     switch (G) {
-        case 1: return pick_dtype<D, 1>(dt, paged, a, grid, st);
-        case 2: return pick_dtype<D, 2>(dt, paged, a, grid, st);
-        case 4: return pick_dtype<D, 4>(dt, paged, a, grid, st);
-        default: return pick_dtype<D, 8>(dt, paged, a, grid, st);
+        case 1: return launch_tokens_g<D, 1>(paged, a, grid, st);
+        case 2: return launch_tokens_g<D, 2>(paged, a, grid, st);
+        case 4: return launch_tokens_g<D, 4>(paged, a, grid, st);
+        default: return launch_tokens_g<D, 8>(paged, a, grid, st);
     }
 }
 
-hipError_t launch_partial_valu(int D, int G, int dt, bool paged, const PartialArgs& a, dim3 grid,
-                               hipStream_t st) {
-    return D == 64 ? pick_group<64>(G, dt, paged, a, grid, st) : pick_group<128>(G, dt, paged, a, grid, st);
-}
-
-template <int D, int G, int DT, int MODE>
-hipError_t launch_heads_mode(const PartialArgs& a, dim3 grid, hipStream_t st) {
-    hipLaunchKernelGGL((partial_valu_heads<D, G, DT, MODE>), grid, dim3(kThreads), 0, st, a.q, a.k, a.v, a.table,
-                       a.lens, a.ws_o, a.ws_ml, a.batch, a.hq, a.hkv, a.chunk, a.s_max, a.max_pages,
-                       a.qk_scale_log2);
-    return hipGetLastError();
-}
-
-template <int D, int G, int DT>
-hipError_t launch_heads_dt(bool paged, const PartialArgs& a, dim3 grid, hipStream_t st) {
-    if (!paged) return launch_heads_mode<D, G, DT, 0>(a, grid, st);
-    const bool aligned = (a.chunk % 16 == 0) && (16 % kUnroll == 0);
-    return aligned ? launch_heads_mode<D, G, DT, 2>(a, grid, st) : launch_heads_mode<D, G, DT, 1>(a, grid, st);
+hipError_t launch_partial_valu(int D, int G, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st) {
+    return D == 64 ? launch_tokens_d<64>(G, paged, a, grid, st) : launch_tokens_d<128>(G, paged, a, grid, st);
 }
 
 template <int D, int G>
-hipError_t launch_heads_g(int dt, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st) {
-    return dt == FD_F16 ? launch_heads_dt<D, G, FD_F16>(paged, a, grid, st)
-                        : launch_heads_dt<D, G, FD_BF16>(paged, a, grid, st);
+hipError_t launch_heads_g(bool paged, const PartialArgs& a, dim3 grid, hipStream_t st) {
+    // Paged splits that start on page boundaries read their page indices 64 at a time.
+    const int mode = !paged ? 0 : ((a.chunk % 16 == 0) && (16 % kUnroll == 0)) ? 2 : 1;
+    return with_types(a, [&]<int KT, int QT>() {
+        if (mode == 0)
+            hipLaunchKernelGGL((partial_valu_heads<D, G, KT, QT, 0>), grid, dim3(kThreads), 0, st, a);
+        else if (mode == 1)
+            hipLaunchKernelGGL((partial_valu_heads<D, G, KT, QT, 1>), grid, dim3(kThreads), 0, st, a);
+        else
+            hipLaunchKernelGGL((partial_valu_heads<D, G, KT, QT, 2>), grid, dim3(kThreads), 0, st, a);
+        return hipGetLastError();
+    });
 }
 
-hipError_t launch_partial_valu_heads(int D, int G, int dt, bool paged, const PartialArgs& a, dim3 grid,
-                                     hipStream_t st) {
-    if (D == 64) return G == 1 ? launch_heads_g<64, 1>(dt, paged, a, grid, st) : launch_heads_g<64, 2>(dt, paged, a, grid, st);
-    return G == 1 ? launch_heads_g<128, 1>(dt, paged, a, grid, st) : launch_heads_g<128, 2>(dt, paged, a, grid, st);
+hipError_t launch_partial_valu_heads(int D, int G, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st) {
+    if (D == 64) return G == 1 ? launch_heads_g<64, 1>(paged, a, grid, st) : launch_heads_g<64, 2>(paged, a, grid, st);
+    return G == 1 ? launch_heads_g<128, 1>(paged, a, grid, st) : launch_heads_g<128, 2>(paged, a, grid, st);
 }
 
 }  // namespace fdk

@@ -251,3 +251,46 @@ def test_multi_query_problems():
         with pytest.raises(fd.FdError) as ei:
             fd.fd_plan_splits(prob(**kw), lens, num_cus=256)
         assert ei.value.status == status, kw
+
+
+def test_fp8_problems():
+    """An FP8 (E4M3) cache: 16 codes per 16-byte load, so a head-rows load
+    covers 8 heads at d = 128 and 16 at d = 64; q is fp16 or bf16; the
+    unscaled calls refuse it (its scales are part of the data)."""
+    import torch
+    f8 = torch.float8_e4m3fn
+    p = prob(kv_dtype=f8, q_dtype=torch.bfloat16)
+    assert p.kv_dtype == fd.FD_FP8_E4M3 and p.q_dtype == fd.FD_BF16
+    assert prob(kv_dtype=f8).q_dtype == fd.FD_F16
+    plan = fd.fd_plan_splits(p, [131072], num_cus=256)
+    assert plan.partial_kernel == 2
+    assert fd.fd_plan_splits(prob(kv_dtype=f8, num_kv_heads=8, num_q_heads=32), [500000],
+                             num_cus=256).partial_kernel == 1
+    # d = 64: 16 heads per load; 8 KV heads cannot fill a head-rows wave
+    assert fd.fd_plan_splits(prob(kv_dtype=f8, num_q_heads=8, num_kv_heads=8, head_dim=64), [500000],
+                             num_cus=256).partial_kernel == 0
+    assert fd.fd_plan_splits(prob(kv_dtype=f8, num_q_heads=16, num_kv_heads=16, head_dim=64), [500000],
+                             num_cus=256).partial_kernel == 2
+    # the workspace does not depend on the cache type
+    assert plan.workspace_bytes == fd.fd_plan_splits(prob(), [131072], num_cus=256,
+                                                     force_num_splits=plan.max_splits).workspace_bytes
+    bad = prob(kv_dtype=f8)
+    bad.q_dtype = fd.FD_F32
+    with pytest.raises(fd.FdError) as ei:
+        fd.fd_plan_splits(bad, [100], num_cus=256)
+    assert ei.value.status == fd.FD_ERR_INVALID_ARGUMENT
+    lib = fd.load_library()
+    fake = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails validation
+    need = plan.workspace_bytes
+    st = lib.fd_decode_partial(ctypes.byref(p), ctypes.byref(plan), fake, fake, fake, None, fake, fake, need, None)
+    assert st == fd.FD_ERR_INVALID_ARGUMENT and b"scaled" in lib.fd_last_error_message()
+    lens = (ctypes.c_int32 * 1)(131072)
+    st = lib.fd_decode_attention(ctypes.byref(p), fake, fake, fake, None, lens, fake, fake, None, fake, need, None)
+    assert st == fd.FD_ERR_INVALID_ARGUMENT
+    # misaligned scales, too-small workspace
+    st = lib.fd_decode_partial_scaled(ctypes.byref(p), ctypes.byref(plan), fake, fake, fake, ctypes.c_void_p(0x10002),
+                                      None, None, fake, fake, need, None)
+    assert st == fd.FD_ERR_INVALID_ARGUMENT
+    st = lib.fd_decode_partial_scaled(ctypes.byref(p), ctypes.byref(plan), fake, fake, fake, None, None, None, fake,
+                                      fake, need - 4, None)
+    assert st == fd.FD_ERR_WORKSPACE_TOO_SMALL
