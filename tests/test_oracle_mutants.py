@@ -12,8 +12,10 @@ import numpy as np
 import pytest
 
 import oracle.attention as A
+import oracle.append as AP
 import oracle.fp8 as F
 import tests.test_oracle as P
+import tests.test_oracle_append as PA
 
 
 def _merge_two_flipped_sign(mA, lA, OA, mB, lB, OB):
@@ -155,7 +157,56 @@ def _logical_kv_scales_swapped(k, v, seq_lens, b, g, block_table=None, page_size
     return _logical_kv_orig(k, v, seq_lens, b, g, block_table, page_size, v_scale, k_scale)
 
 
+def _rope_rotate_flipped(x, pos, base, style):
+    x = A.as_f64(x).copy()
+    if style is None:
+        return x
+    a, b = AP.rope_pairs(x.shape[-1], style)
+    ang = AP.rope_angles(pos, x.shape[-1], base)
+    c, s = np.cos(ang), np.sin(ang)
+    xa, xb = x[..., a].copy(), x[..., b].copy()
+    x[..., a] = xa * c + xb * s
+    x[..., b] = -xa * s + xb * c
+    return x
+
+
+def _rope_angles_wrong_exponent(pos, d, base):
+    return float(pos) * np.power(float(base), -1.0 * np.arange(d // 2) / d)
+
+
+def _round_ties_away(x, fmt, saturate=False):
+    mbits, emin, fmax = AP.FORMATS[fmt]
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    for i, v in enumerate(x.reshape(-1)):
+        if v != v or v == 0.0 or math.isinf(v):
+            out.reshape(-1)[i] = v
+            continue
+        e = max(math.frexp(v)[1] - 1, emin)
+        q = math.ldexp(1.0, e - mbits)
+        val = math.copysign(math.floor(abs(v) / q + 0.5) * q, v)
+        if abs(val) > fmax:
+            val = math.copysign(fmax if saturate else math.inf, v)
+        out.reshape(-1)[i] = val
+    return out
+
+
+_append_orig = AP.append_kv
+
+
+def _append_position_off_by_one(k_cache, v_cache, block_table, seq_lens, k_new, v_new, q=None, **kw):
+    lens = [int(x) + 1 for x in seq_lens.tolist()]
+    return _append_orig(k_cache, v_cache, block_table, lens, k_new, v_new, q, **kw)
+
+
 MUTANTS = [
+    ("append:rope_rotate", _rope_rotate_flipped,
+     [lambda: PA.test_rope_interleaved_is_complex_multiplication_and_half_is_a_permutation()]),
+    ("append:rope_angles", _rope_angles_wrong_exponent,
+     [lambda: PA.test_rope_interleaved_is_complex_multiplication_and_half_is_a_permutation()]),
+    ("append:round_to_format", _round_ties_away, [PA.test_rounding_ties_and_saturation_closed_forms,
+                                                  PA.test_round_to_f16_matches_numpy_float64_cast]),
+    ("append:append_kv", _append_position_off_by_one, [lambda: PA.test_append_writes_only_the_new_tokens_slots(1)]),
     ("fp8:e4m3_value", _e4m3_bias_8, [P.test_e4m3_codes_match_torch_float8_e4m3fn, P.test_e4m3_format_closed_forms]),
     ("logical_kv", _logical_kv_scales_swapped, [P.test_fp8_scales_apply_per_kv_head]),
     ("decode_attention_multi", _multi_causal_off_by_one, [lambda: P.test_multi_query_matches_torch_causal_masked_softmax(4)]),
@@ -182,6 +233,8 @@ def test_mutant_is_caught(monkeypatch, idx):
     mod = A
     if name.startswith("fp8:"):
         mod, name = F, name[4:]
+    elif name.startswith("append:"):
+        mod, name = AP, name[7:]
     monkeypatch.setattr(mod, name, fn)
     caught = 0
     for pin in pins:
