@@ -217,6 +217,49 @@ fd_status fd_decode_attention_scaled(const fd_problem* problem,
                                      void* out, float* lse,
                                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* Rotary position embedding applied by fd_append_kv. */
+typedef enum fd_rope_style {
+    FD_ROPE_NONE = 0,          /* store the new keys as given */
+    FD_ROPE_INTERLEAVED = 1,   /* pairs (2i, 2i+1) */
+    FD_ROPE_HALF = 2           /* pairs (i, i + d/2) */
+} fd_rope_style;
+
+/*
+ * Append each sequence's q_len new tokens to a paged cache (asynchronous on
+ * `stream`), rotating the new keys and the queries by their positions first.
+ *
+ * RoPE belongs before split-KV decode, in a kernel of its own, and applies to
+ * the current step's keys and queries (CUTLASS Split KV article, §5.3); the
+ * cache is the capstone's 16-token paged layout (§4.1). With the lengths L_b
+ * counted *after* the append (the lengths the following decode call uses),
+ * new token j of sequence b is at position pos = L_b - q_len + j, stored at
+ * k_cache[block_table[b, pos / 16], pos % 16] (v_cache likewise). Rotation
+ * (RoFormer's rotary embedding): pair i of each head vector turns by
+ * pos * rope_base^(-2i/d); computed in fp64, then rounded once to the storage
+ * format (ties to even). An FP8 cache stores the E4M3 code of value / scale[g]
+ * saturated at +-448 (k_scale / v_scale as for fd_decode_partial_scaled; NULL
+ * means 1; 16-bit caches divide by the scales too when given).
+ *
+ * problem: paged (page_size 16) with batch, heads, head_dim, kv_dtype,
+ *          q_dtype and q_len (new tokens per sequence, 0 or 1 = one).
+ * k_new, v_new: device [B, q_len, Hkv, d] in q's type (kv_dtype for 16-bit
+ *          caches, q_dtype for FP8 caches).
+ * q:       device [B, q_len, Hq, d], rotated in place; NULL to leave out.
+ * k_cache, v_cache: device pools [num_pages, 16, Hkv, d] in kv_dtype.
+ * block_table: device int32 [B, max_pages_per_seq]; seq_lens_dev: device
+ *          int32 [B] (after the append).
+ * Slots other than the new tokens' are not touched. A position outside the
+ * block table, or a page index outside [0, num_pages), is skipped on the
+ * device (nothing written) rather than trusted. rope_style FD_ROPE_NONE
+ * stores keys unrotated and leaves q alone; otherwise rope_base must be a
+ * positive finite number (10000 in RoFormer).
+ */
+fd_status fd_append_kv(const fd_problem* problem, int32_t rope_style, float rope_base,
+                       const void* k_new, const void* v_new, void* q,
+                       const float* k_scale, const float* v_scale,
+                       void* k_cache, void* v_cache, int32_t num_pages,
+                       const int32_t* block_table, const int32_t* seq_lens_dev, void* stream);
+
 /* A static, human-readable name for a status code. */
 const char* fd_status_string(fd_status status);
 

@@ -19,9 +19,10 @@ sequence lengths *after* the append (L_b) and n new tokens per sequence, new
 token j sits at position L_b - n + j, i.e. in block table entry
 (L_b - n + j) // 16, slot (L_b - n + j) % 16.
 
-Stored values are the exact rotation rounded once to the cache's format,
-round-to-nearest-even (``round_to_format``); an FP8 cache stores the code of
-value / scale[g], saturated to the largest finite magnitude (448).
+Stored values are the exact rotation divided by the head's scale (1 when no
+scales are given) and rounded once to the cache's format, round-to-nearest-
+even (``round_to_format``); an FP8 cache stores the E4M3 code, saturated to
+the largest finite magnitude (448).
 Arithmetic is float64.
 """
 
@@ -135,7 +136,7 @@ def _store(values: np.ndarray, dtype, scale: float = 1.0):
         r = round_to_format(values / scale, "e4m3", saturate=True)
         codes = np.array([e4m3_code(v) for v in r.reshape(-1)], dtype=np.uint8).reshape(r.shape)
         return torch.from_numpy(codes).view(torch.float8_e4m3fn)
-    r = round_to_format(values, fmt)
+    r = round_to_format(values / scale, fmt)
     return torch.from_numpy(r).to(dtype)  # exact: r is representable
 
 
@@ -147,8 +148,8 @@ def append_kv(k_cache, v_cache, block_table, seq_lens, k_new, v_new, q=None, *, 
     k_new, v_new: [B, n, Hkv, d]; q: [B, n, Hq, d] or None; seq_lens: lengths
     after the append. Returns (k_cache', v_cache', q') as new tensors: new
     token j of sequence b goes to position L_b - n + j; K and q are rotated
-    at that position, K/V rounded to the cache format (divided by the head's
-    scale first for an FP8 cache). Every other slot keeps its bytes.
+    at that position, K/V divided by the head's scale and rounded to the cache
+    format. Every other slot keeps its bytes.
     """
     kc, vc = k_cache.clone(), v_cache.clone()
     B, n, hkv, d = k_new.shape

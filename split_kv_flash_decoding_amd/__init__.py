@@ -25,6 +25,10 @@ from ._capi import (  # noqa: F401
     FdPlan,
     FdProblem,
     decode_attention,
+    FD_ROPE_HALF,
+    FD_ROPE_INTERLEAVED,
+    FD_ROPE_NONE,
+    fd_append_kv,
     fd_combine,
     fd_decode_attention,
     fd_decode_partial,

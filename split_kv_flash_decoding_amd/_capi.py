@@ -19,6 +19,8 @@ LIB_PATH = os.path.join(HERE, "libfd.so")
 
 FD_OK, FD_ERR_INVALID_ARGUMENT, FD_ERR_UNSUPPORTED, FD_ERR_WORKSPACE_TOO_SMALL, FD_ERR_HIP = range(5)
 FD_F16, FD_BF16, FD_F32, FD_FP8_E4M3 = range(4)
+FD_ROPE_NONE, FD_ROPE_INTERLEAVED, FD_ROPE_HALF = range(3)
+ROPE_STYLES = {None: FD_ROPE_NONE, "none": FD_ROPE_NONE, "interleaved": FD_ROPE_INTERLEAVED, "half": FD_ROPE_HALF}
 
 # Every function fd.h declares; the CPU tests check the library exports them.
 EXPORTED = (
@@ -28,6 +30,7 @@ EXPORTED = (
     "fd_combine",
     "fd_decode_attention",
     "fd_decode_attention_scaled",
+    "fd_append_kv",
     "fd_status_string",
     "fd_last_error_message",
     "fd_probe_read",
@@ -100,8 +103,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.fd_decode_partial_scaled.argtypes = [P, Pl, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.fd_decode_attention_scaled.argtypes = [P, vp, vp, vp, vp, vp, vp, i32p, vp, vp, f32p, vp,
                                                ctypes.c_size_t, vp]
+    lib.fd_append_kv.argtypes = [P, ctypes.c_int32, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32,
+                                 vp, vp, vp]
     for name in ("fd_plan_splits", "fd_decode_partial", "fd_combine", "fd_decode_attention",
-                 "fd_decode_partial_scaled", "fd_decode_attention_scaled"):
+                 "fd_decode_partial_scaled", "fd_decode_attention_scaled", "fd_append_kv"):
         getattr(lib, name).restype = ctypes.c_int
     lib.fd_status_string.argtypes = [ctypes.c_int]
     lib.fd_status_string.restype = ctypes.c_char_p
@@ -278,6 +283,40 @@ def fd_decode_attention(problem: FdProblem, q, k, v, block_table, seq_lens_host,
     _check(lib.fd_decode_attention(
         ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(block_table), arr, _ptr(seq_lens_dev),
         _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def fd_append_kv(problem: FdProblem, k_new, v_new, q, k_cache, v_cache, block_table, seq_lens_dev, *,
+                 rope_style=None, rope_base: float = 10000.0, k_scale=None, v_scale=None, stream=None) -> None:
+    """Write each sequence's q_len new tokens into the paged cache, keys and
+    (optionally) q rotated in place by RoPE at their positions (include/fd.h).
+    seq_lens_dev holds the lengths after the append."""
+    import torch
+
+    types = {FD_F16: torch.float16, FD_BF16: torch.bfloat16, FD_FP8_E4M3: torch.float8_e4m3fn}
+    B, hq, hkv, d = problem.batch, problem.num_q_heads, problem.num_kv_heads, problem.head_dim
+    n = max(1, problem.q_len)
+    qdt = types.get(problem.q_dtype if problem.kv_dtype == FD_FP8_E4M3 else problem.kv_dtype)
+    kvdt = types.get(problem.kv_dtype)
+    for name, t, shape, dt in (("k_new", k_new, (B, n, hkv, d), qdt), ("v_new", v_new, (B, n, hkv, d), qdt),
+                               ("q", q, (B, n, hq, d), qdt)):
+        if t is None and name == "q":
+            continue
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != dt or t.numel() != math.prod(shape):
+            raise ValueError(f"{name} must be a contiguous {dt} CUDA tensor of {list(shape)} elements")
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != kvdt or t.dim() != 4 \
+                or tuple(t.shape[1:]) != (problem.page_size, hkv, d):
+            raise ValueError(f"{name} must be a contiguous {kvdt} CUDA pool [P, {problem.page_size}, {hkv}, {d}]")
+    if block_table is None or block_table.dtype != torch.int32 or not block_table.is_cuda \
+            or tuple(block_table.shape) != (B, problem.max_pages_per_seq) or not block_table.is_contiguous():
+        raise ValueError(f"block_table must be a contiguous int32 CUDA tensor [{B}, {problem.max_pages_per_seq}]")
+    if seq_lens_dev.dtype != torch.int32 or not seq_lens_dev.is_cuda or seq_lens_dev.numel() != B:
+        raise ValueError("seq_lens_dev must be an int32 CUDA tensor with one entry per sequence")
+    _check_scales(problem, k_scale, v_scale)
+    _check(load_library().fd_append_kv(
+        ctypes.byref(problem), ROPE_STYLES[rope_style], float(rope_base), _ptr(k_new), _ptr(v_new), _ptr(q),
+        _ptr(k_scale), _ptr(v_scale), _ptr(k_cache), _ptr(v_cache), int(k_cache.shape[0]), _ptr(block_table),
+        _ptr(seq_lens_dev), _stream(stream)))
 
 
 # --------------------------------------------------------------- convenience

@@ -173,4 +173,60 @@ fd_status fd_decode_attention(const fd_problem* p, const void* q, const void* k,
                                       lse, workspace, workspace_bytes_avail, stream);
 }
 
+fd_status fd_append_kv(const fd_problem* p, int32_t rope_style, float rope_base, const void* k_new,
+                       const void* v_new, void* q, const float* k_scale, const float* v_scale, void* k_cache,
+                       void* v_cache, int32_t num_pages, const int32_t* block_table, const int32_t* seq_lens_dev,
+                       void* stream) {
+    clear_error();
+    if (!p) return fail(FD_ERR_INVALID_ARGUMENT, "problem is NULL");
+    // Any number of new tokens may be appended; the decode kernels' limits on
+    // q_len do not apply here.
+    fd_problem one = *p;
+    one.q_len = 1;
+    fd_status st = check_problem(&one, nullptr);
+    if (st != FD_OK) return st;
+    if (p->q_len < 0) return fail(FD_ERR_INVALID_ARGUMENT, "q_len %d < 0", p->q_len);
+    if (p->page_size != kPageSize)
+        return fail(FD_ERR_UNSUPPORTED, "fd_append_kv writes a paged cache (page_size 16)");
+    if (rope_style < FD_ROPE_NONE || rope_style > FD_ROPE_HALF)
+        return fail(FD_ERR_INVALID_ARGUMENT, "rope_style %d unknown", rope_style);
+    if (rope_style != FD_ROPE_NONE && !(rope_base > 0.f && rope_base < __builtin_inff()))
+        return fail(FD_ERR_INVALID_ARGUMENT, "rope_base must be positive and finite");
+    if (!k_new || !v_new || !k_cache || !v_cache || !block_table || !seq_lens_dev)
+        return fail(FD_ERR_INVALID_ARGUMENT, "k_new, v_new, k_cache, v_cache, block_table and seq_lens_dev "
+                    "must be non-NULL");
+    if (num_pages < 1) return fail(FD_ERR_INVALID_ARGUMENT, "num_pages %d < 1", num_pages);
+    const uintptr_t a16 = reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new) |
+                          reinterpret_cast<uintptr_t>(q);
+    const uintptr_t acache = reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(v_cache);
+    if ((a16 & 1) || (acache & (kv_elem_bytes(p) - 1)))
+        return fail(FD_ERR_INVALID_ARGUMENT, "tensors must be aligned to their element size");
+    if ((reinterpret_cast<uintptr_t>(k_scale) | reinterpret_cast<uintptr_t>(v_scale)) & 3)
+        return fail(FD_ERR_INVALID_ARGUMENT, "k_scale and v_scale must be 4-byte aligned");
+    const int64_t blocks = (int64_t)p->batch * problem_q_len(p);
+    if (blocks > INT32_MAX) return fail(FD_ERR_INVALID_ARGUMENT, "too many new tokens");
+
+    fdk::AppendArgs a;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.q = q;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.table = block_table;
+    a.lens = seq_lens_dev;
+    a.n = problem_q_len(p);
+    a.hkv = p->num_kv_heads;
+    a.hq = p->num_q_heads;
+    a.d = p->head_dim;
+    a.max_pages = p->max_pages_per_seq;
+    a.num_pages = num_pages;
+    a.style = rope_style;
+    a.rope_base = rope_base;
+    hipError_t e = fdk::launch_append(a, q_dtype_of(p), p->kv_dtype, (int)blocks, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(FD_ERR_HIP, "append kernel launch: %s", hipGetErrorString(e));
+    return FD_OK;
+}
+
 }  // extern "C"

@@ -285,11 +285,27 @@ struct PartialArgs {
 // Scale of KV head g (1 when no scales are given).
 __device__ __forceinline__ float head_scale(const float* __restrict__ sc, int g) { return sc ? sc[g] : 1.f; }
 
+// Arguments of the KV-append kernel (fd_append_kv).
+struct AppendArgs {
+    const void* k_new;
+    const void* v_new;
+    void* q;
+    const float* k_scale;
+    const float* v_scale;
+    void* k_cache;
+    void* v_cache;
+    const int32_t* table;
+    const int32_t* lens;
+    int n, hkv, hq, d, max_pages, num_pages, style;
+    float rope_base;
+};
+
 // Launchers (each defined in the file that holds its kernel). They enqueue on
 // `st` and return hipGetLastError().
 hipError_t launch_partial_valu(int D, int G, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st);
 hipError_t launch_partial_valu_heads(int D, int G, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st);
 hipError_t launch_partial_mfma(int G, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st);
+hipError_t launch_append(const AppendArgs& a, int q_dt, int kv_dt, int blocks, hipStream_t st);
 hipError_t launch_combine(int D, int out_dt, const float* ws_o, const float* ws_ml, const int32_t* lens,
                           void* out, float* lse, int B, int hq, int chunk, int s_max, hipStream_t st);
 

@@ -294,3 +294,30 @@ def test_fp8_problems():
     st = lib.fd_decode_partial_scaled(ctypes.byref(p), ctypes.byref(plan), fake, fake, fake, None, None, None, fake,
                                       fake, need - 4, None)
     assert st == fd.FD_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_append_validates_before_launching():
+    """fd_append_kv: paged caches only, a known RoPE style, a positive base,
+    non-NULL buffers, a page count, aligned pointers; errors launch nothing."""
+    import torch
+    lib = fd.load_library()
+    fake = ctypes.c_void_p(0x10000)
+    p = prob(page_size=16, max_pages_per_seq=64, num_q_heads=8, num_kv_heads=2)
+
+    def call(pp, style=1, base=10000.0, knew=fake, q=None, kc=fake, pages=10, ks=None):
+        return lib.fd_append_kv(ctypes.byref(pp), style, base, knew, fake, q, ks, None, kc, fake, pages, fake,
+                                fake, None)
+    assert call(prob(num_q_heads=8, num_kv_heads=2)) == fd.FD_ERR_UNSUPPORTED   # contiguous
+    assert call(p, style=3) == fd.FD_ERR_INVALID_ARGUMENT
+    assert call(p, base=0.0) == fd.FD_ERR_INVALID_ARGUMENT
+    assert call(p, base=float("inf")) == fd.FD_ERR_INVALID_ARGUMENT
+    assert call(p, knew=None) == fd.FD_ERR_INVALID_ARGUMENT
+    assert call(p, pages=0) == fd.FD_ERR_INVALID_ARGUMENT
+    assert call(p, knew=ctypes.c_void_p(0x10001)) == fd.FD_ERR_INVALID_ARGUMENT
+    assert call(p, kc=ctypes.c_void_p(0x10001)) == fd.FD_ERR_INVALID_ARGUMENT   # 2-byte cache elements
+    assert call(p, ks=ctypes.c_void_p(0x10002)) == fd.FD_ERR_INVALID_ARGUMENT
+    f8 = prob(page_size=16, max_pages_per_seq=64, num_q_heads=8, num_kv_heads=2, kv_dtype=torch.float8_e4m3fn)
+    bad = prob(page_size=16, max_pages_per_seq=64, num_q_heads=8, num_kv_heads=2, kv_dtype=torch.float8_e4m3fn)
+    bad.q_dtype = fd.FD_F32
+    assert call(bad) == fd.FD_ERR_INVALID_ARGUMENT
+    assert f8.q_dtype == fd.FD_F16
