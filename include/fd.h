@@ -217,6 +217,31 @@ fd_status fd_decode_attention_scaled(const fd_problem* problem,
                                      void* out, float* lse,
                                      void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Prefill attention (asynchronous on `stream`): every one of the q_len query
+ * tokens of each sequence attends causally to its cache, in one pass with no
+ * splits and no workspace.
+ *
+ * The FlashAttention-2 forward pass (FlashAttention capstone, §2.1): blocks
+ * of 128 query rows stay on chip while K/V tiles stream past; each row keeps
+ * a running max and sum, the output is divided once at the end, and tiles
+ * wholly past a block's causal limit are skipped. Query i of sequence b is at
+ * position L_b - q_len + i and sees tokens 0 .. L_b - q_len + i (q_len = L_b:
+ * causal self-attention over the whole prompt; smaller q_len: one chunk of a
+ * longer prompt whose earlier tokens are already cached), the same reading
+ * as multi-query decode.
+ * problem: head_dim 128, fp16/bf16 cache (q of the same type), contiguous or
+ *          paged, q_len >= 1 new tokens per sequence (no upper limit), every
+ *          L_b >= q_len (a row with no visible token gets out = 0,
+ *          lse = -inf).
+ * q: device [B, q_len, Hq, d]; k, v: the cache as for fd_decode_partial;
+ * out: device [B, q_len, Hq, d] in out_dtype; lse: device float32
+ * [B, q_len, Hq] or NULL.
+ */
+fd_status fd_prefill_attention(const fd_problem* problem, const void* q, const void* k, const void* v,
+                               const int32_t* block_table, const int32_t* seq_lens_dev,
+                               void* out, float* lse, void* stream);
+
 /* Rotary position embedding applied by fd_append_kv. */
 typedef enum fd_rope_style {
     FD_ROPE_NONE = 0,          /* store the new keys as given */

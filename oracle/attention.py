@@ -270,14 +270,16 @@ def decode_attention(q, k, v, seq_lens, scale: float, block_table=None, page_siz
 
 
 def decode_attention_multi(q, k, v, seq_lens, scale: float, block_table=None, page_size: int = 0,
-                           k_scale=None, v_scale=None):
+                           k_scale=None, v_scale=None, rows: Optional[Sequence[Tuple[int, int, int]]] = None):
     """Several query tokens per sequence: q [B, q_len, Hq, d] -> out
     [B, q_len, Hq, d], lse [B, q_len, Hq] (fp64).
 
     Query i of sequence b is the token at position L_b - q_len + i and
     attends to tokens 0 .. L_b - q_len + i (causal among the new tokens;
     FlashAttention capstone §4.5). Each query is ``attention_row`` over its
-    visible prefix.
+    visible prefix. With q_len = L_b this is causal attention over the whole
+    sequence (prefill). ``rows`` restricts the work to some (b, i, h); entries
+    not computed are NaN.
     """
     qf = as_f64(q)
     B, ql, hq, d = qf.shape
@@ -286,17 +288,20 @@ def decode_attention_multi(q, k, v, seq_lens, scale: float, block_table=None, pa
     lens = _lens(seq_lens)
     out = np.full((B, ql, hq, d), np.nan)
     lse = np.full((B, ql, hq), np.nan)
-    for b in range(B):
+    todo = {}
+    if rows is None:
+        rows = [(b, i, h) for b in range(B) for i in range(ql) for h in range(hq)]
+    for b, i, h in rows:
+        todo.setdefault((int(b), int(h) // G), []).append((int(i), int(h)))
+    for (b, g), items in sorted(todo.items()):
         if lens[b] < ql:
             raise ValueError("every sequence must hold its q_len new tokens")
-        for g in range(hkv):
-            K, V = logical_kv(k, v, seq_lens, b, g, block_table, page_size, k_scale, v_scale)
-            for i in range(ql):
-                n = lens[b] - ql + i + 1
-                for h in range(g * G, (g + 1) * G):
-                    o, ls, _, _ = attention_row(qf[b, i, h], K[:n], V[:n], scale)
-                    out[b, i, h] = o
-                    lse[b, i, h] = ls
+        K, V = logical_kv(k, v, seq_lens, b, g, block_table, page_size, k_scale, v_scale)
+        for i, h in items:
+            n = lens[b] - ql + i + 1
+            o, ls, _, _ = attention_row(qf[b, i, h], K[:n], V[:n], scale)
+            out[b, i, h] = o
+            lse[b, i, h] = ls
     return out, lse
 
 

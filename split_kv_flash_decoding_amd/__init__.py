@@ -33,6 +33,8 @@ from ._capi import (  # noqa: F401
     fd_decode_attention,
     fd_decode_partial,
     fd_plan_splits,
+    fd_prefill_attention,
+    prefill_attention,
     fd_probe_copy,
     fd_probe_read,
     load_library,

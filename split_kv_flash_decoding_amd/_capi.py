@@ -31,6 +31,7 @@ EXPORTED = (
     "fd_decode_attention",
     "fd_decode_attention_scaled",
     "fd_append_kv",
+    "fd_prefill_attention",
     "fd_status_string",
     "fd_last_error_message",
     "fd_probe_read",
@@ -105,8 +106,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                                ctypes.c_size_t, vp]
     lib.fd_append_kv.argtypes = [P, ctypes.c_int32, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32,
                                  vp, vp, vp]
+    lib.fd_prefill_attention.argtypes = [P, vp, vp, vp, vp, vp, vp, f32p, vp]
     for name in ("fd_plan_splits", "fd_decode_partial", "fd_combine", "fd_decode_attention",
-                 "fd_decode_partial_scaled", "fd_decode_attention_scaled", "fd_append_kv"):
+                 "fd_decode_partial_scaled", "fd_decode_attention_scaled", "fd_append_kv", "fd_prefill_attention"):
         getattr(lib, name).restype = ctypes.c_int
     lib.fd_status_string.argtypes = [ctypes.c_int]
     lib.fd_status_string.restype = ctypes.c_char_p
@@ -164,6 +166,12 @@ def _q_shape(problem: FdProblem, d: int):
     return (B, hq, d) if problem.q_len <= 1 else (B, problem.q_len, hq, d)
 
 
+def _q_shapes(problem: FdProblem, d: int):
+    """Accepted q / out shapes: [B, Hq, d] or [B, 1, Hq, d] for one query token."""
+    B, hq = problem.batch, problem.num_q_heads
+    return {_q_shape(problem, d), (B, max(1, problem.q_len), hq, d)}
+
+
 def _lens_array(seq_lens_host: Sequence[int]):
     vals = [int(x) for x in (seq_lens_host.tolist() if hasattr(seq_lens_host, "tolist") else seq_lens_host)]
     return (ctypes.c_int32 * len(vals))(*vals), vals
@@ -191,7 +199,7 @@ def _check_tensors(problem: FdProblem, q, k, v, block_table, seq_lens_dev, total
     for name, t, dt in (("q", q, qdt), ("k", k, kvdt), ("v", v, kvdt)):
         if not t.is_cuda or not t.is_contiguous() or t.dtype != dt:
             raise ValueError(f"{name} must be a contiguous {dt} CUDA tensor")
-    if tuple(q.shape) != _q_shape(problem, d):
+    if tuple(q.shape) not in _q_shapes(problem, d):
         raise ValueError(f"q has shape {tuple(q.shape)}, expected {_q_shape(problem, d)}")
     if k.shape != v.shape:
         raise ValueError("k and v shapes differ")
@@ -249,7 +257,8 @@ def fd_decode_partial(problem: FdProblem, plan: FdPlan, q, k, v, block_table, se
 
 
 def _check_out(problem: FdProblem, out, lse) -> None:
-    oshape = _q_shape(problem, problem.head_dim)
+    oshape = tuple(out.shape) if tuple(out.shape) in _q_shapes(problem, problem.head_dim) else \
+        _q_shape(problem, problem.head_dim)
     if tuple(out.shape) != oshape or not out.is_contiguous() or _dtype_code(out.dtype) != problem.out_dtype \
             or not out.is_cuda:
         raise ValueError(f"out must be a contiguous CUDA tensor {list(oshape)} of the problem's out_dtype")
@@ -283,6 +292,37 @@ def fd_decode_attention(problem: FdProblem, q, k, v, block_table, seq_lens_host,
     _check(lib.fd_decode_attention(
         ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(block_table), arr, _ptr(seq_lens_dev),
         _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def fd_prefill_attention(problem: FdProblem, q, k, v, block_table, seq_lens_dev, out, lse=None,
+                         stream=None) -> None:
+    """Causal attention of every sequence's q_len query tokens over its cache
+    in one pass (include/fd.h). q and out are [B, q_len, Hq, d]."""
+    _check_tensors(problem, q, k, v, block_table, seq_lens_dev, None)
+    _check_out(problem, out, lse)
+    _check(load_library().fd_prefill_attention(
+        ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(block_table), _ptr(seq_lens_dev), _ptr(out),
+        _ptr(lse), _stream(stream)))
+
+
+def prefill_attention(q, k, v, seq_lens, *, block_table=None, page_size: int = 0, max_pages_per_seq: int = 0,
+                      scale: Optional[float] = None, out_dtype=None, stream=None):
+    """fd_prefill_attention with out and lse allocated by torch on q's device;
+    q is [B, q_len, Hq, d]. Returns (out, lse)."""
+    import torch
+
+    B, q_len, hq, d = q.shape
+    problem = make_problem(batch=B, num_q_heads=hq, num_kv_heads=k.shape[-2], head_dim=d, kv_dtype=k.dtype,
+                           out_dtype=out_dtype or torch.float32, scale=scale, page_size=page_size,
+                           max_pages_per_seq=max_pages_per_seq or (block_table.shape[1] if block_table is not None else 0),
+                           q_len=q_len)
+    lens_dev = seq_lens if (hasattr(seq_lens, "is_cuda") and seq_lens.is_cuda) else \
+        torch.tensor(list(seq_lens.tolist() if hasattr(seq_lens, "tolist") else seq_lens), dtype=torch.int32,
+                     device=q.device)
+    out = torch.empty(tuple(q.shape), dtype=out_dtype or torch.float32, device=q.device)
+    lse = torch.empty(tuple(q.shape[:-1]), dtype=torch.float32, device=q.device)
+    fd_prefill_attention(problem, q, k, v, block_table, lens_dev, out, lse, stream)
+    return out, lse
 
 
 def fd_append_kv(problem: FdProblem, k_new, v_new, q, k_cache, v_cache, block_table, seq_lens_dev, *,

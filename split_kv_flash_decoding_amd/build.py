@@ -21,7 +21,7 @@ LIB_NAME = "libfd.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
 SOURCES = ["fd_host.cpp", "fd_api.hip", "fd_partial_valu.hip", "fd_partial_mfma.hip", "fd_combine.hip",
-           "fd_append.hip", "fd_probe.hip"]
+           "fd_append.hip", "fd_prefill.hip", "fd_probe.hip"]
 
 # Packed fp32 instructions stay off (the compiler would otherwise form
 # v_pk_* fp32 ops from float code). MFMA accumulators live in ordinary VGPRs:

@@ -173,6 +173,47 @@ fd_status fd_decode_attention(const fd_problem* p, const void* q, const void* k,
                                       lse, workspace, workspace_bytes_avail, stream);
 }
 
+fd_status fd_prefill_attention(const fd_problem* p, const void* q, const void* k, const void* v,
+                               const int32_t* block_table, const int32_t* seq_lens_dev, void* out, float* lse,
+                               void* stream) {
+    clear_error();
+    if (!p) return fail(FD_ERR_INVALID_ARGUMENT, "problem is NULL");
+    // Any number of query tokens: the decode kernels' q_len limits do not apply.
+    fd_problem one = *p;
+    one.q_len = 1;
+    float scale = 0.f;
+    fd_status st = check_problem(&one, &scale);
+    if (st != FD_OK) return st;
+    if (p->q_len < 0) return fail(FD_ERR_INVALID_ARGUMENT, "q_len %d < 0", p->q_len);
+    if (p->head_dim != 128) return fail(FD_ERR_UNSUPPORTED, "prefill is built for head_dim 128");
+    if (p->kv_dtype == FD_FP8_E4M3) return fail(FD_ERR_UNSUPPORTED, "prefill reads fp16 or bf16 caches");
+    if (!q || !k || !v || !seq_lens_dev || !out)
+        return fail(FD_ERR_INVALID_ARGUMENT, "q, k, v, seq_lens_dev and out must be non-NULL");
+    if (p->page_size && !block_table) return fail(FD_ERR_INVALID_ARGUMENT, "paged cache needs a block table");
+    if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v)) & 15)
+        return fail(FD_ERR_INVALID_ARGUMENT, "q, k and v must be 16-byte aligned");
+    const int64_t blocks = (int64_t)p->batch * p->num_q_heads * ((problem_q_len(p) + 127) / 128);
+    if (blocks > INT32_MAX) return fail(FD_ERR_INVALID_ARGUMENT, "too many query blocks");
+    fdk::PrefillArgs a;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.table = block_table;
+    a.lens = seq_lens_dev;
+    a.out = out;
+    a.lse = lse;
+    a.batch = p->batch;
+    a.hq = p->num_q_heads;
+    a.hkv = p->num_kv_heads;
+    a.q_len = problem_q_len(p);
+    a.max_pages = p->page_size ? p->max_pages_per_seq : 0;
+    a.qk_scale_log2 = scale * fdk::kLog2e;
+    hipError_t e = fdk::launch_prefill(a, p->kv_dtype, p->out_dtype, p->page_size != 0,
+                                       static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(FD_ERR_HIP, "prefill kernel launch: %s", hipGetErrorString(e));
+    return FD_OK;
+}
+
 fd_status fd_append_kv(const fd_problem* p, int32_t rope_style, float rope_base, const void* k_new,
                        const void* v_new, void* q, const float* k_scale, const float* v_scale, void* k_cache,
                        void* v_cache, int32_t num_pages, const int32_t* block_table, const int32_t* seq_lens_dev,

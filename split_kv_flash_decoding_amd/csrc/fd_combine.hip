@@ -12,16 +12,6 @@
 
 namespace fdk {
 
-template <int OUT> __device__ __forceinline__ void store_out(void* out, int64_t i, float x);
-template <> __device__ __forceinline__ void store_out<FD_F32>(void* out, int64_t i, float x) {
-    reinterpret_cast<float*>(out)[i] = x;
-}
-template <> __device__ __forceinline__ void store_out<FD_F16>(void* out, int64_t i, float x) {
-    reinterpret_cast<_Float16*>(out)[i] = (_Float16)x;
-}
-template <> __device__ __forceinline__ void store_out<FD_BF16>(void* out, int64_t i, float x) {
-    reinterpret_cast<__bf16*>(out)[i] = (__bf16)x;
-}
 
 constexpr int kCombineWaves = 4;
 

@@ -285,6 +285,31 @@ struct PartialArgs {
 // Scale of KV head g (1 when no scales are given).
 __device__ __forceinline__ float head_scale(const float* __restrict__ sc, int g) { return sc ? sc[g] : 1.f; }
 
+// Store one output element in the output type (round to nearest even).
+template <int OUT> __device__ __forceinline__ void store_out(void* out, int64_t i, float x);
+template <> __device__ __forceinline__ void store_out<FD_F32>(void* out, int64_t i, float x) {
+    reinterpret_cast<float*>(out)[i] = x;
+}
+template <> __device__ __forceinline__ void store_out<FD_F16>(void* out, int64_t i, float x) {
+    reinterpret_cast<_Float16*>(out)[i] = (_Float16)x;
+}
+template <> __device__ __forceinline__ void store_out<FD_BF16>(void* out, int64_t i, float x) {
+    reinterpret_cast<__bf16*>(out)[i] = (__bf16)x;
+}
+
+// Arguments of the prefill kernel (fd_prefill_attention).
+struct PrefillArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const int32_t* table;
+    const int32_t* lens;
+    void* out;
+    float* lse;
+    int batch, hq, hkv, q_len, max_pages;
+    float qk_scale_log2;
+};
+
 // Arguments of the KV-append kernel (fd_append_kv).
 struct AppendArgs {
     const void* k_new;
@@ -306,6 +331,7 @@ hipError_t launch_partial_valu(int D, int G, bool paged, const PartialArgs& a, d
 hipError_t launch_partial_valu_heads(int D, int G, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st);
 hipError_t launch_partial_mfma(int G, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st);
 hipError_t launch_append(const AppendArgs& a, int q_dt, int kv_dt, int blocks, hipStream_t st);
+hipError_t launch_prefill(const PrefillArgs& a, int dt, int out_dt, bool paged, hipStream_t st);
 hipError_t launch_combine(int D, int out_dt, const float* ws_o, const float* ws_ml, const int32_t* lens,
                           void* out, float* lse, int B, int hq, int chunk, int s_max, hipStream_t st);
 

@@ -1,0 +1,307 @@
+// Prefill attention: the FlashAttention-2 forward pass over a sequence's new
+// tokens, causal, on matrix cores.
+//
+// The method ("FlashAttention 全景演进与大模型 Token 生成全链路性能优化实战",
+// §2.1): the outer loop runs over blocks of query rows, which stay on chip,
+// and the inner loop over K/V blocks; the running max m and sum l of every
+// row are updated per block and the output is divided by l once, after the
+// last block (the tile recurrence of §1.2 / §1.3); K/V blocks wholly past
+// every row's causal limit are not visited. The block sizes follow the same
+// page's on-chip budget for d = 128: 128 query rows, K/V tiles of 32 tokens
+// (the page suggests B_r = 64 or 128 with B_c = 64).
+//
+// Query rows are the q_len new tokens of each sequence, the last q_len
+// positions of its cache: query i of sequence b sees tokens
+// 0 .. L_b - q_len + i (q_len = L_b is plain causal prefill; a smaller q_len
+// is a chunk of a longer prompt).
+//
+// One work-group of four wave64s per (sequence, query head, block of 128
+// query rows); blocks with more visible tokens are dispatched first. Per
+// 32-token tile:
+//   * the work-group loads the K and V tile (256 threads x 16 bytes per
+//     instruction, the next tile's loads in flight during the current tile's
+//     compute) into LDS rows padded to 288 bytes;
+//   * each wave owns 32 query rows as two 16-column MFMA tiles. Scores
+//     S^T [32 tokens x 16 rows] = K_tile . Q^T as v_mfma_f32_16x16x32 with K
+//     read from LDS (A operand) and Q^T held in registers (B operand); lane l
+//     then holds 8 tokens of row l % 16;
+//   * online softmax per row in the log2 domain, with the lazily moved
+//     reference max of the decode kernel (rescale only when a row's max grows
+//     by more than 2^8);
+//   * O^T [128 dims x 16 rows] += V^T . P^T as v_mfma_f32_16x16x32: P^T is
+//     the score layout itself (the contraction's token order is free, so the
+//     A operand's token slots are matched to it), V^T comes from two
+//     transposing LDS reads (ds_read_b64_tr_b16) per 16-dim block. bf16
+//     probabilities are split into high and low parts (two products), so
+//     rounding P to 8 mantissa bits does not reach the output; fp16 keeps one;
+//   * at the end each row's sum is reduced over its four lanes, O is divided
+//     by l once and written with the natural-log LSE.
+
+#include "fd_device.h"
+
+namespace fdk {
+
+namespace {
+
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kD = 128;
+constexpr int kBc = 32;             // tokens per K/V tile
+constexpr int kPW = 4;              // waves per work-group
+constexpr int kQW = 32;             // query rows per wave (two 16-column tiles)
+constexpr int kBr = kPW * kQW;      // query rows per work-group
+constexpr int kPitch = kD + 16;     // LDS row pitch, elements
+
+template <int DT> struct Mma;
+template <> struct Mma<FD_F16> {
+    static constexpr bool kSplitP = false;
+    static __device__ __forceinline__ f32x4_t mma(u32x4 a, u32x4 b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b),
+                                                      c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ uint32_t pack(float a, float b) {
+        return __builtin_bit_cast(uint32_t, half2_t{(_Float16)a, (_Float16)b});
+    }
+    static __device__ __forceinline__ float back(float a) { return (float)(_Float16)a; }
+};
+template <> struct Mma<FD_BF16> {
+    static constexpr bool kSplitP = true;
+    static __device__ __forceinline__ f32x4_t mma(u32x4 a, u32x4 b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ uint32_t pack(float a, float b) {
+        return __builtin_bit_cast(uint32_t, bf162_t{(__bf16)a, (__bf16)b});
+    }
+    static __device__ __forceinline__ float back(float a) { return (float)(__bf16)a; }
+};
+
+__device__ __forceinline__ i16x4_t lds_tr(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4_t*)(const_cast<uint16_t*>(p)));
+}
+
+__device__ __forceinline__ u32x4 join(i16x4_t a, i16x4_t b) {
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    const u32x2_t x = __builtin_bit_cast(u32x2_t, a);
+    const u32x2_t y = __builtin_bit_cast(u32x2_t, b);
+    return u32x4{x[0], x[1], y[0], y[1]};
+}
+
+}  // namespace
+
+template <int DT, int OUT, bool PAGED>
+__global__ __launch_bounds__(64 * kPW) void prefill_fa2(const PrefillArgs a) {
+    using M = Mma<DT>;
+    __shared__ __attribute__((aligned(16))) uint16_t sk[kBc * kPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t sv[kBc * kPitch];
+
+    // Work-group -> (query block, sequence, head), query blocks in descending
+    // order so the longest causal rows start first.
+    const int bh = a.batch * a.hq;
+    const int nqb = (a.q_len + kBr - 1) / kBr;
+    const int qblk = nqb - 1 - (int)(blockIdx.x / bh);
+    const int b = (blockIdx.x % bh) / a.hq;
+    const int h = blockIdx.x % a.hq;
+    const int G = a.hq / a.hkv;
+    const int g = h / G;
+
+    const int L = PAGED ? min(a.lens[b], a.max_pages * 16) : a.lens[b];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int grp = lane >> 4;
+    const int col = lane & 15;
+
+    // Packed cache: sequence b starts after the lengths before it.
+    int64_t row0 = 0;
+    if constexpr (!PAGED) {
+        for (int i = lane; i < b; i += 64) row0 += a.lens[i];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) row0 += __shfl_xor(row0, off);
+    }
+    const int32_t* table = PAGED ? a.table + (int64_t)b * a.max_pages : nullptr;
+
+    // Causal limits: query i sees tokens below L - q_len + i + 1.
+    const int q_first = qblk * kBr;
+    const int q_last = min(a.q_len, q_first + kBr) - 1;
+    const int blk_lim = min(L, L - a.q_len + q_last + 1);  // tokens any row of the block sees
+    const int ntiles = blk_lim > 0 ? (blk_lim + kBc - 1) / kBc : 0;
+
+    // This lane's two query rows (one per 16-column tile).
+    int qi[2], lim[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        qi[nt] = q_first + wave * kQW + 16 * nt + col;
+        lim[nt] = qi[nt] < a.q_len ? max(0, L - a.q_len + qi[nt] + 1) : 0;
+    }
+    int wave_lim = max(lim[0], lim[1]);  // tokens any row of this wave sees
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) wave_lim = max(wave_lim, __shfl_xor(wave_lim, off));
+
+    // Q^T as B operands: lane (grp, col) holds dims 32 j + 8 grp .. +8 of its row.
+    u32x4 qb[2][4];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        const int64_t qrow = ((int64_t)b * a.q_len + min(qi[nt], a.q_len - 1)) * a.hq + h;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            qb[nt][j] = qi[nt] < a.q_len ? *reinterpret_cast<const u32x4*>(a.q + qrow * kD + 32 * j + 8 * grp)
+                                         : u32x4{0u, 0u, 0u, 0u};
+    }
+
+    float m_ref[2], m_use[2], m_true[2], l_run[2];
+    f32x4_t acc[2][8];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        m_ref[nt] = neg_inf();
+        m_use[nt] = 0.f;
+        m_true[nt] = neg_inf();
+        l_run[nt] = 0.f;
+#pragma unroll
+        for (int jd = 0; jd < 8; ++jd) acc[nt][jd] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // Tile loads: thread t covers rows t / 16 and t / 16 + 16, dims 8 (t % 16) .. +8.
+    const int lr = threadIdx.x >> 4;
+    const int lc = threadIdx.x & 15;
+    const int64_t row_stride = (int64_t)a.hkv * kD;
+    const uint16_t* kg = a.k + (int64_t)g * kD + 8 * lc;
+    const uint16_t* vg = a.v + (int64_t)g * kD + 8 * lc;
+    auto row_of = [&](int t) -> int64_t {
+        t = min(t, L - 1);  // rows past the sequence are re-reads of its last row, masked below
+        if constexpr (PAGED) return (int64_t)table[t >> 4] * 16 + (t & 15);
+        return row0 + t;
+    };
+    u32x4 kr[2], vr[2];
+    auto load = [&](int tile) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int64_t off = row_of(tile * kBc + lr + 16 * i) * row_stride;
+            kr[i] = *reinterpret_cast<const u32x4*>(kg + off);
+            vr[i] = *reinterpret_cast<const u32x4*>(vg + off);
+        }
+    };
+
+    const uint16_t* vrd = sv + (4 * grp + ((lane >> 2) & 3)) * kPitch + 4 * (lane & 3);
+    if (ntiles > 0) load(0);
+    for (int tile = 0; tile < ntiles; ++tile) {
+        __syncthreads();  // every wave is done with the previous tile
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            *reinterpret_cast<u32x4*>(sk + (lr + 16 * i) * kPitch + 8 * lc) = kr[i];
+            *reinterpret_cast<u32x4*>(sv + (lr + 16 * i) * kPitch + 8 * lc) = vr[i];
+        }
+        if (tile + 1 < ntiles) load(tile + 1);
+        __syncthreads();
+        const int t0 = tile * kBc;
+        if (t0 >= wave_lim) continue;  // every row of this wave is past its causal limit
+
+        // Scores: S^T tile (mt, nt), lane (grp, col): tokens t0 + 16 mt + 4 grp + i of row col.
+        f32x4_t s[2][2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) s[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const u32x4 ka = *reinterpret_cast<const u32x4*>(sk + (16 * mt + col) * kPitch + 32 * j + 8 * grp);
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) s[mt][nt] = M::mma(ka, qb[nt][j], s[mt][nt]);
+            }
+        }
+
+        // V^T operands of the 8 dim blocks: token slots 8 grp + k <-> tokens
+        // 4 grp + k (k < 4) and 16 + 4 grp + k - 4, the score layout.
+        u32x4 va[8];
+#pragma unroll
+        for (int jd = 0; jd < 8; ++jd) va[jd] = join(lds_tr(vrd + 16 * jd), lds_tr(vrd + 16 * kPitch + 16 * jd));
+
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            float p[8];
+            float mx = neg_inf();
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = t0 + 16 * mt + 4 * grp + i;
+                    p[4 * mt + i] = t < lim[nt] ? s[mt][nt][i] * a.qk_scale_log2 : neg_inf();
+                    mx = fmaxf(mx, p[4 * mt + i]);
+                }
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            m_true[nt] = fmaxf(m_true[nt], mx);
+            if (__ballot(mx > m_ref[nt] + 8.f)) {
+                const float mn = fmaxf(m_ref[nt], mx);
+                const float mu = (mn == neg_inf()) ? 0.f : mn;
+                const float alpha = __builtin_amdgcn_exp2f(m_ref[nt] - mu);
+                l_run[nt] *= alpha;
+#pragma unroll
+                for (int jd = 0; jd < 8; ++jd) acc[nt][jd] = acc[nt][jd] * alpha;
+                m_ref[nt] = mn;
+                m_use[nt] = mu;
+            }
+            float ps = 0.f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                p[k] = __builtin_amdgcn_exp2f(p[k] - m_use[nt]);
+                ps += p[k];
+            }
+            l_run[nt] += ps;
+            u32x4 phi, plo;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                phi[w] = M::pack(p[2 * w], p[2 * w + 1]);
+                if constexpr (M::kSplitP)
+                    plo[w] = M::pack(p[2 * w] - M::back(p[2 * w]), p[2 * w + 1] - M::back(p[2 * w + 1]));
+            }
+#pragma unroll
+            for (int jd = 0; jd < 8; ++jd) {
+                acc[nt][jd] = M::mma(va[jd], phi, acc[nt][jd]);
+                if constexpr (M::kSplitP) acc[nt][jd] = M::mma(va[jd], plo, acc[nt][jd]);
+            }
+        }
+    }
+
+    // Finish every row: sum over its four lanes, divide once, natural-log LSE.
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        float l = l_run[nt];
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        if (qi[nt] >= a.q_len) continue;
+        const int64_t orow = ((int64_t)b * a.q_len + qi[nt]) * a.hq + h;
+        const bool empty = !(l > 0.f);
+        const float inv = empty ? 0.f : 1.f / l;
+#pragma unroll
+        for (int jd = 0; jd < 8; ++jd)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) store_out<OUT>(a.out, orow * kD + 16 * jd + 4 * grp + i, acc[nt][jd][i] * inv);
+        if (a.lse && grp == 0)
+            a.lse[orow] = empty ? neg_inf() : (m_use[nt] + log2f(l)) * kLn2;
+    }
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, int dt, int out_dt, bool paged, hipStream_t st) {
+    const int64_t blocks = (int64_t)a.batch * a.hq * ((a.q_len + kBr - 1) / kBr);
+    const dim3 grid((uint32_t)blocks), block(64 * kPW);
+    auto go = [&]<int DT, int OUT>() {
+        if (paged)
+            hipLaunchKernelGGL((prefill_fa2<DT, OUT, true>), grid, block, 0, st, a);
+        else
+            hipLaunchKernelGGL((prefill_fa2<DT, OUT, false>), grid, block, 0, st, a);
+    };
+    auto by_out = [&]<int DT>() {
+        if (out_dt == FD_F32) go.template operator()<DT, FD_F32>();
+        else if (out_dt == FD_F16) go.template operator()<DT, FD_F16>();
+        else go.template operator()<DT, FD_BF16>();
+    };
+    if (dt == FD_F16) by_out.template operator()<FD_F16>();
+    else by_out.template operator()<FD_BF16>();
+    return hipGetLastError();
+}
+
+}  // namespace fdk

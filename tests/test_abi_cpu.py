@@ -321,3 +321,21 @@ def test_append_validates_before_launching():
     bad.q_dtype = fd.FD_F32
     assert call(bad) == fd.FD_ERR_INVALID_ARGUMENT
     assert f8.q_dtype == fd.FD_F16
+
+
+def test_prefill_validates_before_launching():
+    """fd_prefill_attention: d = 128 and a 16-bit cache; any q_len; bad
+    arguments launch nothing."""
+    import torch
+    lib = fd.load_library()
+    fake = ctypes.c_void_p(0x10000)
+
+    def call(pp, q=fake, out=fake, table=None):
+        return lib.fd_prefill_attention(ctypes.byref(pp), q, fake, fake, table, fake, out, None, None)
+    assert call(prob(head_dim=64, q_len=100)) == fd.FD_ERR_UNSUPPORTED
+    assert call(prob(kv_dtype=torch.float8_e4m3fn, q_len=100)) == fd.FD_ERR_UNSUPPORTED
+    assert call(prob(q_len=100), q=None) == fd.FD_ERR_INVALID_ARGUMENT
+    assert call(prob(q_len=100), out=None) == fd.FD_ERR_INVALID_ARGUMENT
+    assert call(prob(q_len=100), q=ctypes.c_void_p(0x10008)) == fd.FD_ERR_INVALID_ARGUMENT
+    assert call(prob(q_len=100, page_size=16, max_pages_per_seq=8)) == fd.FD_ERR_INVALID_ARGUMENT  # no table
+    assert call(prob(q_len=-2)) == fd.FD_ERR_INVALID_ARGUMENT

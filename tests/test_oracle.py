@@ -436,3 +436,36 @@ def test_fp8_scales_apply_per_kv_head():
         for h in range(wl.num_q_heads):
             ob, lb = A.merge_partials(O[b, h, :S], m[b, h, :S], l[b, h, :S])
             assert np.allclose(ob, o[b, h], rtol=1e-12, atol=1e-13) and abs(lb - lse[b, h]) < 1e-12
+
+
+# ------------------------------------------------------------------ prefill
+
+
+def test_prefill_is_torch_causal_sdpa():
+    """q_len = L (every token of the sequence is a query): causal self-attention,
+    checked against torch's scaled_dot_product_attention(is_causal=True) in
+    float64 on the CPU (an independent implementation), GQA heads repeated."""
+    wl = make_workload(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=32, seq_lens=[37, 37],
+                       dtype=torch.bfloat16, seed=21, q_len=37)
+    out, lse = A.decode_attention_multi(wl.q, wl.k, wl.v, wl.seq_lens, wl.scale)
+    G = wl.group_size
+    for b in range(2):
+        q = wl.q[b].double().permute(1, 0, 2)                                   # [Hq, L, d]
+        kk = wl.k[37 * b: 37 * b + 37].double().permute(1, 0, 2).repeat_interleave(G, 0)
+        vv = wl.v[37 * b: 37 * b + 37].double().permute(1, 0, 2).repeat_interleave(G, 0)
+        ref = torch.nn.functional.scaled_dot_product_attention(q, kk, vv, is_causal=True, scale=wl.scale)
+        assert np.allclose(out[b].transpose(1, 0, 2), ref.numpy(), rtol=1e-12, atol=1e-12)
+        s = (q @ kk.transpose(1, 2)) * wl.scale
+        s = s.masked_fill(torch.triu(torch.ones(37, 37, dtype=torch.bool), 1), float("-inf"))
+        assert np.allclose(lse[b].T, torch.logsumexp(s, -1).numpy(), rtol=0, atol=1e-12)
+
+
+def test_sampled_query_rows_match_the_full_computation():
+    wl = make_workload(batch=2, num_q_heads=4, num_kv_heads=2, head_dim=16, seq_lens=[9, 30],
+                       dtype=torch.float16, seed=22, q_len=5)
+    full = A.decode_attention_multi(wl.q, wl.k, wl.v, wl.seq_lens, wl.scale)
+    rows = [(0, 4, 1), (1, 0, 3), (1, 2, 0)]
+    part = A.decode_attention_multi(wl.q, wl.k, wl.v, wl.seq_lens, wl.scale, rows=rows)
+    for b, i, h in rows:
+        assert np.array_equal(part[0][b, i, h], full[0][b, i, h]) and part[1][b, i, h] == full[1][b, i, h]
+    assert np.isnan(part[1]).sum() == part[1].size - len(rows)
