@@ -66,6 +66,15 @@ def measured_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def blas_threads() -> int:
+    """Threads the oracle's NumPy BLAS runs with."""
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([p.get("num_threads", 1) for p in threadpool_info()] or [1]))
+    except Exception:
+        return 1
+
+
 def cpu_baseline(wl, budget_s: float, out, lse):
     """Time the oracle, unchanged, on whole heads of the workload until the
     budget is spent, and compare the heads it computed with the GPU result."""
@@ -129,12 +138,109 @@ def cpu_baseline(wl, budget_s: float, out, lse):
     }
 
 
+PREFILL_METRIC = "TFLOP/s, causal prefill attention (FA-2 forward), 8K tokens, GQA 32/8, d=128"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 MFMA peak
+
+
+def prefill_flops(wl) -> float:
+    """Algorithmic flops: 4d per (query row, visible token, query head) (2d for
+    the score, 2d for the weighted sum of V)."""
+    q_len = wl.q.shape[1]
+    visible = sum(sum(L - q_len + i + 1 for i in range(q_len)) for L in wl.lens)
+    return 4.0 * wl.head_dim * wl.num_q_heads * visible
+
+
+def run_prefill(args, fd, dev) -> int:
+    """One step = one fd_prefill_attention call over the resident prompt."""
+    import numpy as np
+    import torch
+
+    from workloads import make_prefill
+
+    t = time.perf_counter()
+    wl = make_prefill()
+    log(f"generated {wl.name} in {time.perf_counter() - t:.1f} s")
+    q, k, v = wl.q.to(dev), wl.k.to(dev), wl.v.to(dev)
+    lens_dev = wl.seq_lens.to(dev)
+    q_len = wl.q.shape[1]
+    problem = fd.make_problem(batch=wl.batch, num_q_heads=wl.num_q_heads, num_kv_heads=wl.num_kv_heads,
+                              head_dim=wl.head_dim, kv_dtype=wl.dtype, out_dtype=torch.float32, scale=wl.scale,
+                              q_len=q_len)
+    out = torch.empty(tuple(q.shape), dtype=torch.float32, device=dev)
+    lse = torch.empty(tuple(q.shape[:-1]), dtype=torch.float32, device=dev)
+    flops = prefill_flops(wl)
+    for _ in range(max(1, args.warmup)):
+        fd.fd_prefill_attention(problem, q, k, v, None, lens_dev, out, lse)
+    torch.cuda.synchronize()
+    K = args.steps
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    start.record()
+    for _ in range(K):
+        fd.fd_prefill_attention(problem, q, k, v, None, lens_dev, out, lse)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = start.elapsed_time(end) / K
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"{K} steps: {ms * 1e3:.1f} us/step (events), wall {wall / K * 1e6:.1f} us/step; {tflops:.1f} TFLOP/s")
+    rec = {
+        "metric": PREFILL_METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) q/K/V; no dataset involved)",
+        "config": {"workload": wl.name, "batch": wl.batch, "q_heads": wl.num_q_heads,
+                   "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "q_len": q_len,
+                   "seq_lens_total": wl.total_tokens, "accumulate": "f32", "out_dtype": "f32",
+                   "flops_per_call": flops},
+        # The kernel is the whole step: one launch, timed by the same events.
+        "roofline": {"bound": "mfma", "kernel": "prefill", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        log(f"timing the CPU oracle on sampled query rows for about {args.cpu_budget:.0f} s ...")
+        r = np.random.default_rng(0)
+        done, fl = 0, 0.0
+        t0 = time.perf_counter()
+        ref_rows = []
+        while time.perf_counter() - t0 < args.cpu_budget:
+            rows = [(0, int(r.integers(0, q_len)), int(r.integers(0, wl.num_q_heads))) for _ in range(64)]
+            o, l = oracle.decode_attention_multi(wl.q, wl.k, wl.v, wl.seq_lens, wl.scale, rows=rows)
+            for (b, i, h) in rows:
+                fl += 4.0 * wl.head_dim * (wl.lens[b] - q_len + i + 1)
+                ref_rows.append((b, i, h, o[b, i, h], l[b, i, h]))
+            done += len(rows)
+        el = time.perf_counter() - t0
+        got = out.double().cpu().numpy()
+        got_l = lse.double().cpu().numpy()
+        d_o = np.concatenate([got[b, i, h] - o_ for b, i, h, o_, _ in ref_rows])
+        ref_o = np.concatenate([o_ for _, _, _, o_, _ in ref_rows])
+        rec["cpu_baseline"] = {
+            "value": round(fl / el / 1e12, 6), "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{done} random (row, head) pairs of the same prompt, {el:.1f} s wall",
+            "parity_of_sampled_rows": {
+                "o_max_abs": float(np.max(np.abs(d_o))),
+                "o_rel_rms": float(np.linalg.norm(d_o) / np.linalg.norm(ref_o)),
+                "lse_abs": float(max(abs(got_l[b, i, h] - l_) for b, i, h, _, l_ in ref_rows))}}
+    else:
+        rec["cpu_baseline"] = None
+    line = json.dumps(rec)
+    print(line, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(line + "\n")
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=3, help="workload 1..5 (default: 128K MHA)")
+    ap.add_argument("--workload", choices=("decode", "prefill"), default="decode",
+                    help="decode (default; --config picks the workload) or the 8192-token causal prefill")
+    ap.add_argument("--config", type=int, default=3, help="decode workload 1..5 (default: 128K MHA)")
     ap.add_argument("--q-len", type=int, default=1, help="query tokens per sequence (speculative verification)")
     ap.add_argument("--kv-fp8", action="store_true", help="FP8 (E4M3) cache with per-KV-head scales")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
@@ -158,6 +264,8 @@ def main() -> int:
         return 2
     fd.load_library()
     dev = torch.device("cuda", 0)
+    if args.workload == "prefill":
+        return run_prefill(args, fd, dev)
 
     t = time.perf_counter()
     wl = make_config(args.config, q_len=args.q_len, kv_fp8=args.kv_fp8)

@@ -48,8 +48,19 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
+#ifndef FD_PREFILL_BC
+#define FD_PREFILL_BC 64
+#endif
+#ifndef FD_PREFILL_BUFS
+#define FD_PREFILL_BUFS 2
+#endif
+
 constexpr int kD = 128;
-constexpr int kBc = 32;             // tokens per K/V tile
+constexpr int kBc = FD_PREFILL_BC;  // tokens per K/V tile (32 or 64)
+constexpr int kMT = kBc / 16;       // 16-token score tiles per K/V tile
+constexpr int kKS = kBc / 32;       // 32-token P.V steps per K/V tile
+constexpr int kLoads = kBc / 16;    // 16-byte loads of K (and of V) per thread per tile
+constexpr int kBufs = FD_PREFILL_BUFS;
 constexpr int kPW = 4;              // waves per work-group
 constexpr int kQW = 32;             // query rows per wave (two 16-column tiles)
 constexpr int kBr = kPW * kQW;      // query rows per work-group
@@ -96,8 +107,8 @@ __device__ __forceinline__ u32x4 join(i16x4_t a, i16x4_t b) {
 template <int DT, int OUT, bool PAGED>
 __global__ __launch_bounds__(64 * kPW) void prefill_fa2(const PrefillArgs a) {
     using M = Mma<DT>;
-    __shared__ __attribute__((aligned(16))) uint16_t sk[kBc * kPitch];
-    __shared__ __attribute__((aligned(16))) uint16_t sv[kBc * kPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t sk[kBufs][kBc * kPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t sv[kBufs][kBc * kPitch];
 
     // Work-group -> (query block, sequence, head), query blocks in descending
     // order so the longest causal rows start first.
@@ -152,19 +163,18 @@ __global__ __launch_bounds__(64 * kPW) void prefill_fa2(const PrefillArgs a) {
                                          : u32x4{0u, 0u, 0u, 0u};
     }
 
-    float m_ref[2], m_use[2], m_true[2], l_run[2];
+    float m_ref[2], m_use[2], l_run[2];
     f32x4_t acc[2][8];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
         m_ref[nt] = neg_inf();
         m_use[nt] = 0.f;
-        m_true[nt] = neg_inf();
         l_run[nt] = 0.f;
 #pragma unroll
         for (int jd = 0; jd < 8; ++jd) acc[nt][jd] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    // Tile loads: thread t covers rows t / 16 and t / 16 + 16, dims 8 (t % 16) .. +8.
+    // Tile loads: thread t covers rows t / 16 + 16 i, dims 8 (t % 16) .. +8.
     const int lr = threadIdx.x >> 4;
     const int lc = threadIdx.x & 15;
     const int64_t row_stride = (int64_t)a.hkv * kD;
@@ -175,56 +185,50 @@ __global__ __launch_bounds__(64 * kPW) void prefill_fa2(const PrefillArgs a) {
         if constexpr (PAGED) return (int64_t)table[t >> 4] * 16 + (t & 15);
         return row0 + t;
     };
-    u32x4 kr[2], vr[2];
+    u32x4 kr[kLoads], vr[kLoads];
     auto load = [&](int tile) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < kLoads; ++i) {
             const int64_t off = row_of(tile * kBc + lr + 16 * i) * row_stride;
             kr[i] = *reinterpret_cast<const u32x4*>(kg + off);
             vr[i] = *reinterpret_cast<const u32x4*>(vg + off);
         }
     };
-
-    const uint16_t* vrd = sv + (4 * grp + ((lane >> 2) & 3)) * kPitch + 4 * (lane & 3);
-    if (ntiles > 0) load(0);
-    for (int tile = 0; tile < ntiles; ++tile) {
-        __syncthreads();  // every wave is done with the previous tile
+    auto stage = [&](int buf) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            *reinterpret_cast<u32x4*>(sk + (lr + 16 * i) * kPitch + 8 * lc) = kr[i];
-            *reinterpret_cast<u32x4*>(sv + (lr + 16 * i) * kPitch + 8 * lc) = vr[i];
+        for (int i = 0; i < kLoads; ++i) {
+            *reinterpret_cast<u32x4*>(sk[buf] + (lr + 16 * i) * kPitch + 8 * lc) = kr[i];
+            *reinterpret_cast<u32x4*>(sv[buf] + (lr + 16 * i) * kPitch + 8 * lc) = vr[i];
         }
-        if (tile + 1 < ntiles) load(tile + 1);
-        __syncthreads();
-        const int t0 = tile * kBc;
-        if (t0 >= wave_lim) continue;  // every row of this wave is past its causal limit
+    };
 
+    const int vrd = (4 * grp + ((lane >> 2) & 3)) * kPitch + 4 * (lane & 3);
+    auto compute = [&](int tile, int buf) {
+        const int t0 = tile * kBc;
+        const uint16_t* K = sk[buf];
+        const uint16_t* V = sv[buf];
         // Scores: S^T tile (mt, nt), lane (grp, col): tokens t0 + 16 mt + 4 grp + i of row col.
-        f32x4_t s[2][2];
+        f32x4_t s[kMT][2];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
+        for (int mt = 0; mt < kMT; ++mt) {
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) s[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const u32x4 ka = *reinterpret_cast<const u32x4*>(sk + (16 * mt + col) * kPitch + 32 * j + 8 * grp);
+                const u32x4 ka = *reinterpret_cast<const u32x4*>(K + (16 * mt + col) * kPitch + 32 * j + 8 * grp);
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) s[mt][nt] = M::mma(ka, qb[nt][j], s[mt][nt]);
             }
         }
 
-        // V^T operands of the 8 dim blocks: token slots 8 grp + k <-> tokens
-        // 4 grp + k (k < 4) and 16 + 4 grp + k - 4, the score layout.
-        u32x4 va[8];
-#pragma unroll
-        for (int jd = 0; jd < 8; ++jd) va[jd] = join(lds_tr(vrd + 16 * jd), lds_tr(vrd + 16 * kPitch + 16 * jd));
-
+        // Online softmax per row; P^T packed as the B operands of the P.V steps.
+        u32x4 phi[2][kKS], plo[2][kKS];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-            float p[8];
+            float p[4 * kMT];
             float mx = neg_inf();
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
+            for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int t = t0 + 16 * mt + 4 * grp + i;
@@ -233,7 +237,6 @@ __global__ __launch_bounds__(64 * kPW) void prefill_fa2(const PrefillArgs a) {
                 }
             mx = fmaxf(mx, __shfl_xor(mx, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
-            m_true[nt] = fmaxf(m_true[nt], mx);
             if (__ballot(mx > m_ref[nt] + 8.f)) {
                 const float mn = fmaxf(m_ref[nt], mx);
                 const float mu = (mn == neg_inf()) ? 0.f : mn;
@@ -246,22 +249,64 @@ __global__ __launch_bounds__(64 * kPW) void prefill_fa2(const PrefillArgs a) {
             }
             float ps = 0.f;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
+            for (int k = 0; k < 4 * kMT; ++k) {
                 p[k] = __builtin_amdgcn_exp2f(p[k] - m_use[nt]);
                 ps += p[k];
             }
             l_run[nt] += ps;
-            u32x4 phi, plo;
+            // k-step ks covers score tiles 2 ks and 2 ks + 1: p[8 ks .. 8 ks + 7].
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                phi[w] = M::pack(p[2 * w], p[2 * w + 1]);
-                if constexpr (M::kSplitP)
-                    plo[w] = M::pack(p[2 * w] - M::back(p[2 * w]), p[2 * w + 1] - M::back(p[2 * w + 1]));
-            }
+            for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const float x0 = p[8 * ks + 2 * w], x1 = p[8 * ks + 2 * w + 1];
+                    phi[nt][ks][w] = M::pack(x0, x1);
+                    if constexpr (M::kSplitP) plo[nt][ks][w] = M::pack(x0 - M::back(x0), x1 - M::back(x1));
+                }
+        }
+
+        // O^T += V^T . P^T per 32-token step: the A operand's token slots
+        // 8 grp + k are tokens 32 ks + 4 grp + k (k < 4) and 32 ks + 16 + 4 grp + k - 4,
+        // the score layout; two transposing reads per 16-dim block.
+#pragma unroll
+        for (int ks = 0; ks < kKS; ++ks) {
 #pragma unroll
             for (int jd = 0; jd < 8; ++jd) {
-                acc[nt][jd] = M::mma(va[jd], phi, acc[nt][jd]);
-                if constexpr (M::kSplitP) acc[nt][jd] = M::mma(va[jd], plo, acc[nt][jd]);
+                const u32x4 va = join(lds_tr(V + vrd + 32 * ks * kPitch + 16 * jd),
+                                      lds_tr(V + vrd + (32 * ks + 16) * kPitch + 16 * jd));
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    acc[nt][jd] = M::mma(va, phi[nt][ks], acc[nt][jd]);
+                    if constexpr (M::kSplitP) acc[nt][jd] = M::mma(va, plo[nt][ks], acc[nt][jd]);
+                }
+            }
+        }
+    };
+
+    if (ntiles > 0) {
+        load(0);
+        if constexpr (kBufs == 2) {
+            // Two LDS buffers: tile t+1 is staged while tile t is computed; one
+            // barrier per tile.
+            stage(0);
+            if (1 < ntiles) load(1);
+            __syncthreads();
+            for (int tile = 0; tile < ntiles; ++tile) {
+                const int cur = tile & 1;
+                if (tile * kBc < wave_lim) compute(tile, cur);
+                if (tile + 1 < ntiles) {
+                    stage(cur ^ 1);
+                    if (tile + 2 < ntiles) load(tile + 2);
+                }
+                __syncthreads();
+            }
+        } else {
+            for (int tile = 0; tile < ntiles; ++tile) {
+                __syncthreads();  // every wave is done with the previous tile
+                stage(0);
+                if (tile + 1 < ntiles) load(tile + 1);
+                __syncthreads();
+                if (tile * kBc < wave_lim) compute(tile, 0);
             }
         }
     }

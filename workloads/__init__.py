@@ -11,6 +11,7 @@ from .synth import (  # noqa: F401
     CONFIG_NAMES,
     Workload,
     make_config,
+    make_prefill,
     make_workload,
     poison_value,
 )

@@ -386,3 +386,17 @@ def make_config(i: int, seed: Optional[int] = None, q_len: int = 1, kv_fp8: bool
                              seq_lens=("loguniform", 512, 32768), dtype=torch.bfloat16, seed=s,
                              page_size=16, max_pages_per_seq=32768 // 16)
     raise ValueError(f"no config {i}")
+
+
+PREFILL_NAME = "prefill_gqa_b1_hq32_hkv8_d128_L8192_bf16_causal"
+
+
+def make_prefill(seed: int = 2000, length: int = 8192, dtype: torch.dtype = torch.bfloat16) -> Workload:
+    """Causal prefill of one 8192-token prompt: every token is a query
+    (q [1, L, 32, 128]), 8 KV heads (group 4), d = 128, N(0,1) values."""
+    wl = make_workload(name=PREFILL_NAME if (length, dtype) == (8192, torch.bfloat16) else
+                       f"prefill_gqa_b1_hq32_hkv8_d128_L{length}_{str(dtype).split('.')[-1]}_causal",
+                       batch=1, num_q_heads=32, num_kv_heads=8, head_dim=128, seq_lens=[length], dtype=dtype,
+                       seed=seed, q_len=length)
+    wl.q = wl.q.reshape(1, length, 32, 128)
+    return wl
