@@ -126,8 +126,9 @@ typedef struct fd_plan {
  * two work-groups (three when shorter last splits exist) while at most an
  * eighth of the tokens fall in shorter last splits. Chunks are multiples of
  * 64 and at least 256 tokens (1024 for the kernel whose work-groups cover
- * several heads; that kernel gives way to one head per work-group when its
- * work-groups would be fewer than the compute units).
+ * several heads, 2048 when the cache is FP8; that kernel gives way to one
+ * head per work-group when its work-groups would be fewer than the compute
+ * units).
  * `force_num_splits` > 0 instead sets C = ceil(max_b L_b / force) and accepts
  * any C >= 1. `num_cus` == 0 asks the current HIP device (the only HIP call
  * here; its count is cached per device). Validates the problem and every

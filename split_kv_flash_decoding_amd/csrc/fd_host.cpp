@@ -193,10 +193,13 @@ fd_status fd_plan_splits(const fd_problem* p, const int32_t* lens, int32_t num_c
             c = ceil_div(lmax, force_num_splits);
         } else {
             // Head-rows work-groups cover several heads and slow down below
-            // ~1024 tokens per split (measured: 32K tokens at 512-token chunks
-            // ran 23% slower than at 1024).
+            // ~1024 tokens (2 KB per head of a 16-bit cache) per split
+            // (measured: 32K tokens at 512-token chunks ran 23% slower than at
+            // 1024); an FP8 split needs twice the tokens for the same bytes
+            // (128K-token FP8 cache: 2048-token splits 3% faster than 1024).
+            const int32_t head_rows_min = kHeadRowsMinChunk * 2 / kv_elem_bytes(p);
             const int64_t min_chunk = std::max<int32_t>(
-                1, env_int("FD_MIN_CHUNK", kern == kPartialHeadRows ? kHeadRowsMinChunk : kDefaultMinChunk));
+                1, env_int("FD_MIN_CHUNK", kern == kPartialHeadRows ? head_rows_min : kDefaultMinChunk));
             // Work-groups are (sequence, KV head group, split). A chunk that
             // makes about num_cus * k of them, never below the minimum chunk, a
             // multiple of 64.

@@ -269,8 +269,10 @@ def test_fp8_problems():
     # d = 64: 16 heads per load; 8 KV heads cannot fill a head-rows wave
     assert fd.fd_plan_splits(prob(kv_dtype=f8, num_q_heads=8, num_kv_heads=8, head_dim=64), [500000],
                              num_cus=256).partial_kernel == 0
-    assert fd.fd_plan_splits(prob(kv_dtype=f8, num_q_heads=16, num_kv_heads=16, head_dim=64), [500000],
+    assert fd.fd_plan_splits(prob(kv_dtype=f8, num_q_heads=16, num_kv_heads=16, head_dim=64), [2_000_000],
                              num_cus=256).partial_kernel == 2
+    # FP8 head-rows splits hold at least 2048 tokens (the bytes of 1024 16-bit tokens)
+    assert plan.chunk_tokens == 2048 and fd.fd_plan_splits(prob(), [131072], num_cus=256).chunk_tokens == 2048
     # the workspace does not depend on the cache type
     assert plan.workspace_bytes == fd.fd_plan_splits(prob(), [131072], num_cus=256,
                                                      force_num_splits=plan.max_splits).workspace_bytes
