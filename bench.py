@@ -47,10 +47,13 @@ PARTIAL_SOURCES = ("fd_api.hip", "fd_device.h", "fd_host.cpp", "fd_internal.h", 
                    "fd_partial_valu.hip")
 
 
-def kernel_source_hash() -> str:
-    """Hash of the partial kernels' sources (see PARTIAL_SOURCES)."""
+PREFILL_SOURCES = ("fd_api.hip", "fd_device.h", "fd_internal.h", "fd_prefill.hip")
+
+
+def kernel_source_hash(kernel: str = "partial") -> str:
+    """Hash of the timed kernel's sources (PARTIAL_SOURCES or PREFILL_SOURCES)."""
     h = hashlib.sha256()
-    for name in PARTIAL_SOURCES:
+    for name in (PREFILL_SOURCES if kernel == "prefill" else PARTIAL_SOURCES):
         with open(os.path.join(KERNEL_SOURCES, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -60,15 +63,15 @@ def kv_bytes(wl) -> int:
     return wl.total_tokens * wl.num_kv_heads * wl.head_dim * 2 * wl.k.element_size()
 
 
-def measured_traffic(workload: str):
-    """Per-launch HBM bytes of the partial kernel from committed rocprofv3 PMC
+def measured_traffic(workload: str, kernel: str = "partial"):
+    """Per-launch HBM bytes of the timed kernel from committed rocprofv3 PMC
     runs, if they were taken on the current kernel source; else None."""
-    path = os.path.join(PROFILES, f"partial_{workload}_traffic.json")
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash(kernel):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -191,6 +194,13 @@ def run_prefill(args, fd, dev) -> int:
     ms = start.elapsed_time(end) / K
     tflops = flops / (ms * 1e-3) / 1e12
     log(f"{K} steps: {ms * 1e3:.1f} us/step (events), wall {wall / K * 1e6:.1f} us/step; {tflops:.1f} TFLOP/s")
+    # A plain copy of known size calibrates the HBM counters taken on this run.
+    src = torch.empty((256 << 20) // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    fd.fd_probe_copy(dst, src)
+    torch.cuda.synchronize()
+    del src, dst
+    traffic = measured_traffic(wl.name, "prefill")
     rec = {
         "metric": PREFILL_METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
@@ -201,7 +211,7 @@ def run_prefill(args, fd, dev) -> int:
                    "flops_per_call": flops},
         # The kernel is the whole step: one launch, timed by the same events.
         "roofline": {"bound": "mfma", "kernel": "prefill", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
     }
     if not args.no_cpu_baseline:
         import oracle
