@@ -62,7 +62,11 @@ constexpr int kKS = kBc / 32;       // 32-token P.V steps per K/V tile
 constexpr int kLoads = kBc / 16;    // 16-byte loads of K (and of V) per thread per tile
 constexpr int kBufs = FD_PREFILL_BUFS;
 constexpr int kPW = 4;              // waves per work-group
-constexpr int kQW = 32;             // query rows per wave (two 16-column tiles)
+#ifndef FD_PREFILL_QW
+#define FD_PREFILL_QW 32
+#endif
+constexpr int kQW = FD_PREFILL_QW;  // query rows per wave (16-column tiles)
+constexpr int kNT = kQW / 16;       // 16-column tiles per wave
 constexpr int kBr = kPW * kQW;      // query rows per work-group
 constexpr int kPitch = kD + 16;     // LDS row pitch, elements
 
@@ -132,6 +136,9 @@ __global__ __launch_bounds__(64 * kPW) void prefill_fa2(const PrefillArgs a) {
         for (int i = lane; i < b; i += 64) row0 += a.lens[i];
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) row0 += __shfl_xor(row0, off);
+        // Every lane holds the same sum; keep it in scalar registers.
+        row0 = ((int64_t)__builtin_amdgcn_readfirstlane((int)(row0 >> 32)) << 32) |
+               (uint32_t)__builtin_amdgcn_readfirstlane((int)(row0 & 0xffffffff));
     }
     const int32_t* table = PAGED ? a.table + (int64_t)b * a.max_pages : nullptr;
 
@@ -142,20 +149,31 @@ __global__ __launch_bounds__(64 * kPW) void prefill_fa2(const PrefillArgs a) {
     const int ntiles = blk_lim > 0 ? (blk_lim + kBc - 1) / kBc : 0;
 
     // This lane's two query rows (one per 16-column tile).
-    int qi[2], lim[2];
+    int qi[kNT], lim[kNT];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < kNT; ++nt) {
         qi[nt] = q_first + wave * kQW + 16 * nt + col;
         lim[nt] = qi[nt] < a.q_len ? max(0, L - a.q_len + qi[nt] + 1) : 0;
     }
-    int wave_lim = max(lim[0], lim[1]);  // tokens any row of this wave sees
+    int wave_lim = 0;            // tokens any row of this wave sees
+    int wave_min_lim = INT32_MAX;  // tokens every row of this wave sees
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) wave_lim = max(wave_lim, __shfl_xor(wave_lim, off));
+    for (int nt = 0; nt < kNT; ++nt) {
+        wave_lim = max(wave_lim, lim[nt]);
+        wave_min_lim = min(wave_min_lim, lim[nt]);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        wave_lim = max(wave_lim, __shfl_xor(wave_lim, off));
+        wave_min_lim = min(wave_min_lim, __shfl_xor(wave_min_lim, off));
+    }
+    wave_lim = __builtin_amdgcn_readfirstlane(wave_lim);
+    wave_min_lim = __builtin_amdgcn_readfirstlane(wave_min_lim);
 
     // Q^T as B operands: lane (grp, col) holds dims 32 j + 8 grp .. +8 of its row.
-    u32x4 qb[2][4];
+    u32x4 qb[kNT][4];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < kNT; ++nt) {
         const int64_t qrow = ((int64_t)b * a.q_len + min(qi[nt], a.q_len - 1)) * a.hq + h;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -163,10 +181,10 @@ __global__ __launch_bounds__(64 * kPW) void prefill_fa2(const PrefillArgs a) {
                                          : u32x4{0u, 0u, 0u, 0u};
     }
 
-    float m_ref[2], m_use[2], l_run[2];
-    f32x4_t acc[2][8];
+    float m_ref[kNT], m_use[kNT], l_run[kNT];
+    f32x4_t acc[kNT][8];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < kNT; ++nt) {
         m_ref[nt] = neg_inf();
         m_use[nt] = 0.f;
         l_run[nt] = 0.f;
@@ -174,24 +192,44 @@ __global__ __launch_bounds__(64 * kPW) void prefill_fa2(const PrefillArgs a) {
         for (int jd = 0; jd < 8; ++jd) acc[nt][jd] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    // Tile loads: thread t covers rows t / 16 + 16 i, dims 8 (t % 16) .. +8.
+    // Tile loads: thread t covers rows t / 16 + 16 i, dims 8 (t % 16) .. +8,
+    // as buffer loads from a wave-uniform base with fixed per-lane offsets.
+    // The descriptor ends at the sequence's last row, so rows past it read as
+    // zeros (they are masked) and nothing past the sequence is touched. A
+    // 16-row group of a tile is one page of a paged cache (tiles start on page
+    // boundaries).
     const int lr = threadIdx.x >> 4;
     const int lc = threadIdx.x & 15;
-    const int64_t row_stride = (int64_t)a.hkv * kD;
-    const uint16_t* kg = a.k + (int64_t)g * kD + 8 * lc;
-    const uint16_t* vg = a.v + (int64_t)g * kD + 8 * lc;
-    auto row_of = [&](int t) -> int64_t {
-        t = min(t, L - 1);  // rows past the sequence are re-reads of its last row, masked below
-        if constexpr (PAGED) return (int64_t)table[t >> 4] * 16 + (t & 15);
-        return row0 + t;
-    };
+    const int row_bytes = a.hkv * kD * 2;
+    const uint16_t* kh = a.k + (int64_t)g * kD;  // head g of row 0
+    const uint16_t* vh = a.v + (int64_t)g * kD;
     u32x4 kr[kLoads], vr[kLoads];
     auto load = [&](int tile) {
+        const int t0 = tile * kBc;
+        if constexpr (PAGED) {
 #pragma unroll
-        for (int i = 0; i < kLoads; ++i) {
-            const int64_t off = row_of(tile * kBc + lr + 16 * i) * row_stride;
-            kr[i] = *reinterpret_cast<const u32x4*>(kg + off);
-            vr[i] = *reinterpret_cast<const u32x4*>(vg + off);
+            for (int i = 0; i < kLoads; ++i) {
+                const int tg = t0 + 16 * i;  // first token of this page
+                // (wave-uniform: readfirstlane keeps the descriptor in scalar registers)
+                const int rows = __builtin_amdgcn_readfirstlane(max(0, min(16, L - tg)));
+                const int64_t page = rows > 0 ? (int64_t)table[tg >> 4] : 0;
+                const int voff = lr * row_bytes + 16 * lc;
+                kr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      make_rsrc(kh + page * 16 * a.hkv * kD, rows * row_bytes), voff, 0, 0));
+                vr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      make_rsrc(vh + page * 16 * a.hkv * kD, rows * row_bytes), voff, 0, 0));
+            }
+        } else {
+            const int rows = __builtin_amdgcn_readfirstlane(max(0, min(kBc, L - t0)));
+            const int64_t base = (row0 + t0) * a.hkv * kD;
+            const __amdgpu_buffer_rsrc_t rk = make_rsrc(kh + base, rows * row_bytes);
+            const __amdgpu_buffer_rsrc_t rv = make_rsrc(vh + base, rows * row_bytes);
+#pragma unroll
+            for (int i = 0; i < kLoads; ++i) {
+                const int voff = (16 * i + lr) * row_bytes + 16 * lc;
+                kr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, voff, 0, 0));
+                vr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff, 0, 0));
+            }
         }
     };
     auto stage = [&](int buf) {
@@ -208,23 +246,25 @@ __global__ __launch_bounds__(64 * kPW) void prefill_fa2(const PrefillArgs a) {
         const uint16_t* K = sk[buf];
         const uint16_t* V = sv[buf];
         // Scores: S^T tile (mt, nt), lane (grp, col): tokens t0 + 16 mt + 4 grp + i of row col.
-        f32x4_t s[kMT][2];
+        f32x4_t s[kMT][kNT];
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) {
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) s[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int nt = 0; nt < kNT; ++nt) s[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const u32x4 ka = *reinterpret_cast<const u32x4*>(K + (16 * mt + col) * kPitch + 32 * j + 8 * grp);
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) s[mt][nt] = M::mma(ka, qb[nt][j], s[mt][nt]);
+                for (int nt = 0; nt < kNT; ++nt) s[mt][nt] = M::mma(ka, qb[nt][j], s[mt][nt]);
             }
         }
 
         // Online softmax per row; P^T packed as the B operands of the P.V steps.
-        u32x4 phi[2][kKS], plo[2][kKS];
+        // Only tiles that reach past some row's causal limit need the mask.
+        const bool masked = t0 + kBc > wave_min_lim;
+        u32x4 phi[kNT][kKS], plo[kNT][kKS];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
+        for (int nt = 0; nt < kNT; ++nt) {
             float p[4 * kMT];
             float mx = neg_inf();
 #pragma unroll
@@ -232,7 +272,7 @@ __global__ __launch_bounds__(64 * kPW) void prefill_fa2(const PrefillArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int t = t0 + 16 * mt + 4 * grp + i;
-                    p[4 * mt + i] = t < lim[nt] ? s[mt][nt][i] * a.qk_scale_log2 : neg_inf();
+                    p[4 * mt + i] = (!masked || t < lim[nt]) ? s[mt][nt][i] * a.qk_scale_log2 : neg_inf();
                     mx = fmaxf(mx, p[4 * mt + i]);
                 }
             mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -275,7 +315,7 @@ __global__ __launch_bounds__(64 * kPW) void prefill_fa2(const PrefillArgs a) {
                 const u32x4 va = join(lds_tr(V + vrd + 32 * ks * kPitch + 16 * jd),
                                       lds_tr(V + vrd + (32 * ks + 16) * kPitch + 16 * jd));
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
+                for (int nt = 0; nt < kNT; ++nt) {
                     acc[nt][jd] = M::mma(va, phi[nt][ks], acc[nt][jd]);
                     if constexpr (M::kSplitP) acc[nt][jd] = M::mma(va, plo[nt][ks], acc[nt][jd]);
                 }
@@ -313,7 +353,7 @@ __global__ __launch_bounds__(64 * kPW) void prefill_fa2(const PrefillArgs a) {
 
     // Finish every row: sum over its four lanes, divide once, natural-log LSE.
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < kNT; ++nt) {
         float l = l_run[nt];
         l += __shfl_xor(l, 16);
         l += __shfl_xor(l, 32);
