@@ -53,10 +53,19 @@
  * Errors: no C++ exception crosses this interface. Every call returns an
  * fd_status; on failure fd_last_error_message() (per thread) says why.
  * Argument checks happen on the host before anything is enqueued, so a call
- * that returns an error has launched nothing. The device seq_lens must equal
- * the host seq_lens the plan was made from; the kernels bound every workspace
- * access by the plan and every paged access by max_pages_per_seq, but they
- * cannot check device lengths against the caller's contiguous cache size.
+ * that returns an error has launched nothing. The kernels bound every
+ * workspace access by the plan and every paged access by max_pages_per_seq,
+ * but they cannot check device lengths against the caller's contiguous cache
+ * size.
+ *
+ * Plans and device lengths: each device length must be at least 1 and at
+ * most the host length the plan was made from (equal in the common case).
+ * The kernels derive every sequence's splits from the device lengths, and
+ * work-groups past the resulting work list exit at once, so a plan made for
+ * upper-bound lengths serves every later step within those bounds: partial +
+ * combine can be captured once in a HIP graph and replayed while the
+ * sequences grow, only the contents of seq_lens_dev (and of the cache)
+ * changing. A contiguous cache is packed by the device lengths.
  */
 #ifndef FD_H
 #define FD_H
