@@ -167,6 +167,8 @@ fd_status fd_plan_splits(const fd_problem* problem, const int32_t* seq_lens_host
  *   O  [B, q_len*Hq, S_max, d]     at byte offset 0
  *   ML [B, q_len*Hq, S_max, 2]     after O: (m_s, l_s) pairs, m_s in
  *                                  natural-log units of the scaled score.
+ *   counters uint32 [B, Hkv]       at the next 16-byte boundary; used only by
+ *                                  fd_decode_fused.
  * Entries of splits a sequence does not have are left untouched.
  * q, k, v, block_table (NULL when contiguous), seq_lens_dev: device pointers.
  * q, k and v must be 16-byte aligned. An FP8 cache takes fd_decode_partial_scaled.
@@ -190,6 +192,40 @@ fd_status fd_decode_partial_scaled(const fd_problem* problem, const fd_plan* pla
                                    const float* k_scale, const float* v_scale,
                                    const int32_t* block_table, const int32_t* seq_lens_dev,
                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Partials and merge in one kernel launch (asynchronous on `stream`): every
+ * work-group writes its split's partial exactly as fd_decode_partial does;
+ * the last work-group of each (sequence, KV-head group) to finish then merges
+ * that group's splits as fd_combine does and writes out and lse. "Last" is
+ * decided by an arrival counter per (sequence, KV head) kept at the end of
+ * the workspace (the plan's workspace_bytes includes it): the counters must
+ * be zero before the first call on a workspace (fd_workspace_init), and every
+ * completed call leaves them zero again, so later calls, graph replays
+ * included, need no initialisation. No work-group waits for another. Calls
+ * that share a workspace must not overlap. Same arguments as
+ * fd_decode_partial_scaled (scales NULL for a 16-bit cache without scales),
+ * plus out and lse as for fd_combine.
+ * Cost: every work-group releases its partial at device scope before it
+ * arrives (on gfx950 an L2 write-back per wave), which costs more than the
+ * saved launch once there are more than a few dozen work-groups. Measured on
+ * MI355X: 1024 tokens x 8 heads 19.2 -> 12.7 us per step; 32K-token MHA
+ * 86.5 -> 105.8 us; 128K-token MHA 322.5 -> 393.8 us. Use it for small,
+ * launch-bound steps; fd_decode_partial + fd_combine otherwise.
+ */
+fd_status fd_decode_fused(const fd_problem* problem, const fd_plan* plan,
+                          const void* q, const void* k, const void* v,
+                          const float* k_scale, const float* v_scale,
+                          const int32_t* block_table, const int32_t* seq_lens_dev,
+                          void* workspace, size_t workspace_bytes, void* out, float* lse, void* stream);
+
+/*
+ * Zero the arrival counters of a workspace for fd_decode_fused (a small
+ * kernel on `stream`, no memset, so it may be recorded in a graph). Needed
+ * once per workspace allocation.
+ */
+fd_status fd_workspace_init(const fd_problem* problem, const fd_plan* plan, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /*
  * Merge the partials (asynchronous on `stream`).

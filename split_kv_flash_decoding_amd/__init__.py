@@ -31,12 +31,14 @@ from ._capi import (  # noqa: F401
     fd_append_kv,
     fd_combine,
     fd_decode_attention,
+    fd_decode_fused,
     fd_decode_partial,
     fd_plan_splits,
     fd_prefill_attention,
     prefill_attention,
     fd_probe_copy,
     fd_probe_read,
+    fd_workspace_init,
     load_library,
     make_problem,
     status_string,

@@ -32,6 +32,8 @@ EXPORTED = (
     "fd_decode_attention_scaled",
     "fd_append_kv",
     "fd_prefill_attention",
+    "fd_decode_fused",
+    "fd_workspace_init",
     "fd_status_string",
     "fd_last_error_message",
     "fd_probe_read",
@@ -107,8 +109,11 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.fd_append_kv.argtypes = [P, ctypes.c_int32, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32,
                                  vp, vp, vp]
     lib.fd_prefill_attention.argtypes = [P, vp, vp, vp, vp, vp, vp, f32p, vp]
+    lib.fd_decode_fused.argtypes = [P, Pl, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp, f32p, vp]
+    lib.fd_workspace_init.argtypes = [P, Pl, vp, ctypes.c_size_t, vp]
     for name in ("fd_plan_splits", "fd_decode_partial", "fd_combine", "fd_decode_attention",
-                 "fd_decode_partial_scaled", "fd_decode_attention_scaled", "fd_append_kv", "fd_prefill_attention"):
+                 "fd_decode_partial_scaled", "fd_decode_attention_scaled", "fd_append_kv", "fd_prefill_attention",
+                 "fd_decode_fused", "fd_workspace_init"):
         getattr(lib, name).restype = ctypes.c_int
     lib.fd_status_string.argtypes = [ctypes.c_int]
     lib.fd_status_string.restype = ctypes.c_char_p
@@ -254,6 +259,25 @@ def fd_decode_partial(problem: FdProblem, plan: FdPlan, q, k, v, block_table, se
     _check(lib.fd_decode_partial(
         ctypes.byref(problem), ctypes.byref(plan), _ptr(q), _ptr(k), _ptr(v), _ptr(block_table),
         _ptr(seq_lens_dev), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def fd_workspace_init(problem: FdProblem, plan: FdPlan, workspace, stream=None) -> None:
+    """Zero the fused merge's arrival counters (once per workspace)."""
+    _check(load_library().fd_workspace_init(ctypes.byref(problem), ctypes.byref(plan), _ptr(workspace),
+                                            workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def fd_decode_fused(problem: FdProblem, plan: FdPlan, q, k, v, block_table, seq_lens_dev, workspace, out, lse=None,
+                    stream=None, k_scale=None, v_scale=None) -> None:
+    """Partials and merge in one launch (include/fd.h); the workspace's
+    counters must have been zeroed once with fd_workspace_init."""
+    _check_tensors(problem, q, k, v, block_table, seq_lens_dev, plan.total_tokens)
+    _check_out(problem, out, lse)
+    _check_scales(problem, k_scale, v_scale)
+    _check(load_library().fd_decode_fused(
+        ctypes.byref(problem), ctypes.byref(plan), _ptr(q), _ptr(k), _ptr(v), _ptr(k_scale), _ptr(v_scale),
+        _ptr(block_table), _ptr(seq_lens_dev), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def _check_out(problem: FdProblem, out, lse) -> None:

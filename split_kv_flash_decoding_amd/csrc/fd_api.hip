@@ -2,6 +2,8 @@
 // fd_combine, fd_decode_attention[_scaled]) and the compute-unit query the
 // planner uses. Argument checks run on the host before anything is enqueued.
 
+#include <algorithm>
+
 #include "fd_device.h"
 
 namespace fd {
@@ -26,9 +28,11 @@ fd_status query_num_cus(int32_t* out) {
 
 namespace {
 
+// Partials, and with `out` non-NULL the fused merge as well.
 fd_status decode_partial(const fd_problem* p, const fd_plan* plan, const void* q, const void* k, const void* v,
                          const float* k_scale, const float* v_scale, const int32_t* block_table,
-                         const int32_t* seq_lens_dev, void* workspace, size_t workspace_bytes_avail, void* stream) {
+                         const int32_t* seq_lens_dev, void* workspace, size_t workspace_bytes_avail, void* stream,
+                         void* out = nullptr, float* lse = nullptr) {
     float scale = 0.f;
     fd_status st = check_problem(p, &scale);
     if (st != FD_OK) return st;
@@ -68,6 +72,12 @@ fd_status decode_partial(const fd_problem* p, const fd_plan* plan, const void* q
     a.max_pages = p->page_size ? p->max_pages_per_seq : 0;
     a.q_len = problem_q_len(p);
     a.qk_scale_log2 = scale * fdk::kLog2e;
+    a.counters = out ? reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) +
+                                                   workspace_counters_offset(p, plan->max_splits))
+                     : nullptr;
+    a.out = out;
+    a.lse = lse;
+    a.out_dt = p->out_dtype;
 
     // One work-group per (split, KV head group) of the work list (see locate_unit).
     const int32_t groups = p->num_kv_heads / heads_per_workgroup(p, plan->partial_kernel);
@@ -86,6 +96,11 @@ fd_status decode_partial(const fd_problem* p, const fd_plan* plan, const void* q
     }
     if (e != hipSuccess) return fail(FD_ERR_HIP, "partial kernel launch: %s", hipGetErrorString(e));
     return FD_OK;
+}
+
+__global__ void zero_u32(uint32_t* p, int64_t n) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
 }
 
 fd_status reject_fp8(const fd_problem* p, const char* call) {
@@ -119,6 +134,39 @@ fd_status fd_decode_partial_scaled(const fd_problem* p, const fd_plan* plan, con
     clear_error();
     return decode_partial(p, plan, q, k, v, k_scale, v_scale, block_table, seq_lens_dev, workspace,
                           workspace_bytes_avail, stream);
+}
+
+fd_status fd_workspace_init(const fd_problem* p, const fd_plan* plan, void* workspace, size_t workspace_bytes_avail,
+                            void* stream) {
+    clear_error();
+    fd_status st = check_problem(p, nullptr);
+    if (st != FD_OK) return st;
+    st = check_plan(p, plan);
+    if (st != FD_OK) return st;
+    if (!workspace) return fail(FD_ERR_INVALID_ARGUMENT, "workspace must be non-NULL");
+    if (workspace_bytes_avail < workspace_bytes(p, plan->max_splits))
+        return fail(FD_ERR_WORKSPACE_TOO_SMALL, "workspace holds %zu bytes, the plan needs %llu",
+                    workspace_bytes_avail, (unsigned long long)workspace_bytes(p, plan->max_splits));
+    if (reinterpret_cast<uintptr_t>(workspace) & 15)
+        return fail(FD_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+    // A kernel, not a memset: the call may be recorded in a graph.
+    const int64_t n = (int64_t)p->batch * p->num_kv_heads;
+    uint32_t* c = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + workspace_counters_offset(p, plan->max_splits));
+    const int blocks = (int)std::min<int64_t>((n + 255) / 256, 1024);
+    hipLaunchKernelGGL(zero_u32, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), c, n);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(FD_ERR_HIP, "workspace init launch: %s", hipGetErrorString(e));
+    return FD_OK;
+}
+
+fd_status fd_decode_fused(const fd_problem* p, const fd_plan* plan, const void* q, const void* k, const void* v,
+                          const float* k_scale, const float* v_scale, const int32_t* block_table,
+                          const int32_t* seq_lens_dev, void* workspace, size_t workspace_bytes_avail, void* out,
+                          float* lse, void* stream) {
+    clear_error();
+    if (!out) return fail(FD_ERR_INVALID_ARGUMENT, "out must be non-NULL");
+    return decode_partial(p, plan, q, k, v, k_scale, v_scale, block_table, seq_lens_dev, workspace,
+                          workspace_bytes_avail, stream, out, lse);
 }
 
 fd_status fd_combine(const fd_problem* p, const fd_plan* plan, const int32_t* seq_lens_dev,

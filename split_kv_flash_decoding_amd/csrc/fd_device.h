@@ -280,6 +280,12 @@ struct PartialArgs {
     int batch, hq, hkv, chunk, s_max, max_pages, q_len;
     float qk_scale_log2;
     int kv_dt, q_dt;
+    // Fused merge (fd_decode_fused): per-(sequence, KV head) arrival counters,
+    // zero between calls, and the outputs. counters == nullptr: partials only.
+    uint32_t* counters;
+    void* out;
+    float* lse;
+    int out_dt;
 };
 
 // Scale of KV head g (1 when no scales are given).
@@ -295,6 +301,15 @@ template <> __device__ __forceinline__ void store_out<FD_F16>(void* out, int64_t
 }
 template <> __device__ __forceinline__ void store_out<FD_BF16>(void* out, int64_t i, float x) {
     reinterpret_cast<__bf16*>(out)[i] = (__bf16)x;
+}
+// The same with the output type chosen at run time.
+__device__ __forceinline__ void store_out_dt(int dt, void* out, int64_t i, float x) {
+    if (dt == FD_F32)
+        store_out<FD_F32>(out, i, x);
+    else if (dt == FD_F16)
+        store_out<FD_F16>(out, i, x);
+    else
+        store_out<FD_BF16>(out, i, x);
 }
 
 // Arguments of the prefill kernel (fd_prefill_attention).
@@ -334,5 +349,99 @@ hipError_t launch_append(const AppendArgs& a, int q_dt, int kv_dt, int blocks, h
 hipError_t launch_prefill(const PrefillArgs& a, int dt, int out_dt, bool paged, hipStream_t st);
 hipError_t launch_combine(int D, int out_dt, const float* ws_o, const float* ws_ml, const int32_t* lens,
                           void* out, float* lse, int B, int hq, int chunk, int s_max, hipStream_t st);
+
+// ------------------------------------------------------------ fused merge
+
+// The combine step run by a partial kernel's own last work-group
+// (fd_decode_fused). Every work-group of a (sequence, head group) calls this
+// after writing its split's (O, m, l): it makes those writes visible and bumps
+// the group's arrival counter; the work-group whose arrival completes the
+// count merges every split of the group's ROWS rows (at most ROWS; `nrows`
+// of them) exactly as the combine kernel does (FlashAttention capstone §2.3
+// cross-chunk reduce) and sets the counter back to zero for the next call.
+// No work-group waits for another. Rows: r = i * (nkv * G) + k for query
+// token i and head k of the group, i.e. query row i * Hq + g0 * G + k.
+// `red` is the caller's wave-merge LDS buffer, at least NW * ROWS * D floats
+// for NW waves per work-group.
+template <int D, int ROWS, int NW>
+__device__ void fused_merge(const PartialArgs& a, int b, int L, int g0, int nkv, int nrows, float* red) {
+    constexpr int PER = D / 64;
+    __shared__ int s_last;
+    __shared__ float s_max[ROWS];
+    __shared__ float s_l[NW][ROWS];
+    const int S = (L + a.chunk - 1) / a.chunk;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // this work-group's partials, visible device-wide
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned prev = atomicAdd(a.counters + (int64_t)b * a.hkv + g0, 1u);
+        s_last = (prev + 1 == (unsigned)S);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the other work-groups' partials, not stale cache lines
+
+    const int G = a.hq / a.hkv;
+    const int R = a.q_len * a.hq;
+    const int per_tok = nkv * G;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    auto row_base = [&](int r) -> int64_t {  // first workspace slot of row r
+        const int qrow = (r / per_tok) * a.hq + g0 * G + r % per_tok;
+        return ((int64_t)b * R + qrow) * a.s_max;
+    };
+    // Row maxima: wave w takes rows w, w + NW, ...
+    for (int r = wave; r < nrows; r += NW) {
+        const int64_t base = row_base(r);
+        float m = neg_inf();
+        for (int s = lane; s < S; s += 64) m = fmaxf(m, a.ws_ml[(base + s) * 2]);
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+        if (lane == 0) s_max[r] = m;
+    }
+    __syncthreads();
+    // Wave w sums splits w, w + NW, ... of every row.
+    float acc[ROWS][PER], lsum[ROWS];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+        lsum[r] = 0.f;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[r][e] = 0.f;
+    }
+    for (int s = wave; s < S; s += NW) {
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
+            if (r < nrows) {
+                const int64_t slot = row_base(r) + s;
+                const float w = __builtin_amdgcn_exp2f((a.ws_ml[slot * 2] - s_max[r]) * kLog2e);
+                lsum[r] = fmaf(w, a.ws_ml[slot * 2 + 1], lsum[r]);
+#pragma unroll
+                for (int e = 0; e < PER; ++e) acc[r][e] = fmaf(w, a.ws_o[slot * D + lane * PER + e], acc[r][e]);
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+        if (r < nrows) {
+#pragma unroll
+            for (int e = 0; e < PER; ++e) red[(wave * ROWS + r) * D + lane * PER + e] = acc[r][e];
+            if (lane == 0) s_l[wave][r] = lsum[r];
+        }
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < nrows * D; idx += blockDim.x) {
+        const int r = idx / D, col = idx % D;
+        float l = 0.f, o = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            l += s_l[w][r];
+            o += red[(w * ROWS + r) * D + col];
+        }
+        const int qrow = (r / per_tok) * a.hq + g0 * G + r % per_tok;
+        const int64_t orow = (int64_t)b * R + qrow;
+        store_out_dt(a.out_dt, a.out, orow * D + col, o / l);
+        if (a.lse && col == 0) a.lse[orow] = s_max[r] + __builtin_amdgcn_logf(l) * kLn2;
+    }
+    if (threadIdx.x == 0) a.counters[(int64_t)b * a.hkv + g0] = 0u;  // ready for the next call
+}
 
 }  // namespace fdk

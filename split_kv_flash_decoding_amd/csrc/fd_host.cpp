@@ -82,9 +82,15 @@ uint64_t workspace_o_bytes(const fd_problem* p, int32_t max_splits) {
     return (uint64_t)p->batch * problem_q_len(p) * p->num_q_heads * max_splits * p->head_dim * sizeof(float);
 }
 
+uint64_t workspace_counters_offset(const fd_problem* p, int32_t max_splits) {
+    const uint64_t end = workspace_o_bytes(p, max_splits) +
+                         (uint64_t)p->batch * problem_q_len(p) * p->num_q_heads * max_splits * 2 * sizeof(float);
+    return (end + 15) / 16 * 16;
+}
+
 uint64_t workspace_bytes(const fd_problem* p, int32_t max_splits) {
-    return workspace_o_bytes(p, max_splits) +
-           (uint64_t)p->batch * problem_q_len(p) * p->num_q_heads * max_splits * 2 * sizeof(float);
+    const uint64_t counters = (uint64_t)p->batch * p->num_kv_heads * sizeof(uint32_t);
+    return workspace_counters_offset(p, max_splits) + (counters + 15) / 16 * 16;
 }
 
 bool mfma_applicable(const fd_problem* p) {

@@ -27,8 +27,11 @@ fd_status check_problem(const fd_problem* p, float* scale_out);
 // Checks a plan against the problem it is used with.
 fd_status check_plan(const fd_problem* p, const fd_plan* plan);
 
-// Workspace layout: O [B, Hq, S_max, d] then ML [B, Hq, S_max, 2], float32.
+// Workspace layout: O [B, q_len*Hq, S_max, d] then ML [B, q_len*Hq, S_max, 2],
+// float32, then the fused merge's arrival counters, uint32 [B, Hkv], at a
+// 16-byte aligned offset.
 uint64_t workspace_o_bytes(const fd_problem* p, int32_t max_splits);
+uint64_t workspace_counters_offset(const fd_problem* p, int32_t max_splits);
 uint64_t workspace_bytes(const fd_problem* p, int32_t max_splits);
 
 // Compute units of the current HIP device, cached per device (fd_api.hip).

@@ -441,6 +441,7 @@ __global__ __launch_bounds__(64 * kMW) void partial_mfma(const PartialArgs a) {
             ws_ml[slot * 2 + 1] = lsum;
         }
     }
+    if (a.counters) fused_merge<kD, NQ, kMW>(a, b, wu.L, g, 1, nq, &sm_o[0][0][0]);
 }
 
 template <int NQ, int KT, int QT>

@@ -62,6 +62,13 @@ def ceil_div(a, b):
     return -(-a // b)
 
 
+def workspace_bytes(B, rows, hkv, S, d=128):
+    """O and (m, l) per (sequence, query row, split), then a 16-byte aligned
+    uint32 arrival counter per (sequence, KV head)."""
+    part = B * rows * S * (d + 2) * 4
+    return ceil_div(part, 16) * 16 + ceil_div(B * hkv * 4, 16) * 16
+
+
 @pytest.mark.parametrize("hq,hkv,lens", [
     (32, 32, [32768]),
     (32, 32, [131072]),
@@ -81,7 +88,7 @@ def test_planner_properties(hq, hkv, lens):
     # every split non-empty, splits tile [0, L)
     for L, S in zip(lens, splits):
         assert (S - 1) * C < L <= S * C
-    assert plan.workspace_bytes == len(lens) * hq * plan.max_splits * (128 + 2) * 4
+    assert plan.workspace_bytes == workspace_bytes(len(lens), hq, hkv, plan.max_splits)
     # enough work-groups to cover the chip when there are enough tokens
     if sum(lens) * hkv >= 256 * 4 * 256:
         assert plan.total_splits * hkv >= 256
@@ -237,9 +244,7 @@ def test_multi_query_problems():
     """q_len > 1 runs on the matrix-core kernel: d = 128 and q_len * G <= 16."""
     plan = fd.fd_plan_splits(prob(num_q_heads=32, num_kv_heads=32, q_len=4), [131072], num_cus=256)
     assert plan.partial_kernel == 1
-    base = fd.fd_plan_splits(prob(num_q_heads=32, num_kv_heads=32, q_len=1), [131072], num_cus=256,
-                             force_num_splits=plan.max_splits)
-    assert plan.workspace_bytes == 4 * base.workspace_bytes
+    assert plan.workspace_bytes == workspace_bytes(1, 4 * 32, 32, plan.max_splits)
     assert fd.fd_plan_splits(prob(num_q_heads=64, num_kv_heads=8, q_len=2), [1000], num_cus=256).partial_kernel == 1
     for kw, lens, status in [
         (dict(head_dim=64, q_len=2), [100], fd.FD_ERR_UNSUPPORTED),
@@ -341,3 +346,20 @@ def test_prefill_validates_before_launching():
     assert call(prob(q_len=100), q=ctypes.c_void_p(0x10008)) == fd.FD_ERR_INVALID_ARGUMENT
     assert call(prob(q_len=100, page_size=16, max_pages_per_seq=8)) == fd.FD_ERR_INVALID_ARGUMENT  # no table
     assert call(prob(q_len=-2)) == fd.FD_ERR_INVALID_ARGUMENT
+
+
+def test_fused_calls_validate_before_launching():
+    lib = fd.load_library()
+    p = prob()
+    plan = fd.fd_plan_splits(p, [4096], num_cus=256)
+    fake = ctypes.c_void_p(0x10000)
+    need = plan.workspace_bytes
+    st = lib.fd_decode_fused(ctypes.byref(p), ctypes.byref(plan), fake, fake, fake, None, None, None, fake, fake,
+                             need, None, None, None)
+    assert st == fd.FD_ERR_INVALID_ARGUMENT  # no out
+    st = lib.fd_decode_fused(ctypes.byref(p), ctypes.byref(plan), fake, fake, fake, None, None, None, fake, fake,
+                             need - 16, fake, None, None)
+    assert st == fd.FD_ERR_WORKSPACE_TOO_SMALL
+    assert lib.fd_workspace_init(ctypes.byref(p), ctypes.byref(plan), None, need, None) == fd.FD_ERR_INVALID_ARGUMENT
+    assert lib.fd_workspace_init(ctypes.byref(p), ctypes.byref(plan), fake, need - 16, None) == \
+        fd.FD_ERR_WORKSPACE_TOO_SMALL
