@@ -124,9 +124,10 @@ __global__ __launch_bounds__(kThreads) void partial_valu(const PartialArgs a) {
                 sc[u][j] = valid ? dot * qk_scale_log2 : neg_inf();
             }
         }
-        float vf[U][EPL];
-#pragma unroll
-        for (int u = 0; u < U; ++u) KV::to_f32(vb[u], vf[u]);
+        // Running statistics first, then O = alpha O + sum_u p_u v_u with each
+        // V load widened to fp32 just before its products (one load's worth
+        // of fp32 values live at a time, not U).
+        float p[G][U];
 #pragma unroll
         for (int j = 0; j < G; ++j) {
             float mx = sc[0][j];
@@ -135,22 +136,25 @@ __global__ __launch_bounds__(kThreads) void partial_valu(const PartialArgs a) {
             const float mn = fmaxf(m[j], mx);
             const float mu = (mn == neg_inf()) ? 0.f : mn;
             const float alpha = __builtin_amdgcn_exp2f(m[j] - mu);
-            float p[U];
             float ps = 0.f;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                p[u] = __builtin_amdgcn_exp2f(sc[u][j] - mu);
-                ps += p[u];
+                p[j][u] = __builtin_amdgcn_exp2f(sc[u][j] - mu);
+                ps += p[j][u];
             }
             l[j] = l[j] * alpha + ps;
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-                float acc = o[j][e] * alpha;
-#pragma unroll
-                for (int u = 0; u < U; ++u) acc = fmaf(p[u], vf[u][e], acc);
-                o[j][e] = acc;
-            }
+            for (int e = 0; e < EPL; ++e) o[j][e] *= alpha;
             m[j] = mn;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float vf[EPL];
+            KV::to_f32(vb[u], vf);
+#pragma unroll
+            for (int j = 0; j < G; ++j)
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) o[j][e] = fmaf(p[j][u], vf[e], o[j][e]);
         }
     };
 
@@ -335,9 +339,10 @@ __global__ __launch_bounds__(kThreads) void partial_valu_heads(const PartialArgs
                 sc[u][j] = valid ? dot * qk_scale_log2 : neg_inf();
             }
         }
-        float vf[U][EPL];
-#pragma unroll
-        for (int u = 0; u < U; ++u) KV::to_f32(vb[u], vf[u]);
+        // Running statistics first, then O = alpha O + sum_u p_u v_u with each
+        // V load widened to fp32 just before its products (one load's worth
+        // of fp32 values live at a time, not U).
+        float p[G][U];
 #pragma unroll
         for (int j = 0; j < G; ++j) {
             float mx = sc[0][j];
@@ -346,22 +351,25 @@ __global__ __launch_bounds__(kThreads) void partial_valu_heads(const PartialArgs
             const float mn = fmaxf(m[j], mx);
             const float mu = (mn == neg_inf()) ? 0.f : mn;
             const float alpha = __builtin_amdgcn_exp2f(m[j] - mu);
-            float p[U];
             float ps = 0.f;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                p[u] = __builtin_amdgcn_exp2f(sc[u][j] - mu);
-                ps += p[u];
+                p[j][u] = __builtin_amdgcn_exp2f(sc[u][j] - mu);
+                ps += p[j][u];
             }
             l[j] = l[j] * alpha + ps;
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-                float acc = o[j][e] * alpha;
-#pragma unroll
-                for (int u = 0; u < U; ++u) acc = fmaf(p[u], vf[u][e], acc);
-                o[j][e] = acc;
-            }
+            for (int e = 0; e < EPL; ++e) o[j][e] *= alpha;
             m[j] = mn;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float vf[EPL];
+            KV::to_f32(vb[u], vf);
+#pragma unroll
+            for (int j = 0; j < G; ++j)
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) o[j][e] = fmaf(p[j][u], vf[e], o[j][e]);
         }
     };
 
