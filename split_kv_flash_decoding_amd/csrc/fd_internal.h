@@ -1,5 +1,6 @@
 // Internal declarations shared by the host planner (fd_host.cpp) and the
-// kernels and launchers (fd_kernels.hip). Not part of the public interface.
+// entry points and kernel files (fd_api.hip, fd_partial_*.hip, ...). Not part
+// of the public interface.
 #pragma once
 
 #include <stddef.h>
@@ -9,7 +10,8 @@
 
 namespace fd {
 
-// Largest grid extent used along y (splits) and z (batch).
+// Largest batch (the combine kernel's grid y extent) and largest number of
+// splits of one sequence (the workspace's split stride) accepted.
 constexpr int32_t kMaxGridYZ = 65535;
 // Token rows a partial-kernel work-group consumes per pass (the planner keeps
 // automatic chunks a multiple of it).
