@@ -265,6 +265,7 @@ __global__ __launch_bounds__(64 * kPW) void prefill_fa2(const PrefillArgs a) {
         u32x4 phi[kNT][kKS], plo[kNT][kKS];
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) {
+            // Raw scores here; the (positive) scale joins the exponent's fma below.
             float p[4 * kMT];
             float mx = neg_inf();
 #pragma unroll
@@ -272,11 +273,12 @@ __global__ __launch_bounds__(64 * kPW) void prefill_fa2(const PrefillArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int t = t0 + 16 * mt + 4 * grp + i;
-                    p[4 * mt + i] = (!masked || t < lim[nt]) ? s[mt][nt][i] * a.qk_scale_log2 : neg_inf();
+                    p[4 * mt + i] = (!masked || t < lim[nt]) ? s[mt][nt][i] : neg_inf();
                     mx = fmaxf(mx, p[4 * mt + i]);
                 }
             mx = fmaxf(mx, __shfl_xor(mx, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
+            mx *= a.qk_scale_log2;  // log2 units
             if (__ballot(mx > m_ref[nt] + 8.f)) {
                 const float mn = fmaxf(m_ref[nt], mx);
                 const float mu = (mn == neg_inf()) ? 0.f : mn;
@@ -290,7 +292,7 @@ __global__ __launch_bounds__(64 * kPW) void prefill_fa2(const PrefillArgs a) {
             float ps = 0.f;
 #pragma unroll
             for (int k = 0; k < 4 * kMT; ++k) {
-                p[k] = __builtin_amdgcn_exp2f(p[k] - m_use[nt]);
+                p[k] = __builtin_amdgcn_exp2f(fmaf(p[k], a.qk_scale_log2, -m_use[nt]));
                 ps += p[k];
             }
             l_run[nt] += ps;
