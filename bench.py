@@ -335,8 +335,27 @@ def main() -> int:
     ms_per_step = start.elapsed_time(end) / K
     partial_ms = [a.elapsed_time(b) for a, b in zip(ev_a, ev_b)]
     partial_mean = statistics.fmean(partial_ms)
+    pq = statistics.quantiles(partial_ms, n=10)  # deciles: pq[0] = p10, pq[-1] = p90
     log(f"{K} steps: {ms_per_step * 1e3:.1f} us/step (events), wall {wall / K * 1e6:.1f} us/step; "
-        f"partial kernel mean {partial_mean * 1e3:.1f} us, median {statistics.median(partial_ms) * 1e3:.1f} us")
+        f"partial kernel mean {partial_mean * 1e3:.1f} us, median {statistics.median(partial_ms) * 1e3:.1f} us, "
+        f"p10 {pq[0] * 1e3:.1f}, p90 {pq[-1] * 1e3:.1f}")
+
+    # Cold caches: a 1 GiB write between steps (outside the timed pair) evicts
+    # the K/V from the L2s and the 256 MB Infinity Cache before each partial.
+    scratch = torch.empty((1 << 30) // 4, dtype=torch.float32, device=dev)
+    cold_ms = []
+    for i in range(min(K, 20)):
+        scratch.fill_(float(i))
+        p = fd.fd_plan_splits(problem, lens_host, 0, wl.force_num_splits)
+        ev_a[i].record()
+        fd.fd_decode_partial(problem, p, q, k, v, bt, lens_dev, ws, None, ks, vs)
+        ev_b[i].record()
+        fd.fd_combine(problem, p, lens_dev, ws, out, lse)
+    torch.cuda.synchronize()
+    cold_ms = [ev_a[i].elapsed_time(ev_b[i]) for i in range(min(K, 20))]
+    del scratch
+    cold_mean = statistics.fmean(cold_ms)
+    log(f"cold-cache partial kernel mean {cold_mean * 1e3:.1f} us over {len(cold_ms)} steps")
 
     # achievable streaming-read bandwidth on the same buffers, for context
     sink = torch.empty(fd.PROBE_SINK_FLOATS, dtype=torch.float32, device=dev)
@@ -403,6 +422,11 @@ def main() -> int:
             "frac": round(achieved / PEAK_HBM_GBPS, 4),
             "traffic": traffic,
             "partial_us_mean": round(partial_mean * 1e3, 2),
+            "partial_us_median": round(statistics.median(partial_ms) * 1e3, 2),
+            "partial_us_p10": round(pq[0] * 1e3, 2),
+            "partial_us_p90": round(pq[-1] * 1e3, 2),
+            "cold_partial_us_mean": round(cold_mean * 1e3, 2),
+            "cold_achieved": round(nbytes / (cold_mean * 1e-3) / 1e9, 1),
             "hbm_read_probe_gbps": round(probe_gbps, 1),
             "frac_of_probe": round(achieved / probe_gbps, 4),
         },
