@@ -107,6 +107,8 @@ typedef struct fd_problem {
     int32_t q_len;             /* query tokens per sequence, 0 or 1 = one; q_len > 1 needs d = 128
                                   and q_len * Hq/Hkv <= 16, and every L_b >= q_len */
     int32_t q_dtype;           /* FP8 cache: q's type, FD_F16 or FD_BF16; ignored otherwise */
+    int32_t num_pages;         /* paged: pages in the pool (0 = do not check page indices); a
+                                  table entry outside [0, num_pages) then reads page 0 instead */
 } fd_problem;
 
 /* How the splits are cut. Holds scalars only: nothing is uploaded per call,

@@ -55,6 +55,7 @@ class FdProblem(ctypes.Structure):
         ("max_pages_per_seq", ctypes.c_int32),
         ("q_len", ctypes.c_int32),
         ("q_dtype", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
     ]
 
     @property
@@ -152,7 +153,7 @@ def _dtype_code(dt) -> int:
 
 def make_problem(*, batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int, kv_dtype,
                  out_dtype=None, scale: Optional[float] = None, page_size: int = 0,
-                 max_pages_per_seq: int = 0, q_len: int = 1, q_dtype=None) -> FdProblem:
+                 max_pages_per_seq: int = 0, q_len: int = 1, q_dtype=None, num_pages: int = 0) -> FdProblem:
     """``kv_dtype``: the cache's torch dtype (float16, bfloat16 or
     float8_e4m3fn); ``q_dtype``: q's dtype for an FP8 cache (default
     float16)."""
@@ -163,7 +164,8 @@ def make_problem(*, batch: int, num_q_heads: int, num_kv_heads: int, head_dim: i
         kv_dtype=_dtype_code(kv_dtype), out_dtype=_dtype_code(out_dtype or torch.float32),
         scale=0.0 if scale is None else float(scale), page_size=page_size,
         max_pages_per_seq=max_pages_per_seq, q_len=q_len,
-        q_dtype=_dtype_code(q_dtype or torch.float16) if kv_dtype == torch.float8_e4m3fn else 0)
+        q_dtype=_dtype_code(q_dtype or torch.float16) if kv_dtype == torch.float8_e4m3fn else 0,
+        num_pages=num_pages)
 
 
 def _q_shape(problem: FdProblem, d: int):
@@ -234,6 +236,16 @@ def fd_plan_splits(problem: FdProblem, seq_lens_host, num_cus: int = 0, force_nu
     return plan
 
 
+def _with_pool(problem: FdProblem, k) -> FdProblem:
+    """The problem with the pool size of a paged cache filled in from k, so
+    the kernels check every page index against it."""
+    if problem.page_size and problem.num_pages == 0:
+        p = FdProblem.from_buffer_copy(problem)
+        p.num_pages = int(k.shape[0])
+        return p
+    return problem
+
+
 def _check_scales(problem: FdProblem, k_scale, v_scale) -> None:
     import torch
 
@@ -248,6 +260,7 @@ def fd_decode_partial(problem: FdProblem, plan: FdPlan, q, k, v, block_table, se
     """fd_decode_partial, or fd_decode_partial_scaled when the cache is FP8 or
     scales are given."""
     _check_tensors(problem, q, k, v, block_table, seq_lens_dev, plan.total_tokens)
+    problem = _with_pool(problem, k)
     lib = load_library()
     if problem.kv_dtype == FD_FP8_E4M3 or k_scale is not None or v_scale is not None:
         _check_scales(problem, k_scale, v_scale)
@@ -274,6 +287,7 @@ def fd_decode_fused(problem: FdProblem, plan: FdPlan, q, k, v, block_table, seq_
     _check_tensors(problem, q, k, v, block_table, seq_lens_dev, plan.total_tokens)
     _check_out(problem, out, lse)
     _check_scales(problem, k_scale, v_scale)
+    problem = _with_pool(problem, k)
     _check(load_library().fd_decode_fused(
         ctypes.byref(problem), ctypes.byref(plan), _ptr(q), _ptr(k), _ptr(v), _ptr(k_scale), _ptr(v_scale),
         _ptr(block_table), _ptr(seq_lens_dev), _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -305,6 +319,7 @@ def fd_decode_attention(problem: FdProblem, q, k, v, block_table, seq_lens_host,
     arr, vals = _lens_array(seq_lens_host)
     _check_tensors(problem, q, k, v, block_table, seq_lens_dev, sum(vals))
     _check_out(problem, out, lse)
+    problem = _with_pool(problem, k)
     lib = load_library()
     if problem.kv_dtype == FD_FP8_E4M3 or k_scale is not None or v_scale is not None:
         _check_scales(problem, k_scale, v_scale)
@@ -324,6 +339,7 @@ def fd_prefill_attention(problem: FdProblem, q, k, v, block_table, seq_lens_dev,
     in one pass (include/fd.h). q and out are [B, q_len, Hq, d]."""
     _check_tensors(problem, q, k, v, block_table, seq_lens_dev, None)
     _check_out(problem, out, lse)
+    problem = _with_pool(problem, k)
     _check(load_library().fd_prefill_attention(
         ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(block_table), _ptr(seq_lens_dev), _ptr(out),
         _ptr(lse), _stream(stream)))

@@ -72,6 +72,7 @@ fd_status decode_partial(const fd_problem* p, const fd_plan* plan, const void* q
     a.max_pages = p->page_size ? p->max_pages_per_seq : 0;
     a.q_len = problem_q_len(p);
     a.qk_scale_log2 = scale * fdk::kLog2e;
+    a.num_pages = p->page_size ? p->num_pages : 0;
     a.counters = out ? reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) +
                                                    workspace_counters_offset(p, plan->max_splits))
                      : nullptr;
@@ -256,6 +257,7 @@ fd_status fd_prefill_attention(const fd_problem* p, const void* q, const void* k
     a.q_len = problem_q_len(p);
     a.max_pages = p->page_size ? p->max_pages_per_seq : 0;
     a.qk_scale_log2 = scale * fdk::kLog2e;
+    a.num_pages = p->page_size ? p->num_pages : 0;
     hipError_t e = fdk::launch_prefill(a, p->kv_dtype, p->out_dtype, p->page_size != 0,
                                        static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(FD_ERR_HIP, "prefill kernel launch: %s", hipGetErrorString(e));

@@ -59,6 +59,14 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int byt
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
+// A page index read from a block table, checked against the pool when its
+// size is known (num_pages > 0): an index outside [0, num_pages) reads page 0
+// instead, so a bad table gives wrong numbers but never an access outside the
+// pool.
+__device__ __forceinline__ int checked_page(int page, int num_pages) {
+    return (num_pages > 0 && (unsigned)page >= (unsigned)num_pages) ? 0 : page;
+}
+
 // Reinterpret one 32-bit word as two 16-bit floats. The word is taken by value:
 // bit-casting an element of an ext_vector_type in place reads element 0 for
 // every index with this compiler.
@@ -280,6 +288,7 @@ struct PartialArgs {
     int batch, hq, hkv, chunk, s_max, max_pages, q_len;
     float qk_scale_log2;
     int kv_dt, q_dt;
+    int num_pages;  // pool size of a paged cache (0: indices not checked)
     // Fused merge (fd_decode_fused): per-(sequence, KV head) arrival counters,
     // zero between calls, and the outputs. counters == nullptr: partials only.
     uint32_t* counters;
@@ -323,6 +332,7 @@ struct PrefillArgs {
     float* lse;
     int batch, hq, hkv, q_len, max_pages;
     float qk_scale_log2;
+    int num_pages;  // pool size of a paged cache (0: indices not checked)
 };
 
 // Arguments of the KV-append kernel (fd_append_kv).

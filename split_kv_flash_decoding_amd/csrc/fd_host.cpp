@@ -67,6 +67,7 @@ fd_status check_problem(const fd_problem* p, float* scale_out) {
                     "page_size %d: 0 (contiguous) or 16 only", p->page_size);
     if (p->page_size && p->max_pages_per_seq < 1)
         return fail(FD_ERR_INVALID_ARGUMENT, "paged cache needs max_pages_per_seq >= 1");
+    if (p->num_pages < 0) return fail(FD_ERR_INVALID_ARGUMENT, "num_pages %d < 0", p->num_pages);
     if (!(p->scale == p->scale) || isinf(p->scale))
         return fail(FD_ERR_INVALID_ARGUMENT, "scale is not finite");
     if (p->q_len < 0) return fail(FD_ERR_INVALID_ARGUMENT, "q_len %d < 0", p->q_len);

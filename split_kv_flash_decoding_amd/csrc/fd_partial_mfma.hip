@@ -229,7 +229,7 @@ __global__ __launch_bounds__(64 * kMW) void partial_mfma(const PartialArgs a) {
 
     auto row_of = [&](int t) -> int64_t {
         if constexpr (PAGED) {
-            return (int64_t)table[t >> 4] * 16 + (t & 15);
+            return (int64_t)checked_page(table[t >> 4], a.num_pages) * 16 + (t & 15);
         } else {
             return row0 + t;
         }
@@ -242,7 +242,7 @@ __global__ __launch_bounds__(64 * kMW) void partial_mfma(const PartialArgs a) {
         const int blk = kk >> 6;
         if (blk != pg_blk) {
             const int tidx = wave + kMW * (64 * blk + lane);
-            pg = tidx < ntiles ? table[(t0 >> 4) + tidx] : 0;
+            pg = tidx < ntiles ? checked_page(table[(t0 >> 4) + tidx], a.num_pages) : 0;
             pg_blk = blk;
         }
         return (int64_t)__builtin_amdgcn_readlane(pg, kk & 63) * 16;

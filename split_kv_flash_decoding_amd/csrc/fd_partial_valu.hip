@@ -75,7 +75,7 @@ __global__ __launch_bounds__(kThreads) void partial_valu(const PartialArgs a) {
     auto row_offset = [&](int t) -> int64_t {
         int64_t row;
         if constexpr (PAGED) {
-            row = (int64_t)table[t >> 4] * 16 + (t & 15);
+            row = (int64_t)checked_page(table[t >> 4], a.num_pages) * 16 + (t & 15);
         } else {
             row = row0 + t;
         }
@@ -301,7 +301,7 @@ __global__ __launch_bounds__(kThreads) void partial_valu_heads(const PartialArgs
         const int blk = kk >> 6;
         if (blk != pg_blk) {
             const int st = wave + kWaves * (64 * blk + lane);
-            pg = st < nstages ? table[(t0 + st * U) >> 4] : 0;
+            pg = st < nstages ? checked_page(table[(t0 + st * U) >> 4], a.num_pages) : 0;
             pg_blk = blk;
         }
         return (int64_t)__builtin_amdgcn_readlane(pg, kk & 63) * 16;
@@ -318,7 +318,7 @@ __global__ __launch_bounds__(kThreads) void partial_valu_heads(const PartialArgs
             if constexpr (PAGE_MODE == 2) {
                 row = prow + (t & 15);
             } else if constexpr (PAGE_MODE == 1) {
-                row = (int64_t)table[t >> 4] * 16 + (t & 15);
+                row = (int64_t)checked_page(table[t >> 4], a.num_pages) * 16 + (t & 15);
             } else {
                 row = row0 + t;
             }

@@ -212,7 +212,7 @@ __global__ __launch_bounds__(64 * kPW) void prefill_fa2(const PrefillArgs a) {
                 const int tg = t0 + 16 * i;  // first token of this page
                 // (wave-uniform: readfirstlane keeps the descriptor in scalar registers)
                 const int rows = __builtin_amdgcn_readfirstlane(max(0, min(16, L - tg)));
-                const int64_t page = rows > 0 ? (int64_t)table[tg >> 4] : 0;
+                const int64_t page = rows > 0 ? (int64_t)checked_page(table[tg >> 4], a.num_pages) : 0;
                 const int voff = lr * row_bytes + 16 * lc;
                 kr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                                       make_rsrc(kh + page * 16 * a.hkv * kD, rows * row_bytes), voff, 0, 0));

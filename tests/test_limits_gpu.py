@@ -64,3 +64,34 @@ def test_lengths_around_page_and_chunk_edges(fd, L):
             res = run(fd, w, num_splits=splits)
             ref_out, ref_lse = reference(w)
             parity(res.out, res.lse, ref_out, ref_lse, what=f"L={L} paged={w.paged} splits={splits}")
+
+
+@pytest.mark.parametrize("kernel", [0, 1, 2])
+def test_out_of_pool_page_indices_read_page_zero(fd, monkeypatch, kernel):
+    """With the pool size known (the binding passes it), a table entry outside
+    [0, num_pages) reads page 0 instead of memory outside the pool: the result
+    is the oracle's on the table with those entries replaced by 0."""
+    monkeypatch.setenv("FD_PARTIAL_KERNEL", str(kernel))
+    wl = to_paged(make_workload(name="badpages", batch=2, num_q_heads=16, num_kv_heads=8, head_dim=128,
+                                seq_lens=[3000, 700], dtype=torch.bfloat16, seed=1440), 16, spare_pages=1,
+                  permute=False)  # page 0 is then the first (full) page of sequence 0, no NaN poison
+    bad = wl.block_table.clone()
+    bad[0, 5] = 10 ** 6
+    bad[0, 100] = -7
+    bad[1, 3] = wl.k.shape[0]          # one past the last page
+    fixed = bad.clone()
+    fixed[(bad < 0) | (bad >= wl.k.shape[0])] = 0
+    dev = torch.device("cuda", 0)
+    prob = fd.make_problem(batch=2, num_q_heads=16, num_kv_heads=8, head_dim=128, kv_dtype=torch.bfloat16,
+                           scale=wl.scale, page_size=16, max_pages_per_seq=wl.max_pages_per_seq)
+    plan = fd.fd_plan_splits(prob, wl.lens, 256)
+    assert plan.partial_kernel == kernel
+    ws = torch.empty(-(-plan.workspace_bytes // 4), dtype=torch.float32, device=dev)
+    out = torch.empty((2, 16, 128), dtype=torch.float32, device=dev)
+    lse = torch.empty((2, 16), dtype=torch.float32, device=dev)
+    lens = wl.seq_lens.to(dev)
+    fd.fd_decode_partial(prob, plan, wl.q.to(dev), wl.k.to(dev), wl.v.to(dev), bad.to(dev), lens, ws)
+    fd.fd_combine(prob, plan, lens, ws, out, lse)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle.decode_attention(wl.q, wl.k, wl.v, wl.seq_lens, wl.scale, fixed, 16)
+    parity(out, lse, ref_out, ref_lse, what=f"out-of-pool pages, kernel {kernel}")
