@@ -105,7 +105,7 @@ typedef struct fd_problem {
     int32_t page_size;         /* 0 = contiguous packed cache, 16 = paged */
     int32_t max_pages_per_seq; /* paged: columns of block_table; ignored otherwise */
     int32_t q_len;             /* query tokens per sequence, 0 or 1 = one; q_len > 1 needs d = 128
-                                  and q_len * Hq/Hkv <= 16, and every L_b >= q_len */
+                                  and q_len * Hq/Hkv <= 64, and every L_b >= q_len */
     int32_t q_dtype;           /* FP8 cache: q's type, FD_F16 or FD_BF16; ignored otherwise */
     int32_t num_pages;         /* paged: pages in the pool (0 = do not check page indices); a
                                   table entry outside [0, num_pages) then reads page 0 instead */

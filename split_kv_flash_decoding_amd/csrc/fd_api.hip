@@ -80,9 +80,13 @@ fd_status decode_partial(const fd_problem* p, const fd_plan* plan, const void* q
     a.lse = lse;
     a.out_dt = p->out_dtype;
 
-    // One work-group per (split, KV head group) of the work list (see locate_unit).
+    // One work-group per (split, KV head group) of the work list (see
+    // locate_unit), times the matrix-core kernel's column tiles (the grid is
+    // then padded to whole groups of 8 entries; the padding exits at once).
     const int32_t groups = p->num_kv_heads / heads_per_workgroup(p, plan->partial_kernel);
-    const int64_t units = (int64_t)plan->total_splits * groups;
+    const int32_t tiles = plan->partial_kernel == kPartialMfma ? mfma_column_tiles(p) : 1;
+    int64_t units = (int64_t)plan->total_splits * groups;
+    if (tiles > 1) units = (units + 7) / 8 * 8 * tiles;
     if (plan->total_splits < 1 || units > INT32_MAX)
         return fail(FD_ERR_INVALID_ARGUMENT, "plan has %d splits (x %d head groups)", plan->total_splits, groups);
     dim3 grid((uint32_t)units);

@@ -53,8 +53,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufferRsrcWord3);
 }
 
+template <int POLICY = kBufferLoadPolicy>
 __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int byte_offset) {
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, kBufferLoadPolicy));
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, POLICY));
 }
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
@@ -366,15 +367,15 @@ hipError_t launch_combine(int D, int out_dt, const float* ws_o, const float* ws_
 // (fd_decode_fused). Every work-group of a (sequence, head group) calls this
 // after writing its split's (O, m, l): it makes those writes visible and bumps
 // the group's arrival counter; the work-group whose arrival completes the
-// count merges every split of the group's ROWS rows (at most ROWS; `nrows`
-// of them) exactly as the combine kernel does (FlashAttention capstone §2.3
-// cross-chunk reduce) and sets the counter back to zero for the next call.
-// No work-group waits for another. Rows: r = i * (nkv * G) + k for query
-// token i and head k of the group, i.e. query row i * Hq + g0 * G + k.
-// `red` is the caller's wave-merge LDS buffer, at least NW * ROWS * D floats
-// for NW waves per work-group.
+// count (splits x `tiles` column tiles) merges every split of the group's
+// `nrows` rows, ROWS at a time, exactly as the combine kernel does
+// (FlashAttention capstone §2.3 cross-chunk reduce), and sets the counter back
+// to zero for the next call. No work-group waits for another. Rows:
+// r = i * (nkv * G) + k for query token i and head k of the group, i.e.
+// query row i * Hq + g0 * G + k. `red` is the caller's wave-merge LDS buffer,
+// at least NW * ROWS * D floats for NW waves per work-group.
 template <int D, int ROWS, int NW>
-__device__ void fused_merge(const PartialArgs& a, int b, int L, int g0, int nkv, int nrows, float* red) {
+__device__ void fused_merge(const PartialArgs& a, int b, int L, int g0, int nkv, int nrows, int tiles, float* red) {
     constexpr int PER = D / 64;
     __shared__ int s_last;
     __shared__ float s_max[ROWS];
@@ -384,7 +385,7 @@ __device__ void fused_merge(const PartialArgs& a, int b, int L, int g0, int nkv,
     __syncthreads();
     if (threadIdx.x == 0) {
         const unsigned prev = atomicAdd(a.counters + (int64_t)b * a.hkv + g0, 1u);
-        s_last = (prev + 1 == (unsigned)S);
+        s_last = (prev + 1 == (unsigned)(S * tiles));
     }
     __syncthreads();
     if (!s_last) return;
@@ -395,61 +396,62 @@ __device__ void fused_merge(const PartialArgs& a, int b, int L, int g0, int nkv,
     const int per_tok = nkv * G;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    auto row_base = [&](int r) -> int64_t {  // first workspace slot of row r
-        const int qrow = (r / per_tok) * a.hq + g0 * G + r % per_tok;
-        return ((int64_t)b * R + qrow) * a.s_max;
-    };
-    // Row maxima: wave w takes rows w, w + NW, ...
-    for (int r = wave; r < nrows; r += NW) {
-        const int64_t base = row_base(r);
-        float m = neg_inf();
-        for (int s = lane; s < S; s += 64) m = fmaxf(m, a.ws_ml[(base + s) * 2]);
+    auto qrow_of = [&](int r) { return (r / per_tok) * a.hq + g0 * G + r % per_tok; };
+    for (int r0 = 0; r0 < nrows; r0 += ROWS) {
+        const int nr = min(ROWS, nrows - r0);
+        // Row maxima: wave w takes rows w, w + NW, ...
+        for (int r = wave; r < nr; r += NW) {
+            const int64_t base = ((int64_t)b * R + qrow_of(r0 + r)) * a.s_max;
+            float m = neg_inf();
+            for (int s = lane; s < S; s += 64) m = fmaxf(m, a.ws_ml[(base + s) * 2]);
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-        if (lane == 0) s_max[r] = m;
-    }
-    __syncthreads();
-    // Wave w sums splits w, w + NW, ... of every row.
-    float acc[ROWS][PER], lsum[ROWS];
-#pragma unroll
-    for (int r = 0; r < ROWS; ++r) {
-        lsum[r] = 0.f;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) acc[r][e] = 0.f;
-    }
-    for (int s = wave; s < S; s += NW) {
+            for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+            if (lane == 0) s_max[r] = m;
+        }
+        __syncthreads();
+        // Wave w sums splits w, w + NW, ... of every row.
+        float acc[ROWS][PER], lsum[ROWS];
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) {
-            if (r < nrows) {
-                const int64_t slot = row_base(r) + s;
-                const float w = __builtin_amdgcn_exp2f((a.ws_ml[slot * 2] - s_max[r]) * kLog2e);
-                lsum[r] = fmaf(w, a.ws_ml[slot * 2 + 1], lsum[r]);
+            lsum[r] = 0.f;
 #pragma unroll
-                for (int e = 0; e < PER; ++e) acc[r][e] = fmaf(w, a.ws_o[slot * D + lane * PER + e], acc[r][e]);
+            for (int e = 0; e < PER; ++e) acc[r][e] = 0.f;
+        }
+        for (int s = wave; s < S; s += NW) {
+#pragma unroll
+            for (int r = 0; r < ROWS; ++r) {
+                if (r < nr) {
+                    const int64_t slot = ((int64_t)b * R + qrow_of(r0 + r)) * a.s_max + s;
+                    const float w = __builtin_amdgcn_exp2f((a.ws_ml[slot * 2] - s_max[r]) * kLog2e);
+                    lsum[r] = fmaf(w, a.ws_ml[slot * 2 + 1], lsum[r]);
+#pragma unroll
+                    for (int e = 0; e < PER; ++e)
+                        acc[r][e] = fmaf(w, a.ws_o[slot * D + lane * PER + e], acc[r][e]);
+                }
             }
         }
-    }
 #pragma unroll
-    for (int r = 0; r < ROWS; ++r) {
-        if (r < nrows) {
+        for (int r = 0; r < ROWS; ++r) {
+            if (r < nr) {
 #pragma unroll
-            for (int e = 0; e < PER; ++e) red[(wave * ROWS + r) * D + lane * PER + e] = acc[r][e];
-            if (lane == 0) s_l[wave][r] = lsum[r];
+                for (int e = 0; e < PER; ++e) red[(wave * ROWS + r) * D + lane * PER + e] = acc[r][e];
+                if (lane == 0) s_l[wave][r] = lsum[r];
+            }
         }
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < nrows * D; idx += blockDim.x) {
-        const int r = idx / D, col = idx % D;
-        float l = 0.f, o = 0.f;
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < nr * D; idx += blockDim.x) {
+            const int r = idx / D, col = idx % D;
+            float l = 0.f, o = 0.f;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            l += s_l[w][r];
-            o += red[(w * ROWS + r) * D + col];
+            for (int w = 0; w < NW; ++w) {
+                l += s_l[w][r];
+                o += red[(w * ROWS + r) * D + col];
+            }
+            const int64_t orow = (int64_t)b * R + qrow_of(r0 + r);
+            store_out_dt(a.out_dt, a.out, orow * D + col, o / l);
+            if (a.lse && col == 0) a.lse[orow] = s_max[r] + __builtin_amdgcn_logf(l) * kLn2;
         }
-        const int qrow = (r / per_tok) * a.hq + g0 * G + r % per_tok;
-        const int64_t orow = (int64_t)b * R + qrow;
-        store_out_dt(a.out_dt, a.out, orow * D + col, o / l);
-        if (a.lse && col == 0) a.lse[orow] = s_max[r] + __builtin_amdgcn_logf(l) * kLn2;
+        __syncthreads();  // s_max, s_l and red are reused by the next batch of rows
     }
     if (threadIdx.x == 0) a.counters[(int64_t)b * a.hkv + g0] = 0u;  // ready for the next call
 }

@@ -108,6 +108,11 @@ int32_t heads_per_workgroup(const fd_problem* p, int32_t kernel) {
     return kernel == kPartialHeadRows ? rows_per_load(p) : 1;
 }
 
+int32_t workgroups_per_split(const fd_problem* p, int32_t kernel) {
+    const int32_t groups = p->num_kv_heads / heads_per_workgroup(p, kernel);
+    return kernel == kPartialMfma ? groups * mfma_column_tiles(p) : groups;
+}
+
 fd_status check_plan(const fd_problem* p, const fd_plan* plan) {
     if (!plan) return fail(FD_ERR_INVALID_ARGUMENT, "plan is NULL");
     if (plan->chunk_tokens < 1 || plan->max_splits < 1 || plan->max_splits > kMaxGridYZ)
@@ -194,7 +199,7 @@ fd_status fd_plan_splits(const fd_problem* p, const int32_t* lens, int32_t num_c
     if (force_num_splits == 0) force_num_splits = env_int("FD_NUM_SPLITS", 0);
 
     auto choose_chunk = [&](int32_t kern) -> int64_t {
-        const int64_t wg_heads = p->num_kv_heads / heads_per_workgroup(p, kern);
+        const int64_t wg_heads = workgroups_per_split(p, kern);
         int64_t c;
         if (force_num_splits > 0) {
             c = ceil_div(lmax, force_num_splits);

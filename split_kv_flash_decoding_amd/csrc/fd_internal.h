@@ -48,8 +48,9 @@ enum PartialKernel : int32_t {
 
 // Query tokens per sequence (a q_len of 0 means one).
 inline int32_t problem_q_len(const fd_problem* p) { return p->q_len > 1 ? p->q_len : 1; }
-// Largest q_len * Hq/Hkv the matrix-core kernel handles (one 16-column MFMA tile).
-constexpr int32_t kMaxQueryRows = 16;
+// Largest q_len * Hq/Hkv the matrix-core kernel handles (up to four 16-column
+// MFMA tiles, one work-group each).
+constexpr int32_t kMaxQueryRows = 64;
 
 // Bytes of one cache element (2 for fp16/bf16, 1 for E4M3).
 inline int32_t kv_elem_bytes(const fd_problem* p) { return p->kv_dtype == FD_FP8_E4M3 ? 1 : 2; }
@@ -68,5 +69,12 @@ bool mfma_applicable(const fd_problem* p);
 bool head_rows_applicable(const fd_problem* p);
 // KV heads one work-group of `kernel` handles.
 int32_t heads_per_workgroup(const fd_problem* p, int32_t kernel);
+// Work-groups per split of one sequence: KV-head groups times the matrix-core
+// kernel's column tiles.
+int32_t workgroups_per_split(const fd_problem* p, int32_t kernel);
+// Column tiles (16 query rows each) of the matrix-core kernel.
+inline int32_t mfma_column_tiles(const fd_problem* p) {
+    return (problem_q_len(p) * (p->num_q_heads / p->num_kv_heads) + 15) / 16;
+}
 
 }  // namespace fd

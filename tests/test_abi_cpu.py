@@ -241,15 +241,25 @@ def test_head_rows_fall_back_when_work_groups_are_few(monkeypatch):
 
 
 def test_multi_query_problems():
-    """q_len > 1 runs on the matrix-core kernel: d = 128 and q_len * G <= 16."""
+    """q_len > 1 runs on the matrix-core kernel: d = 128 and q_len * G <= 64
+    (one work-group per 16 query rows of a KV head, so fewer splits fill the
+    chip as the rows grow)."""
     plan = fd.fd_plan_splits(prob(num_q_heads=32, num_kv_heads=32, q_len=4), [131072], num_cus=256)
     assert plan.partial_kernel == 1
     assert plan.workspace_bytes == workspace_bytes(1, 4 * 32, 32, plan.max_splits)
     assert fd.fd_plan_splits(prob(num_q_heads=64, num_kv_heads=8, q_len=2), [1000], num_cus=256).partial_kernel == 1
+    splits = {}
+    for ql in (2, 4, 8):  # 16, 32 and 64 query rows per KV head
+        plan = fd.fd_plan_splits(prob(num_q_heads=64, num_kv_heads=8, q_len=ql), [131072], num_cus=256)
+        assert plan.partial_kernel == 1
+        splits[ql] = plan.max_splits
+    assert splits[2] >= splits[4] >= splits[8]
+    assert fd.fd_plan_splits(prob(num_q_heads=32, num_kv_heads=32, q_len=64), [1000],
+                             num_cus=256).partial_kernel == 1
     for kw, lens, status in [
         (dict(head_dim=64, q_len=2), [100], fd.FD_ERR_UNSUPPORTED),
-        (dict(num_q_heads=64, num_kv_heads=8, q_len=4), [100], fd.FD_ERR_UNSUPPORTED),  # 32 rows
-        (dict(q_len=17), [100], fd.FD_ERR_UNSUPPORTED),
+        (dict(num_q_heads=64, num_kv_heads=8, q_len=9), [100], fd.FD_ERR_UNSUPPORTED),  # 72 rows
+        (dict(num_q_heads=32, num_kv_heads=32, q_len=65), [100], fd.FD_ERR_UNSUPPORTED),
         (dict(q_len=-1), [100], fd.FD_ERR_INVALID_ARGUMENT),
         (dict(q_len=4), [3], fd.FD_ERR_INVALID_ARGUMENT),  # shorter than its query tokens
     ]:

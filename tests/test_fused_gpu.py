@@ -60,6 +60,11 @@ CASES = [
     ("config 3 fp8", lambda: make_config(3, kv_fp8=True)),
     ("config 5 fp8", lambda: make_config(5, kv_fp8=True)),
     ("config 4 q_len 4", lambda: make_config(4, q_len=4)),
+    ("G8 paged q_len 8", lambda: to_paged(make_workload(name="g8q8", batch=4, num_q_heads=64, num_kv_heads=8,
+                                                        head_dim=128, seq_lens=[8, 700, 5000, 129],
+                                                        dtype=torch.bfloat16, seed=1503, q_len=8), 16)),
+    ("MHA q_len 40", lambda: make_workload(name="mq40", batch=2, num_q_heads=8, num_kv_heads=8, head_dim=128,
+                                           seq_lens=[40, 2500], dtype=torch.float16, seed=1502, q_len=40)),
     ("d64 GQA paged", lambda: to_paged(make_workload(name="d64", batch=3, num_q_heads=8, num_kv_heads=2, head_dim=64,
                                                      seq_lens=[1, 300, 4097], dtype=torch.bfloat16, seed=1500), 16)),
     ("d64 fp8 head rows", lambda: quantize_kv_fp8(make_workload(name="d64f8", batch=1, num_q_heads=32,

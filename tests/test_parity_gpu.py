@@ -335,6 +335,10 @@ MQ_CASES = [
     (torch.float16, 4, 2, 8, [8, 9, 777], 16),        # G = 2, 8 tokens, paged
     (torch.float16, 16, 16, 16, [16, 2048], 0),       # MHA, 16 tokens
     (torch.bfloat16, 8, 8, 3, [5, 300], 0),           # 3 rows padded to 4
+    (torch.bfloat16, 64, 8, 4, [100, 3000], 16),      # G = 8, 4 tokens: 32 rows, two column tiles
+    (torch.bfloat16, 64, 8, 8, [8, 5000], 0),         # G = 8, 8 tokens: 64 rows, four column tiles
+    (torch.float16, 8, 2, 10, [10, 700, 33], 16),     # G = 4, 10 tokens: 40 rows, a half-full last tile
+    (torch.float16, 32, 32, 64, [64, 1500], 0),       # MHA, 64 tokens
 ]
 
 
@@ -351,14 +355,17 @@ def test_multi_query_decode_matches_oracle(fd, case, splits):
     parity(res.out, res.lse, ref_out, ref_lse, what=f"multi-query case {case} splits {splits}")
 
 
-def test_multi_query_split_statistics_include_empty_splits(fd):
-    """Splits past a query's causal limit hold (m, l, O) = (-inf, 0, 0)."""
-    ql = 8
-    wl = make_workload(name="mq-stats", batch=2, num_q_heads=4, num_kv_heads=2, head_dim=128, seq_lens=[64, 30],
+@pytest.mark.parametrize("hq,hkv,ql", [(4, 2, 8), (16, 2, 5)])
+def test_multi_query_split_statistics_include_empty_splits(fd, hq, hkv, ql):
+    """Splits past a query's causal limit hold (m, l, O) = (-inf, 0, 0); with
+    40 rows per KV head (three column tiles) the first tile's rows are all
+    past their limits in the last splits."""
+    wl = make_workload(name="mq-stats", batch=2, num_q_heads=hq, num_kv_heads=hkv, head_dim=128, seq_lens=[64, 30],
                        dtype=torch.bfloat16, seed=9, q_len=ql)
     res = run(fd, wl, num_splits=32)  # chunk 2: the last splits lie past the early queries' limits
     C = res.plan.chunk_tokens
-    prob = fd.make_problem(batch=2, num_q_heads=4, num_kv_heads=2, head_dim=128, kv_dtype=torch.bfloat16, q_len=ql)
+    prob = fd.make_problem(batch=2, num_q_heads=hq, num_kv_heads=hkv, head_dim=128, kv_dtype=torch.bfloat16,
+                           q_len=ql)
     O_s, m_s, l_s = (x.double().cpu().numpy() for x in fd.workspace_views(prob, res.plan, res.workspace))
     Oo, mo, lo = oracle.decode_partials(wl.q, wl.k, wl.v, wl.seq_lens, wl.scale, C)
     for b, L in enumerate(wl.lens):
