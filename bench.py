@@ -48,12 +48,14 @@ PARTIAL_SOURCES = ("fd_api.hip", "fd_device.h", "fd_host.cpp", "fd_internal.h", 
 
 
 PREFILL_SOURCES = ("fd_api.hip", "fd_device.h", "fd_internal.h", "fd_prefill.hip")
+APPEND_SOURCES = ("fd_api.hip", "fd_device.h", "fd_internal.h", "fd_append.hip")
+SOURCES = {"partial": PARTIAL_SOURCES, "prefill": PREFILL_SOURCES, "append": APPEND_SOURCES}
 
 
 def kernel_source_hash(kernel: str = "partial") -> str:
-    """Hash of the timed kernel's sources (PARTIAL_SOURCES or PREFILL_SOURCES)."""
+    """Hash of the timed kernel's sources (SOURCES[kernel])."""
     h = hashlib.sha256()
-    for name in (PREFILL_SOURCES if kernel == "prefill" else PARTIAL_SOURCES):
+    for name in SOURCES[kernel]:
         with open(os.path.join(KERNEL_SOURCES, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -254,13 +256,157 @@ def run_prefill(args, fd, dev) -> int:
     return 0
 
 
+APPEND_METRIC = "GB/s, KV append with RoPE into the paged cache (q rotated in place), 8K-token prompt, GQA 32/8, d=128"
+
+
+def append_bytes(n_tokens: int, hq: int, hkv: int, d: int, elem: int, cache_elem: int) -> int:
+    """Algorithmic bytes of an append: per new token, k_new and v_new read,
+    their cache rows written, q read and written back."""
+    return n_tokens * (2 * hkv * d * elem + 2 * hkv * d * cache_elem + 2 * hq * d * elem)
+
+
+def run_append(args, fd, dev) -> int:
+    """One step = one fd_append_kv call: the prompt's keys (rotated) and values
+    into the paged cache, and its queries rotated in place."""
+    import numpy as np
+    import torch
+
+    from workloads import make_append, make_workload
+    from workloads.synth import to_paged
+
+    t = time.perf_counter()
+    wl, k_new_h, v_new_h = make_append()
+    log(f"generated {wl.name} in {time.perf_counter() - t:.1f} s")
+    n = wl.q.shape[1]
+    kc, vc = wl.k.to(dev), wl.v.to(dev)
+    q = wl.q.to(dev).contiguous()
+    k_new, v_new = k_new_h.to(dev), v_new_h.to(dev)
+    bt, lens_dev = wl.block_table.to(dev), wl.seq_lens.to(dev)
+    problem = fd.make_problem(batch=1, num_q_heads=wl.num_q_heads, num_kv_heads=wl.num_kv_heads,
+                              head_dim=wl.head_dim, kv_dtype=wl.dtype, page_size=16,
+                              max_pages_per_seq=wl.max_pages_per_seq, q_len=n)
+    nbytes = append_bytes(n, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, 2, 2)
+
+    def call():
+        fd.fd_append_kv(problem, k_new, v_new, q, kc, vc, bt, lens_dev, rope_style="half", rope_base=10000.0)
+
+    for _ in range(max(1, args.warmup)):
+        call()
+    torch.cuda.synchronize()
+    K = args.steps
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    start.record()
+    for _ in range(K):
+        call()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = start.elapsed_time(end) / K
+    # The spread, from a second run with an event pair around every call.
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(min(K, 50) + 1)]
+    ev[0].record()
+    for i in range(len(ev) - 1):
+        call()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(len(ev) - 1)]
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    pq = statistics.quantiles(per, n=10)
+    log(f"{K} steps: {ms * 1e3:.1f} us/step (events), wall {wall / K * 1e6:.1f} us/step; {gbps:.0f} GB/s; "
+        f"median {statistics.median(per) * 1e3:.1f} us, p10 {pq[0] * 1e3:.1f}, p90 {pq[-1] * 1e3:.1f}")
+
+    # A decode step's append for context (latency-bound): 64 sequences, one
+    # new token each, 64 query / 8 KV heads.
+    st = to_paged(make_workload(name="append_step", batch=64, num_q_heads=64, num_kv_heads=8, head_dim=128,
+                                seq_lens=("uniform", 1, 64), dtype=torch.bfloat16, seed=2200), 16, spare_pages=1)
+    sp = fd.make_problem(batch=64, num_q_heads=64, num_kv_heads=8, head_dim=128, kv_dtype=torch.bfloat16,
+                         page_size=16, max_pages_per_seq=st.max_pages_per_seq, q_len=1)
+    s_q = st.q.reshape(64, 1, 64, 128).to(dev).contiguous()
+    s_k, s_v, s_bt, s_lens = st.k.to(dev), st.v.to(dev), st.block_table.to(dev), st.seq_lens.to(dev)
+    s_new = torch.randn((64, 1, 8, 128), generator=torch.Generator().manual_seed(7)).to(torch.bfloat16).to(dev)
+    for _ in range(10):
+        fd.fd_append_kv(sp, s_new, s_new, s_q, s_k, s_v, s_bt, s_lens, rope_style="half")
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(100):
+        fd.fd_append_kv(sp, s_new, s_new, s_q, s_k, s_v, s_bt, s_lens, rope_style="half")
+    e1.record()
+    torch.cuda.synchronize()
+    step_us = e0.elapsed_time(e1) / 100 * 1e3
+    log(f"decode-step append (64 sequences x 1 token, 64/8 heads): {step_us:.1f} us")
+    # A plain copy of known size calibrates the HBM counters taken on this run.
+    src = torch.empty((256 << 20) // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    fd.fd_probe_copy(dst, src)
+    torch.cuda.synchronize()
+    del src, dst
+
+    rec = {
+        "metric": APPEND_METRIC, "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) q/K/V; no dataset involved)",
+        "config": {"workload": wl.name, "batch": 1, "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads,
+                   "head_dim": wl.head_dim, "new_tokens": n, "page_size": 16, "rope": "half, base 10000",
+                   "bytes_per_call": nbytes, "decode_step_append_us": round(step_us, 2)},
+        # One launch per step, timed by the same events.
+        "roofline": {"bound": "hbm", "kernel": "append", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                     "traffic": measured_traffic(wl.name, "append"),
+                     "us_median": round(statistics.median(per) * 1e3, 2)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle.append as oapp
+
+        # The GPU result of one append on the original queries, then the
+        # oracle token by token (each sampled token as a one-token sequence
+        # ending at its position) until the budget is spent.
+        q.copy_(wl.q.reshape(q.shape))
+        call()
+        torch.cuda.synchronize()
+        got_k, got_v, got_q = kc.cpu(), vc.cpu(), q.cpu()
+        log(f"timing the CPU oracle on sampled tokens for about {args.cpu_budget:.0f} s ...")
+        r = np.random.default_rng(0)
+        done, mism, total_el = 0, 0, 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < args.cpu_budget:
+            js = [int(j) for j in r.integers(0, n, 8)]
+            table = wl.block_table[0:1].repeat(len(js), 1)
+            lens = [j + 1 for j in js]
+            rk, rv, rq = oapp.append_kv(wl.k, wl.v, table, lens, k_new_h[0, js][:, None], v_new_h[0, js][:, None],
+                                        wl.q[0, js][:, None], rope_style="half", rope_base=10000.0)
+            for i, j in enumerate(js):
+                pg, sl = int(wl.block_table[0, j // 16]), j % 16
+                for got, ref in ((got_k[pg, sl], rk[pg, sl]), (got_v[pg, sl], rv[pg, sl]), (got_q[0, j], rq[i, 0])):
+                    mism += int((got.view(torch.int16) != ref.view(torch.int16)).sum())
+                    total_el += got.numel()
+            done += len(js)
+        el = time.perf_counter() - t0
+        rec["cpu_baseline"] = {
+            "value": round(append_bytes(done, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, 2, 2) / el / 1e9, 6),
+            "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} random tokens of the same prompt, each appended alone at its position, "
+                      f"{el:.1f} s wall (pure-Python rounding, one thread)",
+            "parity_of_sampled_tokens": {"elements": total_el, "differing_bits": mism}}
+    else:
+        rec["cpu_baseline"] = None
+    line = json.dumps(rec)
+    print(line, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(line + "\n")
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", choices=("decode", "prefill"), default="decode",
-                    help="decode (default; --config picks the workload) or the 8192-token causal prefill")
+    ap.add_argument("--workload", choices=("decode", "prefill", "append"), default="decode",
+                    help="decode (default; --config picks the workload), the 8192-token causal prefill, or the "
+                         "8192-token KV append with RoPE")
     ap.add_argument("--config", type=int, default=3, help="decode workload 1..5 (default: 128K MHA)")
     ap.add_argument("--q-len", type=int, default=1, help="query tokens per sequence (speculative verification)")
     ap.add_argument("--kv-fp8", action="store_true", help="FP8 (E4M3) cache with per-KV-head scales")
@@ -287,6 +433,8 @@ def main() -> int:
     dev = torch.device("cuda", 0)
     if args.workload == "prefill":
         return run_prefill(args, fd, dev)
+    if args.workload == "append":
+        return run_append(args, fd, dev)
 
     t = time.perf_counter()
     wl = make_config(args.config, q_len=args.q_len, kv_fp8=args.kv_fp8)

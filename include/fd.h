@@ -321,6 +321,8 @@ typedef enum fd_rope_style {
  * k_cache, v_cache: device pools [num_pages, 16, Hkv, d] in kv_dtype.
  * block_table: device int32 [B, max_pages_per_seq]; seq_lens_dev: device
  *          int32 [B] (after the append).
+ * Alignment: k_new, v_new, q and 16-bit caches 16 bytes, FP8 caches 8 bytes
+ * (whole rows move in 16-byte pieces); FD_ERR_INVALID_ARGUMENT otherwise.
  * Slots other than the new tokens' are not touched. A position outside the
  * block table, or a page index outside [0, num_pages), is skipped on the
  * device (nothing written) rather than trusted. rope_style FD_ROPE_NONE

@@ -294,8 +294,9 @@ fd_status fd_append_kv(const fd_problem* p, int32_t rope_style, float rope_base,
     const uintptr_t a16 = reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new) |
                           reinterpret_cast<uintptr_t>(q);
     const uintptr_t acache = reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(v_cache);
-    if ((a16 & 1) || (acache & (kv_elem_bytes(p) - 1)))
-        return fail(FD_ERR_INVALID_ARGUMENT, "tensors must be aligned to their element size");
+    if ((a16 & 15) || (acache & (kv_elem_bytes(p) == 1 ? 7 : 15)))
+        return fail(FD_ERR_INVALID_ARGUMENT, "k_new, v_new, q and 16-bit caches must be 16-byte aligned, "
+                    "FP8 caches 8-byte aligned");
     if ((reinterpret_cast<uintptr_t>(k_scale) | reinterpret_cast<uintptr_t>(v_scale)) & 3)
         return fail(FD_ERR_INVALID_ARGUMENT, "k_scale and v_scale must be 4-byte aligned");
     const int64_t blocks = (int64_t)p->batch * problem_q_len(p);

@@ -332,12 +332,16 @@ def test_append_validates_before_launching():
     assert call(p, pages=0) == fd.FD_ERR_INVALID_ARGUMENT
     assert call(p, knew=ctypes.c_void_p(0x10001)) == fd.FD_ERR_INVALID_ARGUMENT
     assert call(p, kc=ctypes.c_void_p(0x10001)) == fd.FD_ERR_INVALID_ARGUMENT   # 2-byte cache elements
+    # rows move in 16-byte pieces: 16-byte alignment (8 for an FP8 cache)
+    assert call(p, knew=ctypes.c_void_p(0x10008)) == fd.FD_ERR_INVALID_ARGUMENT
+    assert call(p, kc=ctypes.c_void_p(0x10008)) == fd.FD_ERR_INVALID_ARGUMENT
     assert call(p, ks=ctypes.c_void_p(0x10002)) == fd.FD_ERR_INVALID_ARGUMENT
     f8 = prob(page_size=16, max_pages_per_seq=64, num_q_heads=8, num_kv_heads=2, kv_dtype=torch.float8_e4m3fn)
     bad = prob(page_size=16, max_pages_per_seq=64, num_q_heads=8, num_kv_heads=2, kv_dtype=torch.float8_e4m3fn)
     bad.q_dtype = fd.FD_F32
     assert call(bad) == fd.FD_ERR_INVALID_ARGUMENT
     assert f8.q_dtype == fd.FD_F16
+    assert call(f8, kc=ctypes.c_void_p(0x10004)) == fd.FD_ERR_INVALID_ARGUMENT
 
 
 def test_prefill_validates_before_launching():

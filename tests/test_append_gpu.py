@@ -134,3 +134,63 @@ def test_append_skips_positions_outside_the_table(fd):
     changed = (_bits(kc.cpu()) != _bits(wl.k)).reshape(wl.k.shape[0], 16, -1).any(-1)
     pages = torch.nonzero(changed).tolist()
     assert pages == [[int(wl.block_table[0, 0]), 0]]
+
+
+def test_append_scaled_16bit_cache(fd):
+    """A 16-bit cache with per-head scales stores value / scale (rounded once)."""
+    case = (torch.bfloat16, torch.bfloat16, "interleaved", 128, 16, 4, [31, 32, 400], 3)
+    kvdt, qdt, style, d, hq, hkv, lens, n = case
+    wl, k_new, v_new = setup(case, 970)
+    ks = torch.tensor([0.5, 3.0, 0.1, 1.0], dtype=torch.float32)
+    vs = torch.tensor([2.0, 0.3, 1.0, 7.0], dtype=torch.float32)
+    dev = torch.device("cuda", 0)
+    kc, vc, q = wl.k.to(dev), wl.v.to(dev), wl.q.to(dev).contiguous()
+    prob = fd.make_problem(batch=wl.batch, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, kv_dtype=kvdt,
+                           page_size=16, max_pages_per_seq=wl.max_pages_per_seq, q_len=n)
+    fd.fd_append_kv(prob, k_new.to(dev), v_new.to(dev), q, kc, vc, wl.block_table.to(dev), wl.seq_lens.to(dev),
+                    rope_style=style, k_scale=ks.to(dev), v_scale=vs.to(dev))
+    torch.cuda.synchronize()
+    rk, rv, rq = append_kv(wl.k, wl.v, wl.block_table, wl.seq_lens, k_new, v_new, wl.q, rope_style=style,
+                           k_scale=ks, v_scale=vs)
+    mask = np.zeros(tuple(wl.k.shape), dtype=bool)
+    for b, L in enumerate(wl.lens):
+        for j in range(n):
+            pos = L - n + j
+            mask[int(wl.block_table[b, pos // 16]), pos % 16] = True
+    assert_same_storage(kc, rk, "K cache (scaled)", mask)
+    assert_same_storage(vc, rv, "V cache (scaled)", mask)
+    assert_same_storage(q, rq, "q")
+
+
+def test_append_full_size_sampled_tokens(fd):
+    """The 8192-token prompt append the benchmark times (one call, 32 query /
+    8 KV heads, bf16, half pairing, permuted pages): 64 sampled tokens,
+    including the first and last and both sides of page edges, each checked
+    against the oracle appending that token alone at its position; slots the
+    append does not own keep their bytes."""
+    from workloads import make_append
+    wl, k_new, v_new = make_append()
+    n = wl.q.shape[1]
+    dev = torch.device("cuda", 0)
+    kc, vc, q = wl.k.to(dev), wl.v.to(dev), wl.q.to(dev).contiguous()
+    prob = fd.make_problem(batch=1, num_q_heads=32, num_kv_heads=8, head_dim=128, kv_dtype=torch.bfloat16,
+                           page_size=16, max_pages_per_seq=wl.max_pages_per_seq, q_len=n)
+    announce(f"append full size: {wl.name}")
+    fd.fd_append_kv(prob, k_new.to(dev), v_new.to(dev), q, kc, vc, wl.block_table.to(dev), wl.seq_lens.to(dev),
+                    rope_style="half")
+    torch.cuda.synchronize()
+    got_k, got_v, got_q = kc.cpu(), vc.cpu(), q.cpu()
+    r = np.random.default_rng(11)
+    js = sorted(set([0, 1, 15, 16, 17, 4095, 4096, n - 17, n - 16, n - 1] + [int(x) for x in r.integers(0, n, 54)]))
+    table = wl.block_table[0:1].repeat(len(js), 1)
+    rk, rv, rq = append_kv(wl.k, wl.v, table, [j + 1 for j in js], k_new[0, js][:, None], v_new[0, js][:, None],
+                           wl.q[0, js][:, None], rope_style="half")
+    for i, j in enumerate(js):
+        pg, sl = int(wl.block_table[0, j // 16]), j % 16
+        assert_same_storage(got_k[pg, sl], rk[pg, sl], f"K token {j}")
+        assert_same_storage(got_v[pg, sl], rv[pg, sl], f"V token {j}")
+        assert_same_storage(got_q[0, j], rq[i, 0], f"q token {j}")
+    # the spare pages (NaN) keep their bytes
+    used = set(int(p) for p in wl.block_table[0, : n // 16])
+    spare = [p for p in range(wl.k.shape[0]) if p not in used]
+    assert spare and all(torch.equal(_bits(got_k[p]), _bits(wl.k[p])) for p in spare)

@@ -10,6 +10,7 @@ from .synth import (  # noqa: F401
     quantize_kv_fp8,
     CONFIG_NAMES,
     Workload,
+    make_append,
     make_config,
     make_prefill,
     make_workload,

@@ -400,3 +400,27 @@ def make_prefill(seed: int = 2000, length: int = 8192, dtype: torch.dtype = torc
                        seed=seed, q_len=length)
     wl.q = wl.q.reshape(1, length, 32, 128)
     return wl
+
+
+APPEND_NAME = "append_rope_half_b1_hq32_hkv8_d128_n8192_bf16_paged"
+
+
+def make_append(seed: int = 2100, length: int = 8192, dtype: torch.dtype = torch.bfloat16):
+    """The KV append before a prefill: one 8192-token prompt's new keys and
+    values (k_new, v_new [1, L, 8, 128], N(0,1)) to be written, rotated, into a
+    16-token paged pool whose pages are a seeded permutation (the pool's old
+    contents are N(0,1) too, spare pages NaN), and its queries (q [1, L, 32,
+    128]) rotated in place. Returns (workload, k_new, v_new); the workload's
+    lengths are those after the append."""
+    wl = make_workload(name=APPEND_NAME if (length, dtype) == (8192, torch.bfloat16) else
+                       f"append_rope_half_b1_hq32_hkv8_d128_n{length}_{str(dtype).split('.')[-1]}_paged",
+                       batch=1, num_q_heads=32, num_kv_heads=8, head_dim=128, seq_lens=[length], dtype=dtype,
+                       seed=seed, q_len=length)
+    wl = to_paged(wl, 16, spare_pages=2)
+    wl.q = wl.q.reshape(1, length, 32, 128)
+    ss = np.random.SeedSequence(seed + 1)
+    k_new = torch.empty((1, length, 8, 128), dtype=dtype)
+    v_new = torch.empty((1, length, 8, 128), dtype=dtype)
+    _normal_into(k_new, _child(ss, 0))
+    _normal_into(v_new, _child(ss, 1))
+    return wl, k_new, v_new
