@@ -31,9 +31,16 @@
 //   * O^T [128 dims x 16 rows] += V^T . P^T as v_mfma_f32_16x16x32: P^T is
 //     the score layout itself (the contraction's token order is free, so the
 //     A operand's token slots are matched to it), V^T comes from two
-//     transposing LDS reads (ds_read_b64_tr_b16) per 16-dim block. bf16
-//     probabilities are split into high and low parts (two products), so
-//     rounding P to 8 mantissa bits does not reach the output; fp16 keeps one;
+//     transposing LDS reads (ds_read_b64_tr_b16) per 16-dim block. The
+//     product runs in fp16 for both cache types: P in fp16 (11 bits, where
+//     bf16's 8 would show in the output), and a bf16 V tile is converted to
+//     fp16 on its way into LDS. The conversion is exact for values within
+//     fp16's normal range; a work-group vote per tile finds tiles holding a
+//     value beyond fp16's largest, and those are scaled by a power of two
+//     2^-k first (k from the tile's largest exponent), the products rescaled
+//     by 2^k, so nothing overflows; values below fp16's normal range keep an
+//     absolute error under 2^-25 times that scale (one product instead of the
+//     two a high/low split of bf16 P would take);
 //   * at the end each row's sum is reduced over its four lanes, O is divided
 //     by l once and written with the natural-log LSE.
 
@@ -70,29 +77,43 @@ constexpr int kNT = kQW / 16;       // 16-column tiles per wave
 constexpr int kBr = kPW * kQW;      // query rows per work-group
 constexpr int kPitch = kD + 16;     // LDS row pitch, elements
 
+// Score products in the cache's type.
 template <int DT> struct Mma;
 template <> struct Mma<FD_F16> {
-    static constexpr bool kSplitP = false;
     static __device__ __forceinline__ f32x4_t mma(u32x4 a, u32x4 b, f32x4_t c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b),
                                                       c, 0, 0, 0);
     }
-    static __device__ __forceinline__ uint32_t pack(float a, float b) {
-        return __builtin_bit_cast(uint32_t, half2_t{(_Float16)a, (_Float16)b});
-    }
-    static __device__ __forceinline__ float back(float a) { return (float)(_Float16)a; }
 };
 template <> struct Mma<FD_BF16> {
-    static constexpr bool kSplitP = true;
     static __device__ __forceinline__ f32x4_t mma(u32x4 a, u32x4 b, f32x4_t c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                        __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
     }
-    static __device__ __forceinline__ uint32_t pack(float a, float b) {
-        return __builtin_bit_cast(uint32_t, bf162_t{(__bf16)a, (__bf16)b});
-    }
-    static __device__ __forceinline__ float back(float a) { return (float)(__bf16)a; }
 };
+
+// P.V products: fp16 for either cache type.
+__device__ __forceinline__ f32x4_t mma_f16(u32x4 a, u32x4 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c, 0,
+                                                  0, 0);
+}
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, half2_t{(_Float16)a, (_Float16)b});
+}
+// Two bf16 values times 2^-k, as two fp16 values (exact while the products
+// stay in fp16's normal range).
+__device__ __forceinline__ uint32_t bf16_pair_to_f16(uint32_t w, int k) {
+    const float lo = __builtin_bit_cast(float, w << 16), hi = __builtin_bit_cast(float, w & 0xffff0000u);
+    return k ? pack_f16(ldexpf(lo, -k), ldexpf(hi, -k)) : pack_f16(lo, hi);
+}
+// Running maxima of the magnitude fields (exponent and mantissa bits) of the
+// two bf16 halves of words, two 16-bit lanes at a time.
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u16x2_t bf16_pair_max_mag(u16x2_t m, uint32_t w) {
+    return __builtin_elementwise_max(m, __builtin_bit_cast(u16x2_t, w & 0x7fff7fffu));
+}
+__device__ __forceinline__ uint32_t max_of(u16x2_t m) { return max((uint32_t)m[0], (uint32_t)m[1]); }
+constexpr uint32_t kF16MaxAsBf16 = 0x477fu;  // the largest bf16 magnitude at most fp16's 65504
 
 __device__ __forceinline__ i16x4_t lds_tr(const uint16_t* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -113,6 +134,8 @@ __global__ __launch_bounds__(64 * kPW) void prefill_fa2(const PrefillArgs a) {
     using M = Mma<DT>;
     __shared__ __attribute__((aligned(16))) uint16_t sk[kBufs][kBc * kPitch];
     __shared__ __attribute__((aligned(16))) uint16_t sv[kBufs][kBc * kPitch];
+    __shared__ int s_vbad[kBufs];  // per buffer: the last tile staged there with a value past fp16's range
+    __shared__ uint32_t s_vmax;
 
     // Work-group -> (query block, sequence, head), query blocks in descending
     // order so the longest causal rows start first.
@@ -204,7 +227,8 @@ __global__ __launch_bounds__(64 * kPW) void prefill_fa2(const PrefillArgs a) {
     const uint16_t* kh = a.k + (int64_t)g * kD;  // head g of row 0
     const uint16_t* vh = a.v + (int64_t)g * kD;
     u32x4 kr[kLoads], vr[kLoads];
-    auto load = [&](int tile) {
+    // The tile's K (when WITH_K) and V pieces of this thread.
+    auto load_into = [&]<bool WITH_K>(int tile, u32x4* kd, u32x4* vd) {
         const int t0 = tile * kBc;
         if constexpr (PAGED) {
 #pragma unroll
@@ -214,9 +238,10 @@ __global__ __launch_bounds__(64 * kPW) void prefill_fa2(const PrefillArgs a) {
                 const int rows = __builtin_amdgcn_readfirstlane(max(0, min(16, L - tg)));
                 const int64_t page = rows > 0 ? (int64_t)checked_page(table[tg >> 4], a.num_pages) : 0;
                 const int voff = lr * row_bytes + 16 * lc;
-                kr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                      make_rsrc(kh + page * 16 * a.hkv * kD, rows * row_bytes), voff, 0, 0));
-                vr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                if constexpr (WITH_K)
+                    kd[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                          make_rsrc(kh + page * 16 * a.hkv * kD, rows * row_bytes), voff, 0, 0));
+                vd[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                                       make_rsrc(vh + page * 16 * a.hkv * kD, rows * row_bytes), voff, 0, 0));
             }
         } else {
@@ -227,21 +252,66 @@ __global__ __launch_bounds__(64 * kPW) void prefill_fa2(const PrefillArgs a) {
 #pragma unroll
             for (int i = 0; i < kLoads; ++i) {
                 const int voff = (16 * i + lr) * row_bytes + 16 * lc;
-                kr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, voff, 0, 0));
-                vr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff, 0, 0));
+                if constexpr (WITH_K) kd[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, voff, 0, 0));
+                vd[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff, 0, 0));
             }
         }
     };
-    auto stage = [&](int buf) {
+    auto load = [&](int tile) { load_into.template operator()<true>(tile, kr, vr); };
+    // A bf16 V tile is staged as fp16. A thread holding a value beyond
+    // fp16's range marks the buffer with the tile's number (s_vbad), and the
+    // tile is staged again, scaled, before it is used (restage_v).
+    auto stage = [&](int buf, int tile) {
 #pragma unroll
         for (int i = 0; i < kLoads; ++i) {
             *reinterpret_cast<u32x4*>(sk[buf] + (lr + 16 * i) * kPitch + 8 * lc) = kr[i];
-            *reinterpret_cast<u32x4*>(sv[buf] + (lr + 16 * i) * kPitch + 8 * lc) = vr[i];
+            u32x4 w = vr[i];
+            if constexpr (DT == FD_BF16) {
+                u16x2_t mx = {0, 0};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    mx = bf16_pair_max_mag(mx, w[e]);
+                    w[e] = bf16_pair_to_f16(w[e], 0);
+                }
+                if (max_of(mx) > kF16MaxAsBf16) s_vbad[buf] = tile;
+            }
+            *reinterpret_cast<u32x4*>(sv[buf] + (lr + 16 * i) * kPitch + 8 * lc) = w;
         }
+    };
+    // The marked tile's V again (every thread of the work-group, after the
+    // barrier that follows staging): loaded once more, scaled by 2^-k with k
+    // from the tile's largest exponent so that every value stays below 2^15,
+    // staged, and k returned. Rare: only tiles with values past 65504.
+    auto restage_v = [&](int tile, int buf) -> int {
+        u32x4 vt[kLoads];
+        load_into.template operator()<false>(tile, nullptr, vt);
+        u16x2_t mx = {0, 0};
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) mx = bf16_pair_max_mag(mx, vt[i][e]);
+        if (threadIdx.x == 0) s_vmax = 0;
+        __syncthreads();
+        atomicMax(&s_vmax, max_of(mx));
+        __syncthreads();
+        const int k = (int)(s_vmax >> 7) - 127 - 14;  // the largest value's binary exponent (>= 15), less 14
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) {
+            u32x4 w = vt[i];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = bf16_pair_to_f16(w[e], k);
+            *reinterpret_cast<u32x4*>(sv[buf] + (lr + 16 * i) * kPitch + 8 * lc) = w;
+        }
+        __syncthreads();
+        return k;
+    };
+    auto v_scale_of = [&](int tile, int buf) -> int {
+        if constexpr (DT != FD_BF16) return 0;
+        else return s_vbad[buf] == tile ? restage_v(tile, buf) : 0;
     };
 
     const int vrd = (4 * grp + ((lane >> 2) & 3)) * kPitch + 4 * (lane & 3);
-    auto compute = [&](int tile, int buf) {
+    auto compute = [&](int tile, int buf, int vk) {
         const int t0 = tile * kBc;
         const uint16_t* K = sk[buf];
         const uint16_t* V = sv[buf];
@@ -262,7 +332,7 @@ __global__ __launch_bounds__(64 * kPW) void prefill_fa2(const PrefillArgs a) {
         // Online softmax per row; P^T packed as the B operands of the P.V steps.
         // Only tiles that reach past some row's causal limit need the mask.
         const bool masked = t0 + kBc > wave_min_lim;
-        u32x4 phi[kNT][kKS], plo[kNT][kKS];
+        u32x4 pp[kNT][kKS];
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) {
             // Raw scores here; the (positive) scale joins the exponent's fma below.
@@ -301,15 +371,23 @@ __global__ __launch_bounds__(64 * kPW) void prefill_fa2(const PrefillArgs a) {
             for (int ks = 0; ks < kKS; ++ks)
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
-                    const float x0 = p[8 * ks + 2 * w], x1 = p[8 * ks + 2 * w + 1];
-                    phi[nt][ks][w] = M::pack(x0, x1);
-                    if constexpr (M::kSplitP) plo[nt][ks][w] = M::pack(x0 - M::back(x0), x1 - M::back(x1));
+                    pp[nt][ks][w] = pack_f16(p[8 * ks + 2 * w], p[8 * ks + 2 * w + 1]);
                 }
         }
 
         // O^T += V^T . P^T per 32-token step: the A operand's token slots
         // 8 grp + k are tokens 32 ks + 4 grp + k (k < 4) and 32 ks + 16 + 4 grp + k - 4,
-        // the score layout; two transposing reads per 16-dim block.
+        // the score layout; two transposing reads per 16-dim block. A tile
+        // staged at 2^-vk adds its products at that scale (acc * 2^-vk, then
+        // back), every step a power of two.
+        if (vk) {
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+                for (int jd = 0; jd < 8; ++jd)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[nt][jd][i] = ldexpf(acc[nt][jd][i], -vk);
+        }
 #pragma unroll
         for (int ks = 0; ks < kKS; ++ks) {
 #pragma unroll
@@ -317,27 +395,35 @@ __global__ __launch_bounds__(64 * kPW) void prefill_fa2(const PrefillArgs a) {
                 const u32x4 va = join(lds_tr(V + vrd + 32 * ks * kPitch + 16 * jd),
                                       lds_tr(V + vrd + (32 * ks + 16) * kPitch + 16 * jd));
 #pragma unroll
-                for (int nt = 0; nt < kNT; ++nt) {
-                    acc[nt][jd] = M::mma(va, phi[nt][ks], acc[nt][jd]);
-                    if constexpr (M::kSplitP) acc[nt][jd] = M::mma(va, plo[nt][ks], acc[nt][jd]);
-                }
+                for (int nt = 0; nt < kNT; ++nt) acc[nt][jd] = mma_f16(va, pp[nt][ks], acc[nt][jd]);
             }
+        }
+        if (vk) {
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+                for (int jd = 0; jd < 8; ++jd)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[nt][jd][i] = ldexpf(acc[nt][jd][i], vk);
         }
     };
 
     if (ntiles > 0) {
+        if (threadIdx.x < kBufs) s_vbad[threadIdx.x] = -1;
+        __syncthreads();
         load(0);
         if constexpr (kBufs == 2) {
             // Two LDS buffers: tile t+1 is staged while tile t is computed; one
             // barrier per tile.
-            stage(0);
+            stage(0, 0);
             if (1 < ntiles) load(1);
             __syncthreads();
             for (int tile = 0; tile < ntiles; ++tile) {
                 const int cur = tile & 1;
-                if (tile * kBc < wave_lim) compute(tile, cur);
+                const int vk = v_scale_of(tile, cur);
+                if (tile * kBc < wave_lim) compute(tile, cur, vk);
                 if (tile + 1 < ntiles) {
-                    stage(cur ^ 1);
+                    stage(cur ^ 1, tile + 1);
                     if (tile + 2 < ntiles) load(tile + 2);
                 }
                 __syncthreads();
@@ -345,10 +431,11 @@ __global__ __launch_bounds__(64 * kPW) void prefill_fa2(const PrefillArgs a) {
         } else {
             for (int tile = 0; tile < ntiles; ++tile) {
                 __syncthreads();  // every wave is done with the previous tile
-                stage(0);
+                stage(0, tile);
                 if (tile + 1 < ntiles) load(tile + 1);
                 __syncthreads();
-                if (tile * kBc < wave_lim) compute(tile, 0);
+                const int vk = v_scale_of(tile, 0);
+                if (tile * kBc < wave_lim) compute(tile, 0, vk);
             }
         }
     }
