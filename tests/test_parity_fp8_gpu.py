@@ -119,7 +119,9 @@ def test_fp8_split_statistics_match_oracle(fd):
 
 @pytest.mark.parametrize("case", [(torch.float16, 8, 8, 4, [4, 17, 1000], 0),
                                   (torch.bfloat16, 32, 8, 4, [600, 4096], 0),
-                                  (torch.bfloat16, 64, 8, 2, [100, 3000], 16)])
+                                  (torch.bfloat16, 64, 8, 2, [100, 3000], 16),
+                                  (torch.bfloat16, 64, 8, 8, [8, 3000], 16),     # 64 rows: four column tiles
+                                  (torch.float16, 16, 16, 40, [40, 1200], 0)])   # 40 rows: three column tiles
 def test_fp8_multi_query(fd, case):
     qdt, hq, hkv, ql, lens, page = case
     wl = quantize_kv_fp8(make_workload(name="fp8mq", batch=len(lens), num_q_heads=hq, num_kv_heads=hkv,
