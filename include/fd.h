@@ -277,7 +277,10 @@ fd_status fd_decode_attention_scaled(const fd_problem* problem,
  * position L_b - q_len + i and sees tokens 0 .. L_b - q_len + i (q_len = L_b:
  * causal self-attention over the whole prompt; smaller q_len: one chunk of a
  * longer prompt whose earlier tokens are already cached), the same reading
- * as multi-query decode.
+ * as multi-query decode. Arithmetic: q.k products in the cache's type and
+ * P.V products in fp16 (P rounded to fp16; a bf16 V tile converted to fp16,
+ * scaled by a power of two when it holds a value past 65504), all
+ * accumulated in fp32.
  * problem: head_dim 128, fp16/bf16 cache (q of the same type), contiguous or
  *          paged, q_len >= 1 new tokens per sequence (no upper limit), every
  *          L_b >= q_len (a row with no visible token gets out = 0,
