@@ -71,3 +71,77 @@ def test_graph_replay_across_growing_lengths(fd, hq, hkv, dt):
                 assert torch.equal(res.out, out) and torch.equal(res.lse, lse)
             else:
                 assert np.allclose(res.out.cpu().numpy(), out.cpu().numpy(), rtol=1e-5, atol=1e-6)
+
+
+def test_graph_decode_loop_with_append(fd):
+    """A decode loop captured once: append (RoPE on the new key and the
+    query) + partial + combine in one graph, replayed for three steps as each
+    sequence grows by a token; new k/v/q are copied into the graph's input
+    buffers between replays. Each replay is checked against the oracle doing
+    the same append and decode on its own copy of the cache."""
+    from oracle.append import append_kv
+    from tests.test_append_gpu import assert_same_storage
+    B, hq, hkv, d = 3, 32, 8, 128
+    start = [700, 5000, 33]
+    final = [L + 3 for L in start]
+    wl = to_paged(make_workload(name="graphloop", batch=B, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                                seq_lens=final, dtype=torch.bfloat16, seed=1320), 16, spare_pages=2)
+    dev = torch.device("cuda", 0)
+    kc, vc, bt = wl.k.to(dev), wl.v.to(dev), wl.block_table.to(dev)
+    ref_k, ref_v = wl.k.clone(), wl.v.clone()
+    prob_app = fd.make_problem(batch=B, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, kv_dtype=torch.bfloat16,
+                               page_size=16, max_pages_per_seq=wl.max_pages_per_seq, q_len=1)
+    prob = fd.make_problem(batch=B, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, kv_dtype=torch.bfloat16,
+                           scale=wl.scale, page_size=16, max_pages_per_seq=wl.max_pages_per_seq)
+    plan = fd.fd_plan_splits(prob, final)
+    lens_dev = torch.tensor([L + 1 for L in start], dtype=torch.int32, device=dev)
+    q = torch.zeros((B, 1, hq, d), dtype=torch.bfloat16, device=dev)
+    k_new = torch.zeros((B, 1, hkv, d), dtype=torch.bfloat16, device=dev)
+    v_new = torch.zeros((B, 1, hkv, d), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(-(-plan.workspace_bytes // 4), dtype=torch.float32, device=dev)
+    out = torch.empty((B, hq, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, hq), dtype=torch.float32, device=dev)
+
+    def step():
+        fd.fd_append_kv(prob_app, k_new, v_new, q, kc, vc, bt, lens_dev, rope_style="half")
+        fd.fd_decode_partial(prob, plan, q.view(B, hq, d), kc, vc, bt, lens_dev, ws)
+        fd.fd_combine(prob, plan, lens_dev, ws, out, lse)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # a warm-up pass on the capture stream (on scratch copies of the cache)
+        kc_s, vc_s = kc.clone(), vc.clone()
+        fd.fd_append_kv(prob_app, k_new, v_new, q.clone(), kc_s, vc_s, bt, lens_dev, rope_style="half")
+        fd.fd_decode_partial(prob, plan, q.view(B, hq, d), kc_s, vc_s, bt, lens_dev, ws)
+        fd.fd_combine(prob, plan, lens_dev, ws, out, lse)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    del kc_s, vc_s
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+
+    g = torch.Generator().manual_seed(1321)
+    for i in range(3):
+        lens = [L + 1 + i for L in start]
+        qh = torch.randn((B, 1, hq, d), generator=g).to(torch.bfloat16)
+        kh = torch.randn((B, 1, hkv, d), generator=g).to(torch.bfloat16)
+        vh = torch.randn((B, 1, hkv, d), generator=g).to(torch.bfloat16)
+        q.copy_(qh)
+        k_new.copy_(kh)
+        v_new.copy_(vh)
+        lens_dev.copy_(torch.tensor(lens, dtype=torch.int32))
+        graph.replay()
+        torch.cuda.synchronize()
+        ref_k, ref_v, rq = append_kv(ref_k, ref_v, wl.block_table, lens, kh, vh, qh, rope_style="half")
+        ref_out, ref_lse = oracle.decode_attention(rq.view(B, hq, d), ref_k, ref_v, lens, wl.scale, wl.block_table, 16)
+        announce(f"graph decode loop step {i}: lens {lens}")
+        assert_same_storage(q.view(B, hq, d), rq.view(B, hq, d), f"q step {i}")
+        parity(out, lse, ref_out, ref_lse, what=f"graph decode loop step {i}")
+    mask = np.zeros(tuple(wl.k.shape), dtype=bool)
+    for b, L in enumerate(start):
+        for pos in range(L, L + 3):
+            mask[int(wl.block_table[b, pos // 16]), pos % 16] = True
+    assert_same_storage(kc, ref_k, "K cache after 3 steps", mask)
+    assert_same_storage(vc, ref_v, "V cache after 3 steps", mask)
