@@ -336,14 +336,22 @@ __global__ __launch_bounds__(64 * kPW) void prefill_fa2(const PrefillArgs a) {
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) {
             // Raw scores here; the (positive) scale joins the exponent's fma below.
+            // The mask is a separate (wave-uniform) branch, so that the tiles
+            // wholly inside every row's limit skip its compare and select.
+            if (masked) {
+#pragma unroll
+                for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (t0 + 16 * mt + 4 * grp + i >= lim[nt]) s[mt][nt][i] = neg_inf();
+            }
             float p[4 * kMT];
             float mx = neg_inf();
 #pragma unroll
             for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int t = t0 + 16 * mt + 4 * grp + i;
-                    p[4 * mt + i] = (!masked || t < lim[nt]) ? s[mt][nt][i] : neg_inf();
+                    p[4 * mt + i] = s[mt][nt][i];
                     mx = fmaxf(mx, p[4 * mt + i]);
                 }
             mx = fmaxf(mx, __shfl_xor(mx, 16));
