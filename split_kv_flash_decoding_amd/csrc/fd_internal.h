@@ -62,7 +62,7 @@ inline int32_t q_dtype_of(const fd_problem* p) { return p->kv_dtype == FD_FP8_E4
 inline int32_t rows_per_load(const fd_problem* p) { return 64 / (p->head_dim * kv_elem_bytes(p) / 16); }
 
 // Whether the matrix-core partial kernel covers this problem: d = 128 and
-// 2 <= q_len * Hq/Hkv <= 16 query rows per KV head.
+// 2 <= q_len * Hq/Hkv <= kMaxQueryRows query rows per KV head.
 bool mfma_applicable(const fd_problem* p);
 // Whether the head-rows kernel covers it: one query token, G <= 2 and Hkv a
 // multiple of the rows one load covers.
