@@ -563,6 +563,7 @@ def main() -> int:
             "page_size": wl.page_size,
             "accumulate": "f32", "out_dtype": "f32",
             "chunk_tokens": plan.chunk_tokens, "splits": plan.max_splits, "total_splits": plan.total_splits,
+            "split_mode": plan.split_mode,
             "kv_bytes_per_call": nbytes,
         },
         "roofline": {

@@ -112,16 +112,30 @@ typedef struct fd_problem {
 } fd_problem;
 
 /* How the splits are cut. Holds scalars only: nothing is uploaded per call,
- * and each kernel derives a sequence's split count ceil(L_b / chunk_tokens)
- * from the device seq_lens. */
+ * and each kernel derives a sequence's splits from the device seq_lens.
+ *
+ * split_mode 0 (per sequence): split s of sequence b holds tokens
+ * [s*C, min((s+1)*C, L_b)), so S_b = ceil(L_b / C).
+ * split_mode 1 (balanced, ragged batches on the matrix-core kernel): the
+ * n_b = ceil(L_b / 16) 16-token tiles of all sequences, in sequence order,
+ * form one list; T_b = n_0 + ... + n_{b-1} is sequence b's first tile in it.
+ * Work item w takes tiles [w*P, (w+1)*P) of the list, P = C / 16, across
+ * sequence boundaries, so every work-group streams the same bytes whatever
+ * the length mix. Split s of sequence b is its share of item
+ * floor(T_b / P) + s: tokens [16*max(0, (floor(T_b/P)+s)*P - T_b),
+ * min(L_b, 16*((floor(T_b/P)+s+1)*P - T_b))), and
+ * S_b = floor((T_b + n_b - 1) / P) - floor(T_b / P) + 1 <= ceil(n_b / P) + 1. */
 typedef struct fd_plan {
-    int32_t chunk_tokens;      /* C: tokens per split */
-    int32_t max_splits;        /* S_max = max_b ceil(L_b / C): workspace stride */
-    int32_t total_splits;      /* sum_b ceil(L_b / C) */
+    int32_t chunk_tokens;      /* C: tokens per split (mode 0) or per work item (mode 1, a multiple of 16) */
+    int32_t max_splits;        /* S_max: workspace stride, >= every S_b (mode 0: max_b ceil(L_b / C);
+                                  mode 1: ceil(max_b n_b / P) + 1) */
+    int32_t total_splits;      /* work-list entries per KV-head group: sum_b ceil(L_b / C) (mode 0),
+                                  or ceil(sum_b n_b / P) work items (mode 1) */
     int32_t num_cus;           /* compute units the plan was sized for */
     int32_t partial_kernel;    /* which partial kernel runs (0 = vector ALU token rows, 1 = MFMA,
                                   2 = vector ALU head rows) */
-    int32_t reserved;
+    int32_t split_mode;        /* 0 = per-sequence chunks, 1 = balanced tile list (partial_kernel 1 with
+                                  q_len * Hq/Hkv <= 8 only) */
     int64_t total_tokens;      /* sum_b L_b */
     uint64_t workspace_bytes;  /* bytes the workspace must hold */
 } fd_plan;
@@ -140,14 +154,20 @@ typedef struct fd_plan {
  * several heads, 2048 when the cache is FP8; that kernel gives way to one
  * head per work-group when its work-groups would be fewer than the compute
  * units).
+ * A batch of unequal lengths on the matrix-core kernel (q_len * Hq/Hkv <= 8,
+ * at most 4096 sequences, no forced split count) gets split_mode 1 instead:
+ * P = max(16, ceil(sum_b n_b * Hkv / (num_cus * 3))) tiles per work item,
+ * i.e. about three work-groups per compute unit, the kernel's occupancy, all
+ * of them the same size.
  * `force_num_splits` > 0 instead sets C = ceil(max_b L_b / force) and accepts
- * any C >= 1. `num_cus` == 0 asks the current HIP device (the only HIP call
+ * any C >= 1 (split_mode 0). `num_cus` == 0 asks the current HIP device (the only HIP call
  * here; its count is cached per device). Validates the problem and every
  * length (1 <= L_b, and L_b <= max_pages_per_seq * 16 when paged).
  * seq_lens_host: B lengths in host memory. out: receives the plan.
  * The environment variables FD_NUM_SPLITS (forces splits when the argument
- * is 0), FD_MIN_CHUNK, FD_WG_PER_CU (fixes k) and FD_PARTIAL_KERNEL (0, 1 or 2)
- * override these choices for experiments.
+ * is 0), FD_MIN_CHUNK, FD_WG_PER_CU (fixes k, or the work-groups per compute
+ * unit of split_mode 1), FD_PARTIAL_KERNEL (0, 1 or 2) and FD_SPLIT_MODE (0 or
+ * 1, where the balanced mode applies) override these choices for experiments.
  */
 fd_status fd_plan_splits(const fd_problem* problem, const int32_t* seq_lens_host,
                          int32_t num_cus, int32_t force_num_splits, fd_plan* out);
@@ -156,10 +176,11 @@ fd_status fd_plan_splits(const fd_problem* problem, const int32_t* seq_lens_host
  * Per-split partials (asynchronous on `stream`).
  *
  * For every sequence b, query row r (= i * Hq + h for query token i and head
- * h) and split s < ceil(L_b / C) writes the split's running max
+ * h) and split s < S_b writes the split's running max
  * m_s = max_t scale*<q, k_t>, sum l_s = sum_t exp(scale*<q,k_t> - m_s) and
  * unnormalised output O_s = sum_t exp(scale*<q,k_t> - m_s) v_t over the
- * split's tokens t in [s*C, min((s+1)*C, L_b)) that the query may see (the
+ * split's tokens t (with split_mode 0, [s*C, min((s+1)*C, L_b)); with
+ * split_mode 1, the range fd_plan describes) that the query may see (the
  * per-chunk local softmax of capstone §2.3; the running-statistics loop of
  * the lpnh.cn memory-wall article, §2.2). A split holding no such token gets
  * m_s = -inf, l_s = 0, O_s = 0. Tokens at or past L_b are never read.

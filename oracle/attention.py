@@ -305,26 +305,44 @@ def decode_attention_multi(q, k, v, seq_lens, scale: float, block_table=None, pa
     return out, lse
 
 
-def decode_partials(q, k, v, seq_lens, scale: float, chunk: int, block_table=None,
+def _splits_of(lens: List[int], chunk: Optional[int], bounds) -> List[List[Tuple[int, int]]]:
+    """Token ranges of every sequence's splits: consecutive chunks of ``chunk``
+    tokens, or the ranges ``bounds[b]`` a caller gives (any cut of [0, L_b)
+    into consecutive ranges; the statistics of each range follow the same
+    definition)."""
+    if bounds is None:
+        return [split_bounds(L, chunk) for L in lens]
+    out = [[(int(lo), int(hi)) for lo, hi in bounds[b]] for b in range(len(lens))]
+    for b, rs in enumerate(out):
+        if not rs or rs[0][0] != 0 or rs[-1][1] != lens[b] or any(
+                lo >= hi or (i and rs[i - 1][1] != lo) for i, (lo, hi) in enumerate(rs)):
+            raise ValueError(f"bounds of sequence {b} do not cut [0, {lens[b]}) into consecutive ranges")
+    return out
+
+
+def decode_partials(q, k, v, seq_lens, scale: float, chunk: Optional[int], block_table=None,
                     page_size: int = 0, max_splits: Optional[int] = None,
-                    pairs: Optional[Sequence[Tuple[int, int]]] = None, k_scale=None, v_scale=None):
+                    pairs: Optional[Sequence[Tuple[int, int]]] = None, k_scale=None, v_scale=None,
+                    bounds=None):
     """Per-split statistics for every (b, h): O [B, Hq, S, d] (unnormalised),
     m [B, Hq, S] and l [B, Hq, S], S = max_b ceil(L_b / chunk). Splits a
-    sequence does not have are NaN.
+    sequence does not have are NaN. ``bounds`` (a list of (lo, hi) token
+    ranges per sequence) replaces the chunk cut.
 
     With several queries per sequence (q [B, q_len, Hq, d]) the row index is
     i * Hq + h and each query sees its causal prefix; a split past that
     prefix has m = -inf, l = 0, O = 0."""
     qf = as_f64(q)
+    cuts = _splits_of(_lens(seq_lens), chunk, bounds)
     if qf.ndim == 4:
         B, ql, hq, d = qf.shape
-        return _decode_partials_multi(qf, k, v, seq_lens, scale, chunk, block_table, page_size, max_splits,
+        return _decode_partials_multi(qf, k, v, seq_lens, scale, cuts, block_table, page_size, max_splits,
                                       k_scale, v_scale)
     B, hq, d = qf.shape
     hkv = k.shape[-2]
     G = hq // hkv
     lens = _lens(seq_lens)
-    S = max((L + chunk - 1) // chunk for L in lens) if max_splits is None else max_splits
+    S = max(len(c) for c in cuts) if max_splits is None else max_splits
     O = np.full((B, hq, S, d), np.nan)
     m = np.full((B, hq, S), np.nan)
     l = np.full((B, hq, S), np.nan)
@@ -333,26 +351,26 @@ def decode_partials(q, k, v, seq_lens, scale: float, chunk: int, block_table=Non
         todo.setdefault((b, h // G), []).append(h)
     for (b, g), heads in sorted(todo.items()):
         K, V = logical_kv(k, v, seq_lens, b, g, block_table, page_size, k_scale, v_scale)
-        for si, (lo, hi) in enumerate(split_bounds(lens[b], chunk)):
+        for si, (lo, hi) in enumerate(cuts[b]):
             for h in heads:
                 O[b, h, si], m[b, h, si], l[b, h, si] = _split_partial(qf[b, h], K[lo:hi], V[lo:hi], scale)
     return O, m, l
 
 
-def _decode_partials_multi(qf, k, v, seq_lens, scale, chunk, block_table, page_size, max_splits,
+def _decode_partials_multi(qf, k, v, seq_lens, scale, cuts, block_table, page_size, max_splits,
                            k_scale=None, v_scale=None):
     B, ql, hq, d = qf.shape
     hkv = k.shape[-2]
     G = hq // hkv
     lens = _lens(seq_lens)
-    S = max((L + chunk - 1) // chunk for L in lens) if max_splits is None else max_splits
+    S = max(len(c) for c in cuts) if max_splits is None else max_splits
     O = np.full((B, ql * hq, S, d), np.nan)
     m = np.full((B, ql * hq, S), np.nan)
     l = np.full((B, ql * hq, S), np.nan)
     for b in range(B):
         for g in range(hkv):
             K, V = logical_kv(k, v, seq_lens, b, g, block_table, page_size, k_scale, v_scale)
-            for si, (lo, hi) in enumerate(split_bounds(lens[b], chunk)):
+            for si, (lo, hi) in enumerate(cuts[b]):
                 for i in range(ql):
                     top = min(hi, lens[b] - ql + i + 1)
                     for h in range(g * G, (g + 1) * G):

@@ -71,13 +71,13 @@ class FdPlan(ctypes.Structure):
         ("total_splits", ctypes.c_int32),
         ("num_cus", ctypes.c_int32),
         ("partial_kernel", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("split_mode", ctypes.c_int32),
         ("total_tokens", ctypes.c_int64),
         ("workspace_bytes", ctypes.c_uint64),
     ]
 
     def as_dict(self) -> dict:
-        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+        return {name: getattr(self, name) for name, _ in self._fields_}
 
 
 class FdError(RuntimeError):

@@ -69,6 +69,7 @@ fd_status decode_partial(const fd_problem* p, const fd_plan* plan, const void* q
     a.hkv = p->num_kv_heads;
     a.chunk = plan->chunk_tokens;
     a.s_max = plan->max_splits;
+    a.split_mode = plan->split_mode;
     a.max_pages = p->page_size ? p->max_pages_per_seq : 0;
     a.q_len = problem_q_len(p);
     a.qk_scale_log2 = scale * fdk::kLog2e;
@@ -193,7 +194,9 @@ fd_status fd_combine(const fd_problem* p, const fd_plan* plan, const int32_t* se
     hipStream_t hs = static_cast<hipStream_t>(stream);
     // The combine treats the q_len * Hq query rows of a sequence alike.
     hipError_t e = fdk::launch_combine(p->head_dim, p->out_dtype, ws_o, ws_ml, seq_lens_dev, out, lse, p->batch,
-                                       problem_q_len(p) * p->num_q_heads, plan->chunk_tokens, plan->max_splits, hs);
+                                       problem_q_len(p) * p->num_q_heads, plan->chunk_tokens, plan->max_splits,
+                                       plan->split_mode, p->page_size ? p->max_pages_per_seq * kPageSize : INT32_MAX,
+                                       hs);
     if (e != hipSuccess) return fail(FD_ERR_HIP, "combine kernel launch: %s", hipGetErrorString(e));
     return FD_OK;
 }

@@ -6,7 +6,9 @@
 // out = sum_s w_s O_s / sum_s w_s l_s, lse = M + ln(sum_s w_s l_s). This is
 // the cross-chunk reduce of FlashDecoding ("FlashAttention 全景演进与大模型
 // Token 生成全链路性能优化实战", §2.3), with every split rescaled by the
-// two-block identity of the same page's §1.2.
+// two-block identity of the same page's §1.2. Under the balanced split mode
+// a sequence's split count comes from its first tile in the list of all
+// sequences' tiles, a prefix sum each wave computes over seq_lens.
 
 #include "fd_device.h"
 
@@ -20,15 +22,28 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine(const float* __res
                                                               const float* __restrict__ ws_ml,
                                                               const int32_t* __restrict__ seq_lens,
                                                               void* __restrict__ out, float* __restrict__ lse, int hq,
-                                                              int chunk, int s_max) {
+                                                              int chunk, int s_max, int split_mode, int len_cap) {
     constexpr int PER = D / 64;  // output columns per lane
     const int h = blockIdx.x;
     const int b = blockIdx.y;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int L = seq_lens[b];
-    const int S = L > 0 ? min((L + chunk - 1) / chunk, s_max) : 0;
+    int S;
+    if (split_mode == 0) {
+        const int L = seq_lens[b];
+        S = L > 0 ? min((L + chunk - 1) / chunk, s_max) : 0;
+    } else {
+        int64_t T = 0;  // tiles of sequences 0..b-1
+        for (int base = 0; base < b; base += 64) {
+            const int i = base + lane;
+            int64_t n = i < b ? seq_tiles(max(0, min(seq_lens[i], len_cap))) : 0;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) n += __shfl_xor(n, off);
+            T += n;
+        }
+        S = min(balanced_splits(T, seq_tiles(max(0, min(seq_lens[b], len_cap))), chunk >> 4), s_max);
+    }
     const int64_t base = ((int64_t)b * hq + h) * s_max;
     const int64_t orow = ((int64_t)b * hq + h) * D;
     if (S == 0) {
@@ -90,26 +105,28 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine(const float* __res
 
 template <int D>
 hipError_t launch_combine_d(int out_dt, const float* ws_o, const float* ws_ml, const int32_t* lens, void* out,
-                          float* lse, int B, int hq, int chunk, int s_max, hipStream_t st) {
+                          float* lse, int B, int hq, int chunk, int s_max, int split_mode, int len_cap,
+                          hipStream_t st) {
     dim3 grid(hq, B);
     switch (out_dt) {
         case FD_F32:
-            hipLaunchKernelGGL((combine<D, FD_F32>), grid, dim3(64 * kCombineWaves), 0, st, ws_o, ws_ml, lens, out, lse, hq, chunk, s_max);
+            hipLaunchKernelGGL((combine<D, FD_F32>), grid, dim3(64 * kCombineWaves), 0, st, ws_o, ws_ml, lens, out, lse, hq, chunk, s_max, split_mode, len_cap);
             break;
         case FD_F16:
-            hipLaunchKernelGGL((combine<D, FD_F16>), grid, dim3(64 * kCombineWaves), 0, st, ws_o, ws_ml, lens, out, lse, hq, chunk, s_max);
+            hipLaunchKernelGGL((combine<D, FD_F16>), grid, dim3(64 * kCombineWaves), 0, st, ws_o, ws_ml, lens, out, lse, hq, chunk, s_max, split_mode, len_cap);
             break;
         default:
-            hipLaunchKernelGGL((combine<D, FD_BF16>), grid, dim3(64 * kCombineWaves), 0, st, ws_o, ws_ml, lens, out, lse, hq, chunk, s_max);
+            hipLaunchKernelGGL((combine<D, FD_BF16>), grid, dim3(64 * kCombineWaves), 0, st, ws_o, ws_ml, lens, out, lse, hq, chunk, s_max, split_mode, len_cap);
             break;
     }
     return hipGetLastError();
 }
 
 hipError_t launch_combine(int D, int out_dt, const float* ws_o, const float* ws_ml, const int32_t* lens,
-                          void* out, float* lse, int B, int hq, int chunk, int s_max, hipStream_t st) {
-    return D == 64 ? launch_combine_d<64>(out_dt, ws_o, ws_ml, lens, out, lse, B, hq, chunk, s_max, st)
-                   : launch_combine_d<128>(out_dt, ws_o, ws_ml, lens, out, lse, B, hq, chunk, s_max, st);
+                          void* out, float* lse, int B, int hq, int chunk, int s_max, int split_mode,
+                          int len_cap, hipStream_t st) {
+    return D == 64 ? launch_combine_d<64>(out_dt, ws_o, ws_ml, lens, out, lse, B, hq, chunk, s_max, split_mode, len_cap, st)
+                   : launch_combine_d<128>(out_dt, ws_o, ws_ml, lens, out, lse, B, hq, chunk, s_max, split_mode, len_cap, st);
 }
 
 }  // namespace fdk

@@ -212,6 +212,14 @@ __device__ __forceinline__ int64_t wave_incl_scan(int64_t x) {
     return x;
 }
 
+// A wave-uniform value moved to scalar registers (values that come out of
+// wave shuffles are otherwise kept per lane).
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uniform(int64_t x) {
+    return (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(x >> 32)) << 32) |
+                     (uint32_t)__builtin_amdgcn_readfirstlane((int)(x & 0xffffffff)));
+}
+
 // One work-group's share of a partial kernel: KV head g of split s of
 // sequence b, tokens [t0, t1); row0 is the sequence's first row in a packed
 // contiguous cache.
@@ -259,17 +267,102 @@ __device__ inline bool locate_unit(int u, const int32_t* __restrict__ seq_lens, 
             const int64_t incl_j = __shfl(incl, j);
             const int cnt_j = __shfl(cnt, j);
             const int L_j = __shfl(L, j);
-            out.b = base + j;
-            out.g = g;
-            out.s = full ? (int)(target - (acc + incl_j - cnt_j)) : L_j / chunk;
+            out.b = uniform(base + j);
+            out.g = uniform(g);
+            out.s = uniform(full ? (int)(target - (acc + incl_j - cnt_j)) : L_j / chunk);
             out.t0 = out.s * chunk;
-            out.t1 = min(out.t0 + chunk, L_j);
-            out.L = L_j;
-            out.row0 = racc + __shfl(lincl, j) - L_j;
+            out.L = uniform(L_j);
+            out.t1 = min(out.t0 + chunk, out.L);
+            out.row0 = uniform(racc + __shfl(lincl, j) - L_j);
             return true;
         }
         acc += total;
         racc += __shfl(lincl, 63);
+    }
+    return false;
+}
+
+// Tiles of a sequence of L tokens: 16-token tiles (a paged cache's pages).
+__device__ __forceinline__ int seq_tiles(int L) { return (L + 15) >> 4; }
+
+// Split count of a sequence whose n tiles start at tile T of the balanced
+// list (below), with P tiles per work item: the items that hold any of its
+// tiles. 0 for an empty sequence.
+__device__ __forceinline__ int balanced_splits(int64_t T, int n, int P) {
+    return n > 0 ? (int)((T + n - 1) / P - T / P + 1) : 0;
+}
+
+// Balanced work list (plan split mode 1): the 16-token tiles of all
+// sequences, in sequence order, form one list, and work item w takes tiles
+// [w P, (w + 1) P) of it, across sequence boundaries, so every work-group of
+// a ragged batch streams the same bytes. The share of item w in sequence b
+// is split s = w - floor(T_b / P) of b, where T_b is the sequence's first
+// tile in the list. The cursor walks the sequences an item touches.
+struct BalancedCursor {
+    int64_t lo, hi;  // the item's tiles [lo, hi)
+    int64_t T;       // first tile of sequence b in the list
+    int64_t row0;    // first row of sequence b in a packed contiguous cache
+    int b;
+};
+
+// Fills wu (and S, the sequence's split count) with the share of the item in
+// the cursor's sequence, skipping empty sequences. False once the item holds
+// no more tiles.
+__device__ inline bool balanced_share(const int32_t* __restrict__ seq_lens, int B, int P, int len_cap, int g,
+                                      BalancedCursor& c, WorkUnit& wu, int& S) {
+    while (c.b < B && c.T < c.hi) {
+        const int L = max(0, min(seq_lens[c.b], len_cap));
+        const int n = seq_tiles(L);
+        if (n > 0) {
+            const int64_t f = c.T / P;
+            S = balanced_splits(c.T, n, P);
+            wu.b = c.b;
+            wu.g = g;
+            wu.s = (int)(c.lo / P - f);
+            wu.t0 = (int)(max(c.lo, c.T) - c.T) * 16;
+            wu.t1 = min(L, (int)(min(c.hi, c.T + n) - c.T) * 16);
+            wu.L = L;
+            wu.row0 = c.row0;
+            return true;
+        }
+        ++c.b;
+    }
+    return false;
+}
+
+// Moves the cursor to the sequence after the current one.
+__device__ inline void balanced_advance(const int32_t* __restrict__ seq_lens, int len_cap, BalancedCursor& c) {
+    const int L = max(0, min(seq_lens[c.b], len_cap));
+    c.T += seq_tiles(L);
+    c.row0 += L;
+    ++c.b;
+}
+
+// Starts the cursor of work item w at the first sequence holding one of its
+// tiles (two wave-wide scans over seq_lens per 64 sequences). False for an
+// item past the end of the list.
+__device__ inline bool balanced_first(int64_t w, const int32_t* __restrict__ seq_lens, int B, int P, int len_cap,
+                                      BalancedCursor& c) {
+    const int lane = threadIdx.x & 63;
+    c.lo = w * P;
+    c.hi = c.lo + P;
+    int64_t accT = 0, accR = 0;
+    for (int base = 0; base < B; base += 64) {
+        const int i = base + lane;
+        const int L = i < B ? max(0, min(seq_lens[i], len_cap)) : 0;
+        const int n = seq_tiles(L);
+        const int64_t inclT = wave_incl_scan(n);
+        const int64_t inclL = wave_incl_scan(L);
+        const int64_t totalT = __shfl(inclT, 63);
+        if (c.lo < accT + totalT) {
+            const int j = __builtin_ctzll(__ballot(accT + inclT > c.lo));
+            c.b = uniform(base + j);
+            c.T = uniform(accT + __shfl(inclT, j) - __shfl(n, j));
+            c.row0 = uniform(accR + __shfl(inclL, j) - __shfl(L, j));
+            return true;
+        }
+        accT += totalT;
+        accR += __shfl(inclL, 63);
     }
     return false;
 }
@@ -287,6 +380,10 @@ struct PartialArgs {
     float* ws_o;
     float* ws_ml;
     int batch, hq, hkv, chunk, s_max, max_pages, q_len;
+    // 0: split s of a sequence holds tokens [s chunk, (s + 1) chunk) (work
+    // list of locate_unit); 1: balanced list, chunk = 16 * tiles per item
+    // (BalancedCursor; matrix-core kernel only).
+    int split_mode;
     float qk_scale_log2;
     int kv_dt, q_dt;
     int num_pages;  // pool size of a paged cache (0: indices not checked)
@@ -359,7 +456,8 @@ hipError_t launch_partial_mfma(int G, bool paged, const PartialArgs& a, dim3 gri
 hipError_t launch_append(const AppendArgs& a, int q_dt, int kv_dt, int blocks, hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, int dt, int out_dt, bool paged, hipStream_t st);
 hipError_t launch_combine(int D, int out_dt, const float* ws_o, const float* ws_ml, const int32_t* lens,
-                          void* out, float* lse, int B, int hq, int chunk, int s_max, hipStream_t st);
+                          void* out, float* lse, int B, int hq, int chunk, int s_max, int split_mode,
+                          int len_cap, hipStream_t st);
 
 // ------------------------------------------------------------ fused merge
 
@@ -370,17 +468,17 @@ hipError_t launch_combine(int D, int out_dt, const float* ws_o, const float* ws_
 // count (splits x `tiles` column tiles) merges every split of the group's
 // `nrows` rows, ROWS at a time, exactly as the combine kernel does
 // (FlashAttention capstone §2.3 cross-chunk reduce), and sets the counter back
-// to zero for the next call. No work-group waits for another. Rows:
+// to zero for the next call. No work-group waits for another. S: the
+// sequence's split count under the plan's split mode. Rows:
 // r = i * (nkv * G) + k for query token i and head k of the group, i.e.
 // query row i * Hq + g0 * G + k. `red` is the caller's wave-merge LDS buffer,
 // at least NW * ROWS * D floats for NW waves per work-group.
 template <int D, int ROWS, int NW>
-__device__ void fused_merge(const PartialArgs& a, int b, int L, int g0, int nkv, int nrows, int tiles, float* red) {
+__device__ void fused_merge(const PartialArgs& a, int b, int S, int g0, int nkv, int nrows, int tiles, float* red) {
     constexpr int PER = D / 64;
     __shared__ int s_last;
     __shared__ float s_max[ROWS];
     __shared__ float s_l[NW][ROWS];
-    const int S = (L + a.chunk - 1) / a.chunk;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // this work-group's partials, visible device-wide
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -390,12 +488,16 @@ __device__ void fused_merge(const PartialArgs& a, int b, int L, int g0, int nkv,
     __syncthreads();
     if (!s_last) return;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the other work-groups' partials, not stale cache lines
+    // Lane indices kept opaque: a caller that loops over several splits would
+    // otherwise get this merge's lane-derived addresses hoisted out of its loop.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
 
     const int G = a.hq / a.hkv;
     const int R = a.q_len * a.hq;
     const int per_tok = nkv * G;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
     auto qrow_of = [&](int r) { return (r / per_tok) * a.hq + g0 * G + r % per_tok; };
     for (int r0 = 0; r0 < nrows; r0 += ROWS) {
         const int nr = min(ROWS, nrows - r0);
@@ -439,7 +541,7 @@ __device__ void fused_merge(const PartialArgs& a, int b, int L, int g0, int nkv,
             }
         }
         __syncthreads();
-        for (int idx = threadIdx.x; idx < nr * D; idx += blockDim.x) {
+        for (int idx = tid; idx < nr * D; idx += blockDim.x) {
             const int r = idx / D, col = idx % D;
             float l = 0.f, o = 0.f;
 #pragma unroll

@@ -120,6 +120,13 @@ fd_status check_plan(const fd_problem* p, const fd_plan* plan) {
                     plan->chunk_tokens, plan->max_splits);
     if (plan->workspace_bytes < workspace_bytes(p, plan->max_splits))
         return fail(FD_ERR_INVALID_ARGUMENT, "plan does not belong to this problem (workspace_bytes)");
+    if (plan->split_mode != 0 &&
+        (plan->split_mode != 1 || plan->partial_kernel != kPartialMfma || plan->chunk_tokens % kTileTokens ||
+         problem_q_len(p) * (p->num_q_heads / p->num_kv_heads) > kBalancedMaxRows))
+        return fail(FD_ERR_INVALID_ARGUMENT, "plan split_mode %d with kernel %d and chunk %d: the balanced mode "
+                    "needs the matrix-core kernel, a chunk that is a multiple of %d and at most %d query rows "
+                    "per KV head", plan->split_mode, plan->partial_kernel, plan->chunk_tokens, kTileTokens,
+                    kBalancedMaxRows);
     if ((plan->partial_kernel != kPartialMfma && problem_q_len(p) > 1) ||
         (plan->partial_kernel == kPartialMfma && !mfma_applicable(p)) ||
         (plan->partial_kernel == kPartialHeadRows && !head_rows_applicable(p)) ||
@@ -261,12 +268,43 @@ fd_status fd_plan_splits(const fd_problem* p, const int32_t* lens, int32_t num_c
             chunk = choose_chunk(kernel);
         }
     }
-    int64_t smax = ceil_div(lmax, chunk);
+    // A ragged batch on the matrix-core kernel: per-sequence chunks leave
+    // short last splits and a last round of work-groups that occupies part of
+    // the chip, so the tiles of all sequences are dealt out in equal work
+    // items instead (split_mode 1), about num_cus * kBalancedWgPerCu
+    // work-groups: the matrix-core kernel's occupancy, one round.
+    // FD_SPLIT_MODE=0/1 overrides; FD_WG_PER_CU sets the work-groups per CU.
+    bool ragged = false;
+    for (int32_t b = 1; b < p->batch; ++b) ragged |= lens[b] != lens[0];
+    const bool balanced_ok = kernel == kPartialMfma && problem_q_len(p) * G <= kBalancedMaxRows;
+    int32_t split_mode = (balanced_ok && force_num_splits == 0 && ragged && p->batch <= kBalancedMaxBatch) ? 1 : 0;
+    const int32_t forced_mode = env_int("FD_SPLIT_MODE", -1);
+    if (forced_mode == 0 || (forced_mode == 1 && balanced_ok)) split_mode = forced_mode;
+
+    int64_t smax, nsplit = 0;
+    if (split_mode == 1) {
+        int64_t tiles = 0, nmax = 0;
+        for (int32_t b = 0; b < p->batch; ++b) {
+            const int64_t n = ceil_div(lens[b], kTileTokens);
+            tiles += n;
+            nmax = std::max(nmax, n);
+        }
+        const int32_t per_cu = env_int("FD_WG_PER_CU", 0) > 0 ? env_int("FD_WG_PER_CU", 0) : kBalancedWgPerCu;
+        const int64_t target = std::max<int64_t>(1, (int64_t)num_cus * per_cu);
+        const int64_t P = std::max<int64_t>(ceil_div(tiles * workgroups_per_split(p, kernel), target),
+                                            kBalancedMinTiles);
+        if (P * kTileTokens > INT32_MAX)
+            return fail(FD_ERR_UNSUPPORTED, "work items of %lld tiles exceed the chunk range", (long long)P);
+        chunk = P * kTileTokens;
+        smax = ceil_div(nmax, P) + 1;
+        nsplit = ceil_div(tiles, P);
+    } else {
+        smax = ceil_div(lmax, chunk);
+        for (int32_t b = 0; b < p->batch; ++b) nsplit += ceil_div(lens[b], chunk);
+    }
     if (smax > kMaxGridYZ)
         return fail(FD_ERR_UNSUPPORTED, "%lld splits exceed the grid limit %d", (long long)smax,
                     kMaxGridYZ);
-    int64_t nsplit = 0;
-    for (int32_t b = 0; b < p->batch; ++b) nsplit += ceil_div(lens[b], chunk);
 
     fd_plan plan;
     memset(&plan, 0, sizeof(plan));
@@ -275,13 +313,14 @@ fd_status fd_plan_splits(const fd_problem* p, const int32_t* lens, int32_t num_c
     plan.total_splits = (int32_t)std::min<int64_t>(nsplit, INT32_MAX);
     plan.num_cus = num_cus;
     plan.partial_kernel = kernel;
+    plan.split_mode = split_mode;
     plan.total_tokens = total;
     plan.workspace_bytes = workspace_bytes(p, plan.max_splits);
     *out = plan;
     if (getenv("FD_LOG"))
-        fprintf(stderr, "[fd] plan: B=%d Hq=%d Hkv=%d d=%d tokens=%lld chunk=%d S_max=%d splits=%d cus=%d kernel=%d ws=%llu\n",
+        fprintf(stderr, "[fd] plan: B=%d Hq=%d Hkv=%d d=%d tokens=%lld chunk=%d S_max=%d splits=%d cus=%d kernel=%d mode=%d ws=%llu\n",
                 p->batch, p->num_q_heads, p->num_kv_heads, p->head_dim, (long long)total, plan.chunk_tokens,
-                plan.max_splits, plan.total_splits, plan.num_cus, plan.partial_kernel,
+                plan.max_splits, plan.total_splits, plan.num_cus, plan.partial_kernel, plan.split_mode,
                 (unsigned long long)plan.workspace_bytes);
     return FD_OK;
 }

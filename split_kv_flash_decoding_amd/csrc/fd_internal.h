@@ -19,6 +19,17 @@ constexpr int32_t kChunkGranule = 64;
 constexpr int32_t kDefaultMinChunk = 256;
 constexpr int32_t kHeadRowsMinChunk = 1024;
 constexpr int32_t kPageSize = 16;
+// Balanced split mode (fd_plan.split_mode 1): tokens per tile of the list,
+// the smallest work item in tiles (256 tokens), the work-groups per compute
+// unit it aims at, and the largest batch it is chosen for (the combine walks
+// the lengths before its sequence).
+constexpr int32_t kTileTokens = 16;
+constexpr int32_t kBalancedMinTiles = 16;
+constexpr int32_t kBalancedWgPerCu = 3;
+constexpr int32_t kBalancedMaxBatch = 4096;
+// ... and the most query rows per KV head (q_len * Hq/Hkv) it is built for:
+// wider column tiles need more registers than the loop over shares leaves.
+constexpr int32_t kBalancedMaxRows = 8;
 
 // Records `msg` as this thread's last error and returns `st`.
 fd_status fail(fd_status st, const char* fmt, ...);

@@ -188,14 +188,35 @@ __global__ __launch_bounds__(64 * kMW) void partial_mfma(const PartialArgs a) {
         ct = rem / 8;
         unit = blockIdx.x / (8 * NT) * 8 + rem % 8;
     }
+    // Split mode 0: the work-list entry is one split (locate_unit). Mode 1
+    // (NQ <= 8 only): it is work item unit / hkv of the balanced tile list,
+    // whose shares of consecutive sequences run one after the other (the
+    // body below, once per share).
+    const int len_cap = PAGED ? max_pages * 16 : INT32_MAX;
     WorkUnit wu;
-    if (!locate_unit(unit, seq_lens, batch, hkv, chunk, PAGED ? max_pages * 16 : INT32_MAX, wu)) return;
+    int S_b = 0;
+    BalancedCursor cur;
+    if (a.split_mode == 0) {
+        if (!locate_unit(unit, seq_lens, batch, hkv, chunk, len_cap, wu)) return;
+        S_b = (wu.L + chunk - 1) / chunk;
+    } else {
+        if (NQ > 8) return;  // not planned: the share loop would cost this width its third wave
+        if (!balanced_first(unit / hkv, seq_lens, batch, chunk >> 4, len_cap, cur) ||
+            !balanced_share(seq_lens, batch, chunk >> 4, len_cap, unit % hkv, cur, wu, S_b))
+            return;
+    }
+next_share:
     if (wu.s >= s_max) return;
     const int g = wu.g, s = wu.s, b = wu.b, t0 = wu.t0, t1 = wu.t1;
     const int64_t row0 = wu.row0;
 
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    // The thread index is made opaque on every pass, so the compiler cannot
+    // hoist lane-derived addresses (the epilogue's) out of the loop over
+    // shares and hold them in registers across the tile loop.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
     const int grp = lane >> 4;  // 0..3
     const int col = lane & 15;  // query row (scores, output) / token (K operand) / d-slice (V load)
 
@@ -442,7 +463,7 @@ __global__ __launch_bounds__(64 * kMW) void partial_mfma(const PartialArgs a) {
     }
     __syncthreads();
     const float v_sc = head_scale(a.v_scale, g);
-    for (int idx = threadIdx.x; idx < nq * kD; idx += 64 * kMW) {
+    for (int idx = tid; idx < nq * kD; idx += 64 * kMW) {
         const int n = idx / kD;
         const int d = idx % kD;
         float Mx = sm_m[0][n];
@@ -465,7 +486,16 @@ __global__ __launch_bounds__(64 * kMW) void partial_mfma(const PartialArgs a) {
             ws_ml[slot * 2 + 1] = lsum;
         }
     }
-    if (a.counters) fused_merge<kD, NQ, kMW>(a, b, wu.L, g, 1, nq_all, NT, &sm_o[0][0][0]);
+    if (a.counters) fused_merge<kD, NQ, kMW>(a, b, S_b, g, 1, nq_all, NT, &sm_o[0][0][0]);
+    if constexpr (NQ <= 8) {
+        if (a.split_mode != 0) {
+            balanced_advance(seq_lens, len_cap, cur);
+            if (balanced_share(seq_lens, batch, chunk >> 4, len_cap, unit % hkv, cur, wu, S_b)) {
+                __syncthreads();  // the last share's merge area is the next share's staging area
+                goto next_share;
+            }
+        }
+    }
 }
 
 template <int NQ, int KT, int QT, bool KEEP = false>

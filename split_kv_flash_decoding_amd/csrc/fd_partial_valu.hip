@@ -226,7 +226,7 @@ __global__ __launch_bounds__(kThreads) void partial_valu(const PartialArgs a) {
             ws_ml[slot * 2 + 1] = lsum;
         }
     }
-    if (a.counters) fused_merge<D, G, kWaves>(a, b, wu.L, g, 1, G, 1, &sm_o[0][0][0]);
+    if (a.counters) fused_merge<D, G, kWaves>(a, b, (wu.L + chunk - 1) / chunk, g, 1, G, 1, &sm_o[0][0][0]);
 }
 
 // ------------------------------------------------- partial kernel, head rows
@@ -425,7 +425,7 @@ __global__ __launch_bounds__(kThreads) void partial_valu_heads(const PartialArgs
             ws_ml[slot * 2 + 1] = lsum;
         }
     }
-    if (a.counters) fused_merge<D, RPW * G, kWaves>(a, b, wu.L, wu.g * RPW, RPW, RPW * G, 1, &sm_o[0][0][0][0]);
+    if (a.counters) fused_merge<D, RPW * G, kWaves>(a, b, (wu.L + chunk - 1) / chunk, wu.g * RPW, RPW, RPW * G, 1, &sm_o[0][0][0][0]);
 }
 
 // ------------------------------------------------------------------ dispatch

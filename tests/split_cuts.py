@@ -1,0 +1,23 @@
+"""Token ranges of every sequence's splits under a plan, restated from the
+partition rules fd.h documents for fd_plan.split_mode (host arithmetic only,
+no attention)."""
+
+
+def ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def plan_cuts(lens, plan):
+    """[(lo, hi), ...] per sequence: split s of sequence b holds tokens [lo, hi)."""
+    C = plan.chunk_tokens
+    if plan.split_mode == 0:
+        return [[(s, min(s + C, L)) for s in range(0, L, C)] for L in lens]
+    P = C // 16
+    cuts, T = [], 0
+    for L in lens:
+        n = ceil_div(L, 16)
+        first, last = T // P, (T + n - 1) // P
+        cuts.append([(16 * (max(T, w * P) - T), min(L, 16 * (min(T + n, (w + 1) * P) - T)))
+                     for w in range(first, last + 1)])
+        T += n
+    return cuts

@@ -14,6 +14,7 @@ import pytest
 
 import split_kv_flash_decoding_amd as fd
 from split_kv_flash_decoding_amd import _capi
+from tests.split_cuts import plan_cuts
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 INCLUDE = os.path.join(ROOT, "include")
@@ -77,9 +78,11 @@ def workspace_bytes(B, rows, hkv, S, d=128):
     (8, 8, [1024]),
     (8, 2, [1, 2, 3, 300]),
 ])
-def test_planner_properties(hq, hkv, lens):
+def test_planner_properties(hq, hkv, lens, monkeypatch):
+    monkeypatch.setenv("FD_SPLIT_MODE", "0")  # the balanced mode has its own test below
     p = prob(batch=len(lens), num_q_heads=hq, num_kv_heads=hkv)
     plan = fd.fd_plan_splits(p, lens, num_cus=256)
+    assert plan.split_mode == 0
     C = plan.chunk_tokens
     assert C % 64 == 0 and C >= 256 or C == max(lens)
     splits = [ceil_div(L, C) for L in lens]
@@ -92,6 +95,93 @@ def test_planner_properties(hq, hkv, lens):
     # enough work-groups to cover the chip when there are enough tokens
     if sum(lens) * hkv >= 256 * 4 * 256:
         assert plan.total_splits * hkv >= 256
+
+
+@pytest.mark.parametrize("hq,hkv,lens,page", [
+    (32, 8, [2915, 4487, 5931, 8309, 8336, 8684, 8905, 10375, 10902, 12067, 12486, 12967, 15191, 15198, 15709,
+             15847], 0),
+    (64, 8, [512, 32768, 900, 20000, 574, 604, 7006, 31712] * 8, 16),
+    (64, 8, [1, 2, 15, 16, 17, 3000, 1, 40000], 16),
+    (16, 4, [7, 100000, 3, 5], 0),
+])
+def test_balanced_plan(hq, hkv, lens, page):
+    """Ragged batches on the matrix-core kernel get the balanced tile list:
+    every work item but the last holds P tiles, the items cover every tile
+    once, each sequence's splits cut [0, L_b) into consecutive non-empty
+    ranges, and S_max bounds every sequence's split count."""
+    p = prob(batch=len(lens), num_q_heads=hq, num_kv_heads=hkv, page_size=page,
+             max_pages_per_seq=ceil_div(max(lens), 16) if page else 0)
+    plan = fd.fd_plan_splits(p, lens, num_cus=256)
+    assert plan.partial_kernel == 1 and plan.split_mode == 1
+    C = plan.chunk_tokens
+    assert C % 16 == 0 and C >= 256
+    P = C // 16
+    tiles = [ceil_div(L, 16) for L in lens]
+    assert plan.total_splits == ceil_div(sum(tiles), P)
+    assert plan.max_splits == ceil_div(max(tiles), P) + 1
+    cuts = plan_cuts(lens, plan)
+    for L, rs in zip(lens, cuts):
+        assert rs[0][0] == 0 and rs[-1][1] == L and len(rs) <= plan.max_splits
+        assert all(lo < hi for lo, hi in rs) and all(rs[i][1] == rs[i + 1][0] for i in range(len(rs) - 1))
+        assert all(lo % 16 == 0 for lo, _ in rs)  # splits start on a page / tile
+    # tiles per work item: P for all but the last (the list is dealt out evenly)
+    per_item = [0] * plan.total_splits
+    T = 0
+    for n in tiles:
+        for t in range(T, T + n):
+            per_item[t // P] += 1
+        T += n
+    assert all(c == P for c in per_item[:-1]) and 0 < per_item[-1] <= P
+    # about three work-groups per compute unit (one round of the kernel's occupancy)
+    if sum(tiles) * hkv >= 256 * 3 * 16:
+        assert plan.total_splits * hkv <= 256 * 3 + hkv
+    assert plan.workspace_bytes == workspace_bytes(len(lens), hq, hkv, plan.max_splits)
+
+
+def test_balanced_plan_choice(monkeypatch):
+    """Only ragged matrix-core batches without forced splits get split_mode 1;
+    FD_SPLIT_MODE overrides where the mode applies."""
+    ragged = [1000, 5000, 300, 9000]
+    gqa = prob(batch=4, num_q_heads=32, num_kv_heads=8)
+    assert fd.fd_plan_splits(gqa, ragged, num_cus=256).split_mode == 1
+    assert fd.fd_plan_splits(gqa, [5000] * 4, num_cus=256).split_mode == 0          # equal lengths
+    assert fd.fd_plan_splits(gqa, ragged, num_cus=256, force_num_splits=3).split_mode == 0
+    assert fd.fd_plan_splits(prob(batch=4), ragged, num_cus=256).split_mode == 0    # MHA: vector kernels
+    wide = prob(batch=4, num_q_heads=32, num_kv_heads=8, q_len=4)                   # 16 query rows per KV head
+    assert fd.fd_plan_splits(wide, ragged, num_cus=256).split_mode == 0
+    assert fd.fd_plan_splits(prob(batch=4, num_q_heads=32, num_kv_heads=8, q_len=2), ragged,
+                             num_cus=256).split_mode == 1
+    monkeypatch.setenv("FD_SPLIT_MODE", "0")
+    assert fd.fd_plan_splits(gqa, ragged, num_cus=256).split_mode == 0
+    monkeypatch.setenv("FD_SPLIT_MODE", "1")
+    assert fd.fd_plan_splits(gqa, [5000] * 4, num_cus=256).split_mode == 1
+    assert fd.fd_plan_splits(prob(batch=4), ragged, num_cus=256).split_mode == 0    # not applicable
+
+
+def test_balanced_plan_is_checked():
+    """A balanced plan is refused for the vector kernels, for chunks that are not
+    a multiple of 16 and for more than 8 query rows per KV head."""
+    lib = fd.load_library()
+    fake = ctypes.c_void_p(0x10000)
+    gqa = prob(batch=2, num_q_heads=32, num_kv_heads=8)
+    plan = fd.fd_plan_splits(gqa, [1000, 3000], num_cus=256)
+    assert plan.split_mode == 1
+    need = plan.workspace_bytes
+    for field, value in (("chunk_tokens", plan.chunk_tokens + 8), ("partial_kernel", 0), ("split_mode", 2)):
+        bad = fd.FdPlan.from_buffer_copy(plan)
+        setattr(bad, field, value)
+        st = lib.fd_decode_partial(ctypes.byref(gqa), ctypes.byref(bad), fake, fake, fake, None, fake, fake,
+                                   need, None)
+        assert st == fd.FD_ERR_INVALID_ARGUMENT, field
+        st = lib.fd_combine(ctypes.byref(gqa), ctypes.byref(bad), fake, fake, need, fake, None, None)
+        assert st == fd.FD_ERR_INVALID_ARGUMENT, field
+    wide = prob(batch=2, num_q_heads=32, num_kv_heads=8, q_len=4)
+    bad = fd.fd_plan_splits(wide, [1000, 3000], num_cus=256)
+    bad.split_mode = 1
+    bad.chunk_tokens = 1024
+    st = lib.fd_decode_partial(ctypes.byref(wide), ctypes.byref(bad), fake, fake, fake, None, fake, fake,
+                               bad.workspace_bytes, None)
+    assert st == fd.FD_ERR_INVALID_ARGUMENT
 
 
 def test_planner_sizes_long_contexts_to_fill_the_chip(monkeypatch):

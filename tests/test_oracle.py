@@ -272,6 +272,36 @@ def test_decode_partials_merge_to_decode_attention():
                 assert abs(ls - lse[b, h]) < 1e-12
 
 
+def test_decode_partials_over_given_cuts_merge_to_decode_attention():
+    """Any cut of [0, L) into consecutive ranges merges to the full result
+    (the split-invariance of capstone §2.3, for cuts that are not a fixed
+    chunk: the balanced tile list cuts sequences at arbitrary tile offsets);
+    malformed cuts are refused."""
+    wl = _wl(seq_lens=[300, 64, 1], num_q_heads=4, num_kv_heads=2)
+    out, lse = A.decode_attention(wl.q, wl.k, wl.v, wl.seq_lens, wl.scale)
+    rng = np.random.default_rng(11)
+    for _ in range(3):
+        cuts = []
+        for L in wl.lens:
+            inner = sorted(rng.choice(np.arange(1, L), size=min(L - 1, int(rng.integers(0, 5))), replace=False)) \
+                if L > 1 else []
+            edges = [0, *[int(x) for x in inner], L]
+            cuts.append(list(zip(edges[:-1], edges[1:])))
+        O, m, l = A.decode_partials(wl.q, wl.k, wl.v, wl.seq_lens, wl.scale, None, bounds=cuts)
+        for b, rs in enumerate(cuts):
+            S = len(rs)
+            assert np.isnan(m[b, :, S:]).all()
+            for h in range(wl.num_q_heads):
+                o, ls = A.merge_partials(O[b, h, :S], m[b, h, :S], l[b, h, :S])
+                assert np.allclose(o, out[b, h], rtol=1e-12, atol=1e-14)
+                assert abs(ls - lse[b, h]) < 1e-12
+    for bad in ([[(0, 150), (151, 300)], [(0, 64)], [(0, 1)]],    # gap
+                [[(0, 300)], [(0, 64)], [(0, 2)]],                # past L
+                [[(0, 300)], [(0, 32), (32, 32), (32, 64)], [(0, 1)]]):  # empty range
+        with pytest.raises(ValueError):
+            A.decode_partials(wl.q, wl.k, wl.v, wl.seq_lens, wl.scale, None, bounds=bad)
+
+
 def test_sampled_pairs_match_full_batch():
     wl = _wl()
     out, lse = A.decode_attention(wl.q, wl.k, wl.v, wl.seq_lens, wl.scale)
