@@ -117,20 +117,21 @@ typedef struct fd_problem {
  * split_mode 0 (per sequence): split s of sequence b holds tokens
  * [s*C, min((s+1)*C, L_b)), so S_b = ceil(L_b / C).
  * split_mode 1 (balanced, ragged batches on the matrix-core kernel): the
- * n_b = ceil(L_b / 16) 16-token tiles of all sequences, in sequence order,
- * form one list; T_b = n_0 + ... + n_{b-1} is sequence b's first tile in it.
- * Work item w takes tiles [w*P, (w+1)*P) of the list, P = C / 16, across
- * sequence boundaries, so every work-group streams the same bytes whatever
- * the length mix. Split s of sequence b is its share of item
- * floor(T_b / P) + s: tokens [16*max(0, (floor(T_b/P)+s)*P - T_b),
- * min(L_b, 16*((floor(T_b/P)+s+1)*P - T_b))), and
- * S_b = floor((T_b + n_b - 1) / P) - floor(T_b / P) + 1 <= ceil(n_b / P) + 1. */
+ * sequences, in order, take consecutive positions of one list: 2 positions
+ * for the cost of starting a share (pipeline start, wave merge, store), then
+ * one per 16-token tile, n_b = ceil(L_b / 16) of them. So sequence b's first
+ * tile sits at T_b = 2*(b+1) + n_0 + ... + n_{b-1}. Work item w takes
+ * positions [w*P, (w+1)*P) of the list, P = C / 16, across sequence
+ * boundaries, so every work-group has the same work whatever the length mix.
+ * Split s of sequence b is its share of item floor(T_b / P) + s: tokens
+ * [16*max(0, (floor(T_b/P)+s)*P - T_b), min(L_b, 16*((floor(T_b/P)+s+1)*P - T_b))),
+ * and S_b = floor((T_b + n_b - 1) / P) - floor(T_b / P) + 1 <= ceil(n_b / P) + 1. */
 typedef struct fd_plan {
     int32_t chunk_tokens;      /* C: tokens per split (mode 0) or per work item (mode 1, a multiple of 16) */
     int32_t max_splits;        /* S_max: workspace stride, >= every S_b (mode 0: max_b ceil(L_b / C);
                                   mode 1: ceil(max_b n_b / P) + 1) */
     int32_t total_splits;      /* work-list entries per KV-head group: sum_b ceil(L_b / C) (mode 0),
-                                  or ceil(sum_b n_b / P) work items (mode 1) */
+                                  or ceil(sum_b (n_b + 2) / P) work items (mode 1) */
     int32_t num_cus;           /* compute units the plan was sized for */
     int32_t partial_kernel;    /* which partial kernel runs (0 = vector ALU token rows, 1 = MFMA,
                                   2 = vector ALU head rows) */
@@ -156,7 +157,7 @@ typedef struct fd_plan {
  * units).
  * A batch of unequal lengths on the matrix-core kernel (q_len * Hq/Hkv <= 8,
  * at most 4096 sequences, no forced split count) gets split_mode 1 instead:
- * P = max(16, ceil(sum_b n_b * Hkv / (num_cus * 3))) tiles per work item,
+ * P = max(16, ceil(sum_b (n_b + 2) * Hkv / (num_cus * 3))) positions per work item,
  * i.e. about three work-groups per compute unit, the kernel's occupancy, all
  * of them the same size.
  * `force_num_splits` > 0 instead sets C = ceil(max_b L_b / force) and accepts

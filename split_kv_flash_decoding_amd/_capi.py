@@ -15,7 +15,9 @@ from dataclasses import dataclass
 from typing import Optional, Sequence
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libfd.so")
+# FD_LIBRARY names another build of the library to load instead (an
+# experiment with different compile-time settings).
+LIB_PATH = os.environ.get("FD_LIBRARY") or os.path.join(HERE, "libfd.so")
 
 FD_OK, FD_ERR_INVALID_ARGUMENT, FD_ERR_UNSUPPORTED, FD_ERR_WORKSPACE_TOO_SMALL, FD_ERR_HIP = range(5)
 FD_F16, FD_BF16, FD_F32, FD_FP8_E4M3 = range(4)

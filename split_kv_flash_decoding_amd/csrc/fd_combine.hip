@@ -7,8 +7,8 @@
 // the cross-chunk reduce of FlashDecoding ("FlashAttention 全景演进与大模型
 // Token 生成全链路性能优化实战", §2.3), with every split rescaled by the
 // two-block identity of the same page's §1.2. Under the balanced split mode
-// a sequence's split count comes from its first tile in the list of all
-// sequences' tiles, a prefix sum each wave computes over seq_lens.
+// a sequence's split count comes from the position of its first tile in the
+// list of all sequences, a prefix sum each wave computes over seq_lens.
 
 #include "fd_device.h"
 
@@ -34,15 +34,16 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine(const float* __res
         const int L = seq_lens[b];
         S = L > 0 ? min((L + chunk - 1) / chunk, s_max) : 0;
     } else {
-        int64_t T = 0;  // tiles of sequences 0..b-1
+        int64_t U = 0;  // list positions of sequences 0..b-1
         for (int base = 0; base < b; base += 64) {
             const int i = base + lane;
-            int64_t n = i < b ? seq_tiles(max(0, min(seq_lens[i], len_cap))) : 0;
+            int64_t u = i < b ? seq_positions(seq_tiles(max(0, min(seq_lens[i], len_cap)))) : 0;
 #pragma unroll
-            for (int off = 32; off > 0; off >>= 1) n += __shfl_xor(n, off);
-            T += n;
+            for (int off = 32; off > 0; off >>= 1) u += __shfl_xor(u, off);
+            U += u;
         }
-        S = min(balanced_splits(T, seq_tiles(max(0, min(seq_lens[b], len_cap))), chunk >> 4), s_max);
+        S = min(balanced_splits(U + fd::kShareCost, seq_tiles(max(0, min(seq_lens[b], len_cap))), chunk >> 4),
+                s_max);
     }
     const int64_t base = ((int64_t)b * hq + h) * s_max;
     const int64_t orow = ((int64_t)b * hq + h) * D;

@@ -285,22 +285,29 @@ __device__ inline bool locate_unit(int u, const int32_t* __restrict__ seq_lens, 
 // Tiles of a sequence of L tokens: 16-token tiles (a paged cache's pages).
 __device__ __forceinline__ int seq_tiles(int L) { return (L + 15) >> 4; }
 
-// Split count of a sequence whose n tiles start at tile T of the balanced
-// list (below), with P tiles per work item: the items that hold any of its
-// tiles. 0 for an empty sequence.
+// Positions a sequence of n tiles takes in the balanced list: its tiles after
+// kShareCost positions that stand for the cost of starting a share; none when
+// empty.
+__device__ __forceinline__ int64_t seq_positions(int n) { return n > 0 ? n + fd::kShareCost : 0; }
+
+// Split count of a sequence whose n tiles start at position T of the
+// balanced list (below), with P positions per work item: the items that hold
+// any of its tiles. 0 for an empty sequence.
 __device__ __forceinline__ int balanced_splits(int64_t T, int n, int P) {
     return n > 0 ? (int)((T + n - 1) / P - T / P + 1) : 0;
 }
 
-// Balanced work list (plan split mode 1): the 16-token tiles of all
-// sequences, in sequence order, form one list, and work item w takes tiles
-// [w P, (w + 1) P) of it, across sequence boundaries, so every work-group of
-// a ragged batch streams the same bytes. The share of item w in sequence b
-// is split s = w - floor(T_b / P) of b, where T_b is the sequence's first
-// tile in the list. The cursor walks the sequences an item touches.
+// Balanced work list (plan split mode 1): the sequences, in order, take
+// consecutive positions of one list, kShareCost positions and then one per
+// 16-token tile each, and work item w takes positions [w P, (w + 1) P) of it,
+// across sequence boundaries, so every work-group of a ragged batch has the
+// same work. Item w holds a share of sequence b when it holds one of b's
+// tiles; that share is split s = w - floor(T_b / P) of b, where T_b is the
+// position of the sequence's first tile. The cursor walks the sequences an
+// item touches.
 struct BalancedCursor {
-    int64_t lo, hi;  // the item's tiles [lo, hi)
-    int64_t T;       // first tile of sequence b in the list
+    int64_t lo, hi;  // the item's positions [lo, hi)
+    int64_t U;       // first position of sequence b (its share cost, then its tiles)
     int64_t row0;    // first row of sequence b in a packed contiguous cache
     int b;
 };
@@ -310,17 +317,17 @@ struct BalancedCursor {
 // no more tiles.
 __device__ inline bool balanced_share(const int32_t* __restrict__ seq_lens, int B, int P, int len_cap, int g,
                                       BalancedCursor& c, WorkUnit& wu, int& S) {
-    while (c.b < B && c.T < c.hi) {
+    while (c.b < B && c.U + fd::kShareCost < c.hi) {
         const int L = max(0, min(seq_lens[c.b], len_cap));
         const int n = seq_tiles(L);
         if (n > 0) {
-            const int64_t f = c.T / P;
-            S = balanced_splits(c.T, n, P);
+            const int64_t T = c.U + fd::kShareCost;
+            S = balanced_splits(T, n, P);
             wu.b = c.b;
             wu.g = g;
-            wu.s = (int)(c.lo / P - f);
-            wu.t0 = (int)(max(c.lo, c.T) - c.T) * 16;
-            wu.t1 = min(L, (int)(min(c.hi, c.T + n) - c.T) * 16);
+            wu.s = (int)(c.lo / P - T / P);
+            wu.t0 = (int)(max(c.lo, T) - T) * 16;
+            wu.t1 = min(L, (int)(min(c.hi, T + n) - T) * 16);
             wu.L = L;
             wu.row0 = c.row0;
             return true;
@@ -333,35 +340,36 @@ __device__ inline bool balanced_share(const int32_t* __restrict__ seq_lens, int 
 // Moves the cursor to the sequence after the current one.
 __device__ inline void balanced_advance(const int32_t* __restrict__ seq_lens, int len_cap, BalancedCursor& c) {
     const int L = max(0, min(seq_lens[c.b], len_cap));
-    c.T += seq_tiles(L);
+    c.U += seq_positions(seq_tiles(L));
     c.row0 += L;
     ++c.b;
 }
 
-// Starts the cursor of work item w at the first sequence holding one of its
-// tiles (two wave-wide scans over seq_lens per 64 sequences). False for an
-// item past the end of the list.
+// Starts the cursor of work item w at the first sequence whose tiles reach
+// into the item (two wave-wide scans over seq_lens per 64 sequences). False
+// for an item past the end of the list.
 __device__ inline bool balanced_first(int64_t w, const int32_t* __restrict__ seq_lens, int B, int P, int len_cap,
                                       BalancedCursor& c) {
     const int lane = threadIdx.x & 63;
     c.lo = w * P;
     c.hi = c.lo + P;
-    int64_t accT = 0, accR = 0;
+    int64_t accU = 0, accR = 0;
     for (int base = 0; base < B; base += 64) {
         const int i = base + lane;
         const int L = i < B ? max(0, min(seq_lens[i], len_cap)) : 0;
-        const int n = seq_tiles(L);
-        const int64_t inclT = wave_incl_scan(n);
+        const int64_t u = seq_positions(seq_tiles(L));
+        const int64_t inclU = wave_incl_scan(u);
         const int64_t inclL = wave_incl_scan(L);
-        const int64_t totalT = __shfl(inclT, 63);
-        if (c.lo < accT + totalT) {
-            const int j = __builtin_ctzll(__ballot(accT + inclT > c.lo));
+        const int64_t totalU = __shfl(inclU, 63);
+        if (c.lo < accU + totalU) {
+            // the first sequence whose positions end past lo (its tiles end there)
+            const int j = __builtin_ctzll(__ballot(accU + inclU > c.lo));
             c.b = uniform(base + j);
-            c.T = uniform(accT + __shfl(inclT, j) - __shfl(n, j));
+            c.U = uniform(accU + __shfl(inclU, j) - __shfl(u, j));
             c.row0 = uniform(accR + __shfl(inclL, j) - __shfl(L, j));
             return true;
         }
-        accT += totalT;
+        accU += totalU;
         accR += __shfl(inclL, 63);
     }
     return false;

@@ -283,21 +283,22 @@ fd_status fd_plan_splits(const fd_problem* p, const int32_t* lens, int32_t num_c
 
     int64_t smax, nsplit = 0;
     if (split_mode == 1) {
-        int64_t tiles = 0, nmax = 0;
+        // List positions: per sequence kShareCost, then one per tile.
+        int64_t positions = 0, nmax = 0;
         for (int32_t b = 0; b < p->batch; ++b) {
             const int64_t n = ceil_div(lens[b], kTileTokens);
-            tiles += n;
+            positions += n + kShareCost;
             nmax = std::max(nmax, n);
         }
         const int32_t per_cu = env_int("FD_WG_PER_CU", 0) > 0 ? env_int("FD_WG_PER_CU", 0) : kBalancedWgPerCu;
         const int64_t target = std::max<int64_t>(1, (int64_t)num_cus * per_cu);
-        const int64_t P = std::max<int64_t>(ceil_div(tiles * workgroups_per_split(p, kernel), target),
+        const int64_t P = std::max<int64_t>(ceil_div(positions * workgroups_per_split(p, kernel), target),
                                             kBalancedMinTiles);
         if (P * kTileTokens > INT32_MAX)
             return fail(FD_ERR_UNSUPPORTED, "work items of %lld tiles exceed the chunk range", (long long)P);
         chunk = P * kTileTokens;
         smax = ceil_div(nmax, P) + 1;
-        nsplit = ceil_div(tiles, P);
+        nsplit = ceil_div(positions, P);
     } else {
         smax = ceil_div(lmax, chunk);
         for (int32_t b = 0; b < p->batch; ++b) nsplit += ceil_div(lens[b], chunk);

@@ -27,6 +27,14 @@ constexpr int32_t kTileTokens = 16;
 constexpr int32_t kBalancedMinTiles = 16;
 constexpr int32_t kBalancedWgPerCu = 3;
 constexpr int32_t kBalancedMaxBatch = 4096;
+// List positions a sequence takes before its tiles in the balanced list: the
+// cost of starting a share (the pipeline's first loads, the wave merge and the
+// partial's store), in tiles, so an item that holds many short sequences gets
+// fewer tiles.
+#ifndef FD_SHARE_COST
+#define FD_SHARE_COST 2
+#endif
+constexpr int32_t kShareCost = FD_SHARE_COST;
 // ... and the most query rows per KV head (q_len * Hq/Hkv) it is built for:
 // wider column tiles need more registers than the loop over shares leaves.
 constexpr int32_t kBalancedMaxRows = 8;

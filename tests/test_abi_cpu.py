@@ -14,7 +14,7 @@ import pytest
 
 import split_kv_flash_decoding_amd as fd
 from split_kv_flash_decoding_amd import _capi
-from tests.split_cuts import plan_cuts
+from tests.split_cuts import SHARE_COST, plan_cuts
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 INCLUDE = os.path.join(ROOT, "include")
@@ -117,23 +117,25 @@ def test_balanced_plan(hq, hkv, lens, page):
     assert C % 16 == 0 and C >= 256
     P = C // 16
     tiles = [ceil_div(L, 16) for L in lens]
-    assert plan.total_splits == ceil_div(sum(tiles), P)
+    positions = sum(tiles) + SHARE_COST * len(lens)
+    assert plan.total_splits == ceil_div(positions, P)
     assert plan.max_splits == ceil_div(max(tiles), P) + 1
     cuts = plan_cuts(lens, plan)
     for L, rs in zip(lens, cuts):
         assert rs[0][0] == 0 and rs[-1][1] == L and len(rs) <= plan.max_splits
         assert all(lo < hi for lo, hi in rs) and all(rs[i][1] == rs[i + 1][0] for i in range(len(rs) - 1))
         assert all(lo % 16 == 0 for lo, _ in rs)  # splits start on a page / tile
-    # tiles per work item: P for all but the last (the list is dealt out evenly)
+    # work per item, in list positions (a share's cost, then its tiles): P for
+    # every item but the last (the list is dealt out evenly)
     per_item = [0] * plan.total_splits
-    T = 0
+    U = 0
     for n in tiles:
-        for t in range(T, T + n):
+        for t in range(U, U + SHARE_COST + n):
             per_item[t // P] += 1
-        T += n
+        U += SHARE_COST + n
     assert all(c == P for c in per_item[:-1]) and 0 < per_item[-1] <= P
     # about three work-groups per compute unit (one round of the kernel's occupancy)
-    if sum(tiles) * hkv >= 256 * 3 * 16:
+    if positions * hkv >= 256 * 3 * 16:
         assert plan.total_splits * hkv <= 256 * 3 + hkv
     assert plan.workspace_bytes == workspace_bytes(len(lens), hq, hkv, plan.max_splits)
 
