@@ -153,6 +153,11 @@ def test_balanced_plan_choice(monkeypatch):
     assert fd.fd_plan_splits(wide, ragged, num_cus=256).split_mode == 0
     assert fd.fd_plan_splits(prob(batch=4, num_q_heads=32, num_kv_heads=8, q_len=2), ragged,
                              num_cus=256).split_mode == 1
+    # past the batch bound (the combine walks the lengths before its sequence) the chunks stay per sequence
+    assert fd.fd_plan_splits(prob(batch=4096, num_q_heads=32, num_kv_heads=8), [1, 2] * 2048,
+                             num_cus=256).split_mode == 1
+    assert fd.fd_plan_splits(prob(batch=4097, num_q_heads=32, num_kv_heads=8), [1, 2] * 2048 + [3],
+                             num_cus=256).split_mode == 0
     monkeypatch.setenv("FD_SPLIT_MODE", "0")
     assert fd.fd_plan_splits(gqa, ragged, num_cus=256).split_mode == 0
     monkeypatch.setenv("FD_SPLIT_MODE", "1")
