@@ -135,8 +135,7 @@ typedef struct fd_plan {
     int32_t num_cus;           /* compute units the plan was sized for */
     int32_t partial_kernel;    /* which partial kernel runs (0 = vector ALU token rows, 1 = MFMA,
                                   2 = vector ALU head rows) */
-    int32_t split_mode;        /* 0 = per-sequence chunks, 1 = balanced tile list (partial_kernel 1 with
-                                  q_len * Hq/Hkv <= 8 only) */
+    int32_t split_mode;        /* 0 = per-sequence chunks, 1 = balanced list (partial_kernel 1 only) */
     int64_t total_tokens;      /* sum_b L_b */
     uint64_t workspace_bytes;  /* bytes the workspace must hold */
 } fd_plan;
@@ -155,8 +154,8 @@ typedef struct fd_plan {
  * several heads, 2048 when the cache is FP8; that kernel gives way to one
  * head per work-group when its work-groups would be fewer than the compute
  * units).
- * A batch of unequal lengths on the matrix-core kernel (q_len * Hq/Hkv <= 8,
- * at most 4096 sequences, no forced split count) gets split_mode 1 instead:
+ * A batch of unequal lengths on the matrix-core kernel (at most 4096
+ * sequences, no forced split count) gets split_mode 1 instead:
  * P = max(16, ceil(sum_b (n_b + 2) * Hkv / (num_cus * 3))) positions per work item,
  * i.e. about three work-groups per compute unit, the kernel's occupancy, all
  * of them the same size.

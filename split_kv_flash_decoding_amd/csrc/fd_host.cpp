@@ -121,12 +121,10 @@ fd_status check_plan(const fd_problem* p, const fd_plan* plan) {
     if (plan->workspace_bytes < workspace_bytes(p, plan->max_splits))
         return fail(FD_ERR_INVALID_ARGUMENT, "plan does not belong to this problem (workspace_bytes)");
     if (plan->split_mode != 0 &&
-        (plan->split_mode != 1 || plan->partial_kernel != kPartialMfma || plan->chunk_tokens % kTileTokens ||
-         problem_q_len(p) * (p->num_q_heads / p->num_kv_heads) > kBalancedMaxRows))
+        (plan->split_mode != 1 || plan->partial_kernel != kPartialMfma || plan->chunk_tokens % kTileTokens))
         return fail(FD_ERR_INVALID_ARGUMENT, "plan split_mode %d with kernel %d and chunk %d: the balanced mode "
-                    "needs the matrix-core kernel, a chunk that is a multiple of %d and at most %d query rows "
-                    "per KV head", plan->split_mode, plan->partial_kernel, plan->chunk_tokens, kTileTokens,
-                    kBalancedMaxRows);
+                    "needs the matrix-core kernel and a chunk that is a multiple of %d",
+                    plan->split_mode, plan->partial_kernel, plan->chunk_tokens, kTileTokens);
     if ((plan->partial_kernel != kPartialMfma && problem_q_len(p) > 1) ||
         (plan->partial_kernel == kPartialMfma && !mfma_applicable(p)) ||
         (plan->partial_kernel == kPartialHeadRows && !head_rows_applicable(p)) ||
@@ -276,7 +274,7 @@ fd_status fd_plan_splits(const fd_problem* p, const int32_t* lens, int32_t num_c
     // FD_SPLIT_MODE=0/1 overrides; FD_WG_PER_CU sets the work-groups per CU.
     bool ragged = false;
     for (int32_t b = 1; b < p->batch; ++b) ragged |= lens[b] != lens[0];
-    const bool balanced_ok = kernel == kPartialMfma && problem_q_len(p) * G <= kBalancedMaxRows;
+    const bool balanced_ok = kernel == kPartialMfma;
     int32_t split_mode = (balanced_ok && force_num_splits == 0 && ragged && p->batch <= kBalancedMaxBatch) ? 1 : 0;
     const int32_t forced_mode = env_int("FD_SPLIT_MODE", -1);
     if (forced_mode == 0 || (forced_mode == 1 && balanced_ok)) split_mode = forced_mode;

@@ -35,9 +35,6 @@ constexpr int32_t kBalancedMaxBatch = 4096;
 #define FD_SHARE_COST 2
 #endif
 constexpr int32_t kShareCost = FD_SHARE_COST;
-// ... and the most query rows per KV head (q_len * Hq/Hkv) it is built for:
-// wider column tiles need more registers than the loop over shares leaves.
-constexpr int32_t kBalancedMaxRows = 8;
 
 // Records `msg` as this thread's last error and returns `st`.
 fd_status fail(fd_status st, const char* fmt, ...);

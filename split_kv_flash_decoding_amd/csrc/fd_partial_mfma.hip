@@ -188,10 +188,10 @@ __global__ __launch_bounds__(64 * kMW) void partial_mfma(const PartialArgs a) {
         ct = rem / 8;
         unit = blockIdx.x / (8 * NT) * 8 + rem % 8;
     }
-    // Split mode 0: the work-list entry is one split (locate_unit). Mode 1
-    // (NQ <= 8 only): it is work item unit / hkv of the balanced tile list,
-    // whose shares of consecutive sequences run one after the other (the
-    // body below, once per share).
+    // Split mode 0: the work-list entry is one split (locate_unit). Mode 1: it
+    // is work item unit / hkv of the balanced list, whose shares of
+    // consecutive sequences run one after the other (the body below, once
+    // per share).
     const int len_cap = PAGED ? max_pages * 16 : INT32_MAX;
     WorkUnit wu;
     int S_b = 0;
@@ -200,7 +200,6 @@ __global__ __launch_bounds__(64 * kMW) void partial_mfma(const PartialArgs a) {
         if (!locate_unit(unit, seq_lens, batch, hkv, chunk, len_cap, wu)) return;
         S_b = (wu.L + chunk - 1) / chunk;
     } else {
-        if (NQ > 8) return;  // not planned: the share loop would cost this width its third wave
         if (!balanced_first(unit / hkv, seq_lens, batch, chunk >> 4, len_cap, cur) ||
             !balanced_share(seq_lens, batch, chunk >> 4, len_cap, unit % hkv, cur, wu, S_b))
             return;
@@ -486,14 +485,14 @@ next_share:
             ws_ml[slot * 2 + 1] = lsum;
         }
     }
-    if (a.counters) fused_merge<kD, NQ, kMW>(a, b, S_b, g, 1, nq_all, NT, &sm_o[0][0][0]);
-    if constexpr (NQ <= 8) {
-        if (a.split_mode != 0) {
-            balanced_advance(seq_lens, len_cap, cur);
-            if (balanced_share(seq_lens, batch, chunk >> 4, len_cap, unit % hkv, cur, wu, S_b)) {
-                __syncthreads();  // the last share's merge area is the next share's staging area
-                goto next_share;
-            }
+    // The fused merge takes four rows at a time: with sixteen, its accumulators
+    // would cost the kernel its third wave per SIMD inside the loop over shares.
+    if (a.counters) fused_merge<kD, (NQ < 4 ? NQ : 4), kMW>(a, b, S_b, g, 1, nq_all, NT, &sm_o[0][0][0]);
+    if (a.split_mode != 0) {
+        balanced_advance(seq_lens, len_cap, cur);
+        if (balanced_share(seq_lens, batch, chunk >> 4, len_cap, unit % hkv, cur, wu, S_b)) {
+            __syncthreads();  // the last share's merge area is the next share's staging area
+            goto next_share;
         }
     }
 }

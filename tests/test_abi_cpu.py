@@ -149,10 +149,9 @@ def test_balanced_plan_choice(monkeypatch):
     assert fd.fd_plan_splits(gqa, [5000] * 4, num_cus=256).split_mode == 0          # equal lengths
     assert fd.fd_plan_splits(gqa, ragged, num_cus=256, force_num_splits=3).split_mode == 0
     assert fd.fd_plan_splits(prob(batch=4), ragged, num_cus=256).split_mode == 0    # MHA: vector kernels
-    wide = prob(batch=4, num_q_heads=32, num_kv_heads=8, q_len=4)                   # 16 query rows per KV head
-    assert fd.fd_plan_splits(wide, ragged, num_cus=256).split_mode == 0
-    assert fd.fd_plan_splits(prob(batch=4, num_q_heads=32, num_kv_heads=8, q_len=2), ragged,
-                             num_cus=256).split_mode == 1
+    for ql in (2, 4, 16):                                                           # 8, 16 and 64 query rows
+        plan = fd.fd_plan_splits(prob(batch=4, num_q_heads=32, num_kv_heads=8, q_len=ql), ragged, num_cus=256)
+        assert plan.split_mode == 1 and plan.partial_kernel == 1
     # past the batch bound (the combine walks the lengths before its sequence) the chunks stay per sequence
     assert fd.fd_plan_splits(prob(batch=4096, num_q_heads=32, num_kv_heads=8), [1, 2] * 2048,
                              num_cus=256).split_mode == 1
@@ -166,8 +165,8 @@ def test_balanced_plan_choice(monkeypatch):
 
 
 def test_balanced_plan_is_checked():
-    """A balanced plan is refused for the vector kernels, for chunks that are not
-    a multiple of 16 and for more than 8 query rows per KV head."""
+    """A balanced plan is refused for the vector kernels and for chunks that are
+    not a multiple of 16."""
     lib = fd.load_library()
     fake = ctypes.c_void_p(0x10000)
     gqa = prob(batch=2, num_q_heads=32, num_kv_heads=8)
@@ -182,11 +181,12 @@ def test_balanced_plan_is_checked():
         assert st == fd.FD_ERR_INVALID_ARGUMENT, field
         st = lib.fd_combine(ctypes.byref(gqa), ctypes.byref(bad), fake, fake, need, fake, None, None)
         assert st == fd.FD_ERR_INVALID_ARGUMENT, field
-    wide = prob(batch=2, num_q_heads=32, num_kv_heads=8, q_len=4)
-    bad = fd.fd_plan_splits(wide, [1000, 3000], num_cus=256)
+    mha = prob(batch=2)
+    bad = fd.fd_plan_splits(mha, [1000, 3000], num_cus=256)
+    assert bad.partial_kernel != 1
     bad.split_mode = 1
     bad.chunk_tokens = 1024
-    st = lib.fd_decode_partial(ctypes.byref(wide), ctypes.byref(bad), fake, fake, fake, None, fake, fake,
+    st = lib.fd_decode_partial(ctypes.byref(mha), ctypes.byref(bad), fake, fake, fake, None, fake, fake,
                                bad.workspace_bytes, None)
     assert st == fd.FD_ERR_INVALID_ARGUMENT
 

@@ -45,6 +45,15 @@ CASES = [
     ("G2 q_len 4 paged", lambda: to_paged(make_workload(
         name="bal-mq", batch=6, num_q_heads=16, num_kv_heads=8, head_dim=128, seq_lens=[4, 900, 31, 5000, 17, 64],
         dtype=torch.bfloat16, seed=1602, q_len=4), 16), None),
+    ("G4 q_len 4 contiguous (16 rows)", lambda: make_workload(
+        name="bal-mq16", batch=7, num_q_heads=32, num_kv_heads=8, head_dim=128,
+        seq_lens=[4, 3000, 17, 700, 64, 9000, 5], dtype=torch.bfloat16, seed=1604, q_len=4), None),
+    ("G8 q_len 8 paged (64 rows, 4 column tiles)", lambda: to_paged(make_workload(
+        name="bal-mq64", batch=5, num_q_heads=64, num_kv_heads=8, head_dim=128, seq_lens=[8, 2500, 33, 700, 4100],
+        dtype=torch.bfloat16, seed=1605, q_len=8), 16), None),
+    ("G4 q_len 4 fp8 paged", lambda: quantize_kv_fp8(to_paged(make_workload(
+        name="bal-mq-fp8", batch=6, num_q_heads=16, num_kv_heads=4, head_dim=128, seq_lens=[4, 1500, 20, 3000, 64, 9],
+        dtype=torch.float16, seed=1606, q_len=4), 16)), None),
     ("G8 fp8 paged", lambda: quantize_kv_fp8(to_paged(make_workload(
         name="bal-fp8", batch=40, num_q_heads=64, num_kv_heads=8, head_dim=128, seq_lens=_tiny_and_long(40, 4),
         dtype=torch.bfloat16, seed=1603), 16)), 64),
