@@ -1,14 +1,17 @@
 // Combine kernel: merges the per-split statistics of every (sequence, query
-// head) into the output and its log-sum-exp. One work-group of four waves per
-// (b, h): M = max_s m_s over all splits, then each wave accumulates
-// w_s = exp(m_s - M) times l_s and O_s over every fourth split (eight splits'
-// loads in flight; the kernel is latency-bound) and the waves add up in LDS;
+// head) into the output and its log-sum-exp. M = max_s m_s over all splits,
+// then w_s = exp(m_s - M) weighs l_s and O_s;
 // out = sum_s w_s O_s / sum_s w_s l_s, lse = M + ln(sum_s w_s l_s). This is
 // the cross-chunk reduce of FlashDecoding ("FlashAttention 全景演进与大模型
 // Token 生成全链路性能优化实战", §2.3), with every split rescaled by the
-// two-block identity of the same page's §1.2. Under the balanced split mode
-// a sequence's split count comes from the position of its first tile in the
-// list of all sequences, a prefix sum each wave computes over seq_lens.
+// two-block identity of the same page's §1.2. Two forms: four waves per row
+// (each sums every fourth split, eight splits' loads in flight, the waves add
+// up in LDS) for batches with few rows and many splits; one wave per row,
+// four rows per work-group, for batches with many rows, where four waves per
+// row would take several rounds of the chip's wave slots for rows that have
+// few splits. Under the balanced split mode a sequence's split count comes
+// from the position of its first tile in the list of all sequences, a prefix
+// sum each wave computes over seq_lens.
 
 #include "fd_device.h"
 
@@ -17,6 +20,70 @@ namespace fdk {
 
 constexpr int kCombineWaves = 4;
 
+// Splits of sequence b under the plan's split mode (a whole wave calls this).
+__device__ inline int combine_split_count(const int32_t* __restrict__ seq_lens, int b, int chunk, int s_max,
+                                          int split_mode, int len_cap) {
+    if (split_mode == 0) {
+        const int L = seq_lens[b];
+        return L > 0 ? min((L + chunk - 1) / chunk, s_max) : 0;
+    }
+    const int lane = threadIdx.x & 63;
+    int64_t U = 0;  // list positions of sequences 0..b-1
+    for (int base = 0; base < b; base += 64) {
+        const int i = base + lane;
+        int64_t u = i < b ? seq_positions(seq_tiles(max(0, min(seq_lens[i], len_cap)))) : 0;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) u += __shfl_xor(u, off);
+        U += u;
+    }
+    return min(balanced_splits(U + fd::kShareCost, seq_tiles(max(0, min(seq_lens[b], len_cap))), chunk >> 4),
+               s_max);
+}
+
+// One wave per (sequence, query row) r = b * hq + h, four rows per work-group.
+template <int D, int OUT>
+__global__ __launch_bounds__(64 * kCombineWaves) void combine_rows(const float* __restrict__ ws_o,
+                                                                   const float* __restrict__ ws_ml,
+                                                                   const int32_t* __restrict__ seq_lens,
+                                                                   void* __restrict__ out, float* __restrict__ lse,
+                                                                   int rows, int hq, int chunk, int s_max,
+                                                                   int split_mode, int len_cap) {
+    constexpr int PER = D / 64;  // output columns per lane
+    const int lane = threadIdx.x & 63;
+    const int r = blockIdx.x * kCombineWaves + (threadIdx.x >> 6);
+    if (r >= rows) return;  // a whole wave: no barrier follows
+    const int b = r / hq;
+    const int S = combine_split_count(seq_lens, b, chunk, s_max, split_mode, len_cap);
+    const int64_t base = (int64_t)r * s_max;
+    const int64_t orow = (int64_t)r * D;
+    if (S == 0) {
+#pragma unroll
+        for (int e = 0; e < PER; ++e) store_out<OUT>(out, orow + lane * PER + e, 0.f);
+        if (lse && lane == 0) lse[r] = neg_inf();
+        return;
+    }
+    float M = neg_inf();
+    for (int i = lane; i < S; i += 64) M = fmaxf(M, ws_ml[(base + i) * 2]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    float acc[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+    float l = 0.f;
+#pragma unroll 8
+    for (int i = 0; i < S; ++i) {
+        const float w = __builtin_amdgcn_exp2f((ws_ml[(base + i) * 2] - M) * kLog2e);
+        l = fmaf(w, ws_ml[(base + i) * 2 + 1], l);
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, ws_o[(base + i) * D + lane * PER + e], acc[e]);
+    }
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) store_out<OUT>(out, orow + lane * PER + e, acc[e] * inv);
+    if (lse && lane == 0) lse[r] = M + __builtin_amdgcn_logf(l) * kLn2;
+}
+
+// Four waves per (sequence, query row): grid (hq, B).
 template <int D, int OUT>
 __global__ __launch_bounds__(64 * kCombineWaves) void combine(const float* __restrict__ ws_o,
                                                               const float* __restrict__ ws_ml,
@@ -29,22 +96,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine(const float* __res
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    int S;
-    if (split_mode == 0) {
-        const int L = seq_lens[b];
-        S = L > 0 ? min((L + chunk - 1) / chunk, s_max) : 0;
-    } else {
-        int64_t U = 0;  // list positions of sequences 0..b-1
-        for (int base = 0; base < b; base += 64) {
-            const int i = base + lane;
-            int64_t u = i < b ? seq_positions(seq_tiles(max(0, min(seq_lens[i], len_cap)))) : 0;
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1) u += __shfl_xor(u, off);
-            U += u;
-        }
-        S = min(balanced_splits(U + fd::kShareCost, seq_tiles(max(0, min(seq_lens[b], len_cap))), chunk >> 4),
-                s_max);
-    }
+    const int S = combine_split_count(seq_lens, b, chunk, s_max, split_mode, len_cap);
     const int64_t base = ((int64_t)b * hq + h) * s_max;
     const int64_t orow = ((int64_t)b * hq + h) * D;
     if (S == 0) {
@@ -104,20 +156,37 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine(const float* __res
     }
 }
 
+template <int D, int OUT>
+void launch_combine_out(bool per_wave, const float* ws_o, const float* ws_ml, const int32_t* lens, void* out,
+                        float* lse, int B, int hq, int chunk, int s_max, int split_mode, int len_cap,
+                        hipStream_t st) {
+    if (per_wave) {
+        const int rows = B * hq;
+        hipLaunchKernelGGL((combine_rows<D, OUT>), dim3((rows + kCombineWaves - 1) / kCombineWaves),
+                           dim3(64 * kCombineWaves), 0, st, ws_o, ws_ml, lens, out, lse, rows, hq, chunk, s_max,
+                           split_mode, len_cap);
+    } else {
+        hipLaunchKernelGGL((combine<D, OUT>), dim3(hq, B), dim3(64 * kCombineWaves), 0, st, ws_o, ws_ml, lens, out,
+                           lse, hq, chunk, s_max, split_mode, len_cap);
+    }
+}
+
 template <int D>
-hipError_t launch_combine_d(int out_dt, const float* ws_o, const float* ws_ml, const int32_t* lens, void* out,
-                          float* lse, int B, int hq, int chunk, int s_max, int split_mode, int len_cap,
-                          hipStream_t st) {
-    dim3 grid(hq, B);
+hipError_t launch_combine_d(bool per_wave, int out_dt, const float* ws_o, const float* ws_ml, const int32_t* lens,
+                            void* out, float* lse, int B, int hq, int chunk, int s_max, int split_mode, int len_cap,
+                            hipStream_t st) {
     switch (out_dt) {
         case FD_F32:
-            hipLaunchKernelGGL((combine<D, FD_F32>), grid, dim3(64 * kCombineWaves), 0, st, ws_o, ws_ml, lens, out, lse, hq, chunk, s_max, split_mode, len_cap);
+            launch_combine_out<D, FD_F32>(per_wave, ws_o, ws_ml, lens, out, lse, B, hq, chunk, s_max, split_mode,
+                                          len_cap, st);
             break;
         case FD_F16:
-            hipLaunchKernelGGL((combine<D, FD_F16>), grid, dim3(64 * kCombineWaves), 0, st, ws_o, ws_ml, lens, out, lse, hq, chunk, s_max, split_mode, len_cap);
+            launch_combine_out<D, FD_F16>(per_wave, ws_o, ws_ml, lens, out, lse, B, hq, chunk, s_max, split_mode,
+                                          len_cap, st);
             break;
         default:
-            hipLaunchKernelGGL((combine<D, FD_BF16>), grid, dim3(64 * kCombineWaves), 0, st, ws_o, ws_ml, lens, out, lse, hq, chunk, s_max, split_mode, len_cap);
+            launch_combine_out<D, FD_BF16>(per_wave, ws_o, ws_ml, lens, out, lse, B, hq, chunk, s_max, split_mode,
+                                           len_cap, st);
             break;
     }
     return hipGetLastError();
@@ -125,9 +194,11 @@ hipError_t launch_combine_d(int out_dt, const float* ws_o, const float* ws_ml, c
 
 hipError_t launch_combine(int D, int out_dt, const float* ws_o, const float* ws_ml, const int32_t* lens,
                           void* out, float* lse, int B, int hq, int chunk, int s_max, int split_mode,
-                          int len_cap, hipStream_t st) {
-    return D == 64 ? launch_combine_d<64>(out_dt, ws_o, ws_ml, lens, out, lse, B, hq, chunk, s_max, split_mode, len_cap, st)
-                   : launch_combine_d<128>(out_dt, ws_o, ws_ml, lens, out, lse, B, hq, chunk, s_max, split_mode, len_cap, st);
+                          int len_cap, bool per_wave, hipStream_t st) {
+    return D == 64 ? launch_combine_d<64>(per_wave, out_dt, ws_o, ws_ml, lens, out, lse, B, hq, chunk, s_max,
+                                          split_mode, len_cap, st)
+                   : launch_combine_d<128>(per_wave, out_dt, ws_o, ws_ml, lens, out, lse, B, hq, chunk, s_max,
+                                           split_mode, len_cap, st);
 }
 
 }  // namespace fdk

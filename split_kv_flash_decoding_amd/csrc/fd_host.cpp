@@ -113,6 +113,12 @@ int32_t workgroups_per_split(const fd_problem* p, int32_t kernel) {
     return kernel == kPartialMfma ? groups * mfma_column_tiles(p) : groups;
 }
 
+bool combine_per_wave(const fd_problem* p) {
+    const int32_t forced = env_int("FD_COMBINE_WAVES", 0);
+    if (forced == 1 || forced == 4) return forced == 1;
+    return (int64_t)p->batch * problem_q_len(p) * p->num_q_heads >= kCombinePerWaveRows;
+}
+
 fd_status check_plan(const fd_problem* p, const fd_plan* plan) {
     if (!plan) return fail(FD_ERR_INVALID_ARGUMENT, "plan is NULL");
     if (plan->chunk_tokens < 1 || plan->max_splits < 1 || plan->max_splits > kMaxGridYZ)

@@ -375,3 +375,43 @@ def test_multi_query_split_statistics_include_empty_splits(fd, hq, hkv, ql):
         assert np.allclose(m_s[b, :, :S][fin], mo[b, :, :S][fin], rtol=0, atol=1e-5)
         assert np.allclose(l_s[b, :, :S], lo[b, :, :S], rtol=1e-5, atol=0)
         assert np.allclose(O_s[b, :, :S], Oo[b, :, :S], rtol=1e-5, atol=1e-5)
+
+
+# ------------------------------------------------------- the two combine forms
+
+
+@pytest.mark.parametrize("case", [
+    # (d, dtype, Hq, Hkv, lens, page, q_len, out dtype)
+    (128, torch.bfloat16, 64, 8, [7, 3000, 600, 17, 12000, 1] * 4, 16, 1, torch.float32),   # balanced list
+    (64, torch.float16, 8, 2, [1, 300, 4097, 2, 900], 0, 1, torch.bfloat16),                # d = 64, bf16 out
+    (128, torch.float16, 16, 16, [70000, 5], 0, 1, torch.float16),                          # many splits per row
+    (128, torch.bfloat16, 32, 8, [40, 2500, 9, 800], 16, 4, torch.float32),                 # 4 query tokens
+])
+def test_combine_forms_agree(fd, monkeypatch, case):
+    """One wave per (sequence, query row) and four waves per row merge the
+    same partials to the oracle's result; FD_COMBINE_WAVES forces either."""
+    d, dt, hq, hkv, lens, page, ql, od = case
+    wl = make_workload(name="combine-forms", batch=len(lens), num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                       seq_lens=lens, dtype=dt, seed=1700 + d + hq + ql, q_len=ql)
+    if page:
+        wl = to_paged(wl, 16)
+    dev = to_dev(wl)
+    outs = {}
+    for waves in (1, 4):
+        monkeypatch.setenv("FD_COMBINE_WAVES", str(waves))
+        res = run(fd, wl, num_splits=0, out_dtype=od, dev_tensors=dev)
+        outs[waves] = res
+    if ql > 1:
+        ref_out, ref_lse = oracle.decode_attention_multi(wl.q, wl.k, wl.v, wl.seq_lens, wl.scale, wl.block_table,
+                                                         wl.page_size)
+    else:
+        ref_out, ref_lse = reference(wl)
+    rnd = {torch.float32: 0.0, torch.float16: 2.0 ** -11, torch.bfloat16: 2.0 ** -8}[od]
+    for waves, res in outs.items():
+        o = res.out.double().cpu().numpy()
+        assert np.isfinite(o).all()
+        assert np.max(np.abs(o - ref_out)) <= O_MAX_ABS + rnd * np.abs(ref_out).max(), waves
+        assert np.max(np.abs(res.lse.double().cpu().numpy() - ref_lse)) <= LSE_ABS, waves
+    # the same partials: the two forms differ by fp32 summation order (and one output rounding)
+    diff = (outs[1].out.double() - outs[4].out.double()).abs().max().item()
+    assert diff <= 1e-5 + 2 * rnd * float(outs[4].out.double().abs().max()), diff
