@@ -148,8 +148,9 @@ typedef struct fd_plan {
  * example chunk). The planner tries chunks that make about num_cus * k
  * work-groups (sequence, KV head, split) for k = 1, 2, 3, 4, 6, 8, ... and
  * keeps the largest one whose full-size splits alone give every compute unit
- * two work-groups (three when shorter last splits exist) while at most an
- * eighth of the tokens fall in shorter last splits. Chunks are multiples of
+ * two work-groups (three when shorter last splits exist; twice that for the
+ * token-rows kernel on an FP8 cache) while at most an eighth of the tokens
+ * fall in shorter last splits. Chunks are multiples of
  * 64 and at least 256 tokens (1024 for the kernel whose work-groups cover
  * several heads, 2048 when the cache is FP8; that kernel gives way to one
  * head per work-group when its work-groups would be fewer than the compute

@@ -10,9 +10,12 @@
 // they run on MFMA instead of the vector ALU, which would spend ~G times the
 // instructions of the MHA kernel per byte read.
 //
-// One work-group of four wave64s per (sequence, KV head, split); each wave
-// takes 16-token tiles of the split in turn (a tile is one page of a paged
-// cache). Per tile, with lane l in group g = l/16 at column c = l%16:
+// One work-group of four wave64s per (sequence, KV head, split), or, under
+// the balanced split list, per (work item, KV head): the item's shares of
+// consecutive sequences then run through this same body one after the
+// other. Each wave takes 16-token tiles of its split in turn (a tile is one
+// page of a paged cache). Per tile, with lane l in group g = l/16 at column
+// c = l%16:
 //   * K and V tiles are read from HBM the same way: each 16-byte load
 //     instruction covers four whole 256-byte token rows (loading K straight
 //     into the MFMA operand layout instead, 16 rows x 64 bytes per

@@ -365,7 +365,7 @@ def test_multi_query_problems():
         assert ei.value.status == status, kw
 
 
-def test_fp8_problems():
+def test_fp8_problems(monkeypatch):
     """An FP8 (E4M3) cache: 16 codes per 16-byte load, so a head-rows load
     covers 8 heads at d = 128 and 16 at d = 64; q is fp16 or bf16; the
     unscaled calls refuse it (its scales are part of the data)."""
@@ -385,6 +385,11 @@ def test_fp8_problems():
                              num_cus=256).partial_kernel == 2
     # FP8 head-rows splits hold at least 2048 tokens (the bytes of 1024 16-bit tokens)
     assert plan.chunk_tokens == 2048 and fd.fd_plan_splits(prob(), [131072], num_cus=256).chunk_tokens == 2048
+    # FP8 token rows: twice the work-groups a 16-bit cache would get (32K-token MHA: 32 heads x 32 splits)
+    p2 = fd.fd_plan_splits(prob(kv_dtype=f8), [32768], num_cus=256)
+    assert (p2.partial_kernel, p2.chunk_tokens) == (0, 1024)
+    monkeypatch.setenv("FD_PARTIAL_KERNEL", "0")
+    assert fd.fd_plan_splits(prob(), [32768], num_cus=256).chunk_tokens == 2048
     # the workspace does not depend on the cache type
     assert plan.workspace_bytes == fd.fd_plan_splits(prob(), [131072], num_cus=256,
                                                      force_num_splits=plan.max_splits).workspace_bytes
