@@ -53,17 +53,20 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_rows(const float* 
     const int r = blockIdx.x * kCombineWaves + (threadIdx.x >> 6);
     if (r >= rows) return;  // a whole wave: no barrier follows
     const int b = r / hq;
-    const int S = combine_split_count(seq_lens, b, chunk, s_max, split_mode, len_cap);
     const int64_t base = (int64_t)r * s_max;
     const int64_t orow = (int64_t)r * D;
+    // The first 64 slots' m_s are read while the split count is worked out
+    // (slots past it exist and are masked).
+    const float m_first = lane < s_max ? ws_ml[(base + lane) * 2] : neg_inf();
+    const int S = combine_split_count(seq_lens, b, chunk, s_max, split_mode, len_cap);
     if (S == 0) {
 #pragma unroll
         for (int e = 0; e < PER; ++e) store_out<OUT>(out, orow + lane * PER + e, 0.f);
         if (lse && lane == 0) lse[r] = neg_inf();
         return;
     }
-    float M = neg_inf();
-    for (int i = lane; i < S; i += 64) M = fmaxf(M, ws_ml[(base + i) * 2]);
+    float M = lane < S ? m_first : neg_inf();
+    for (int i = lane + 64; i < S; i += 64) M = fmaxf(M, ws_ml[(base + i) * 2]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
     float acc[PER];
@@ -96,9 +99,13 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine(const float* __res
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int S = combine_split_count(seq_lens, b, chunk, s_max, split_mode, len_cap);
     const int64_t base = ((int64_t)b * hq + h) * s_max;
     const int64_t orow = ((int64_t)b * hq + h) * D;
+    // Every wave takes M = max_s m_s over all splits by itself (no barrier);
+    // the first 64 slots' m_s are read while the split count is worked out
+    // (slots past it exist and are masked).
+    const float m_first = lane < s_max ? ws_ml[(base + lane) * 2] : neg_inf();
+    const int S = combine_split_count(seq_lens, b, chunk, s_max, split_mode, len_cap);
     if (S == 0) {
         if (wave == 0) {
 #pragma unroll
@@ -107,20 +114,13 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine(const float* __res
         }
         return;
     }
-    __shared__ float red_m[kCombineWaves];
     __shared__ float red_l[kCombineWaves];
     __shared__ float red_o[kCombineWaves][D];
 
-    // M = max_s m_s over the whole block.
-    float M = neg_inf();
-    for (int i = tid; i < S; i += 64 * kCombineWaves) M = fmaxf(M, ws_ml[(base + i) * 2]);
+    float M = lane < S ? m_first : neg_inf();
+    for (int i = lane + 64; i < S; i += 64) M = fmaxf(M, ws_ml[(base + i) * 2]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    if (lane == 0) red_m[wave] = M;
-    __syncthreads();
-    M = red_m[0];
-#pragma unroll
-    for (int w = 1; w < kCombineWaves; ++w) M = fmaxf(M, red_m[w]);
 
     // Wave w takes splits w, w + 4, ...; loads of eight splits in flight.
     float acc[PER];
