@@ -157,9 +157,9 @@ typedef struct fd_plan {
  * units).
  * A batch of unequal lengths on the matrix-core kernel (at most 4096
  * sequences, no forced split count) gets split_mode 1 instead:
- * P = max(16, ceil(sum_b (n_b + 2) * Hkv / (num_cus * 3))) positions per work item,
- * i.e. about three work-groups per compute unit, the kernel's occupancy, all
- * of them the same size.
+ * P = max(16, ceil(sum_b (n_b + 2) * Hkv / (num_cus * k))) positions per work item,
+ * i.e. about k work-groups per compute unit, all of them the same size: k = 2
+ * for a 16-bit cache, 3 (the kernel's occupancy) for FP8.
  * `force_num_splits` > 0 instead sets C = ceil(max_b L_b / force) and accepts
  * any C >= 1 (split_mode 0). `num_cus` == 0 asks the current HIP device (the only HIP call
  * here; its count is cached per device). Validates the problem and every

@@ -21,11 +21,14 @@ constexpr int32_t kHeadRowsMinChunk = 1024;
 constexpr int32_t kPageSize = 16;
 // Balanced split mode (fd_plan.split_mode 1): tokens per tile of the list,
 // the smallest work item in tiles (256 tokens), the work-groups per compute
-// unit it aims at, and the largest batch it is chosen for (the combine walks
-// the lengths before its sequence).
+// unit it aims at (16-bit caches: two, fewer and longer items; FP8 caches:
+// three, the kernel's occupancy, since an FP8 item does twice the work per
+// byte), and the largest batch it is chosen for (the combine walks the
+// lengths before its sequence).
 constexpr int32_t kTileTokens = 16;
 constexpr int32_t kBalancedMinTiles = 16;
-constexpr int32_t kBalancedWgPerCu = 3;
+constexpr int32_t kBalancedWgPerCu16 = 2;
+constexpr int32_t kBalancedWgPerCuFp8 = 3;
 constexpr int32_t kBalancedMaxBatch = 4096;
 // List positions a sequence takes before its tiles in the balanced list: the
 // cost of starting a share (the pipeline's first loads, the wave merge and the

@@ -134,10 +134,20 @@ def test_balanced_plan(hq, hkv, lens, page):
             per_item[t // P] += 1
         U += SHARE_COST + n
     assert all(c == P for c in per_item[:-1]) and 0 < per_item[-1] <= P
-    # about three work-groups per compute unit (one round of the kernel's occupancy)
-    if positions * hkv >= 256 * 3 * 16:
-        assert plan.total_splits * hkv <= 256 * 3 + hkv
+    # about two work-groups per compute unit for a 16-bit cache (one round)
+    if positions * hkv >= 256 * 2 * 16:
+        assert 256 * 2 - hkv <= plan.total_splits * hkv <= 256 * 2 + hkv
     assert plan.workspace_bytes == workspace_bytes(len(lens), hq, hkv, plan.max_splits)
+
+
+def test_balanced_plan_fp8_aims_at_three_per_cu():
+    """An FP8 cache's items are sized for three work-groups per compute unit."""
+    import torch
+    lens = [2915, 4487, 5931, 8309, 8336, 8684, 8905, 10375] * 2
+    p = prob(batch=len(lens), num_q_heads=32, num_kv_heads=8, kv_dtype=torch.float8_e4m3fn, q_dtype=torch.bfloat16)
+    plan = fd.fd_plan_splits(p, lens, num_cus=256)
+    assert plan.split_mode == 1
+    assert 256 * 3 - 8 <= plan.total_splits * 8 <= 256 * 3 + 8
 
 
 def test_balanced_plan_choice(monkeypatch):
