@@ -34,8 +34,8 @@ def _tiny_and_long(B, seed):
 
 CASES = [
     # (name, workload maker, oracle pairs sampled per call or None for all)
-    ("config 4", lambda: make_config(4), None),
-    ("config 5", lambda: make_config(5), 96),
+    ("GQA varlen: 16 sequences of 1024-16384 tokens, 32/8 heads", lambda: make_config(4), None),
+    ("paged GQA: 64 sequences of 512-32768 tokens, 64/8 heads", lambda: make_config(5), 96),
     ("G8 paged, 200 mixed sequences", lambda: to_paged(make_workload(
         name="bal200", batch=200, num_q_heads=64, num_kv_heads=8, head_dim=128, seq_lens=_tiny_and_long(200, 3),
         dtype=torch.bfloat16, seed=1600), 16), 128),
