@@ -174,3 +174,49 @@ def test_balanced_plan_for_upper_bound_lengths(fd, page):
         ref_out, ref_lse = oracle.decode_attention(ref_wl.q, ref_wl.k, ref_wl.v, lens, wl.scale,
                                                    ref_wl.block_table if page else None, page)
         parity(out, lse, ref_out, ref_lse, what=f"upper-bound plan, lengths {lens}")
+
+
+def _random_case(seed):
+    """A seeded ragged batch: group size, query tokens, cache type and layout,
+    and a length mix of single tokens, page edges and long sequences."""
+    r = np.random.default_rng(seed)
+    G = int(r.choice([4, 8]))
+    hkv = int(r.choice([1, 2, 4, 8]))
+    ql = int(r.choice([1, 1, 2, 4, 8]))
+    if ql * G > 64:
+        ql = 64 // G
+    B = int(r.integers(2, 160))
+    pool = [1, 2, 15, 16, 17, 33, 100, 257, 1000, 3000, 9000]
+    lens = [max(ql, int(x)) for x in r.choice(pool, size=B)]
+    if len(set(lens)) == 1:  # equal lengths keep per-sequence chunks
+        lens[-1] += 1
+    dt = torch.float16 if r.random() < 0.5 else torch.bfloat16
+    wl = make_workload(name=f"bal-rand{seed}", batch=B, num_q_heads=G * hkv, num_kv_heads=hkv, head_dim=128,
+                       seq_lens=lens, dtype=dt, seed=seed, q_len=ql)
+    if r.random() < 0.5:
+        wl = to_paged(wl, 16, spare_pages=2)
+    if ql == 1 and r.random() < 0.3:
+        wl = quantize_kv_fp8(wl)
+    return wl
+
+
+@pytest.mark.parametrize("seed", range(1650, 1662))
+def test_balanced_random_ragged_batches(fd, seed):
+    """Seeded random ragged batches on the balanced list against the oracle,
+    every query row of a sampled set of (sequence, head) pairs."""
+    wl = _random_case(seed)
+    res = _run(fd, wl)
+    assert res.plan.split_mode == 1, res.plan.as_dict()
+    r = np.random.default_rng(seed + 1)
+    bs = sorted({int(x) for x in r.integers(0, wl.batch, size=24)} | {0, wl.batch - 1, int(np.argmax(wl.lens))})
+    tol = O_MAX_ABS * (8 if wl.kv_dtype == torch.float8_e4m3fn else 1)
+    if wl.q_len > 1:
+        rows = [(b, i, h) for b in bs for i in range(wl.q_len) for h in range(wl.num_q_heads)]
+        ref_out, ref_lse = oracle.decode_attention_multi(wl.q, wl.k, wl.v, wl.seq_lens, wl.scale, wl.block_table,
+                                                         wl.page_size, rows=rows)
+    else:
+        pairs = [(b, h) for b in bs for h in range(wl.num_q_heads)]
+        ref_out, ref_lse = _reference(wl, pairs)
+    parity(res.out, res.lse, ref_out, ref_lse, o_tol=tol,
+           what=f"random ragged seed={seed} B={wl.batch} G={wl.num_q_heads // wl.num_kv_heads} "
+                f"q_len={wl.q_len} {wl.kv_dtype} page={wl.page_size} plan={res.plan.as_dict()}")
