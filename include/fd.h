@@ -117,10 +117,10 @@ typedef struct fd_problem {
  * split_mode 0 (per sequence): split s of sequence b holds tokens
  * [s*C, min((s+1)*C, L_b)), so S_b = ceil(L_b / C).
  * split_mode 1 (balanced, ragged batches on the matrix-core kernel): the
- * sequences, in order, take consecutive positions of one list: 2 positions
+ * sequences, in order, take consecutive positions of one list: 4 positions
  * for the cost of starting a share (pipeline start, wave merge, store), then
  * one per 16-token tile, n_b = ceil(L_b / 16) of them. So sequence b's first
- * tile sits at T_b = 2*(b+1) + n_0 + ... + n_{b-1}. Work item w takes
+ * tile sits at T_b = 4*(b+1) + n_0 + ... + n_{b-1}. Work item w takes
  * positions [w*P, (w+1)*P) of the list, P = C / 16, across sequence
  * boundaries, so every work-group has the same work whatever the length mix.
  * Split s of sequence b is its share of item floor(T_b / P) + s: tokens
@@ -131,7 +131,7 @@ typedef struct fd_plan {
     int32_t max_splits;        /* S_max: workspace stride, >= every S_b (mode 0: max_b ceil(L_b / C);
                                   mode 1: ceil(max_b n_b / P) + 1) */
     int32_t total_splits;      /* work-list entries per KV-head group: sum_b ceil(L_b / C) (mode 0),
-                                  or ceil(sum_b (n_b + 2) / P) work items (mode 1) */
+                                  or ceil(sum_b (n_b + 4) / P) work items (mode 1) */
     int32_t num_cus;           /* compute units the plan was sized for */
     int32_t partial_kernel;    /* which partial kernel runs (0 = vector ALU token rows, 1 = MFMA,
                                   2 = vector ALU head rows) */
@@ -157,7 +157,7 @@ typedef struct fd_plan {
  * units).
  * A batch of unequal lengths on the matrix-core kernel (at most 4096
  * sequences, no forced split count) gets split_mode 1 instead:
- * P = max(16, ceil(sum_b (n_b + 2) * Hkv / (num_cus * k))) positions per work item,
+ * P = max(16, ceil(sum_b (n_b + 4) * Hkv / (num_cus * k))) positions per work item,
  * i.e. about k work-groups per compute unit, all of them the same size: k = 2
  * for a 16-bit cache, 3 (the kernel's occupancy) for FP8.
  * `force_num_splits` > 0 instead sets C = ceil(max_b L_b / force) and accepts

@@ -35,7 +35,7 @@ constexpr int32_t kBalancedMaxBatch = 4096;
 // partial's store), in tiles, so an item that holds many short sequences gets
 // fewer tiles.
 #ifndef FD_SHARE_COST
-#define FD_SHARE_COST 2
+#define FD_SHARE_COST 4
 #endif
 constexpr int32_t kShareCost = FD_SHARE_COST;
 

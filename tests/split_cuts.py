@@ -9,7 +9,7 @@ def ceil_div(a: int, b: int) -> int:
 
 # List positions a sequence takes before its tiles in the balanced list (the
 # library's share cost, FD_SHARE_COST when it is built).
-SHARE_COST = 2
+SHARE_COST = 4
 
 
 def plan_cuts(lens, plan, share_cost: int = SHARE_COST):
