@@ -220,3 +220,39 @@ def test_balanced_random_ragged_batches(fd, seed):
     parity(res.out, res.lse, ref_out, ref_lse, o_tol=tol,
            what=f"random ragged seed={seed} B={wl.batch} G={wl.num_q_heads // wl.num_kv_heads} "
                 f"q_len={wl.q_len} {wl.kv_dtype} page={wl.page_size} plan={res.plan.as_dict()}")
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float16, torch.bfloat16])
+def test_balanced_low_precision_outputs_and_fused(fd, out_dtype):
+    """16-bit outputs on the balanced list, through the combine and through the
+    fused merge (three calls in a row on one workspace), against the oracle
+    with the output's own rounding added to the bar."""
+    wl = to_paged(make_workload(name="bal-out", batch=12, num_q_heads=32, num_kv_heads=4, head_dim=128,
+                                seq_lens=[1, 700, 33, 5000, 16, 2600, 3, 129, 9000, 64, 1500, 17],
+                                dtype=torch.bfloat16, seed=1670), 16)
+    res = run(fd, wl, num_splits=0, out_dtype=out_dtype)
+    assert res.plan.split_mode == 1
+    ref_out, ref_lse = oracle.decode_attention(wl.q, wl.k, wl.v, wl.seq_lens, wl.scale, wl.block_table, 16)
+    rnd = 2.0 ** -11 if out_dtype == torch.float16 else 2.0 ** -8
+    bar = O_MAX_ABS + rnd * float(np.abs(ref_out).max())
+    o = res.out.double().cpu().numpy()
+    assert np.max(np.abs(o - ref_out)) <= bar
+    assert np.max(np.abs(res.lse.double().cpu().numpy() - ref_lse)) <= 1e-4
+    dev = torch.device("cuda", 0)
+    q, k, v, bt = wl.q.to(dev), wl.k.to(dev), wl.v.to(dev), wl.block_table.to(dev)
+    lens = wl.seq_lens.to(dev)
+    prob = fd.make_problem(batch=wl.batch, num_q_heads=32, num_kv_heads=4, head_dim=128, kv_dtype=torch.bfloat16,
+                           out_dtype=out_dtype, scale=wl.scale, page_size=16, max_pages_per_seq=wl.max_pages_per_seq)
+    plan = fd.fd_plan_splits(prob, wl.lens)
+    assert plan.split_mode == 1
+    ws = torch.empty(-(-plan.workspace_bytes // 4), dtype=torch.float32, device=dev)
+    fd.fd_workspace_init(prob, plan, ws)
+    for _ in range(3):
+        out = torch.full(tuple(wl.q.shape), float("nan"), dtype=out_dtype, device=dev)
+        lse = torch.full(tuple(wl.q.shape[:-1]), float("nan"), dtype=torch.float32, device=dev)
+        fd.fd_decode_fused(prob, plan, q, k, v, bt, lens, ws, out, lse)
+        torch.cuda.synchronize()
+        of = out.double().cpu().numpy()
+        assert np.isfinite(of).all()
+        assert np.max(np.abs(of - ref_out)) <= bar
+        assert np.max(np.abs(lse.double().cpu().numpy() - ref_lse)) <= 1e-4
