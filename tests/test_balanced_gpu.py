@@ -256,3 +256,28 @@ def test_balanced_low_precision_outputs_and_fused(fd, out_dtype):
         assert np.isfinite(of).all()
         assert np.max(np.abs(of - ref_out)) <= bar
         assert np.max(np.abs(lse.double().cpu().numpy() - ref_lse)) <= 1e-4
+
+
+def test_balanced_upper_bound_plan_multi_query(fd):
+    """Four query tokens per sequence on a balanced plan made for longer
+    lengths: each step's shorter device lengths move the cuts and every
+    query's causal limit with them."""
+    final = [900, 40, 3000, 17, 5000, 260]
+    wl = to_paged(make_workload(name="bal-ub-mq", batch=len(final), num_q_heads=32, num_kv_heads=8, head_dim=128,
+                                seq_lens=final, dtype=torch.bfloat16, seed=1680, q_len=4), 16, spare_pages=2)
+    dev = torch.device("cuda", 0)
+    q, k, v, bt = wl.q.to(dev), wl.k.to(dev), wl.v.to(dev), wl.block_table.to(dev)
+    prob = fd.make_problem(batch=wl.batch, num_q_heads=32, num_kv_heads=8, head_dim=128, kv_dtype=torch.bfloat16,
+                           scale=wl.scale, page_size=16, max_pages_per_seq=wl.max_pages_per_seq, q_len=4)
+    plan = fd.fd_plan_splits(prob, final)
+    assert plan.split_mode == 1 and plan.partial_kernel == 1
+    ws = torch.empty(-(-plan.workspace_bytes // 4), dtype=torch.float32, device=dev)
+    out = torch.empty(tuple(wl.q.shape), dtype=torch.float32, device=dev)
+    lse = torch.empty(tuple(wl.q.shape[:-1]), dtype=torch.float32, device=dev)
+    for lens in (final, [4, 40, 2999, 5, 4000, 260], [900, 4, 7, 17, 33, 100]):
+        lens_dev = torch.tensor(lens, dtype=torch.int32, device=dev)
+        fd.fd_decode_partial(prob, plan, q, k, v, bt, lens_dev, ws)
+        fd.fd_combine(prob, plan, lens_dev, ws, out, lse)
+        torch.cuda.synchronize()
+        ref_out, ref_lse = oracle.decode_attention_multi(wl.q, wl.k, wl.v, lens, wl.scale, wl.block_table, 16)
+        parity(out, lse, ref_out, ref_lse, what=f"multi-query upper-bound plan, lengths {lens}")
