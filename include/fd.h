@@ -259,8 +259,10 @@ fd_status fd_workspace_init(const fd_problem* problem, const fd_plan* plan, void
  * cross-chunk reduce of capstone §2.3, by the two-block identity of §1.2
  * applied to every split). out: device [B, q_len, Hq, d] in out_dtype.
  * lse: device float32 [B, q_len, Hq], or NULL. Batches of 512 query rows or
- * more (B * q_len * Hq) merge one row per wave, smaller ones with four waves
- * per row; FD_COMBINE_WAVES (1 or 4) forces either, for experiments.
+ * more (B * q_len * Hq) merge one row per wave, from 4096 rows two rows per
+ * wave (when a sequence has an even number of rows), smaller batches with
+ * four waves per row; FD_COMBINE_FORM (0 four waves per row, 1 one wave per
+ * row, 2 two rows per wave) forces one, for experiments.
  */
 fd_status fd_combine(const fd_problem* problem, const fd_plan* plan,
                      const int32_t* seq_lens_dev, const void* workspace,

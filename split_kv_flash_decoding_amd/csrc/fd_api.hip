@@ -196,7 +196,7 @@ fd_status fd_combine(const fd_problem* p, const fd_plan* plan, const int32_t* se
     hipError_t e = fdk::launch_combine(p->head_dim, p->out_dtype, ws_o, ws_ml, seq_lens_dev, out, lse, p->batch,
                                        problem_q_len(p) * p->num_q_heads, plan->chunk_tokens, plan->max_splits,
                                        plan->split_mode, p->page_size ? p->max_pages_per_seq * kPageSize : INT32_MAX,
-                                       combine_per_wave(p), hs);
+                                       combine_form(p), hs);
     if (e != hipSuccess) return fail(FD_ERR_HIP, "combine kernel launch: %s", hipGetErrorString(e));
     return FD_OK;
 }

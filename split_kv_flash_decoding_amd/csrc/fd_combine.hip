@@ -9,7 +9,7 @@
 // up in LDS) for batches with few rows and many splits; one wave per row,
 // four rows per work-group, for batches with many rows, where four waves per
 // row would take several rounds of the chip's wave slots for rows that have
-// few splits. Under the balanced split mode a sequence's split count comes
+// few splits; two rows per wave for the largest batches. Under the balanced split mode a sequence's split count comes
 // from the position of its first tile in the list of all sequences, a prefix
 // sum each wave computes over seq_lens.
 
@@ -86,6 +86,55 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_rows(const float* 
     if (lse && lane == 0) lse[r] = M + __builtin_amdgcn_logf(l) * kLn2;
 }
 
+// Two rows per wave (lanes 0-31 row r0, lanes 32-63 row r0 + 1, each lane D/32
+// columns), four waves per work-group: for the largest batches, half the waves
+// of one row per wave. The rows of a sequence must be even in number, so both
+// rows of a wave belong to the same sequence.
+template <int D, int OUT>
+__global__ __launch_bounds__(64 * kCombineWaves) void combine_rows2(const float* __restrict__ ws_o,
+                                                                    const float* __restrict__ ws_ml,
+                                                                    const int32_t* __restrict__ seq_lens,
+                                                                    void* __restrict__ out, float* __restrict__ lse,
+                                                                    int rows, int hq, int chunk, int s_max,
+                                                                    int split_mode, int len_cap) {
+    constexpr int PER = D / 32;  // output columns per lane
+    const int lane = threadIdx.x & 63;
+    const int hl = lane & 31;
+    const int r0 = 2 * (blockIdx.x * kCombineWaves + (threadIdx.x >> 6));
+    if (r0 >= rows) return;  // a whole wave (rows is even): no barrier follows
+    const int r = r0 + (lane >> 5);
+    const int b = r0 / hq;
+    const int64_t base = (int64_t)r * s_max;
+    const int64_t orow = (int64_t)r * D;
+    const float m_first = hl < s_max ? ws_ml[(base + hl) * 2] : neg_inf();
+    const int S = combine_split_count(seq_lens, b, chunk, s_max, split_mode, len_cap);
+    if (S == 0) {
+#pragma unroll
+        for (int e = 0; e < PER; ++e) store_out<OUT>(out, orow + hl * PER + e, 0.f);
+        if (lse && hl == 0) lse[r] = neg_inf();
+        return;
+    }
+    float M = hl < S ? m_first : neg_inf();
+    for (int i = hl + 32; i < S; i += 32) M = fmaxf(M, ws_ml[(base + i) * 2]);
+#pragma unroll
+    for (int off = 16; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    float acc[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+    float l = 0.f;
+#pragma unroll 8
+    for (int i = 0; i < S; ++i) {
+        const float w = __builtin_amdgcn_exp2f((ws_ml[(base + i) * 2] - M) * kLog2e);
+        l = fmaf(w, ws_ml[(base + i) * 2 + 1], l);
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, ws_o[(base + i) * D + hl * PER + e], acc[e]);
+    }
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) store_out<OUT>(out, orow + hl * PER + e, acc[e] * inv);
+    if (lse && hl == 0) lse[r] = M + __builtin_amdgcn_logf(l) * kLn2;
+}
+
 // Four waves per (sequence, query row): grid (hq, B).
 template <int D, int OUT>
 __global__ __launch_bounds__(64 * kCombineWaves) void combine(const float* __restrict__ ws_o,
@@ -157,10 +206,16 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine(const float* __res
 }
 
 template <int D, int OUT>
-void launch_combine_out(bool per_wave, const float* ws_o, const float* ws_ml, const int32_t* lens, void* out,
+void launch_combine_out(int form, const float* ws_o, const float* ws_ml, const int32_t* lens, void* out,
                         float* lse, int B, int hq, int chunk, int s_max, int split_mode, int len_cap,
                         hipStream_t st) {
-    if (per_wave) {
+    if (form == 2) {
+        const int rows = B * hq;
+        const int waves = rows / 2;
+        hipLaunchKernelGGL((combine_rows2<D, OUT>), dim3((waves + kCombineWaves - 1) / kCombineWaves),
+                           dim3(64 * kCombineWaves), 0, st, ws_o, ws_ml, lens, out, lse, rows, hq, chunk, s_max,
+                           split_mode, len_cap);
+    } else if (form == 1) {
         const int rows = B * hq;
         hipLaunchKernelGGL((combine_rows<D, OUT>), dim3((rows + kCombineWaves - 1) / kCombineWaves),
                            dim3(64 * kCombineWaves), 0, st, ws_o, ws_ml, lens, out, lse, rows, hq, chunk, s_max,
@@ -172,20 +227,20 @@ void launch_combine_out(bool per_wave, const float* ws_o, const float* ws_ml, co
 }
 
 template <int D>
-hipError_t launch_combine_d(bool per_wave, int out_dt, const float* ws_o, const float* ws_ml, const int32_t* lens,
+hipError_t launch_combine_d(int form, int out_dt, const float* ws_o, const float* ws_ml, const int32_t* lens,
                             void* out, float* lse, int B, int hq, int chunk, int s_max, int split_mode, int len_cap,
                             hipStream_t st) {
     switch (out_dt) {
         case FD_F32:
-            launch_combine_out<D, FD_F32>(per_wave, ws_o, ws_ml, lens, out, lse, B, hq, chunk, s_max, split_mode,
+            launch_combine_out<D, FD_F32>(form, ws_o, ws_ml, lens, out, lse, B, hq, chunk, s_max, split_mode,
                                           len_cap, st);
             break;
         case FD_F16:
-            launch_combine_out<D, FD_F16>(per_wave, ws_o, ws_ml, lens, out, lse, B, hq, chunk, s_max, split_mode,
+            launch_combine_out<D, FD_F16>(form, ws_o, ws_ml, lens, out, lse, B, hq, chunk, s_max, split_mode,
                                           len_cap, st);
             break;
         default:
-            launch_combine_out<D, FD_BF16>(per_wave, ws_o, ws_ml, lens, out, lse, B, hq, chunk, s_max, split_mode,
+            launch_combine_out<D, FD_BF16>(form, ws_o, ws_ml, lens, out, lse, B, hq, chunk, s_max, split_mode,
                                            len_cap, st);
             break;
     }
@@ -194,10 +249,10 @@ hipError_t launch_combine_d(bool per_wave, int out_dt, const float* ws_o, const 
 
 hipError_t launch_combine(int D, int out_dt, const float* ws_o, const float* ws_ml, const int32_t* lens,
                           void* out, float* lse, int B, int hq, int chunk, int s_max, int split_mode,
-                          int len_cap, bool per_wave, hipStream_t st) {
-    return D == 64 ? launch_combine_d<64>(per_wave, out_dt, ws_o, ws_ml, lens, out, lse, B, hq, chunk, s_max,
+                          int len_cap, int form, hipStream_t st) {
+    return D == 64 ? launch_combine_d<64>(form, out_dt, ws_o, ws_ml, lens, out, lse, B, hq, chunk, s_max,
                                           split_mode, len_cap, st)
-                   : launch_combine_d<128>(per_wave, out_dt, ws_o, ws_ml, lens, out, lse, B, hq, chunk, s_max,
+                   : launch_combine_d<128>(form, out_dt, ws_o, ws_ml, lens, out, lse, B, hq, chunk, s_max,
                                            split_mode, len_cap, st);
 }
 

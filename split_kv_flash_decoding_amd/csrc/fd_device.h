@@ -463,10 +463,11 @@ hipError_t launch_partial_valu_heads(int D, int G, bool paged, const PartialArgs
 hipError_t launch_partial_mfma(int G, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st);
 hipError_t launch_append(const AppendArgs& a, int q_dt, int kv_dt, int blocks, hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, int dt, int out_dt, bool paged, hipStream_t st);
-// per_wave: one wave per (sequence, query row) instead of four (batches with many rows).
+// form: 0 four waves per (sequence, query row), 1 one wave per row, 2 two rows
+// per wave (rows per sequence even).
 hipError_t launch_combine(int D, int out_dt, const float* ws_o, const float* ws_ml, const int32_t* lens,
                           void* out, float* lse, int B, int hq, int chunk, int s_max, int split_mode,
-                          int len_cap, bool per_wave, hipStream_t st);
+                          int len_cap, int form, hipStream_t st);
 
 // ------------------------------------------------------------ fused merge
 

@@ -113,10 +113,13 @@ int32_t workgroups_per_split(const fd_problem* p, int32_t kernel) {
     return kernel == kPartialMfma ? groups * mfma_column_tiles(p) : groups;
 }
 
-bool combine_per_wave(const fd_problem* p) {
-    const int32_t forced = env_int("FD_COMBINE_WAVES", 0);
-    if (forced == 1 || forced == 4) return forced == 1;
-    return (int64_t)p->batch * problem_q_len(p) * p->num_q_heads >= kCombinePerWaveRows;
+int32_t combine_form(const fd_problem* p) {
+    const int64_t per_seq = (int64_t)problem_q_len(p) * p->num_q_heads;
+    const int64_t rows = (int64_t)p->batch * per_seq;
+    const int32_t forced = env_int("FD_COMBINE_FORM", -1);
+    if (forced == 0 || forced == 1 || (forced == 2 && per_seq % 2 == 0)) return forced;
+    if (rows >= kCombineTwoRowRows && per_seq % 2 == 0) return 2;
+    return rows >= kCombinePerWaveRows ? 1 : 0;
 }
 
 fd_status check_plan(const fd_problem* p, const fd_plan* plan) {

@@ -55,12 +55,15 @@ uint64_t workspace_o_bytes(const fd_problem* p, int32_t max_splits);
 uint64_t workspace_counters_offset(const fd_problem* p, int32_t max_splits);
 uint64_t workspace_bytes(const fd_problem* p, int32_t max_splits);
 
-// Whether the combine runs one wave per (sequence, query row) instead of four:
-// for batches of at least kCombinePerWaveRows rows (B * q_len * Hq), where
-// four waves per row would take several rounds of the chip's wave slots.
-// FD_COMBINE_WAVES=1/4 overrides.
+// The combine's form: 0 four waves per (sequence, query row); 1 one wave per
+// row, for batches of at least kCombinePerWaveRows rows (B * q_len * Hq),
+// where four waves per row would take several rounds of the chip's wave
+// slots; 2 two rows per wave, from kCombineTwoRowRows rows when a sequence has
+// an even number of rows. FD_COMBINE_FORM=0/1/2 overrides (2 only with even
+// rows per sequence).
 constexpr int64_t kCombinePerWaveRows = 512;
-bool combine_per_wave(const fd_problem* p);
+constexpr int64_t kCombineTwoRowRows = 4096;
+int32_t combine_form(const fd_problem* p);
 
 // Compute units of the current HIP device, cached per device (fd_api.hip).
 fd_status query_num_cus(int32_t* out);

@@ -388,8 +388,9 @@ def test_multi_query_split_statistics_include_empty_splits(fd, hq, hkv, ql):
     (128, torch.bfloat16, 32, 8, [40, 2500, 9, 800], 16, 4, torch.float32),                 # 4 query tokens
 ])
 def test_combine_forms_agree(fd, monkeypatch, case):
-    """One wave per (sequence, query row) and four waves per row merge the
-    same partials to the oracle's result; FD_COMBINE_WAVES forces either."""
+    """Four waves per (sequence, query row), one wave per row and two rows per
+    wave merge the same partials to the oracle's result; FD_COMBINE_FORM
+    forces each."""
     d, dt, hq, hkv, lens, page, ql, od = case
     wl = make_workload(name="combine-forms", batch=len(lens), num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
                        seq_lens=lens, dtype=dt, seed=1700 + d + hq + ql, q_len=ql)
@@ -397,21 +398,22 @@ def test_combine_forms_agree(fd, monkeypatch, case):
         wl = to_paged(wl, 16)
     dev = to_dev(wl)
     outs = {}
-    for waves in (1, 4):
-        monkeypatch.setenv("FD_COMBINE_WAVES", str(waves))
+    for form in (0, 1, 2):
+        monkeypatch.setenv("FD_COMBINE_FORM", str(form))
         res = run(fd, wl, num_splits=0, out_dtype=od, dev_tensors=dev)
-        outs[waves] = res
+        outs[form] = res
     if ql > 1:
         ref_out, ref_lse = oracle.decode_attention_multi(wl.q, wl.k, wl.v, wl.seq_lens, wl.scale, wl.block_table,
                                                          wl.page_size)
     else:
         ref_out, ref_lse = reference(wl)
     rnd = {torch.float32: 0.0, torch.float16: 2.0 ** -11, torch.bfloat16: 2.0 ** -8}[od]
-    for waves, res in outs.items():
+    for form, res in outs.items():
         o = res.out.double().cpu().numpy()
         assert np.isfinite(o).all()
-        assert np.max(np.abs(o - ref_out)) <= O_MAX_ABS + rnd * np.abs(ref_out).max(), waves
-        assert np.max(np.abs(res.lse.double().cpu().numpy() - ref_lse)) <= LSE_ABS, waves
-    # the same partials: the two forms differ by fp32 summation order (and one output rounding)
-    diff = (outs[1].out.double() - outs[4].out.double()).abs().max().item()
-    assert diff <= 1e-5 + 2 * rnd * float(outs[4].out.double().abs().max()), diff
+        assert np.max(np.abs(o - ref_out)) <= O_MAX_ABS + rnd * np.abs(ref_out).max(), form
+        assert np.max(np.abs(res.lse.double().cpu().numpy() - ref_lse)) <= LSE_ABS, form
+    # the same partials: the forms differ by fp32 summation order (and one output rounding)
+    for form in (1, 2):
+        diff = (outs[form].out.double() - outs[0].out.double()).abs().max().item()
+        assert diff <= 1e-5 + 2 * rnd * float(outs[0].out.double().abs().max()), (form, diff)
