@@ -386,6 +386,8 @@ def test_multi_query_split_statistics_include_empty_splits(fd, hq, hkv, ql):
     (64, torch.float16, 8, 2, [1, 300, 4097, 2, 900], 0, 1, torch.bfloat16),                # d = 64, bf16 out
     (128, torch.float16, 16, 16, [70000, 5], 0, 1, torch.float16),                          # many splits per row
     (128, torch.bfloat16, 32, 8, [40, 2500, 9, 800], 16, 4, torch.float32),                 # 4 query tokens
+    (128, torch.float16, 3, 3, [5000, 17, 900], 0, 1, torch.float32),                       # odd rows: no pairs
+    (128, torch.float16, 3, 3, [1 + (i * 37) % 700 for i in range(1500)], 0, 1, torch.float32),  # 4500 odd rows
 ])
 def test_combine_forms_agree(fd, monkeypatch, case):
     """Four waves per (sequence, query row), one wave per row and two rows per
