@@ -3,25 +3,33 @@
 // planner uses. Argument checks run on the host before anything is enqueued.
 
 #include <algorithm>
+#include <atomic>
 
 #include "fd_device.h"
 
 namespace fd {
 
 fd_status query_num_cus(int32_t* out) {
-    static int32_t cache[64] = {0};
+    // One slot per device, read and written atomically: host threads that
+    // plan at the same time may both query the device on first use, and both
+    // store the same count.
+    static std::atomic<int32_t> cache[64];
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail(FD_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
-    if (dev >= 0 && dev < 64 && cache[dev] > 0) {
-        *out = cache[dev];
-        return FD_OK;
+    const bool cached = dev >= 0 && dev < 64;
+    if (cached) {
+        const int32_t c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) {
+            *out = c;
+            return FD_OK;
+        }
     }
     int n = 0;
     e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess || n <= 0)
         return fail(FD_ERR_HIP, "compute-unit query failed: %s", hipGetErrorString(e));
-    if (dev >= 0 && dev < 64) cache[dev] = n;
+    if (cached) cache[dev].store(n, std::memory_order_relaxed);
     *out = n;
     return FD_OK;
 }

@@ -4,14 +4,15 @@
 // out = sum_s w_s O_s / sum_s w_s l_s, lse = M + ln(sum_s w_s l_s). This is
 // the cross-chunk reduce of FlashDecoding ("FlashAttention 全景演进与大模型
 // Token 生成全链路性能优化实战", §2.3), with every split rescaled by the
-// two-block identity of the same page's §1.2. Two forms: four waves per row
-// (each sums every fourth split, eight splits' loads in flight, the waves add
-// up in LDS) for batches with few rows and many splits; one wave per row,
+// two-block identity of the same page's §1.2. Three forms: four waves per
+// row (each sums every fourth split, eight splits' loads in flight, the waves
+// add up in LDS) for batches with few rows and many splits; one wave per row,
 // four rows per work-group, for batches with many rows, where four waves per
 // row would take several rounds of the chip's wave slots for rows that have
-// few splits; two rows per wave for the largest batches. Under the balanced split mode a sequence's split count comes
-// from the position of its first tile in the list of all sequences, a prefix
-// sum each wave computes over seq_lens.
+// few splits; two rows per wave (32 lanes each) for the largest batches with
+// an even number of rows per sequence. Under the balanced split mode a
+// sequence's split count comes from the position of its first tile in the
+// list of all sequences, a prefix sum each wave computes over seq_lens.
 
 #include "fd_device.h"
 

@@ -377,7 +377,7 @@ def test_multi_query_split_statistics_include_empty_splits(fd, hq, hkv, ql):
         assert np.allclose(O_s[b, :, :S], Oo[b, :, :S], rtol=1e-5, atol=1e-5)
 
 
-# ------------------------------------------------------- the two combine forms
+# ------------------------------------------------------- the three combine forms
 
 
 @pytest.mark.parametrize("case", [
@@ -388,6 +388,7 @@ def test_multi_query_split_statistics_include_empty_splits(fd, hq, hkv, ql):
     (128, torch.bfloat16, 32, 8, [40, 2500, 9, 800], 16, 4, torch.float32),                 # 4 query tokens
     (128, torch.float16, 3, 3, [5000, 17, 900], 0, 1, torch.float32),                       # odd rows: no pairs
     (128, torch.float16, 3, 3, [1 + (i * 37) % 700 for i in range(1500)], 0, 1, torch.float32),  # 4500 odd rows
+    (128, torch.bfloat16, 2, 2, [900, 17, 3000, 1, 64], 0, 1, torch.float32),      # 10 rows: a part-filled last group
 ])
 def test_combine_forms_agree(fd, monkeypatch, case):
     """Four waves per (sequence, query row), one wave per row and two rows per
