@@ -158,6 +158,82 @@ def cpu_baseline(wl, budget_s: float, out, lse):
     }
 
 
+def time_gbps(fn, nbytes: int, reps: int = 10) -> float:
+    """GB/s of `fn` (which reads nbytes) over reps calls, timed by events."""
+    import torch
+
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return reps * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
+def probe_patterns(fd, k, v, sink, row_bytes: int, chunks=None) -> dict:
+    """Read bandwidth of K and V (equal byte sizes) by access pattern: the
+    plain streaming read (K, then V), and the row pattern of the decode
+    kernels (include/fd_probe.h) over rows of row_bytes: 1 KB column blocks
+    with the waves splitting the rows (head rows), at chunks that give about
+    1, 2 and 4 work-groups per compute unit, and 8 KB blocks with the waves
+    across them (head columns) where the rows hold 8 KB."""
+    nbytes = 2 * k.numel() * k.element_size()
+    out = {"stream": time_gbps(lambda: (fd.fd_probe_read(k, sink), fd.fd_probe_read(v, sink)), nbytes)}
+    if row_bytes % 1024:
+        return out
+    rows = k.numel() * k.element_size() // row_bytes
+    for per_cu in (1, 2, 4):
+        chunk = max(16, -(-rows * (row_bytes // 1024) // (256 * per_cu)))
+        out[f"rows_1k_{per_cu}wg_per_cu"] = time_gbps(
+            lambda: fd.fd_probe_read_rows(k, v, row_bytes, chunk, False, sink), nbytes)
+    if row_bytes % 8192 == 0:
+        for per_cu in (1, 2):
+            chunk = max(16, -(-rows * (row_bytes // 8192) // (256 * per_cu)))
+            out[f"cols_8k_{per_cu}wg_per_cu"] = time_gbps(
+                lambda: fd.fd_probe_read_rows(k, v, row_bytes, chunk, True, sink), nbytes)
+    return out
+
+
+PROBE_METRIC = "HBM read GB/s of the decode access patterns, 2 GiB K/V pair shaped as the 128K-token cache"
+
+
+def run_probe(args, fd, dev) -> int:
+    """One step = one read of a 1 GiB K and a 1 GiB V buffer shaped as the
+    128K-token, 32-head, d = 128 fp16 cache ([131072, 8192 B]) in each
+    pattern of probe_patterns; value = the best pattern's GB/s."""
+    import torch
+
+    rows, row_bytes = 131072, 8192
+    k = torch.empty(rows * row_bytes // 2, dtype=torch.float16, device=dev).fill_(1.0)
+    v = torch.empty_like(k).fill_(2.0)
+    sink = torch.empty(fd.PROBE_SINK_FLOATS, dtype=torch.float32, device=dev)
+    runs = [probe_patterns(fd, k, v, sink, row_bytes) for _ in range(max(1, args.steps // 10))]
+    pats = {n: max(r[n] for r in runs) for n in runs[0]}
+    for n, g in pats.items():
+        log(f"{n}: {g:.0f} GB/s (best of {len(runs)} runs of 10 reads)")
+    best, gbps = max(pats.items(), key=lambda kv: kv[1])
+    rec = {
+        "metric": PROBE_METRIC, "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": len(runs) * 10,
+        "warmup": 3, "ms_per_step": round(2 * rows * row_bytes / (gbps * 1e9) * 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic (constant-filled buffers)",
+        "config": {"workload": "hbm_read_patterns_2x1GiB_rows8192", "rows": rows, "row_bytes": row_bytes,
+                   "best_pattern": best, "patterns_gbps": {n: round(g, 1) for n, g in pats.items()}},
+        "roofline": {"bound": "hbm", "kernel": f"probe ({best})", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    line = json.dumps(rec)
+    print(line, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(line + "\n")
+    return 0
+
+
 PREFILL_METRIC = "TFLOP/s, causal prefill attention (FA-2 forward), 8K tokens, GQA 32/8, d=128"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 MFMA peak
 
@@ -408,9 +484,9 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", choices=("decode", "prefill", "append"), default="decode",
-                    help="decode (default; --config picks the workload), the 8192-token causal prefill, or the "
-                         "8192-token KV append with RoPE")
+    ap.add_argument("--workload", choices=("decode", "prefill", "append", "probe"), default="decode",
+                    help="decode (default; --config picks the workload), the 8192-token causal prefill, the "
+                         "8192-token KV append with RoPE, or the HBM read probes' access patterns")
     ap.add_argument("--config", type=int, default=3, help="decode workload 1..5 (default: 128K MHA)")
     ap.add_argument("--q-len", type=int, default=1, help="query tokens per sequence (speculative verification)")
     ap.add_argument("--kv-fp8", action="store_true", help="FP8 (E4M3) cache with per-KV-head scales")
@@ -439,6 +515,8 @@ def main() -> int:
         return run_prefill(args, fd, dev)
     if args.workload == "append":
         return run_append(args, fd, dev)
+    if args.workload == "probe":
+        return run_probe(args, fd, dev)
 
     t = time.perf_counter()
     wl = make_config(args.config, q_len=args.q_len, kv_fp8=args.kv_fp8)
@@ -537,26 +615,19 @@ def main() -> int:
     cold_mean = statistics.fmean(cold_ms)
     log(f"cold-cache partial kernel mean {cold_mean * 1e3:.1f} us over {len(cold_ms)} steps")
 
-    # achievable streaming-read bandwidth on the same buffers, for context
+    # What the memory delivers on the same buffers: the best of a plain
+    # streaming read and the decode kernels' row pattern (K and V read
+    # together, 1 KB of a token row per wave instruction), for context.
     sink = torch.empty(fd.PROBE_SINK_FLOATS, dtype=torch.float32, device=dev)
-    for _ in range(3):
-        fd.fd_probe_read(k, sink)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = 10
-    e0.record()
-    for _ in range(reps):
-        fd.fd_probe_read(k, sink)
-        fd.fd_probe_read(v, sink)
-    e1.record()
-    torch.cuda.synchronize()
-    probe_gbps = 2 * reps * k.numel() * k.element_size() / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    log(f"streaming-read probe over K and V: {probe_gbps:.0f} GB/s")
+    probes = probe_patterns(fd, k, v, sink, wl.num_kv_heads * wl.head_dim * k.element_size())
+    probe_name, probe_gbps = max(probes.items(), key=lambda kv: kv[1])
+    log("read probes over K and V: " + ", ".join(f"{n} {g:.0f} GB/s" for n, g in probes.items()))
     # A plain copy of known size: its HBM counter readings calibrate the
     # FETCH_SIZE / WRITE_SIZE counters taken on the decode kernels.
     copy_bytes = 256 << 20
     src = torch.empty(copy_bytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
     dst = torch.empty_like(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
     fd.fd_probe_copy(dst, src)
@@ -611,6 +682,7 @@ def main() -> int:
             "cold_partial_us_mean": round(cold_mean * 1e3, 2),
             "cold_achieved": round(nbytes / (cold_mean * 1e-3) / 1e9, 1),
             "hbm_read_probe_gbps": round(probe_gbps, 1),
+            "hbm_read_probe_pattern": probe_name,
             "frac_of_probe": round(achieved / probe_gbps, 4),
         },
     }

@@ -134,8 +134,9 @@ typedef struct fd_plan {
                                   or ceil(sum_b (n_b + 4) / P) work items (mode 1) */
     int32_t num_cus;           /* compute units the plan was sized for */
     int32_t partial_kernel;    /* which partial kernel runs (0 = vector ALU token rows, 1 = MFMA,
-                                  2 = vector ALU head rows) */
-    int32_t split_mode;        /* 0 = per-sequence chunks, 1 = balanced list (partial_kernel 1 only) */
+                                  2 = vector ALU head rows, 3 = vector ALU head columns,
+                                  4 = MFMA with each wave owning a head) */
+    int32_t split_mode;        /* 0 = per-sequence chunks, 1 = balanced list (partial_kernel 1 or 4) */
     int64_t total_tokens;      /* sum_b L_b */
     uint64_t workspace_bytes;  /* bytes the workspace must hold */
 } fd_plan;
@@ -261,8 +262,9 @@ fd_status fd_workspace_init(const fd_problem* problem, const fd_plan* plan, void
  * lse: device float32 [B, q_len, Hq], or NULL. Batches of 512 query rows or
  * more (B * q_len * Hq) merge one row per wave, from 4096 rows two rows per
  * wave (when a sequence has an even number of rows), smaller batches with
- * four waves per row; FD_COMBINE_FORM (0 four waves per row, 1 one wave per
- * row, 2 two rows per wave) forces one, for experiments.
+ * four waves per row, or sixteen when the plan has 128 splits or more;
+ * FD_COMBINE_FORM (0 four waves per row, 1 one wave per row, 2 two rows per
+ * wave, 3 sixteen waves per row) forces one, for experiments.
  */
 fd_status fd_combine(const fd_problem* problem, const fd_plan* plan,
                      const int32_t* seq_lens_dev, const void* workspace,

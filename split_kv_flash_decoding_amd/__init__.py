@@ -38,6 +38,7 @@ from ._capi import (  # noqa: F401
     prefill_attention,
     fd_probe_copy,
     fd_probe_read,
+    fd_probe_read_rows,
     fd_workspace_init,
     load_library,
     make_problem,

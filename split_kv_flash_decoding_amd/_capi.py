@@ -39,6 +39,7 @@ EXPORTED = (
     "fd_status_string",
     "fd_last_error_message",
     "fd_probe_read",
+    "fd_probe_read_rows",
     "fd_probe_copy",
 )
 PROBE_SINK_FLOATS = 4096
@@ -115,7 +116,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.fd_decode_fused.argtypes = [P, Pl, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp, f32p, vp]
     lib.fd_workspace_init.argtypes = [P, Pl, vp, ctypes.c_size_t, vp]
     for name in ("fd_plan_splits", "fd_decode_partial", "fd_combine", "fd_decode_attention",
-                 "fd_decode_partial_scaled", "fd_decode_attention_scaled", "fd_append_kv", "fd_prefill_attention",
+                 "fd_decode_partial_scaled", "fd_decode_attention_scaled", "fd_append_kv",
+                 "fd_prefill_attention",
                  "fd_decode_fused", "fd_workspace_init"):
         getattr(lib, name).restype = ctypes.c_int
     lib.fd_status_string.argtypes = [ctypes.c_int]
@@ -124,6 +126,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.fd_last_error_message.restype = ctypes.c_char_p
     lib.fd_probe_read.argtypes = [vp, ctypes.c_size_t, vp, vp]
     lib.fd_probe_read.restype = ctypes.c_int
+    lib.fd_probe_read_rows.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_int32, vp, vp]
+    lib.fd_probe_read_rows.restype = ctypes.c_int
     lib.fd_probe_copy.argtypes = [vp, vp, ctypes.c_size_t, vp]
     lib.fd_probe_copy.restype = ctypes.c_int
     if path is None:
@@ -472,6 +477,21 @@ def fd_probe_read(src, sink, stream=None) -> None:
     if not src.is_cuda or not sink.is_cuda or sink.numel() * sink.element_size() < PROBE_SINK_FLOATS * 4:
         raise ValueError("src and sink must be CUDA tensors; sink holds PROBE_SINK_FLOATS floats")
     _check(load_library().fd_probe_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(stream)))
+
+
+def fd_probe_read_rows(a, b, row_bytes: int, chunk_rows: int, waves_across: bool, sink, stream=None) -> None:
+    """Read the CUDA tensors ``a`` and ``b`` (the same byte size, a whole
+    number of ``row_bytes`` rows) in the decode kernels' row pattern
+    (include/fd_probe.h): 1 KB column blocks with the eight waves splitting
+    the rows, or 8 KB blocks with wave w reading column w."""
+    nbytes = a.numel() * a.element_size()
+    if not a.is_cuda or not b.is_cuda or b.numel() * b.element_size() != nbytes or nbytes % row_bytes:
+        raise ValueError("a and b must be CUDA tensors of one size, a whole number of rows")
+    if not sink.is_cuda or sink.numel() * sink.element_size() < PROBE_SINK_FLOATS * 4:
+        raise ValueError("sink must be a CUDA tensor of PROBE_SINK_FLOATS floats")
+    _check(load_library().fd_probe_read_rows(_ptr(a), _ptr(b), nbytes // row_bytes, row_bytes,
+                                             8192 if waves_across else 1024, chunk_rows, int(bool(waves_across)),
+                                             _ptr(sink), _stream(stream)))
 
 
 def fd_probe_copy(dst, src, stream=None) -> None:

@@ -105,7 +105,9 @@ fd_status decode_partial(const fd_problem* p, const fd_plan* plan, const void* q
     hipError_t e;
     switch (plan->partial_kernel) {
         case kPartialMfma: e = fdk::launch_partial_mfma(G, paged, a, grid, hs); break;
+        case kPartialMfmaHeads: e = fdk::launch_partial_mfma_heads(G, paged, a, grid, hs); break;
         case kPartialHeadRows: e = fdk::launch_partial_valu_heads(p->head_dim, G, paged, a, grid, hs); break;
+        case kPartialHeadCols: e = fdk::launch_partial_valu_head_cols(p->head_dim, G, paged, a, grid, hs); break;
         default: e = fdk::launch_partial_valu(p->head_dim, G, paged, a, grid, hs); break;
     }
     if (e != hipSuccess) return fail(FD_ERR_HIP, "partial kernel launch: %s", hipGetErrorString(e));
@@ -204,7 +206,7 @@ fd_status fd_combine(const fd_problem* p, const fd_plan* plan, const int32_t* se
     hipError_t e = fdk::launch_combine(p->head_dim, p->out_dtype, ws_o, ws_ml, seq_lens_dev, out, lse, p->batch,
                                        problem_q_len(p) * p->num_q_heads, plan->chunk_tokens, plan->max_splits,
                                        plan->split_mode, p->page_size ? p->max_pages_per_seq * kPageSize : INT32_MAX,
-                                       combine_form(p), hs);
+                                       combine_form(p, plan->max_splits), hs);
     if (e != hipSuccess) return fail(FD_ERR_HIP, "combine kernel launch: %s", hipGetErrorString(e));
     return FD_OK;
 }

@@ -4,9 +4,10 @@
 // out = sum_s w_s O_s / sum_s w_s l_s, lse = M + ln(sum_s w_s l_s). This is
 // the cross-chunk reduce of FlashDecoding ("FlashAttention 全景演进与大模型
 // Token 生成全链路性能优化实战", §2.3), with every split rescaled by the
-// two-block identity of the same page's §1.2. Three forms: four waves per
+// two-block identity of the same page's §1.2. Four forms: four waves per
 // row (each sums every fourth split, eight splits' loads in flight, the waves
-// add up in LDS) for batches with few rows and many splits; one wave per row,
+// add up in LDS) for batches with few rows, sixteen waves per row when those
+// rows have many splits; one wave per row,
 // four rows per work-group, for batches with many rows, where four waves per
 // row would take several rounds of the chip's wave slots for rows that have
 // few splits; two rows per wave (32 lanes each) for the largest batches with
@@ -136,9 +137,12 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_rows2(const float*
     if (lse && hl == 0) lse[r] = M + __builtin_amdgcn_logf(l) * kLn2;
 }
 
-// Four waves per (sequence, query row): grid (hq, B).
-template <int D, int OUT>
-__global__ __launch_bounds__(64 * kCombineWaves) void combine(const float* __restrict__ ws_o,
+// NW waves per (sequence, query row): grid (hq, B). Four for most batches
+// under kCombinePerWaveRows rows; sixteen when such a batch has many splits
+// per row (a 128K-token cache cut into hundreds of splits), whose sums would
+// otherwise be a long chain of loads for each of four waves.
+template <int D, int OUT, int NW = kCombineWaves>
+__global__ __launch_bounds__(64 * NW) void combine(const float* __restrict__ ws_o,
                                                               const float* __restrict__ ws_ml,
                                                               const int32_t* __restrict__ seq_lens,
                                                               void* __restrict__ out, float* __restrict__ lse, int hq,
@@ -164,21 +168,21 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine(const float* __res
         }
         return;
     }
-    __shared__ float red_l[kCombineWaves];
-    __shared__ float red_o[kCombineWaves][D];
+    __shared__ float red_l[NW];
+    __shared__ float red_o[NW][D];
 
     float M = lane < S ? m_first : neg_inf();
     for (int i = lane + 64; i < S; i += 64) M = fmaxf(M, ws_ml[(base + i) * 2]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
 
-    // Wave w takes splits w, w + 4, ...; loads of eight splits in flight.
+    // Wave w takes splits w, w + NW, ...; loads of eight splits in flight.
     float acc[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) acc[e] = 0.f;
     float lsum = 0.f;
 #pragma unroll 8
-    for (int i = wave; i < S; i += kCombineWaves) {
+    for (int i = wave; i < S; i += NW) {
         const float ms = ws_ml[(base + i) * 2];
         const float ls = ws_ml[(base + i) * 2 + 1];
         const float w = __builtin_amdgcn_exp2f((ms - M) * kLog2e);
@@ -193,13 +197,13 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine(const float* __res
     if (wave == 0) {
         float l = red_l[0];
 #pragma unroll
-        for (int w = 1; w < kCombineWaves; ++w) l += red_l[w];
+        for (int w = 1; w < NW; ++w) l += red_l[w];
         const float inv = 1.0f / l;
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
             float o = red_o[0][lane * PER + e];
 #pragma unroll
-            for (int w = 1; w < kCombineWaves; ++w) o += red_o[w][lane * PER + e];
+            for (int w = 1; w < NW; ++w) o += red_o[w][lane * PER + e];
             store_out<OUT>(out, orow + lane * PER + e, o * inv);
         }
         if (lse && lane == 0) lse[(int64_t)b * hq + h] = M + __builtin_amdgcn_logf(l) * kLn2;
@@ -221,6 +225,9 @@ void launch_combine_out(int form, const float* ws_o, const float* ws_ml, const i
         hipLaunchKernelGGL((combine_rows<D, OUT>), dim3((rows + kCombineWaves - 1) / kCombineWaves),
                            dim3(64 * kCombineWaves), 0, st, ws_o, ws_ml, lens, out, lse, rows, hq, chunk, s_max,
                            split_mode, len_cap);
+    } else if (form == 3) {
+        hipLaunchKernelGGL((combine<D, OUT, 16>), dim3(hq, B), dim3(64 * 16), 0, st, ws_o, ws_ml, lens, out, lse, hq,
+                           chunk, s_max, split_mode, len_cap);
     } else {
         hipLaunchKernelGGL((combine<D, OUT>), dim3(hq, B), dim3(64 * kCombineWaves), 0, st, ws_o, ws_ml, lens, out,
                            lse, hq, chunk, s_max, split_mode, len_cap);

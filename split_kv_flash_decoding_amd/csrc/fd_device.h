@@ -460,11 +460,13 @@ struct AppendArgs {
 // `st` and return hipGetLastError().
 hipError_t launch_partial_valu(int D, int G, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st);
 hipError_t launch_partial_valu_heads(int D, int G, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st);
+hipError_t launch_partial_valu_head_cols(int D, int G, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st);
 hipError_t launch_partial_mfma(int G, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st);
+hipError_t launch_partial_mfma_heads(int G, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st);
 hipError_t launch_append(const AppendArgs& a, int q_dt, int kv_dt, int blocks, hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, int dt, int out_dt, bool paged, hipStream_t st);
 // form: 0 four waves per (sequence, query row), 1 one wave per row, 2 two rows
-// per wave (rows per sequence even).
+// per wave (rows per sequence even), 3 sixteen waves per row.
 hipError_t launch_combine(int D, int out_dt, const float* ws_o, const float* ws_ml, const int32_t* lens,
                           void* out, float* lse, int B, int hq, int chunk, int s_max, int split_mode,
                           int len_cap, int form, hipStream_t st);

@@ -99,12 +99,23 @@ bool mfma_applicable(const fd_problem* p) {
     return p->head_dim == 128 && rows >= 2 && rows <= kMaxQueryRows;
 }
 
+bool mfma_heads_applicable(const fd_problem* p) {
+    const int32_t nt = mfma_column_tiles(p);
+    return mfma_applicable(p) && (nt == 1 || nt == 2 || nt == 4) && p->num_kv_heads % (kMfmaWaves / nt) == 0;
+}
+
 bool head_rows_applicable(const fd_problem* p) {
     const int32_t G = p->num_q_heads / p->num_kv_heads;
     return problem_q_len(p) == 1 && G <= 2 && p->num_kv_heads % rows_per_load(p) == 0;
 }
 
+bool head_cols_applicable(const fd_problem* p) {
+    return head_rows_applicable(p) && p->num_kv_heads % (rows_per_load(p) * head_rows_waves(p)) == 0;
+}
+
 int32_t heads_per_workgroup(const fd_problem* p, int32_t kernel) {
+    if (kernel == kPartialHeadCols) return rows_per_load(p) * head_rows_waves(p);
+    if (kernel == kPartialMfmaHeads) return kMfmaWaves / mfma_column_tiles(p);
     return kernel == kPartialHeadRows ? rows_per_load(p) : 1;
 }
 
@@ -113,13 +124,14 @@ int32_t workgroups_per_split(const fd_problem* p, int32_t kernel) {
     return kernel == kPartialMfma ? groups * mfma_column_tiles(p) : groups;
 }
 
-int32_t combine_form(const fd_problem* p) {
+int32_t combine_form(const fd_problem* p, int32_t max_splits) {
     const int64_t per_seq = (int64_t)problem_q_len(p) * p->num_q_heads;
     const int64_t rows = (int64_t)p->batch * per_seq;
     const int32_t forced = env_int("FD_COMBINE_FORM", -1);
-    if (forced == 0 || forced == 1 || (forced == 2 && per_seq % 2 == 0)) return forced;
+    if (forced == 0 || forced == 1 || forced == 3 || (forced == 2 && per_seq % 2 == 0)) return forced;
     if (rows >= kCombineTwoRowRows && per_seq % 2 == 0) return 2;
-    return rows >= kCombinePerWaveRows ? 1 : 0;
+    if (rows >= kCombinePerWaveRows) return 1;
+    return max_splits >= kCombineWideSplits ? 3 : 0;
 }
 
 fd_status check_plan(const fd_problem* p, const fd_plan* plan) {
@@ -130,14 +142,16 @@ fd_status check_plan(const fd_problem* p, const fd_plan* plan) {
     if (plan->workspace_bytes < workspace_bytes(p, plan->max_splits))
         return fail(FD_ERR_INVALID_ARGUMENT, "plan does not belong to this problem (workspace_bytes)");
     if (plan->split_mode != 0 &&
-        (plan->split_mode != 1 || plan->partial_kernel != kPartialMfma || plan->chunk_tokens % kTileTokens))
+        (plan->split_mode != 1 || !is_mfma_kernel(plan->partial_kernel) || plan->chunk_tokens % kTileTokens))
         return fail(FD_ERR_INVALID_ARGUMENT, "plan split_mode %d with kernel %d and chunk %d: the balanced mode "
                     "needs the matrix-core kernel and a chunk that is a multiple of %d",
                     plan->split_mode, plan->partial_kernel, plan->chunk_tokens, kTileTokens);
-    if ((plan->partial_kernel != kPartialMfma && problem_q_len(p) > 1) ||
+    if ((!is_mfma_kernel(plan->partial_kernel) && problem_q_len(p) > 1) ||
         (plan->partial_kernel == kPartialMfma && !mfma_applicable(p)) ||
+        (plan->partial_kernel == kPartialMfmaHeads && !mfma_heads_applicable(p)) ||
         (plan->partial_kernel == kPartialHeadRows && !head_rows_applicable(p)) ||
-        plan->partial_kernel < kPartialTokenRows || plan->partial_kernel > kPartialHeadRows)
+        (plan->partial_kernel == kPartialHeadCols && !head_cols_applicable(p)) ||
+        plan->partial_kernel < kPartialTokenRows || plan->partial_kernel > kPartialMfmaHeads)
         return fail(FD_ERR_INVALID_ARGUMENT, "plan names partial kernel %d, which does not cover this problem",
                     plan->partial_kernel);
     return FD_OK;
@@ -201,15 +215,21 @@ fd_status fd_plan_splits(const fd_problem* p, const int32_t* lens, int32_t num_c
     // whole multi-head rows when Hkv allows. FD_PARTIAL_KERNEL=0/1/2 overrides
     // (when the forced kernel covers the problem).
     const int32_t G = p->num_q_heads / p->num_kv_heads;
+    // Of the two matrix-core forms, the one whose waves each own a (KV head,
+    // column tile) wherever the heads fill its work-groups (measured on
+    // MI355X, same GPU, twice: GQA varlen 114.5 -> 109.3 us, paged GQA
+    // 335.4 -> 324.8 us, paged GQA with 8 query tokens 704 -> 604 us).
     int32_t kernel = kPartialTokenRows;
     if (mfma_applicable(p) && (G >= 4 || problem_q_len(p) > 1))
-        kernel = kPartialMfma;
+        kernel = mfma_heads_applicable(p) ? kPartialMfmaHeads : kPartialMfma;
     else if (head_rows_applicable(p))
         kernel = kPartialHeadRows;
     const int32_t forced = env_int("FD_PARTIAL_KERNEL", -1);
     if (forced == kPartialTokenRows && problem_q_len(p) == 1) kernel = kPartialTokenRows;
     if (forced == kPartialMfma && mfma_applicable(p)) kernel = kPartialMfma;
     if (forced == kPartialHeadRows && head_rows_applicable(p)) kernel = kPartialHeadRows;
+    if (forced == kPartialHeadCols && head_cols_applicable(p)) kernel = kPartialHeadCols;
+    if (forced == kPartialMfmaHeads && mfma_heads_applicable(p)) kernel = kPartialMfmaHeads;
     if (force_num_splits == 0) force_num_splits = env_int("FD_NUM_SPLITS", 0);
 
     auto choose_chunk = [&](int32_t kern) -> int64_t {
@@ -224,8 +244,13 @@ fd_status fd_plan_splits(const fd_problem* p, const int32_t* lens, int32_t num_c
             // 1024); an FP8 split needs twice the tokens for the same bytes
             // (128K-token FP8 cache: 2048-token splits 3% faster than 1024).
             const int32_t head_rows_min = kHeadRowsMinChunk * 2 / kv_elem_bytes(p);
+            // Head columns: the same bytes per work-group as head rows.
+            const int32_t head_cols_min =
+                std::max<int32_t>(kChunkGranule, head_rows_min / head_rows_waves(p));
             const int64_t min_chunk = std::max<int32_t>(
-                1, env_int("FD_MIN_CHUNK", kern == kPartialHeadRows ? head_rows_min : kDefaultMinChunk));
+                1, env_int("FD_MIN_CHUNK", kern == kPartialHeadRows   ? head_rows_min
+                                           : kern == kPartialHeadCols ? head_cols_min
+                                                                      : kDefaultMinChunk));
             // Work-groups are (sequence, KV head group, split). A chunk that
             // makes about num_cus * k of them, never below the minimum chunk, a
             // multiple of 64.
@@ -288,7 +313,7 @@ fd_status fd_plan_splits(const fd_problem* p, const int32_t* lens, int32_t num_c
     // FD_SPLIT_MODE=0/1 overrides; FD_WG_PER_CU sets the work-groups per CU.
     bool ragged = false;
     for (int32_t b = 1; b < p->batch; ++b) ragged |= lens[b] != lens[0];
-    const bool balanced_ok = kernel == kPartialMfma;
+    const bool balanced_ok = is_mfma_kernel(kernel);
     int32_t split_mode = (balanced_ok && force_num_splits == 0 && ragged && p->batch <= kBalancedMaxBatch) ? 1 : 0;
     const int32_t forced_mode = env_int("FD_SPLIT_MODE", -1);
     if (forced_mode == 0 || (forced_mode == 1 && balanced_ok)) split_mode = forced_mode;

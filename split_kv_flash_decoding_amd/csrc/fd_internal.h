@@ -55,15 +55,17 @@ uint64_t workspace_o_bytes(const fd_problem* p, int32_t max_splits);
 uint64_t workspace_counters_offset(const fd_problem* p, int32_t max_splits);
 uint64_t workspace_bytes(const fd_problem* p, int32_t max_splits);
 
-// The combine's form: 0 four waves per (sequence, query row); 1 one wave per
-// row, for batches of at least kCombinePerWaveRows rows (B * q_len * Hq),
-// where four waves per row would take several rounds of the chip's wave
-// slots; 2 two rows per wave, from kCombineTwoRowRows rows when a sequence has
-// an even number of rows. FD_COMBINE_FORM=0/1/2 overrides (2 only with even
-// rows per sequence).
+// The combine's form: 0 four waves per (sequence, query row); 3 sixteen waves
+// per row, for those batches when rows have kCombineWideSplits splits or more;
+// 1 one wave per row, for batches of at least kCombinePerWaveRows rows
+// (B * q_len * Hq), where four waves per row would take several rounds of the
+// chip's wave slots; 2 two rows per wave, from kCombineTwoRowRows rows when a
+// sequence has an even number of rows. FD_COMBINE_FORM=0/1/2/3 overrides (2
+// only with even rows per sequence).
 constexpr int64_t kCombinePerWaveRows = 512;
 constexpr int64_t kCombineTwoRowRows = 4096;
-int32_t combine_form(const fd_problem* p);
+constexpr int32_t kCombineWideSplits = 128;
+int32_t combine_form(const fd_problem* p, int32_t max_splits);
 
 // Compute units of the current HIP device, cached per device (fd_api.hip).
 fd_status query_num_cus(int32_t* out);
@@ -72,14 +74,21 @@ fd_status query_num_cus(int32_t* out);
 enum PartialKernel : int32_t {
     kPartialTokenRows = 0,  // vector ALU, lane rows are tokens of one KV head
     kPartialMfma = 1,       // matrix cores, grouped-query heads
-    kPartialHeadRows = 2,   // vector ALU, lane rows are consecutive KV heads
+    kPartialHeadRows = 2,   // vector ALU, lane rows are consecutive KV heads, waves split the tokens
+    kPartialHeadCols = 3,   // vector ALU, lane rows are consecutive KV heads, waves split the heads
+    kPartialMfmaHeads = 4,  // matrix cores, each wave owns one (KV head, column tile) of the work-group
 };
+
+// Whether a kernel is one of the two matrix-core forms.
+inline bool is_mfma_kernel(int32_t kernel) { return kernel == kPartialMfma || kernel == kPartialMfmaHeads; }
 
 // Query tokens per sequence (a q_len of 0 means one).
 inline int32_t problem_q_len(const fd_problem* p) { return p->q_len > 1 ? p->q_len : 1; }
 // Largest q_len * Hq/Hkv the matrix-core kernel handles (up to four 16-column
 // MFMA tiles, one work-group each).
 constexpr int32_t kMaxQueryRows = 64;
+// Waves per work-group of the matrix-core kernel (fd_partial_mfma.hip).
+constexpr int32_t kMfmaWaves = 4;
 
 // Bytes of one cache element (2 for fp16/bf16, 1 for E4M3).
 inline int32_t kv_elem_bytes(const fd_problem* p) { return p->kv_dtype == FD_FP8_E4M3 ? 1 : 2; }
@@ -90,12 +99,23 @@ inline int32_t q_dtype_of(const fd_problem* p) { return p->kv_dtype == FD_FP8_E4
 // d * bytes / 16 lanes per row.
 inline int32_t rows_per_load(const fd_problem* p) { return 64 / (p->head_dim * kv_elem_bytes(p) / 16); }
 
+// Waves per work-group of the head-rows kernels (fd_partial_valu.hip): eight
+// for 16-bit caches, four for FP8.
+inline int32_t head_rows_waves(const fd_problem* p) { return kv_elem_bytes(p) == 1 ? 4 : 8; }
+
 // Whether the matrix-core partial kernel covers this problem: d = 128 and
 // 2 <= q_len * Hq/Hkv <= kMaxQueryRows query rows per KV head.
 bool mfma_applicable(const fd_problem* p);
+// Whether the matrix-core kernel with waves owning heads covers it: as the
+// matrix-core kernel, with 1, 2 or 4 column tiles (so the four waves of a
+// work-group hold whole heads) and Hkv a multiple of the heads per work-group.
+bool mfma_heads_applicable(const fd_problem* p);
 // Whether the head-rows kernel covers it: one query token, G <= 2 and Hkv a
 // multiple of the rows one load covers.
 bool head_rows_applicable(const fd_problem* p);
+// Whether the head-columns kernel covers it: as head rows, with Hkv a multiple
+// of the heads all waves of a work-group cover together.
+bool head_cols_applicable(const fd_problem* p);
 // KV heads one work-group of `kernel` handles.
 int32_t heads_per_workgroup(const fd_problem* p, int32_t kernel);
 // Work-groups per split of one sequence: KV-head groups times the matrix-core

@@ -82,7 +82,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 128;
 constexpr int kTile = 16;                  // tokens per tile (one 16-token page)
-constexpr int kMW = 4;                     // waves per work-group
+constexpr int kMW = fd::kMfmaWaves;        // waves per work-group
 constexpr int kPitch = kD + 16;            // LDS row pitch of a V tile, elements (288 B)
 
 template <int DT> struct Mfma;
@@ -150,7 +150,19 @@ __device__ __forceinline__ uint32_t widen_fp8_pair(uint32_t w) {
 // K/V row, so the loads leave it in L2 for the other tiles' work-groups
 // instead of streaming it past (measured on MI355X: 64 rows, 128K tokens
 // x 32 heads, 922 -> 665 us; one tile is faster with streaming loads).
-template <int NQ, int KT, int QT, int PAGE_MODE, bool KEEP>
+// WH (waves own heads): the four waves of a work-group take 4 / NT KV heads
+// times the NT column tiles of each, and every wave runs every tile of the
+// work item's shares for its own (head, column tile) pair: no two waves share
+// an output row, so each writes its own partial, with no merge through LDS
+// and no barrier between shares, and the NT waves of a head read the same K/V
+// tiles on one compute unit. Needs NT in {1, 2, 4} and Hkv a multiple of
+// 4 / NT.
+// NTS (WH with NT = NTS > 1 column tiles): the NT waves of a head split the
+// loads of each K/V tile between them, stage it once into a tile buffer they
+// share (two buffers per head, one barrier per tile) and each run their own
+// column tile from it, so a K/V byte is loaded and staged once per work-group
+// instead of once per column tile.
+template <int NQ, int KT, int QT, int PAGE_MODE, bool KEEP, bool WH = false, int NTS = 1>
 __global__ __launch_bounds__(64 * kMW) void partial_mfma(const PartialArgs a) {
     using M = Mfma<QT>;
     constexpr bool PAGED = PAGE_MODE != 0;
@@ -186,13 +198,16 @@ __global__ __launch_bounds__(64 * kMW) void partial_mfma(const PartialArgs a) {
     const int nq_all = q_len * G;
     const int NT = (nq_all + 15) / 16;
     int unit = blockIdx.x, ct = 0;
-    if (NT > 1) {
+    if (!WH && NT > 1) {
         const int rem = blockIdx.x % (8 * NT);
         ct = rem / 8;
         unit = blockIdx.x / (8 * NT) * 8 + rem % 8;
     }
+    // KV heads per work-group, and head blocks per work item.
+    const int hpw = WH ? kMW / NT : 1;
+    const int blocks = hkv / hpw;
     // Split mode 0: the work-list entry is one split (locate_unit). Mode 1: it
-    // is work item unit / hkv of the balanced list, whose shares of
+    // is work item unit / blocks of the balanced list, whose shares of
     // consecutive sequences run one after the other (the body below, once
     // per share).
     const int len_cap = PAGED ? max_pages * 16 : INT32_MAX;
@@ -200,16 +215,17 @@ __global__ __launch_bounds__(64 * kMW) void partial_mfma(const PartialArgs a) {
     int S_b = 0;
     BalancedCursor cur;
     if (a.split_mode == 0) {
-        if (!locate_unit(unit, seq_lens, batch, hkv, chunk, len_cap, wu)) return;
+        if (!locate_unit(unit, seq_lens, batch, blocks, chunk, len_cap, wu)) return;
         S_b = (wu.L + chunk - 1) / chunk;
     } else {
-        if (!balanced_first(unit / hkv, seq_lens, batch, chunk >> 4, len_cap, cur) ||
-            !balanced_share(seq_lens, batch, chunk >> 4, len_cap, unit % hkv, cur, wu, S_b))
+        if (!balanced_first(unit / blocks, seq_lens, batch, chunk >> 4, len_cap, cur) ||
+            !balanced_share(seq_lens, batch, chunk >> 4, len_cap, unit % blocks, cur, wu, S_b))
             return;
     }
+    int phase = 0;  // shared tile buffers (NTS > 1): the one the next tile is staged into
 next_share:
     if (wu.s >= s_max) return;
-    const int g = wu.g, s = wu.s, b = wu.b, t0 = wu.t0, t1 = wu.t1;
+    const int s = wu.s, b = wu.b, t0 = wu.t0, t1 = wu.t1;
     const int64_t row0 = wu.row0;
 
     // The thread index is made opaque on every pass, so the compiler cannot
@@ -221,11 +237,14 @@ next_share:
     const int wave = tid >> 6;
     const int grp = lane >> 4;  // 0..3
     const int col = lane & 15;  // query row (scores, output) / token (K operand) / d-slice (V load)
+    // This wave's KV head and column tile.
+    const int g = WH ? wu.g * hpw + wave / NT : wu.g;
+    const int ctw = WH ? wave % NT : ct;
 
     // Column `col` is query row c0 + col of the group: head qj for query
     // token qi; it may see tokens below `lim` (its causal limit, inside this
     // split). nq: the rows of this column tile.
-    const int c0 = 16 * ct;
+    const int c0 = 16 * ctw;
     const int nq = min(16, nq_all - c0);
     const int qi = (c0 + col) / G;
     const int qj = c0 + col - qi * G;
@@ -277,44 +296,78 @@ next_share:
         }
     };
 
+    // A wave's tiles: wave, wave + kMW, ... of the split, or all of them (WH).
+    const int tfirst = WH ? 0 : wave;
+    constexpr int TSTEP = WH ? 1 : kMW;
     // Tile-aligned pages: lane i holds the page of this wave's tile 64 blk + i.
     int pg = 0, pg_blk = -1;
     auto tile_page = [&](int tile) -> int64_t {
-        const int kk = (tile - wave) / kMW;
+        const int kk = (tile - tfirst) / TSTEP;
         const int blk = kk >> 6;
         if (blk != pg_blk) {
-            const int tidx = wave + kMW * (64 * blk + lane);
+            const int tidx = tfirst + TSTEP * (64 * blk + lane);
             pg = tidx < ntiles ? checked_page(table[(t0 >> 4) + tidx], a.num_pages) : 0;
             pg_blk = blk;
         }
         return (int64_t)__builtin_amdgcn_readlane(pg, kk & 63) * 16;
     };
 
-    auto load = [&](int tile, u32x4* kr, u32x4* vr) {
-        const int tt = t0 + tile * kTile;
+    // Where a tile's rows come from: buffer descriptors over its rows (the
+    // descriptor's size ends at the split, so rows past it read as zeros), or,
+    // for pages that may start mid-tile, one table lookup per row.
+    struct TileSrc {
+        __amdgpu_buffer_rsrc_t rk, rv;
+        int tt;
+    };
+    auto tile_src = [&](int tile) -> TileSrc {
+        TileSrc ts;
+        ts.tt = t0 + tile * kTile;
+        if constexpr (PAGE_MODE != 1) {
+            const int64_t first = (PAGE_MODE == 2) ? tile_page(tile) : row0 + ts.tt;
+            const int bytes = min(kTile, t1 - ts.tt) * row_bytes;
+            ts.rk = make_rsrc(kbase + first * row_bytes, bytes);
+            ts.rv = make_rsrc(vbase + first * row_bytes, bytes);
+        }
+        return ts;
+    };
+    // Load instruction i of the tile's K (or V) rows: rows RPI i .. + RPI.
+    auto load_one = [&](const TileSrc& ts, int i, bool is_v) -> u32x4 {
         if constexpr (PAGE_MODE == 1) {
             // Pages may start mid-tile: one table lookup per row, clamped to the split.
-#pragma unroll
-            for (int i = 0; i < KL; ++i) {
-                const int64_t row = row_of(min(tt + RPI * i + lrow, t1 - 1)) * row_bytes;
-                if constexpr (KEEP) {
-                    kr[i] = *reinterpret_cast<const u32x4*>(kbase + row + 16 * lcol);
-                    vr[i] = *reinterpret_cast<const u32x4*>(vbase + row + 16 * lcol);
-                } else {
-                    kr[i] = load16(kbase + row + 16 * lcol);
-                    vr[i] = load16(vbase + row + 16 * lcol);
-                }
-            }
+            const int64_t row = row_of(min(ts.tt + RPI * i + lrow, t1 - 1)) * row_bytes;
+            const uint8_t* src = (is_v ? vbase : kbase) + row + 16 * lcol;
+            if constexpr (KEEP) return *reinterpret_cast<const u32x4*>(src);
+            else return load16(src);
         } else {
-            const int64_t first = (PAGE_MODE == 2) ? tile_page(tile) : row0 + tt;
-            const int bytes = min(kTile, t1 - tt) * row_bytes;
-            const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + first * row_bytes, bytes);
-            const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + first * row_bytes, bytes);
+            return buffer_load16<kPolicy>(is_v ? ts.rv : ts.rk, (RPI * i + lrow) * row_bytes + 16 * lcol);
+        }
+    };
+    // Stage a landed load i as 16-bit rows RPI i .. + RPI of the tile at dst.
+    auto stage_one = [&](u32x4 x, int i, uint16_t* dst) {
+        if constexpr (FP8) {
+            // codes 4 w .. 4 w + 3 sit in word w; dims 16 lcol .. +16
+            u32x4 lo, hi;
 #pragma unroll
-            for (int i = 0; i < KL; ++i) {
-                kr[i] = buffer_load16<kPolicy>(rk, voff_v[i]);
-                vr[i] = buffer_load16<kPolicy>(rv, voff_v[i]);
+            for (int w = 0; w < 2; ++w) {
+                lo[2 * w] = widen_fp8_pair<QT, false>(x[w]);
+                lo[2 * w + 1] = widen_fp8_pair<QT, true>(x[w]);
+                hi[2 * w] = widen_fp8_pair<QT, false>(x[w + 2]);
+                hi[2 * w + 1] = widen_fp8_pair<QT, true>(x[w + 2]);
             }
+            uint16_t* d = dst + (RPI * i + lrow) * kPitch + 16 * lcol;
+            *reinterpret_cast<u32x4*>(d) = lo;
+            *reinterpret_cast<u32x4*>(d + 8) = hi;
+        } else {
+            *reinterpret_cast<u32x4*>(dst + (RPI * i + lrow) * kPitch + 8 * lcol) = x;
+        }
+    };
+
+    auto load = [&](int tile, u32x4* kr, u32x4* vr) {
+        const TileSrc ts = tile_src(tile);
+#pragma unroll
+        for (int i = 0; i < KL; ++i) {
+            kr[i] = load_one(ts, i, false);
+            vr[i] = load_one(ts, i, true);
         }
     };
 
@@ -323,30 +376,8 @@ next_share:
     auto stage = [&](const u32x4* kr, const u32x4* vr) {
 #pragma unroll
         for (int i = 0; i < KL; ++i) {
-            if constexpr (FP8) {
-                // codes 4 w .. 4 w + 3 sit in word w; dims 16 lcol .. +16
-                u32x4 klo, khi, vlo, vhi;
-#pragma unroll
-                for (int w = 0; w < 2; ++w) {
-                    klo[2 * w] = widen_fp8_pair<QT, false>(kr[i][w]);
-                    klo[2 * w + 1] = widen_fp8_pair<QT, true>(kr[i][w]);
-                    khi[2 * w] = widen_fp8_pair<QT, false>(kr[i][w + 2]);
-                    khi[2 * w + 1] = widen_fp8_pair<QT, true>(kr[i][w + 2]);
-                    vlo[2 * w] = widen_fp8_pair<QT, false>(vr[i][w]);
-                    vlo[2 * w + 1] = widen_fp8_pair<QT, true>(vr[i][w]);
-                    vhi[2 * w] = widen_fp8_pair<QT, false>(vr[i][w + 2]);
-                    vhi[2 * w + 1] = widen_fp8_pair<QT, true>(vr[i][w + 2]);
-                }
-                uint16_t* dk = my_sk + (RPI * i + lrow) * kPitch + 16 * lcol;
-                uint16_t* dv = my_sv + (RPI * i + lrow) * kPitch + 16 * lcol;
-                *reinterpret_cast<u32x4*>(dk) = klo;
-                *reinterpret_cast<u32x4*>(dk + 8) = khi;
-                *reinterpret_cast<u32x4*>(dv) = vlo;
-                *reinterpret_cast<u32x4*>(dv + 8) = vhi;
-            } else {
-                *reinterpret_cast<u32x4*>(my_sk + (RPI * i + lrow) * kPitch + 8 * lcol) = kr[i];
-                *reinterpret_cast<u32x4*>(my_sv + (RPI * i + lrow) * kPitch + 8 * lcol) = vr[i];
-            }
+            stage_one(kr[i], i, my_sk);
+            stage_one(vr[i], i, my_sv);
         }
     };
 
@@ -404,8 +435,41 @@ next_share:
         }
     };
 
-    int tile = wave;
-    if constexpr (!FP8) {
+    int tile = tfirst;
+    if constexpr (NTS > 1) {
+        // The NTS waves of head hh take turns over the tile's 2 KL loads (K
+        // loads first, then V): wave ctw takes loads ctw, ctw + NTS, ...
+        constexpr int NL = 2 * KL / NTS;
+        static_assert(2 * KL % NTS == 0, "loads per wave");
+        const int hh = wave / NTS;
+        const int part = uniform(ctw);
+        constexpr int kTileElems = kTile * kPitch;
+        u32x4 r[NL];
+        auto load_part = [&](int tl) {
+            const TileSrc ts = tile_src(tl);
+#pragma unroll
+            for (int j = 0; j < NL; ++j) {
+                const int f = part + NTS * j;
+                r[j] = load_one(ts, f % KL, f >= KL);
+            }
+        };
+        if (ntiles > 0) load_part(0);
+        for (; tile < ntiles; ++tile) {
+            my_sk = reinterpret_cast<uint16_t*>(smem) + (hh * 2 + phase) * 2 * kTileElems;
+            my_sv = my_sk + kTileElems;
+#pragma unroll
+            for (int j = 0; j < NL; ++j) {
+                const int f = part + NTS * j;
+                stage_one(r[j], f % KL, f >= KL ? my_sv : my_sk);
+            }
+            // The whole tile is staged; every wave of the work-group is also
+            // past the tile before it, whose buffer the next tile reuses.
+            __syncthreads();
+            if (tile + 1 < ntiles) load_part(tile + 1);
+            compute(tile);
+            phase ^= 1;
+        }
+    } else if constexpr (!FP8) {
         // The wave's next tile loads into the registers its current tile has
         // just left for LDS, so they are in flight while the current tile is
         // computed and the register file holds one tile, not two: 3 waves per
@@ -414,9 +478,9 @@ next_share:
         if (tile < ntiles) load(tile, kr, vr);
         while (tile < ntiles) {
             stage(kr, vr);
-            if (tile + kMW < ntiles) load(tile + kMW, kr, vr);
+            if (tile + TSTEP < ntiles) load(tile + TSTEP, kr, vr);
             compute(tile);
-            tile += kMW;
+            tile += TSTEP;
         }
     } else {
         // FP8 tiles are half the registers but take longer to stage (the codes
@@ -425,15 +489,15 @@ next_share:
         u32x4 ka[KL], va[KL], kb[KL], vb[KL];
         if (tile < ntiles) load(tile, ka, va);
         while (tile < ntiles) {
-            if (tile + kMW < ntiles) load(tile + kMW, kb, vb);
+            if (tile + TSTEP < ntiles) load(tile + TSTEP, kb, vb);
             stage(ka, va);
             compute(tile);
-            tile += kMW;
+            tile += TSTEP;
             if (tile >= ntiles) break;
-            if (tile + kMW < ntiles) load(tile + kMW, ka, va);
+            if (tile + TSTEP < ntiles) load(tile + TSTEP, ka, va);
             stage(kb, vb);
             compute(tile);
-            tile += kMW;
+            tile += TSTEP;
         }
     }
 
@@ -449,6 +513,32 @@ next_share:
         for (int jd = 0; jd < 8; ++jd) acc[jd] = acc[jd] * alpha;
     }
     const float m_run = m_true;
+
+    if constexpr (WH) {
+        // This wave alone holds its rows' statistics: lane (grp, col) writes
+        // O[row col][16 jd + 4 grp .. + 4] straight to the workspace.
+        if (col < nq) {
+            const float v_sc = head_scale(a.v_scale, g);
+            const int n = c0 + col;
+            const int ni = n / G;
+            const int64_t slot = (((int64_t)b * q_len + ni) * hq + g * G + (n - ni * G)) * s_max + s;
+#pragma unroll
+            for (int jd = 0; jd < 8; ++jd)
+                *reinterpret_cast<f32x4_t*>(ws_o + slot * kD + 16 * jd + 4 * grp) = acc[jd] * v_sc;
+            if (grp == 0) {
+                ws_ml[slot * 2] = m_run * kLn2;
+                ws_ml[slot * 2 + 1] = l_run;
+            }
+        }
+        if (a.counters)
+            fused_merge<kD, (NQ < 4 ? NQ : 4), kMW>(a, b, S_b, wu.g * hpw, hpw, q_len * hpw * G, 1,
+                                                    reinterpret_cast<float*>(smem));
+        if (a.split_mode != 0) {
+            balanced_advance(seq_lens, len_cap, cur);
+            if (balanced_share(seq_lens, batch, chunk >> 4, len_cap, unit % blocks, cur, wu, S_b)) goto next_share;
+        }
+        return;
+    }
 
     // Lane (grp, col) holds O[row col][16 jd + 4 grp + i]; the merge area
     // overlaps the other waves' staging tiles.
@@ -493,41 +583,57 @@ next_share:
     if (a.counters) fused_merge<kD, (NQ < 4 ? NQ : 4), kMW>(a, b, S_b, g, 1, nq_all, NT, &sm_o[0][0][0]);
     if (a.split_mode != 0) {
         balanced_advance(seq_lens, len_cap, cur);
-        if (balanced_share(seq_lens, batch, chunk >> 4, len_cap, unit % hkv, cur, wu, S_b)) {
+        if (balanced_share(seq_lens, batch, chunk >> 4, len_cap, unit % blocks, cur, wu, S_b)) {
             __syncthreads();  // the last share's merge area is the next share's staging area
             goto next_share;
         }
     }
 }
 
-template <int NQ, int KT, int QT, bool KEEP = false>
+template <int NQ, int KT, int QT, bool WH, bool KEEP = false, int NTS = 1>
 hipError_t launch_nq(bool paged, const PartialArgs& a, dim3 grid, hipStream_t st) {
     // Paged splits that start on page boundaries read their page indices 64 at a time.
     if (!paged)
-        hipLaunchKernelGGL((partial_mfma<NQ, KT, QT, 0, KEEP>), grid, dim3(64 * kMW), 0, st, a);
+        hipLaunchKernelGGL((partial_mfma<NQ, KT, QT, 0, KEEP, WH, NTS>), grid, dim3(64 * kMW), 0, st, a);
     else if (a.chunk % 16 == 0)
-        hipLaunchKernelGGL((partial_mfma<NQ, KT, QT, 2, KEEP>), grid, dim3(64 * kMW), 0, st, a);
+        hipLaunchKernelGGL((partial_mfma<NQ, KT, QT, 2, KEEP, WH, NTS>), grid, dim3(64 * kMW), 0, st, a);
     else
-        hipLaunchKernelGGL((partial_mfma<NQ, KT, QT, 1, KEEP>), grid, dim3(64 * kMW), 0, st, a);
+        hipLaunchKernelGGL((partial_mfma<NQ, KT, QT, 1, KEEP, WH, NTS>), grid, dim3(64 * kMW), 0, st, a);
     return hipGetLastError();
 }
 
-template <int KT, int QT>
+template <int KT, int QT, bool WH>
 hipError_t launch_types(int nq, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st) {
-    if (nq <= 2) return launch_nq<2, KT, QT>(paged, a, grid, st);
-    if (nq <= 4) return launch_nq<4, KT, QT>(paged, a, grid, st);
-    if (nq <= 8) return launch_nq<8, KT, QT>(paged, a, grid, st);
-    if (nq <= 16) return launch_nq<16, KT, QT>(paged, a, grid, st);
-    return launch_nq<16, KT, QT, true>(paged, a, grid, st);
+    if (nq <= 2) return launch_nq<2, KT, QT, WH>(paged, a, grid, st);
+    if (nq <= 4) return launch_nq<4, KT, QT, WH>(paged, a, grid, st);
+    if (nq <= 8) return launch_nq<8, KT, QT, WH>(paged, a, grid, st);
+    if (nq <= 16) return launch_nq<16, KT, QT, WH>(paged, a, grid, st);
+    if constexpr (WH) {
+        // The column tiles of a head share each staged tile (2 or 4 of them;
+        // the planner gives three-tile problems to the other form).
+        if (nq <= 32) return launch_nq<16, KT, QT, true, false, 2>(paged, a, grid, st);
+        return launch_nq<16, KT, QT, true, false, 4>(paged, a, grid, st);
+    } else {
+        return launch_nq<16, KT, QT, false, true>(paged, a, grid, st);
+    }
+}
+
+template <bool WH>
+hipError_t launch_mfma(int G, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st) {
+    const int nq = G * a.q_len;  // query rows per KV head (16 per column tile)
+    if (a.kv_dt == FD_FP8_E4M3)
+        return a.q_dt == FD_F16 ? launch_types<FD_FP8_E4M3, FD_F16, WH>(nq, paged, a, grid, st)
+                                : launch_types<FD_FP8_E4M3, FD_BF16, WH>(nq, paged, a, grid, st);
+    return a.kv_dt == FD_F16 ? launch_types<FD_F16, FD_F16, WH>(nq, paged, a, grid, st)
+                             : launch_types<FD_BF16, FD_BF16, WH>(nq, paged, a, grid, st);
 }
 
 hipError_t launch_partial_mfma(int G, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st) {
-    const int nq = G * a.q_len;  // query rows per KV head (16 per column tile)
-    if (a.kv_dt == FD_FP8_E4M3)
-        return a.q_dt == FD_F16 ? launch_types<FD_FP8_E4M3, FD_F16>(nq, paged, a, grid, st)
-                                : launch_types<FD_FP8_E4M3, FD_BF16>(nq, paged, a, grid, st);
-    return a.kv_dt == FD_F16 ? launch_types<FD_F16, FD_F16>(nq, paged, a, grid, st)
-                             : launch_types<FD_BF16, FD_BF16>(nq, paged, a, grid, st);
+    return launch_mfma<false>(G, paged, a, grid, st);
+}
+
+hipError_t launch_partial_mfma_heads(int G, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st) {
+    return launch_mfma<true>(G, paged, a, grid, st);
 }
 
 }  // namespace fdk

@@ -247,14 +247,23 @@ __global__ __launch_bounds__(kThreads) void partial_valu(const PartialArgs a) {
 // launch with eight; the FP8 128K cache is no faster with eight.
 constexpr int head_rows_waves(int kt) { return kt == FD_FP8_E4M3 ? 4 : 8; }
 
-template <int D, int G, int KT, int QT, int PAGE_MODE>
+// WH (head columns): the waves of a work-group take different heads of the
+// same tokens instead of different tokens of the same heads. Wave w owns KV
+// heads (blk * NW + w) * RPW .. +RPW for every token of the split, so the
+// work-group reads NW * RPW * 2d bytes of each token row together (8 KB at
+// 32 heads, d = 128: whole rows of the token-major cache), and no two waves
+// share a head: each writes its own partial, with no merge through LDS and
+// no barrier. Requires Hkv % (NW * RPW) == 0.
+template <int D, int G, int KT, int QT, int PAGE_MODE, bool WH = false>
 __global__ __launch_bounds__(64 * head_rows_waves(KT)) void partial_valu_heads(const PartialArgs a) {
     using KV = KvLoad<KT, QT>;
     constexpr int NW = head_rows_waves(KT);  // waves per work-group
     constexpr int EPL = KV::kElems;  // elements per 16-byte load
     constexpr int EB = 16 / EPL;     // bytes per element
     constexpr int LPR = D / EPL;     // lanes per head row
-    constexpr int RPW = 64 / LPR;    // heads per work-group
+    constexpr int RPW = 64 / LPR;    // heads per wave
+    constexpr int HPW = WH ? NW * RPW : RPW;  // heads per work-group
+    constexpr int SSTEP = WH ? 1 : NW;         // a wave's stride through the split's stages
     constexpr int U = kUnroll;       // tokens per wave stage
     constexpr int QW = KV::kQWords;
     constexpr bool PAGED = PAGE_MODE != 0;
@@ -266,7 +275,7 @@ __global__ __launch_bounds__(64 * head_rows_waves(KT)) void partial_valu_heads(c
     const int batch = a.batch, hq = a.hq, hkv = a.hkv, chunk = a.chunk, s_max = a.s_max, max_pages = a.max_pages;
 
     WorkUnit wu;
-    if (!locate_unit(blockIdx.x, seq_lens, batch, hkv / RPW, chunk, PAGED ? max_pages * 16 : INT32_MAX, wu)) return;
+    if (!locate_unit(blockIdx.x, seq_lens, batch, hkv / HPW, chunk, PAGED ? max_pages * 16 : INT32_MAX, wu)) return;
     if (wu.s >= s_max) return;
     const int s = wu.s, b = wu.b, t0 = wu.t0, t1 = wu.t1;
     const int64_t row0 = wu.row0;
@@ -275,7 +284,8 @@ __global__ __launch_bounds__(64 * head_rows_waves(KT)) void partial_valu_heads(c
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane / LPR;
     const int c = lane % LPR;
-    const int g = wu.g * RPW + r;  // this row's KV head
+    const int g0 = WH ? (wu.g * NW + wave) * RPW : wu.g * RPW;  // this wave's first KV head
+    const int g = g0 + r;                                      // this row's KV head
 
     const int32_t* table = PAGED ? block_table + (int64_t)b * max_pages : nullptr;
     const int64_t row_stride = (int64_t)hkv * D * EB;  // bytes
@@ -302,12 +312,13 @@ __global__ __launch_bounds__(64 * head_rows_waves(KT)) void partial_valu_heads(c
     const int nstages = (t1 - t0 + U - 1) / U;
 
     // Page-aligned splits: lane i holds the page of this wave's stage 64 blk + i.
+    const int first_stage = WH ? 0 : wave;
     int pg = 0, pg_blk = -1;
     auto stage_page_row = [&](int stage) -> int64_t {
-        const int kk = (stage - wave) / NW;
+        const int kk = (stage - first_stage) / SSTEP;
         const int blk = kk >> 6;
         if (blk != pg_blk) {
-            const int st = wave + NW * (64 * blk + lane);
+            const int st = first_stage + SSTEP * (64 * blk + lane);
             pg = st < nstages ? checked_page(table[(t0 + st * U) >> 4], a.num_pages) : 0;
             pg_blk = blk;
         }
@@ -381,18 +392,41 @@ __global__ __launch_bounds__(64 * head_rows_waves(KT)) void partial_valu_heads(c
     };
 
     u32x4 ka[U], va[U], kb2[U], vb2[U];
-    int stage = wave;
+    int stage = first_stage;
     if (stage < nstages) load(stage, ka, va);
     while (stage < nstages) {
-        int nxt = stage + NW;
+        int nxt = stage + SSTEP;
         if (nxt < nstages) load(nxt, kb2, vb2);
         compute(stage, ka, va);
         stage = nxt;
         if (stage >= nstages) break;
-        nxt = stage + NW;
+        nxt = stage + SSTEP;
         if (nxt < nstages) load(nxt, ka, va);
         compute(stage, kb2, vb2);
         stage = nxt;
+    }
+
+    if constexpr (WH) {
+        // Each wave holds whole heads: lane (r, c) writes its slice of head
+        // g's outputs; every lane of a row holds the same m and l.
+        const float v_sc = head_scale(a.v_scale, g);
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const int64_t slot = ((int64_t)b * hq + g * G + j) * s_max + s;
+#pragma unroll
+            for (int e = 0; e < EPL; e += 4)
+                *reinterpret_cast<float4*>(ws_o + slot * D + c * EPL + e) =
+                    make_float4(o[j][e] * v_sc, o[j][e + 1] * v_sc, o[j][e + 2] * v_sc, o[j][e + 3] * v_sc);
+            if (c == 0) {
+                ws_ml[slot * 2] = m[j] * kLn2;
+                ws_ml[slot * 2 + 1] = l[j];
+            }
+        }
+        if (a.counters) {
+            __shared__ float sm_red[NW * 4 * D];
+            fused_merge<D, 4, NW>(a, b, (wu.L + chunk - 1) / chunk, wu.g * HPW, HPW, HPW * G, 1, sm_red);
+        }
+        return;
     }
 
     // Merge the waves through LDS (every lane of a row holds the same m, l).
@@ -471,24 +505,37 @@ hipError_t launch_partial_valu(int D, int G, bool paged, const PartialArgs& a, d
     return D == 64 ? launch_tokens_d<64>(G, paged, a, grid, st) : launch_tokens_d<128>(G, paged, a, grid, st);
 }
 
-template <int D, int G>
+template <int D, int G, bool WH>
 hipError_t launch_heads_g(bool paged, const PartialArgs& a, dim3 grid, hipStream_t st) {
     // Paged splits that start on page boundaries read their page indices 64 at a time.
     const int mode = !paged ? 0 : ((a.chunk % 16 == 0) && (16 % kUnroll == 0)) ? 2 : 1;
     return with_types(a, [&]<int KT, int QT>() {
         if (mode == 0)
-            hipLaunchKernelGGL((partial_valu_heads<D, G, KT, QT, 0>), grid, dim3(64 * head_rows_waves(KT)), 0, st, a);
+            hipLaunchKernelGGL((partial_valu_heads<D, G, KT, QT, 0, WH>), grid, dim3(64 * head_rows_waves(KT)), 0, st,
+                               a);
         else if (mode == 1)
-            hipLaunchKernelGGL((partial_valu_heads<D, G, KT, QT, 1>), grid, dim3(64 * head_rows_waves(KT)), 0, st, a);
+            hipLaunchKernelGGL((partial_valu_heads<D, G, KT, QT, 1, WH>), grid, dim3(64 * head_rows_waves(KT)), 0, st,
+                               a);
         else
-            hipLaunchKernelGGL((partial_valu_heads<D, G, KT, QT, 2>), grid, dim3(64 * head_rows_waves(KT)), 0, st, a);
+            hipLaunchKernelGGL((partial_valu_heads<D, G, KT, QT, 2, WH>), grid, dim3(64 * head_rows_waves(KT)), 0, st,
+                               a);
         return hipGetLastError();
     });
 }
 
+template <bool WH>
+hipError_t launch_heads(int D, int G, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st) {
+    if (D == 64)
+        return G == 1 ? launch_heads_g<64, 1, WH>(paged, a, grid, st) : launch_heads_g<64, 2, WH>(paged, a, grid, st);
+    return G == 1 ? launch_heads_g<128, 1, WH>(paged, a, grid, st) : launch_heads_g<128, 2, WH>(paged, a, grid, st);
+}
+
 hipError_t launch_partial_valu_heads(int D, int G, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st) {
-    if (D == 64) return G == 1 ? launch_heads_g<64, 1>(paged, a, grid, st) : launch_heads_g<64, 2>(paged, a, grid, st);
-    return G == 1 ? launch_heads_g<128, 1>(paged, a, grid, st) : launch_heads_g<128, 2>(paged, a, grid, st);
+    return launch_heads<false>(D, G, paged, a, grid, st);
+}
+
+hipError_t launch_partial_valu_head_cols(int D, int G, bool paged, const PartialArgs& a, dim3 grid, hipStream_t st) {
+    return launch_heads<true>(D, G, paged, a, grid, st);
 }
 
 }  // namespace fdk

@@ -1,8 +1,9 @@
-// HBM probes: a streaming read and a plain copy (see include/fd_probe.h).
-// A fixed grid of FD_PROBE_SINK_FLOATS work-groups of 256 threads; each
-// work-group streams one contiguous slice with non-temporal 16-byte loads,
-// eight in flight per thread (the fastest of the read patterns measured on
-// MI355X: about 7.1 TB/s on a 2 GiB buffer).
+// HBM probes (see include/fd_probe.h): a streaming read, a read of two
+// row-major buffers in the decode kernels' pattern, and a plain copy.
+// The streaming read: a fixed grid of FD_PROBE_SINK_FLOATS work-groups of 256
+// threads; each work-group streams one contiguous slice with non-temporal
+// 16-byte loads, eight in flight per thread (measured on MI355X over a 1 GiB
+// K and a 1 GiB V buffer, one after the other: about 6.5 TB/s).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -44,6 +45,61 @@ __global__ __launch_bounds__(kThreads) void read_kernel(const u32x4* __restrict_
     if (threadIdx.x == 0) sink[blockIdx.x] = (float)(red[0] & 0xffffu);
 }
 
+// Two buffers a and b of `rows` rows of `row_bytes` bytes, read the way the
+// decode kernels read a token-major K and V cache: one work-group of eight
+// waves per (chunk of chunk_rows rows, column block of block_bytes), column
+// blocks fastest; every wave instruction reads 1 KB of one row (16 bytes per
+// lane), and a stage is 4 rows of a and 4 of b, the next stage's eight loads
+// in flight while the current one is consumed. ACROSS = false: the waves take
+// stages w, w + 8, ... of the chunk in a 1 KB column block (the head-rows
+// kernel); ACROSS = true: wave w takes every stage of column w of an 8 KB
+// block (the head-columns kernel). Rows past the chunk re-read its last row.
+constexpr int kRowWaves = 8;
+template <bool ACROSS>
+__global__ __launch_bounds__(64 * kRowWaves) void read_rows_kernel(const uint8_t* __restrict__ a,
+                                                                   const uint8_t* __restrict__ b, int64_t rows,
+                                                                   int row_bytes, int block_bytes, int chunk_rows,
+                                                                   float* __restrict__ sink) {
+    const int nblk = row_bytes / block_bytes;
+    const int blk = blockIdx.x % nblk;
+    const int64_t r0 = (int64_t)(blockIdx.x / nblk) * chunk_rows;
+    const int64_t r1 = r0 + chunk_rows < rows ? r0 + chunk_rows : rows;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t col = (int64_t)blk * block_bytes + (ACROSS ? wave * 1024 : 0) + lane * 16;
+    const int nst = (int)((r1 - r0 + 3) / 4);
+    const int step = ACROSS ? 1 : kRowWaves;
+    auto load = [&](int st, u32x4* x) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            int64_t r = r0 + 4 * st + u;
+            r = r < r1 ? r : r1 - 1;
+            x[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a + r * row_bytes + col));
+            x[4 + u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(b + r * row_bytes + col));
+        }
+    };
+    uint32_t acc = 0;
+    auto use = [&](const u32x4* x) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc ^= x[u].x ^ x[u].y ^ x[u].z ^ x[u].w;
+    };
+    u32x4 x[8], y[8];
+    int st = ACROSS ? 0 : wave;
+    if (st < nst) load(st, x);
+    while (st < nst) {
+        if (st + step < nst) load(st + step, y);
+        use(x);
+        st += step;
+        if (st >= nst) break;
+        if (st + step < nst) load(st + step, x);
+        use(y);
+        st += step;
+    }
+    // A store the compiler cannot rule out keeps the loads; it practically
+    // never happens.
+    if (acc == 0x9e3779b9u) sink[blockIdx.x % FD_PROBE_SINK_FLOATS] = (float)threadIdx.x;
+}
+
 __global__ __launch_bounds__(kThreads) void copy_kernel(u32x4* __restrict__ dst, const u32x4* __restrict__ src,
                                                         uint64_t n) {
     const uint64_t stride = (uint64_t)gridDim.x * kThreads;
@@ -65,6 +121,34 @@ fd_status fd_probe_read(const void* src, size_t bytes, float* sink, void* stream
                        (uint64_t)(bytes / 16), sink);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(FD_ERR_HIP, "probe_read launch: %s", hipGetErrorString(e));
+    return FD_OK;
+}
+
+fd_status fd_probe_read_rows(const void* a, const void* b, int64_t rows, int32_t row_bytes, int32_t block_bytes,
+                             int32_t chunk_rows, int32_t waves_across, float* sink, void* stream) {
+    clear_error();
+    if (!a || !b || !sink || ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b)) & 15))
+        return fail(FD_ERR_INVALID_ARGUMENT, "probe_read_rows needs 16-byte aligned a, b and a sink");
+    if (rows < 1 || chunk_rows < 1 || row_bytes < 1024 || row_bytes % 1024)
+        return fail(FD_ERR_INVALID_ARGUMENT, "probe_read_rows: rows %lld, chunk_rows %d, row_bytes %d (a multiple "
+                    "of 1024)", (long long)rows, chunk_rows, row_bytes);
+    const int32_t want_block = waves_across ? 1024 * fdp::kRowWaves : 1024;
+    if (block_bytes != want_block || row_bytes % block_bytes)
+        return fail(FD_ERR_INVALID_ARGUMENT, "probe_read_rows: block_bytes must be %d and divide row_bytes %d",
+                    want_block, row_bytes);
+    const int64_t wgs = (rows + chunk_rows - 1) / chunk_rows * (row_bytes / block_bytes);
+    if (wgs > INT32_MAX) return fail(FD_ERR_INVALID_ARGUMENT, "probe_read_rows: too many work-groups");
+    const uint8_t* pa = static_cast<const uint8_t*>(a);
+    const uint8_t* pb = static_cast<const uint8_t*>(b);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (waves_across)
+        hipLaunchKernelGGL(fdp::read_rows_kernel<true>, dim3((uint32_t)wgs), dim3(64 * fdp::kRowWaves), 0, hs, pa,
+                           pb, rows, row_bytes, block_bytes, chunk_rows, sink);
+    else
+        hipLaunchKernelGGL(fdp::read_rows_kernel<false>, dim3((uint32_t)wgs), dim3(64 * fdp::kRowWaves), 0, hs, pa,
+                           pb, rows, row_bytes, block_bytes, chunk_rows, sink);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(FD_ERR_HIP, "probe_read_rows launch: %s", hipGetErrorString(e));
     return FD_OK;
 }
 

@@ -44,6 +44,14 @@ def test_probe_calls_validate_before_launching():
     assert lib.fd_probe_read(fake, 24, fake, None) == fd.FD_ERR_INVALID_ARGUMENT
     assert lib.fd_probe_copy(fake, ctypes.c_void_p(0x10010), 64, None) == fd.FD_ERR_INVALID_ARGUMENT  # overlap
     assert lib.fd_probe_copy(fake, ctypes.c_void_p(0x10008), 16, None) == fd.FD_ERR_INVALID_ARGUMENT  # misaligned
+    # row probe: 1 KB blocks with the waves along the rows, 8 KB blocks with the waves across
+    rp = lib.fd_probe_read_rows
+    assert rp(fake, fake, 16, 8192, 4096, 64, 0, fake, None) == fd.FD_ERR_INVALID_ARGUMENT   # block size
+    assert rp(fake, fake, 16, 8192, 1024, 64, 1, fake, None) == fd.FD_ERR_INVALID_ARGUMENT   # block size
+    assert rp(fake, fake, 16, 1536, 1024, 64, 0, fake, None) == fd.FD_ERR_INVALID_ARGUMENT   # row not whole KB
+    assert rp(fake, fake, 16, 4096, 8192, 64, 1, fake, None) == fd.FD_ERR_INVALID_ARGUMENT   # block wider than row
+    assert rp(fake, fake, 0, 8192, 1024, 64, 0, fake, None) == fd.FD_ERR_INVALID_ARGUMENT    # no rows
+    assert rp(fake, ctypes.c_void_p(0x10008), 16, 8192, 1024, 64, 0, fake, None) == fd.FD_ERR_INVALID_ARGUMENT
 
 
 def test_status_strings():
@@ -61,6 +69,20 @@ def prob(**kw):
 
 def ceil_div(a, b):
     return -(-a // b)
+
+
+def mfma_kernel(hq, hkv, q_len=1):
+    """The matrix-core form the planner picks: each wave owning a (KV head,
+    column tile) (kernel 4) when the column tiles divide the four waves of a
+    work-group and the heads fill them, else kernel 1."""
+    nt = ceil_div(q_len * (hq // hkv), 16)
+    return 4 if nt in (1, 2, 4) and hkv % (4 // nt) == 0 else 1
+
+
+def mfma_work_groups(hq, hkv, q_len, kernel):
+    """Work-groups per split (or balanced work item) of a matrix-core kernel."""
+    nt = ceil_div(q_len * (hq // hkv), 16)
+    return hkv * nt // 4 if kernel == 4 else hkv * nt
 
 
 def workspace_bytes(B, rows, hkv, S, d=128):
@@ -87,7 +109,7 @@ def test_planner_properties(hq, hkv, lens, monkeypatch):
     assert C % 64 == 0 and C >= 256 or C == max(lens)
     splits = [ceil_div(L, C) for L in lens]
     assert plan.max_splits == max(splits) and plan.total_splits == sum(splits)
-    assert plan.total_tokens == sum(lens) and plan.num_cus == 256 and plan.partial_kernel in (0, 1, 2)
+    assert plan.total_tokens == sum(lens) and plan.num_cus == 256 and plan.partial_kernel in (0, 1, 2, 4)
     # every split non-empty, splits tile [0, L)
     for L, S in zip(lens, splits):
         assert (S - 1) * C < L <= S * C
@@ -112,7 +134,8 @@ def test_balanced_plan(hq, hkv, lens, page):
     p = prob(batch=len(lens), num_q_heads=hq, num_kv_heads=hkv, page_size=page,
              max_pages_per_seq=ceil_div(max(lens), 16) if page else 0)
     plan = fd.fd_plan_splits(p, lens, num_cus=256)
-    assert plan.partial_kernel == 1 and plan.split_mode == 1
+    assert plan.partial_kernel == mfma_kernel(hq, hkv) and plan.split_mode == 1
+    wg = mfma_work_groups(hq, hkv, 1, plan.partial_kernel)
     C = plan.chunk_tokens
     assert C % 16 == 0 and C >= 256
     P = C // 16
@@ -134,9 +157,11 @@ def test_balanced_plan(hq, hkv, lens, page):
             per_item[t // P] += 1
         U += SHARE_COST + n
     assert all(c == P for c in per_item[:-1]) and 0 < per_item[-1] <= P
-    # about two work-groups per compute unit for a 16-bit cache (one round)
-    if positions * hkv >= 256 * 2 * 16:
-        assert 256 * 2 - hkv <= plan.total_splits * hkv <= 256 * 2 + hkv
+    # about two work-groups per compute unit for a 16-bit cache (one round):
+    # P = ceil(positions * wg / 512) tiles, so the items fall short of 512 / wg
+    # by at most the fraction 1 / P that the ceiling adds, plus one item
+    if positions * wg >= 256 * 2 * 16:
+        assert 256 * 2 * (P - 1) / P - wg <= plan.total_splits * wg <= 256 * 2 + wg
     assert plan.workspace_bytes == workspace_bytes(len(lens), hq, hkv, plan.max_splits)
 
 
@@ -146,8 +171,10 @@ def test_balanced_plan_fp8_aims_at_three_per_cu():
     lens = [2915, 4487, 5931, 8309, 8336, 8684, 8905, 10375] * 2
     p = prob(batch=len(lens), num_q_heads=32, num_kv_heads=8, kv_dtype=torch.float8_e4m3fn, q_dtype=torch.bfloat16)
     plan = fd.fd_plan_splits(p, lens, num_cus=256)
-    assert plan.split_mode == 1
-    assert 256 * 3 - 8 <= plan.total_splits * 8 <= 256 * 3 + 8
+    assert plan.split_mode == 1 and plan.partial_kernel == 4
+    wg = mfma_work_groups(32, 8, 1, 4)  # two work-groups of four KV heads per item
+    P = plan.chunk_tokens // 16
+    assert 256 * 3 * (P - 1) / P - wg <= plan.total_splits * wg <= 256 * 3 + wg
 
 
 def test_balanced_plan_choice(monkeypatch):
@@ -161,7 +188,7 @@ def test_balanced_plan_choice(monkeypatch):
     assert fd.fd_plan_splits(prob(batch=4), ragged, num_cus=256).split_mode == 0    # MHA: vector kernels
     for ql in (2, 4, 16):                                                           # 8, 16 and 64 query rows
         plan = fd.fd_plan_splits(prob(batch=4, num_q_heads=32, num_kv_heads=8, q_len=ql), ragged, num_cus=256)
-        assert plan.split_mode == 1 and plan.partial_kernel == 1
+        assert plan.split_mode == 1 and plan.partial_kernel == mfma_kernel(32, 8, ql)
     # past the batch bound (the combine walks the lengths before its sequence) the chunks stay per sequence
     assert fd.fd_plan_splits(prob(batch=4096, num_q_heads=32, num_kv_heads=8), [1, 2] * 2048,
                              num_cus=256).split_mode == 1
@@ -319,8 +346,8 @@ def test_one_shot_without_gpu_reports_hip_error():
 
 
 @pytest.mark.parametrize("hq,hkv,d,expect", [
-    (32, 32, 128, 2), (32, 8, 128, 1), (64, 8, 128, 1), (16, 8, 128, 2), (32, 8, 64, 0), (8, 8, 64, 2),
-    (4, 4, 64, 0), (6, 6, 128, 0), (4, 2, 128, 0)])
+    (32, 32, 128, 2), (32, 8, 128, 4), (64, 8, 128, 4), (16, 2, 128, 1), (16, 8, 128, 2), (32, 8, 64, 0),
+    (8, 8, 64, 2), (4, 4, 64, 0), (6, 6, 128, 0), (4, 2, 128, 0)])
 def test_planner_picks_the_partial_kernel(hq, hkv, d, expect, monkeypatch):
     monkeypatch.delenv("FD_PARTIAL_KERNEL", raising=False)
     mk = lambda: fd.fd_plan_splits(prob(num_q_heads=hq, num_kv_heads=hkv, head_dim=d), [500000], num_cus=256)
@@ -352,16 +379,19 @@ def test_multi_query_problems():
     (one work-group per 16 query rows of a KV head, so fewer splits fill the
     chip as the rows grow)."""
     plan = fd.fd_plan_splits(prob(num_q_heads=32, num_kv_heads=32, q_len=4), [131072], num_cus=256)
-    assert plan.partial_kernel == 1
+    assert plan.partial_kernel == 4
     assert plan.workspace_bytes == workspace_bytes(1, 4 * 32, 32, plan.max_splits)
-    assert fd.fd_plan_splits(prob(num_q_heads=64, num_kv_heads=8, q_len=2), [1000], num_cus=256).partial_kernel == 1
+    assert fd.fd_plan_splits(prob(num_q_heads=64, num_kv_heads=8, q_len=2), [1000], num_cus=256).partial_kernel == 4
     splits = {}
     for ql in (2, 4, 8):  # 16, 32 and 64 query rows per KV head
         plan = fd.fd_plan_splits(prob(num_q_heads=64, num_kv_heads=8, q_len=ql), [131072], num_cus=256)
-        assert plan.partial_kernel == 1
+        assert plan.partial_kernel == 4
         splits[ql] = plan.max_splits
     assert splits[2] >= splits[4] >= splits[8]
     assert fd.fd_plan_splits(prob(num_q_heads=32, num_kv_heads=32, q_len=64), [1000],
+                             num_cus=256).partial_kernel == 4
+    # 40 query rows (three column tiles) keep the kernel with one work-group per column tile
+    assert fd.fd_plan_splits(prob(num_q_heads=16, num_kv_heads=16, q_len=40), [1000],
                              num_cus=256).partial_kernel == 1
     for kw, lens, status in [
         (dict(head_dim=64, q_len=2), [100], fd.FD_ERR_UNSUPPORTED),
@@ -387,7 +417,7 @@ def test_fp8_problems(monkeypatch):
     plan = fd.fd_plan_splits(p, [131072], num_cus=256)
     assert plan.partial_kernel == 2
     assert fd.fd_plan_splits(prob(kv_dtype=f8, num_kv_heads=8, num_q_heads=32), [500000],
-                             num_cus=256).partial_kernel == 1
+                             num_cus=256).partial_kernel == 4
     # d = 64: 16 heads per load; 8 KV heads cannot fill a head-rows wave
     assert fd.fd_plan_splits(prob(kv_dtype=f8, num_q_heads=8, num_kv_heads=8, head_dim=64), [500000],
                              num_cus=256).partial_kernel == 0
@@ -489,3 +519,70 @@ def test_fused_calls_validate_before_launching():
     assert lib.fd_workspace_init(ctypes.byref(p), ctypes.byref(plan), None, need, None) == fd.FD_ERR_INVALID_ARGUMENT
     assert lib.fd_workspace_init(ctypes.byref(p), ctypes.byref(plan), fake, need - 16, None) == \
         fd.FD_ERR_WORKSPACE_TOO_SMALL
+
+
+@pytest.mark.parametrize("hq,hkv,d,f8,k3,k4", [
+    # (Hq, Hkv, d, FP8 cache, head columns applies, matrix cores with waves owning heads applies)
+    (32, 32, 128, False, True, False),   # 4 heads per wave x 8 waves = 32
+    (16, 16, 128, False, False, False),  # 16 heads: not a multiple of 32
+    (64, 64, 64, False, True, False),    # d = 64: 8 heads per wave x 8 waves = 64
+    (32, 32, 128, True, True, False),    # FP8: 8 heads per wave x 4 waves = 32
+    (32, 8, 128, False, False, True),    # G = 4: four heads per work-group
+    (64, 8, 128, False, False, True),    # G = 8
+    (8, 2, 128, False, False, False),    # two KV heads cannot fill four waves
+    (32, 8, 64, False, False, False),    # no matrix-core form at d = 64
+])
+def test_head_columns_and_mfma_heads_applicability(hq, hkv, d, f8, k3, k4, monkeypatch):
+    """Kernels 3 (head columns) and 4 (matrix cores, each wave owning a head)
+    are chosen when forced and they cover the problem; otherwise the planner
+    keeps its own choice."""
+    import torch
+    kw = dict(num_q_heads=hq, num_kv_heads=hkv, head_dim=d)
+    if f8:
+        kw.update(kv_dtype=torch.float8_e4m3fn, q_dtype=torch.bfloat16)
+    monkeypatch.delenv("FD_PARTIAL_KERNEL", raising=False)
+    base = fd.fd_plan_splits(prob(**kw), [300000], num_cus=256).partial_kernel
+    monkeypatch.setenv("FD_PARTIAL_KERNEL", "3")
+    assert fd.fd_plan_splits(prob(**kw), [300000], num_cus=256).partial_kernel == (3 if k3 else base)
+    monkeypatch.setenv("FD_PARTIAL_KERNEL", "4")
+    assert fd.fd_plan_splits(prob(**kw), [300000], num_cus=256).partial_kernel == (4 if k4 else base)
+
+
+def test_mfma_heads_work_items_and_column_tiles(monkeypatch):
+    """Kernel 4 puts 4 / NT KV heads in a work-group (NT column tiles of 16
+    query rows each), so a split of Hkv heads takes Hkv * NT / 4 work-groups,
+    and the balanced list sizes its items for that count."""
+    monkeypatch.setenv("FD_PARTIAL_KERNEL", "4")
+    lens = [3000, 700, 12000, 64]
+    for ql, nt in ((1, 1), (2, 1), (4, 2), (8, 4)):
+        p = prob(batch=4, num_q_heads=64, num_kv_heads=8, q_len=ql)
+        plan = fd.fd_plan_splits(p, lens, num_cus=256)
+        assert plan.partial_kernel == 4 and plan.split_mode == 1
+        per_split = 8 // (4 // nt)
+        positions = sum(-(-L // 16) + 4 for L in lens)
+        P = plan.chunk_tokens // 16
+        assert P == max(16, -(-positions * per_split // 512))
+        assert plan.total_splits == -(-positions // P)
+    # three column tiles (40 query rows) do not divide four waves: kernel 1 stays
+    p = prob(batch=1, num_q_heads=16, num_kv_heads=16, q_len=40)
+    assert fd.fd_plan_splits(p, [5000], num_cus=256).partial_kernel == 1
+
+
+def test_plans_naming_kernels_that_do_not_apply_are_refused():
+    """A plan that names kernel 3 or 4 for a problem they do not cover is an
+    argument error, before anything is launched."""
+    lib = fd.load_library()
+    fake = ctypes.c_void_p(0x10000)
+    for kw, kernel in ((dict(num_q_heads=16, num_kv_heads=16), 3), (dict(num_q_heads=8, num_kv_heads=2), 4),
+                       (dict(num_q_heads=32, num_kv_heads=32), 4), (dict(num_q_heads=32, num_kv_heads=8), 3)):
+        p = prob(**kw)
+        plan = fd.fd_plan_splits(p, [4096], num_cus=256)
+        plan.partial_kernel = kernel
+        plan.split_mode = 0
+        st = lib.fd_decode_partial(ctypes.byref(p), ctypes.byref(plan), fake, fake, fake, None, fake, fake,
+                                   plan.workspace_bytes, None)
+        assert st == fd.FD_ERR_INVALID_ARGUMENT, (kw, kernel)
+        plan.partial_kernel = 5
+        st = lib.fd_decode_partial(ctypes.byref(p), ctypes.byref(plan), fake, fake, fake, None, fake, fake,
+                                   plan.workspace_bytes, None)
+        assert st == fd.FD_ERR_INVALID_ARGUMENT

@@ -201,9 +201,13 @@ def _random_case(seed):
 
 
 @pytest.mark.parametrize("seed", range(1650, 1662))
-def test_balanced_random_ragged_batches(fd, seed):
+def test_balanced_random_ragged_batches(fd, monkeypatch, seed):
     """Seeded random ragged batches on the balanced list against the oracle,
-    every query row of a sampled set of (sequence, head) pairs."""
+    every query row of a sampled set of (sequence, head) pairs. Odd seeds
+    force the matrix-core kernel with one work-group per column tile (kernel
+    1); even seeds take the planner's choice."""
+    if seed % 2:
+        monkeypatch.setenv("FD_PARTIAL_KERNEL", "1")
     wl = _random_case(seed)
     res = _run(fd, wl)
     assert res.plan.split_mode == 1, res.plan.as_dict()
@@ -270,7 +274,7 @@ def test_balanced_upper_bound_plan_multi_query(fd):
     prob = fd.make_problem(batch=wl.batch, num_q_heads=32, num_kv_heads=8, head_dim=128, kv_dtype=torch.bfloat16,
                            scale=wl.scale, page_size=16, max_pages_per_seq=wl.max_pages_per_seq, q_len=4)
     plan = fd.fd_plan_splits(prob, final)
-    assert plan.split_mode == 1 and plan.partial_kernel == 1
+    assert plan.split_mode == 1 and plan.partial_kernel in (1, 4)
     ws = torch.empty(-(-plan.workspace_bytes // 4), dtype=torch.float32, device=dev)
     out = torch.empty(tuple(wl.q.shape), dtype=torch.float32, device=dev)
     lse = torch.empty(tuple(wl.q.shape[:-1]), dtype=torch.float32, device=dev)

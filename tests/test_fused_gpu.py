@@ -104,10 +104,12 @@ def test_fused_matches_two_launches_and_oracle(fd, case):
     parity(outs[-1][0], outs[-1][1], ref_out, ref_lse, what=f"fused {name}")
 
 
-@pytest.mark.parametrize("kernel", [0, 1, 2])
+@pytest.mark.parametrize("kernel", [0, 1, 2, 3, 4])
 def test_fused_each_partial_kernel_and_output_type(fd, monkeypatch, kernel):
     monkeypatch.setenv("FD_PARTIAL_KERNEL", str(kernel))
-    wl = make_workload(name="fk", batch=3, num_q_heads=16, num_kv_heads=8, head_dim=128, seq_lens=[5000, 17, 2300],
+    # head columns (3) need a multiple of 32 KV heads at d = 128
+    hq, hkv = (64, 32) if kernel == 3 else (16, 8)
+    wl = make_workload(name="fk", batch=3, num_q_heads=hq, num_kv_heads=hkv, head_dim=128, seq_lens=[5000, 17, 2300],
                        dtype=torch.bfloat16, seed=1510)
     for od in (torch.float32, torch.bfloat16):
         prob, plan, ws, t, shape = _setup(fd, wl, num_splits=0, out_dtype=od)
@@ -115,7 +117,10 @@ def test_fused_each_partial_kernel_and_output_type(fd, monkeypatch, kernel):
         fused = _fused(fd, prob, plan, ws, t, shape, od)
         two = _two_launch(fd, prob, plan, t, shape, od)
         torch.cuda.synchronize()
-        assert torch.allclose(fused[0].float(), two[0].float(), rtol=1e-6, atol=1e-7)
+        # the fused merge and the combine add the S splits in different orders:
+        # fp32 sums of S terms that differ by up to about S rounding steps
+        rtol = max(1e-6, plan.max_splits * 2.0 ** -23)
+        assert torch.allclose(fused[0].float(), two[0].float(), rtol=rtol, atol=1e-7)
         assert torch.allclose(fused[1], two[1], rtol=0, atol=1e-6)
 
 

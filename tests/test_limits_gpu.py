@@ -41,7 +41,7 @@ def test_thousands_of_tiny_paged_sequences(fd):
     parity(res.out, res.lse, ref_out, ref_lse, what="4096 tiny paged sequences (400 sampled pairs)")
 
 
-@pytest.mark.parametrize("kernel", [0, 1])
+@pytest.mark.parametrize("kernel", [0, 1, 4])
 def test_many_query_heads(fd, monkeypatch, kernel):
     """128 query heads over 16 KV heads (group 8)."""
     monkeypatch.setenv("FD_PARTIAL_KERNEL", str(kernel))
@@ -66,7 +66,7 @@ def test_lengths_around_page_and_chunk_edges(fd, L):
             parity(res.out, res.lse, ref_out, ref_lse, what=f"L={L} paged={w.paged} splits={splits}")
 
 
-@pytest.mark.parametrize("kernel", [0, 1, 2])
+@pytest.mark.parametrize("kernel", [0, 1, 2, 4])
 def test_out_of_pool_page_indices_read_page_zero(fd, monkeypatch, kernel):
     """With the pool size known (the binding passes it), a table entry outside
     [0, num_pages) reads page 0 instead of memory outside the pool: the result

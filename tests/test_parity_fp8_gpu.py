@@ -57,6 +57,7 @@ FP8_SHAPES = [
     (128, torch.float16, 16, 16, [70000], 0),
     (128, torch.bfloat16, 32, 8, [513, 1, 2500], 16),              # paged, matrix cores
     (128, torch.float16, 16, 8, [100, 4000, 33], 16),              # paged, G = 2
+    (128, torch.bfloat16, 32, 32, [40000, 77], 0),                 # 32 heads: head columns apply
 ]
 
 
@@ -72,8 +73,8 @@ def test_fp8_shapes_and_forced_splits(fd, shape, splits):
     parity(res.out, res.lse, ref_out, ref_lse, what=f"fp8 shape {shape} splits {splits}")
 
 
-@pytest.mark.parametrize("shape", [0, 1, 3, 4, 5, 6, 7])
-@pytest.mark.parametrize("kernel", [0, 1, 2])
+@pytest.mark.parametrize("shape", [0, 1, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("kernel", [0, 1, 2, 3, 4])
 def test_fp8_every_partial_kernel(fd, monkeypatch, shape, kernel):
     """Each partial kernel that covers a shape (the planner keeps its own
     choice when the forced one does not apply)."""
@@ -128,6 +129,6 @@ def test_fp8_multi_query(fd, case):
                                        head_dim=128, seq_lens=lens, dtype=qdt, seed=740 + hq, page_size=page,
                                        q_len=ql))
     res = run_fp8(fd, wl, num_splits=0)
-    assert res.plan.partial_kernel == 1
+    assert res.plan.partial_kernel in (1, 4)
     ref_out, ref_lse = reference_fp8(wl)
     parity(res.out, res.lse, ref_out, ref_lse, what=f"fp8 multi-query {hq}/{hkv} q_len {ql}")

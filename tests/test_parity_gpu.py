@@ -249,12 +249,15 @@ GQA_CASES = [
 ]
 
 
-@pytest.mark.parametrize("kernel", [0, 1])
+@pytest.mark.parametrize("kernel", [0, 1, 4])
 @pytest.mark.parametrize("case", range(len(GQA_CASES)))
 @pytest.mark.parametrize("splits", [0, 3])
 def test_gqa_partial_kernels_agree_with_oracle(fd, monkeypatch, kernel, case, splits):
-    """The vector-ALU (0) and MFMA (1) partial kernels on the same GQA inputs."""
+    """The vector-ALU (0) and both matrix-core (1: four waves share a head;
+    4: each wave owns a head) partial kernels on the same GQA inputs."""
     dt, hq, hkv, lens, page = GQA_CASES[case]
+    if kernel == 4 and hkv % 4:
+        pytest.skip("kernel 4 needs a multiple of four KV heads (one per wave)")
     monkeypatch.setenv("FD_PARTIAL_KERNEL", str(kernel))
     wl = make_workload(name=f"gqa{case}-k{kernel}", batch=len(lens), num_q_heads=hq, num_kv_heads=hkv,
                        head_dim=128, seq_lens=lens, dtype=dt, seed=300 + case, page_size=page)
@@ -264,14 +267,15 @@ def test_gqa_partial_kernels_agree_with_oracle(fd, monkeypatch, kernel, case, sp
     parity(res.out, res.lse, ref_out, ref_lse, what=f"gqa case {case} kernel {kernel} splits {splits}")
 
 
-def test_mfma_split_statistics_match_oracle(fd, monkeypatch):
-    monkeypatch.setenv("FD_PARTIAL_KERNEL", "1")
-    wl = make_workload(name="stats-mfma", batch=2, num_q_heads=16, num_kv_heads=2, head_dim=128,
+@pytest.mark.parametrize("kernel", [1, 4])
+def test_mfma_split_statistics_match_oracle(fd, monkeypatch, kernel):
+    monkeypatch.setenv("FD_PARTIAL_KERNEL", str(kernel))
+    wl = make_workload(name="stats-mfma", batch=2, num_q_heads=32, num_kv_heads=4, head_dim=128,
                        seq_lens=[1000, 257], dtype=torch.bfloat16, seed=6)
     res = run(fd, wl, num_splits=4)
-    assert res.plan.partial_kernel == 1
+    assert res.plan.partial_kernel == kernel
     C = res.plan.chunk_tokens
-    prob = fd.make_problem(batch=2, num_q_heads=16, num_kv_heads=2, head_dim=128, kv_dtype=torch.bfloat16)
+    prob = fd.make_problem(batch=2, num_q_heads=32, num_kv_heads=4, head_dim=128, kv_dtype=torch.bfloat16)
     O_s, m_s, l_s = (x.double().cpu().numpy() for x in fd.workspace_views(prob, res.plan, res.workspace))
     Oo, mo, lo = oracle.decode_partials(wl.q, wl.k, wl.v, wl.seq_lens, wl.scale, C)
     for b, L in enumerate(wl.lens):
@@ -282,7 +286,7 @@ def test_mfma_split_statistics_match_oracle(fd, monkeypatch):
         assert np.max(np.abs(O_s[b, :, :S] - Oo[b, :, :S])) <= 1e-5 * max(1.0, scale) * 8
 
 
-@pytest.mark.parametrize("kernel", [0, 1])
+@pytest.mark.parametrize("kernel", [0, 1, 4])
 @pytest.mark.parametrize("page", [0, 16])
 def test_large_batch_work_list(fd, monkeypatch, kernel, page):
     """More than 64 sequences: the work-list lookup scans the lengths in
@@ -290,7 +294,7 @@ def test_large_batch_work_list(fd, monkeypatch, kernel, page):
     monkeypatch.setenv("FD_PARTIAL_KERNEL", str(kernel))
     g = np.random.default_rng(77)
     lens = [int(x) for x in g.integers(1, 700, size=150)] + [64, 128, 1]
-    wl = make_workload(name=f"bigbatch-k{kernel}-p{page}", batch=len(lens), num_q_heads=8, num_kv_heads=2,
+    wl = make_workload(name=f"bigbatch-k{kernel}-p{page}", batch=len(lens), num_q_heads=16, num_kv_heads=4,
                        head_dim=128, seq_lens=lens, dtype=torch.bfloat16, seed=78, page_size=page)
     for splits in (0, 5):
         res = run(fd, wl, num_splits=splits)
@@ -305,16 +309,20 @@ MHA_CASES = [
     (64, torch.float16, 16, 16, [5, 999, 4096], 0),     # d = 64: 8 heads per load
     (128, torch.float16, 32, 32, [1500, 33], 16),       # paged
     (64, torch.bfloat16, 8, 8, [17, 260], 16),          # paged, d = 64
+    (64, torch.float16, 64, 64, [300, 2100], 0),        # d = 64, 64 heads: head columns apply
+    (128, torch.bfloat16, 64, 32, [900, 64, 1], 16),    # G = 2, 32 KV heads, paged: head columns apply
 ]
 
 
-@pytest.mark.parametrize("kernel", [0, 2])
+@pytest.mark.parametrize("kernel", [0, 2, 3])
 @pytest.mark.parametrize("case", range(len(MHA_CASES)))
 @pytest.mark.parametrize("splits", [0, 3, 7])
 def test_token_rows_and_head_rows_kernels_agree_with_oracle(fd, monkeypatch, kernel, case, splits):
-    """The two vector-ALU partial kernels on the same inputs; forced split
+    """The three vector-ALU partial kernels on the same inputs; forced split
     counts make paged splits start mid-page (per-token page lookups)."""
     d, dt, hq, hkv, lens, page = MHA_CASES[case]
+    if kernel == 3 and hkv % (8 * 64 // (d // 8)):
+        pytest.skip("head columns need a multiple of 8 waves x the heads of one load")
     monkeypatch.setenv("FD_PARTIAL_KERNEL", str(kernel))
     wl = make_workload(name=f"mha{case}-k{kernel}", batch=len(lens), num_q_heads=hq, num_kv_heads=hkv,
                        head_dim=d, seq_lens=lens, dtype=dt, seed=400 + case, page_size=page)
@@ -349,7 +357,7 @@ def test_multi_query_decode_matches_oracle(fd, case, splits):
     wl = make_workload(name=f"mq{case}", batch=len(lens), num_q_heads=hq, num_kv_heads=hkv, head_dim=128,
                        seq_lens=lens, dtype=dt, seed=500 + case, page_size=page, q_len=ql)
     res = run(fd, wl, num_splits=splits)
-    assert res.plan.partial_kernel == 1 and tuple(res.out.shape) == (len(lens), ql, hq, 128)
+    assert res.plan.partial_kernel in (1, 4) and tuple(res.out.shape) == (len(lens), ql, hq, 128)
     ref_out, ref_lse = oracle.decode_attention_multi(wl.q, wl.k, wl.v, wl.seq_lens, wl.scale, wl.block_table,
                                                      wl.page_size)
     parity(res.out, res.lse, ref_out, ref_lse, what=f"multi-query case {case} splits {splits}")
@@ -377,7 +385,7 @@ def test_multi_query_split_statistics_include_empty_splits(fd, hq, hkv, ql):
         assert np.allclose(O_s[b, :, :S], Oo[b, :, :S], rtol=1e-5, atol=1e-5)
 
 
-# ------------------------------------------------------- the three combine forms
+# ------------------------------------------------------- the four combine forms
 
 
 @pytest.mark.parametrize("case", [
@@ -389,11 +397,12 @@ def test_multi_query_split_statistics_include_empty_splits(fd, hq, hkv, ql):
     (128, torch.float16, 3, 3, [5000, 17, 900], 0, 1, torch.float32),                       # odd rows: no pairs
     (128, torch.float16, 3, 3, [1 + (i * 37) % 700 for i in range(1500)], 0, 1, torch.float32),  # 4500 odd rows
     (128, torch.bfloat16, 2, 2, [900, 17, 3000, 1, 64], 0, 1, torch.float32),      # 10 rows: a part-filled last group
+    (128, torch.float16, 4, 4, [600000, 3], 0, 1, torch.float32),                # hundreds of splits per row
 ])
 def test_combine_forms_agree(fd, monkeypatch, case):
-    """Four waves per (sequence, query row), one wave per row and two rows per
-    wave merge the same partials to the oracle's result; FD_COMBINE_FORM
-    forces each."""
+    """Four waves per (sequence, query row), one wave per row, two rows per
+    wave and sixteen waves per row merge the same partials to the oracle's
+    result; FD_COMBINE_FORM forces each."""
     d, dt, hq, hkv, lens, page, ql, od = case
     wl = make_workload(name="combine-forms", batch=len(lens), num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
                        seq_lens=lens, dtype=dt, seed=1700 + d + hq + ql, q_len=ql)
@@ -401,7 +410,7 @@ def test_combine_forms_agree(fd, monkeypatch, case):
         wl = to_paged(wl, 16)
     dev = to_dev(wl)
     outs = {}
-    for form in (0, 1, 2):
+    for form in (0, 1, 2, 3):
         monkeypatch.setenv("FD_COMBINE_FORM", str(form))
         res = run(fd, wl, num_splits=0, out_dtype=od, dev_tensors=dev)
         outs[form] = res
@@ -417,6 +426,6 @@ def test_combine_forms_agree(fd, monkeypatch, case):
         assert np.max(np.abs(o - ref_out)) <= O_MAX_ABS + rnd * np.abs(ref_out).max(), form
         assert np.max(np.abs(res.lse.double().cpu().numpy() - ref_lse)) <= LSE_ABS, form
     # the same partials: the forms differ by fp32 summation order (and one output rounding)
-    for form in (1, 2):
+    for form in (1, 2, 3):
         diff = (outs[form].out.double() - outs[0].out.double()).abs().max().item()
         assert diff <= 1e-5 + 2 * rnd * float(outs[0].out.double().abs().max()), (form, diff)
