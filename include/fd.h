@@ -41,8 +41,10 @@
  * block_table, seq_lens_dev, out, lse and the workspace; host memory for
  * seq_lens_host and the structs). The library allocates no device memory,
  * never frees anything and keeps no state except a per-device cache of the
- * compute-unit count. It reads the inputs and writes only out, lse and the
- * workspace.
+ * compute-unit count and the fixed per-GPU buffer that
+ * fd_decode_attention_noalloc uses in place of a workspace (set aside when the
+ * library's code is loaded on a device). It reads the inputs and writes only
+ * out, lse and the workspace (or that buffer).
  *
  * Streams: `stream` is a hipStream_t passed as void* (NULL = the default
  * stream). Every call that takes one only enqueues work on it and returns;
@@ -292,6 +294,33 @@ fd_status fd_decode_attention_scaled(const fd_problem* problem,
                                      const int32_t* seq_lens_host, const int32_t* seq_lens_dev,
                                      void* out, float* lse,
                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of partials fd_decode_attention_noalloc can hold on each GPU (64 MiB). */
+#define FD_NOALLOC_WORKSPACE_BYTES ((size_t)64 << 20)
+
+/*
+ * fd_decode_attention_scaled without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. The partials go to a buffer the
+ * library holds in device memory, FD_NOALLOC_WORKSPACE_BYTES on every GPU it
+ * runs on, until the process ends; the call itself allocates and frees
+ * nothing. Same plan, kernels and results as fd_decode_attention_scaled
+ * (k_scale and v_scale NULL for a 16-bit cache without scales); the caller
+ * still passes the inputs and out / lse.
+ * Errors: FD_ERR_WORKSPACE_TOO_SMALL, having launched nothing, when the plan's
+ * workspace_bytes (fd_plan_splits) exceed FD_NOALLOC_WORKSPACE_BYTES; FD_ERR_HIP
+ * if the buffer's address cannot be found on the current device.
+ * Sharing: every call on one GPU uses that GPU's one buffer. Calls on one
+ * stream are ordered; calls that overlap on one GPU (two streams, or two host
+ * threads with different streams) race on it. Nothing in the buffer needs
+ * clearing: the partial kernel writes every slot the merge reads.
+ */
+fd_status fd_decode_attention_noalloc(const fd_problem* problem,
+                                      const void* q, const void* k, const void* v,
+                                      const float* k_scale, const float* v_scale,
+                                      const int32_t* block_table,
+                                      const int32_t* seq_lens_host, const int32_t* seq_lens_dev,
+                                      void* out, float* lse, void* stream);
 
 /*
  * Prefill attention (asynchronous on `stream`): every one of the q_len query

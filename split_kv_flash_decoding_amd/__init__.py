@@ -19,6 +19,7 @@ from ._capi import (  # noqa: F401
     FD_FP8_E4M3,
     FD_OK,
     LIB_PATH,
+    NOALLOC_WORKSPACE_BYTES,
     PROBE_SINK_FLOATS,
     DecodeResult,
     FdError,
@@ -31,6 +32,7 @@ from ._capi import (  # noqa: F401
     fd_append_kv,
     fd_combine,
     fd_decode_attention,
+    fd_decode_attention_noalloc,
     fd_decode_fused,
     fd_decode_partial,
     fd_plan_splits,

@@ -32,6 +32,7 @@ EXPORTED = (
     "fd_combine",
     "fd_decode_attention",
     "fd_decode_attention_scaled",
+    "fd_decode_attention_noalloc",
     "fd_append_kv",
     "fd_prefill_attention",
     "fd_decode_fused",
@@ -110,14 +111,15 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.fd_decode_partial_scaled.argtypes = [P, Pl, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.fd_decode_attention_scaled.argtypes = [P, vp, vp, vp, vp, vp, vp, i32p, vp, vp, f32p, vp,
                                                ctypes.c_size_t, vp]
+    lib.fd_decode_attention_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, i32p, vp, vp, f32p, vp]
     lib.fd_append_kv.argtypes = [P, ctypes.c_int32, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32,
                                  vp, vp, vp]
     lib.fd_prefill_attention.argtypes = [P, vp, vp, vp, vp, vp, vp, f32p, vp]
     lib.fd_decode_fused.argtypes = [P, Pl, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp, f32p, vp]
     lib.fd_workspace_init.argtypes = [P, Pl, vp, ctypes.c_size_t, vp]
     for name in ("fd_plan_splits", "fd_decode_partial", "fd_combine", "fd_decode_attention",
-                 "fd_decode_partial_scaled", "fd_decode_attention_scaled", "fd_append_kv",
-                 "fd_prefill_attention",
+                 "fd_decode_partial_scaled", "fd_decode_attention_scaled", "fd_decode_attention_noalloc",
+                 "fd_append_kv", "fd_prefill_attention",
                  "fd_decode_fused", "fd_workspace_init"):
         getattr(lib, name).restype = ctypes.c_int
     lib.fd_status_string.argtypes = [ctypes.c_int]
@@ -338,6 +340,24 @@ def fd_decode_attention(problem: FdProblem, q, k, v, block_table, seq_lens_host,
     _check(lib.fd_decode_attention(
         ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(block_table), arr, _ptr(seq_lens_dev),
         _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+NOALLOC_WORKSPACE_BYTES = 64 << 20  # FD_NOALLOC_WORKSPACE_BYTES
+
+
+def fd_decode_attention_noalloc(problem: FdProblem, q, k, v, block_table, seq_lens_host, seq_lens_dev, out, lse,
+                                stream=None, k_scale=None, v_scale=None) -> None:
+    """fd_decode_attention_noalloc: plan, partials and merge with the partials
+    in the library's fixed per-GPU buffer (no workspace argument, nothing
+    allocated). Calls that overlap on one GPU race on that buffer."""
+    arr, vals = _lens_array(seq_lens_host)
+    _check_tensors(problem, q, k, v, block_table, seq_lens_dev, sum(vals))
+    _check_out(problem, out, lse)
+    _check_scales(problem, k_scale, v_scale)
+    problem = _with_pool(problem, k)
+    _check(load_library().fd_decode_attention_noalloc(
+        ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(k_scale), _ptr(v_scale), _ptr(block_table), arr,
+        _ptr(seq_lens_dev), _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def fd_prefill_attention(problem: FdProblem, q, k, v, block_table, seq_lens_dev, out, lse=None,

@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "fd_device.h"
 
@@ -117,6 +118,36 @@ fd_status decode_partial(const fd_problem* p, const fd_plan* plan, const void* q
 __global__ void zero_u32(uint32_t* p, int64_t n) {
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
         p[i] = 0u;
+}
+
+// The partials of fd_decode_attention_noalloc: one copy per GPU, set aside
+// when the library's code is loaded on that device and held until the
+// process ends. Host code never uses this name as an address (on the host it
+// stands for the variable, not its device memory); scratch_address looks the
+// device address up.
+static __device__ __align__(256) uint8_t scratch[FD_NOALLOC_WORKSPACE_BYTES];
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+
+fd_status scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(FD_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= 64) return fail(FD_ERR_UNSUPPORTED, "device %d: the allocation-free call serves devices 0-63", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(FD_ERR_HIP, "address of the allocation-free workspace on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return FD_OK;
 }
 
 fd_status reject_fp8(const fd_problem* p, const char* call) {
@@ -237,6 +268,27 @@ fd_status fd_decode_attention(const fd_problem* p, const void* q, const void* k,
     if (st != FD_OK) return st;
     return fd_decode_attention_scaled(p, q, k, v, nullptr, nullptr, block_table, seq_lens_host, seq_lens_dev, out,
                                       lse, workspace, workspace_bytes_avail, stream);
+}
+
+fd_status fd_decode_attention_noalloc(const fd_problem* p, const void* q, const void* k, const void* v,
+                                      const float* k_scale, const float* v_scale, const int32_t* block_table,
+                                      const int32_t* seq_lens_host, const int32_t* seq_lens_dev, void* out,
+                                      float* lse, void* stream) {
+    fd_plan plan;
+    fd_status st = fd_plan_splits(p, seq_lens_host, 0, 0, &plan);
+    if (st != FD_OK) return st;
+    if (!out) return fail(FD_ERR_INVALID_ARGUMENT, "out must be non-NULL");
+    if (plan.workspace_bytes > FD_NOALLOC_WORKSPACE_BYTES)
+        return fail(FD_ERR_WORKSPACE_TOO_SMALL, "the plan needs %llu bytes of partials; the allocation-free call "
+                    "holds %zu per GPU (use fd_decode_attention_scaled with a workspace)",
+                    (unsigned long long)plan.workspace_bytes, FD_NOALLOC_WORKSPACE_BYTES);
+    void* ws = nullptr;
+    st = scratch_address(&ws);
+    if (st != FD_OK) return st;
+    st = fd_decode_partial_scaled(p, &plan, q, k, v, k_scale, v_scale, block_table, seq_lens_dev, ws,
+                                  FD_NOALLOC_WORKSPACE_BYTES, stream);
+    if (st != FD_OK) return st;
+    return fd_combine(p, &plan, seq_lens_dev, ws, FD_NOALLOC_WORKSPACE_BYTES, out, lse, stream);
 }
 
 fd_status fd_prefill_attention(const fd_problem* p, const void* q, const void* k, const void* v,
