@@ -261,7 +261,7 @@ fd_status fd_workspace_init(const fd_problem* problem, const fd_plan* plan, void
  * l = sum_s w_s l_s, out = sum_s w_s O_s / l and lse = M + ln l (the
  * cross-chunk reduce of capstone §2.3, by the two-block identity of §1.2
  * applied to every split). out: device [B, q_len, Hq, d] in out_dtype.
- * lse: device float32 [B, q_len, Hq], or NULL. Batches of 512 query rows or
+ * lse: device float32 [B, q_len, Hq], or NULL. Batches of 1024 query rows or
  * more (B * q_len * Hq) merge one row per wave, from 4096 rows two rows per
  * wave (when a sequence has an even number of rows), smaller batches with
  * four waves per row, or sixteen when the plan has 128 splits or more;

@@ -187,6 +187,24 @@ __device__ __forceinline__ float row_sum(float x) {
     return x;
 }
 
+// Max and sum over the four lane groups l, l ^ 16, l ^ 32 and l ^ 48 (every
+// lane receives the result), with gfx950's row swaps (v_permlane16_swap,
+// v_permlane32_swap: the odd 16- or 32-lane rows of one operand trade places
+// with the even rows of the other; given one value twice, each lane ends up
+// with its own value and its partner's) instead of two LDS shuffles.
+__device__ __forceinline__ float max_lane_groups(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_lane_groups(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Merge running statistics (m, l, o) with another set, all in log2 units.
 template <int N>
 __device__ __forceinline__ void merge_stats(float& m, float& l, float* o, float m2, float l2,

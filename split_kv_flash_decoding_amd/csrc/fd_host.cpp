@@ -259,7 +259,9 @@ fd_status fd_plan_splits(const fd_problem* p, const int32_t* lens, int32_t num_c
                 cc = std::max(cc, min_chunk);
                 return ceil_div(cc, kChunkGranule) * kChunkGranule;
             };
-            const int32_t wg_per_cu = env_int("FD_WG_PER_CU", 0);
+            int32_t wg_per_cu = env_int("FD_WG_PER_CU", 0);
+            if (wg_per_cu == 0 && kern == kPartialMfmaHeads && mfma_column_tiles(p) == 4)
+                wg_per_cu = kWideMultiQueryWgPerCu;
             if (wg_per_cu > 0) {
                 c = chunk_for(wg_per_cu);
             } else {
@@ -328,8 +330,10 @@ fd_status fd_plan_splits(const fd_problem* p, const int32_t* lens, int32_t num_c
             nmax = std::max(nmax, n);
         }
         const int32_t per_cu = env_int("FD_WG_PER_CU", 0) > 0 ? env_int("FD_WG_PER_CU", 0)
-                               : kv_elem_bytes(p) == 1                ? kBalancedWgPerCuFp8
-                                                                      : kBalancedWgPerCu16;
+                               : (kv_elem_bytes(p) == 1 ||
+                                  (kernel == kPartialMfmaHeads && mfma_column_tiles(p) == 4))
+                                   ? kBalancedWgPerCuFp8
+                                   : kBalancedWgPerCu16;
         const int64_t target = std::max<int64_t>(1, (int64_t)num_cus * per_cu);
         const int64_t P = std::max<int64_t>(ceil_div(positions * workgroups_per_split(p, kernel), target),
                                             kBalancedMinTiles);

@@ -29,6 +29,13 @@ constexpr int32_t kTileTokens = 16;
 constexpr int32_t kBalancedMinTiles = 16;
 constexpr int32_t kBalancedWgPerCu16 = 2;
 constexpr int32_t kBalancedWgPerCuFp8 = 3;
+// The matrix-core kernel with waves owning heads and four column tiles (49 to
+// 64 query rows per KV head) does four times the matrix work per byte of a
+// single tile: it wants a third work-group per compute unit, whatever the
+// split mode (measured on MI355X, same GPU: paged GQA with 8 query tokens
+// 492.8 -> 429.5 us, 128K-token MHA with 64 query tokens 458.3 -> 425.2 us;
+// two column tiles lose with it: 121.6 -> 149.1 us, 348.5 -> 412.7 us).
+constexpr int32_t kWideMultiQueryWgPerCu = 3;
 constexpr int32_t kBalancedMaxBatch = 4096;
 // List positions a sequence takes before its tiles in the balanced list: the
 // cost of starting a share (the pipeline's first loads, the wave merge and the
@@ -58,11 +65,13 @@ uint64_t workspace_bytes(const fd_problem* p, int32_t max_splits);
 // The combine's form: 0 four waves per (sequence, query row); 3 sixteen waves
 // per row, for those batches when rows have kCombineWideSplits splits or more;
 // 1 one wave per row, for batches of at least kCombinePerWaveRows rows
+// (measured on MI355X: 512 rows of up to 25 splits merge in 2.0-2.6 us with
+// four waves per row, 3.7-4.5 us with one)
 // (B * q_len * Hq), where four waves per row would take several rounds of the
 // chip's wave slots; 2 two rows per wave, from kCombineTwoRowRows rows when a
 // sequence has an even number of rows. FD_COMBINE_FORM=0/1/2/3 overrides (2
 // only with even rows per sequence).
-constexpr int64_t kCombinePerWaveRows = 512;
+constexpr int64_t kCombinePerWaveRows = 1024;
 constexpr int64_t kCombineTwoRowRows = 4096;
 constexpr int32_t kCombineWideSplits = 128;
 int32_t combine_form(const fd_problem* p, int32_t max_splits);

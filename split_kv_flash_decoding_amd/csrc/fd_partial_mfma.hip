@@ -28,7 +28,7 @@
 //     past head G-1). The result leaves lane l holding tokens 4g..4g+3 of
 //     head c;
 //   * online softmax per head, log2 domain: the tile max is reduced over the
-//     four lanes of a head (two shuffles); each lane keeps a partial running
+//     four lanes of a head (two row swaps); each lane keeps a partial running
 //     sum over its own tokens (summed at the end). The exponentials use a
 //     reference max that only moves when a tile's max exceeds it by more than
 //     8 (a wave-uniform branch), so probabilities stay <= 2^8 and the
@@ -38,7 +38,10 @@
 //     (p = hi + lo exactly to ~2^-17), so the 16-bit matrix product loses
 //     nothing the tolerance would see;
 //   * O^T [128 x 16 heads] += V^T [128 x 16 tokens] . P^T [16 tokens x 16]
-//     as eight 16x16x16 MFMAs per part. P^T is exactly the layout the score
+//     as eight 16x16x16 MFMAs per part, or (waves owning heads) for both
+//     parts at once as eight v_mfma_f32_16x16x32, whose 32-long contraction
+//     takes the tile's tokens twice (high parts, then low parts of P; the
+//     same V values twice). P^T is exactly the layout the score
 //     MFMA produced; V^T comes from the V tile staged in LDS (row-major,
 //     padded rows) and read back transposed with ds_read_b64_tr_b16, so
 //     every lane's output column is its own head and the per-head rescale
@@ -96,6 +99,9 @@ template <> struct Mfma<FD_F16> {
     static __device__ __forceinline__ f32x4_t pv(i16x4_t a, v4 b, f32x4_t c) {
         return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(v4, a), b, c, 0, 0, 0);
     }
+    static __device__ __forceinline__ f32x4_t pv2(u32x4 a, u32x4 b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8, a), __builtin_bit_cast(v8, b), c, 0, 0, 0);
+    }
     static __device__ __forceinline__ void split(const float* p, v4& hi, v4& lo) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -114,6 +120,9 @@ template <> struct Mfma<FD_BF16> {
     }
     static __device__ __forceinline__ f32x4_t pv(i16x4_t a, v4 b, f32x4_t c) {
         return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4, a), b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4_t pv2(u32x4 a, u32x4 b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8, a), __builtin_bit_cast(v8, b), c, 0, 0, 0);
     }
     static __device__ __forceinline__ void split(const float* p, v4& hi, v4& lo) {
 #pragma unroll
@@ -249,6 +258,12 @@ next_share:
     const int qi = (c0 + col) / G;
     const int qj = c0 + col - qi * G;
     const int lim = min(t1, wu.L - q_len + qi + 1);
+    // Tiles wholly below every active row's limit need no mask (all but the
+    // last tile or two of a share).
+    int lim_lo = col < nq ? lim : INT32_MAX;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) lim_lo = min(lim_lo, __shfl_xor(lim_lo, off));
+    lim_lo = uniform(lim_lo);
 
     const int32_t* table = PAGED ? block_table + (int64_t)b * max_pages : nullptr;
     const int row_bytes = hkv * kD * EB;
@@ -354,9 +369,15 @@ next_share:
                 hi[2 * w] = widen_fp8_pair<QT, false>(x[w + 2]);
                 hi[2 * w + 1] = widen_fp8_pair<QT, true>(x[w + 2]);
             }
+            // Lane lcol's 32 bytes are chunks 2 lcol and 2 lcol + 1 of the row.
+            // Lanes 4..7 of each eight store their high chunk first, so each
+            // store instruction's eight-lane groups cover 128 distinct bytes
+            // modulo 128 (with low chunks first everywhere, every bank is hit
+            // twice: measured 0.37 conflict cycles per LDS-active cycle).
             uint16_t* d = dst + (RPI * i + lrow) * kPitch + 16 * lcol;
-            *reinterpret_cast<u32x4*>(d) = lo;
-            *reinterpret_cast<u32x4*>(d + 8) = hi;
+            const bool hi_first = (lcol >> 2) & 1;
+            *reinterpret_cast<u32x4*>(d + (hi_first ? 8 : 0)) = hi_first ? hi : lo;
+            *reinterpret_cast<u32x4*>(d + (hi_first ? 0 : 8)) = hi_first ? lo : hi;
         } else {
             *reinterpret_cast<u32x4*>(dst + (RPI * i + lrow) * kPitch + 8 * lcol) = x;
         }
@@ -395,13 +416,20 @@ next_share:
 
         float p[4];
         float mx = neg_inf();
+        if (tt + kTile <= lim_lo) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            p[i] = (tt + 4 * grp + i < lim) ? sc[i] * qk_scale_log2 : neg_inf();
-            mx = fmaxf(mx, p[i]);
+            for (int i = 0; i < 4; ++i) {
+                p[i] = sc[i] * qk_scale_log2;
+                mx = fmaxf(mx, p[i]);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p[i] = (tt + 4 * grp + i < lim) ? sc[i] * qk_scale_log2 : neg_inf();
+                mx = fmaxf(mx, p[i]);
+            }
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = max_lane_groups(mx);
         m_true = fmaxf(m_true, mx);
         // Move the reference only when some head's scores outgrow it by 2^8.
         if (__ballot(mx > m_ref + 8.f)) {
@@ -428,10 +456,27 @@ next_share:
         // dims 16 jd + 4 j .. +4; the transposing read hands lane 16 g' + i
         // the dims-i column of rows 4 g' .. 4 g' + 3.
         const uint16_t* rd = my_sv + (4 * grp + ((lane >> 2) & 3)) * kPitch + 4 * (lane & 3);
+        if constexpr (WH) {
+            // Both parts in one double-rate product: the contraction runs over
+            // the tile's 16 tokens twice, slots 8 g .. 8 g + 3 of lane group g
+            // taking the high parts of its tokens 4 g .. 4 g + 3 and slots
+            // 8 g + 4 .. 8 g + 7 the low parts, so B = [hi, lo] and A holds the
+            // same four V values twice.
+            typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+            const u32x2_t hw = __builtin_bit_cast(u32x2_t, phi), lw = __builtin_bit_cast(u32x2_t, plo);
+            const u32x4 pb = {hw[0], hw[1], lw[0], lw[1]};
 #pragma unroll
-        for (int jd = 0; jd < 8; ++jd) {
-            const i16x4_t vt = lds_read_transposed(rd + 16 * jd);
-            acc[jd] = M::pv(vt, plo, M::pv(vt, phi, acc[jd]));
+            for (int jd = 0; jd < 8; ++jd) {
+                const u32x2_t vt = __builtin_bit_cast(u32x2_t, lds_read_transposed(rd + 16 * jd));
+                acc[jd] = M::pv2(u32x4{vt[0], vt[1], vt[0], vt[1]}, pb, acc[jd]);
+            }
+        } else {
+            // Two products (the other form's registers stay within 3 waves per SIMD).
+#pragma unroll
+            for (int jd = 0; jd < 8; ++jd) {
+                const i16x4_t vt = lds_read_transposed(rd + 16 * jd);
+                acc[jd] = M::pv(vt, plo, M::pv(vt, phi, acc[jd]));
+            }
         }
     };
 
@@ -502,8 +547,7 @@ next_share:
     }
 
     // Each head's sum is spread over the four lanes that hold it.
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
+    l_run = sum_lane_groups(l_run);
     // Express (O, l) relative to the true max (a factor in [2^-8, 1]).
     {
         const float mu = (m_true == neg_inf()) ? 0.f : m_true;
