@@ -56,12 +56,38 @@ APPEND_SOURCES = ("fd_api.hip", "fd_device.h", "fd_internal.h", "fd_append.hip")
 SOURCES = {"partial": PARTIAL_SOURCES, "prefill": PREFILL_SOURCES, "append": APPEND_SOURCES}
 
 
+def strip_comments(src: str) -> str:
+    """C/C++ source without its // and /* */ comments (string and character
+    literals kept), trailing blanks and blank lines, so that a comment-only
+    edit keeps the hash."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return "\n".join(l.rstrip() for l in "".join(out).splitlines() if l.strip())
+
+
 def kernel_source_hash(kernel: str = "partial") -> str:
-    """Hash of the timed kernel's sources (SOURCES[kernel])."""
+    """Hash of the timed kernel's sources (SOURCES[kernel]), comments stripped:
+    counters taken on a kernel stay current until its code changes."""
     h = hashlib.sha256()
     for name in SOURCES[kernel]:
-        with open(os.path.join(KERNEL_SOURCES, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(KERNEL_SOURCES, name), encoding="utf-8") as f:
+            h.update(name.encode() + strip_comments(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -20,8 +20,9 @@
 //     instruction covers four whole 256-byte token rows (loading K straight
 //     into the MFMA operand layout instead, 16 rows x 64 bytes per
 //     instruction, measured 5.3 TB/s against 6.5-7.1 TB/s for whole rows);
-//     both tiles are staged in LDS (rows padded to 288 bytes, so the column
-//     reads below are bank-conflict free);
+//     both tiles are staged in LDS (rows padded to 288 bytes; rocprofv3 counts
+//     no LDS bank-conflict cycles for these reads and stores on MI355X, 16-bit
+//     and FP8 caches alike, SQ_LDS_BANK_CONFLICT against SQ_LDS_IDX_ACTIVE);
 //   * scores: S^T[16 tokens x 16 heads] = K_tile [16 x 128] . Q^T [128 x 16]
 //     as four v_mfma_f32_16x16x32 (the A operand, K row c with 8 dims per
 //     lane, is read back from LDS; Q^T is a register-resident B operand, zero
