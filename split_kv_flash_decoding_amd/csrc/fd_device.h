@@ -300,6 +300,18 @@ __device__ inline bool locate_unit(int u, const int32_t* __restrict__ seq_lens, 
     return false;
 }
 
+// Every field through a scalar register (the lookups below end in branches
+// that the compiler cannot prove wave-uniform).
+__device__ __forceinline__ void uniform_unit(WorkUnit& u) {
+    u.b = uniform(u.b);
+    u.g = uniform(u.g);
+    u.s = uniform(u.s);
+    u.t0 = uniform(u.t0);
+    u.t1 = uniform(u.t1);
+    u.L = uniform(u.L);
+    u.row0 = uniform(u.row0);
+}
+
 // Tiles of a sequence of L tokens: 16-token tiles (a paged cache's pages).
 __device__ __forceinline__ int seq_tiles(int L) { return (L + 15) >> 4; }
 

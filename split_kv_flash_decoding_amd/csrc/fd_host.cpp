@@ -310,8 +310,8 @@ fd_status fd_plan_splits(const fd_problem* p, const int32_t* lens, int32_t num_c
     // A ragged batch on the matrix-core kernel: per-sequence chunks leave
     // short last splits and a last round of work-groups that occupies part of
     // the chip, so the tiles of all sequences are dealt out in equal work
-    // items instead (split_mode 1): one round of num_cus * 2 work-groups for
-    // a 16-bit cache, num_cus * 3 (the kernel's occupancy) for FP8.
+    // items instead (split_mode 1): one round of a few work-groups per
+    // compute unit (kBalancedWgPerCu16 and the constants beside it).
     // FD_SPLIT_MODE=0/1 overrides; FD_WG_PER_CU sets the work-groups per CU.
     bool ragged = false;
     for (int32_t b = 1; b < p->batch; ++b) ragged |= lens[b] != lens[0];
@@ -330,10 +330,9 @@ fd_status fd_plan_splits(const fd_problem* p, const int32_t* lens, int32_t num_c
             nmax = std::max(nmax, n);
         }
         const int32_t per_cu = env_int("FD_WG_PER_CU", 0) > 0 ? env_int("FD_WG_PER_CU", 0)
-                               : (kv_elem_bytes(p) == 1 ||
-                                  (kernel == kPartialMfmaHeads && mfma_column_tiles(p) == 4))
-                                   ? kBalancedWgPerCuFp8
-                                   : kBalancedWgPerCu16;
+                               : (kernel == kPartialMfmaHeads && mfma_column_tiles(p) == 4) ? kWideMultiQueryWgPerCu
+                               : (kernel == kPartialMfma && kv_elem_bytes(p) == 1)        ? kBalancedWgPerCuFp8
+                                                                                          : kBalancedWgPerCu16;
         const int64_t target = std::max<int64_t>(1, (int64_t)num_cus * per_cu);
         const int64_t P = std::max<int64_t>(ceil_div(positions * workgroups_per_split(p, kernel), target),
                                             kBalancedMinTiles);

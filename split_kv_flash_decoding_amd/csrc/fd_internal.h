@@ -21,21 +21,25 @@ constexpr int32_t kHeadRowsMinChunk = 1024;
 constexpr int32_t kPageSize = 16;
 // Balanced split mode (fd_plan.split_mode 1): tokens per tile of the list,
 // the smallest work item in tiles (256 tokens), the work-groups per compute
-// unit it aims at (16-bit caches: two, fewer and longer items; FP8 caches:
-// three, the kernel's occupancy, since an FP8 item does twice the work per
-// byte), and the largest batch it is chosen for (the combine walks the
-// lengths before its sequence).
+// unit it aims at, and the largest batch it is chosen for (the combine walks
+// the lengths before its sequence). Work-groups per compute unit: two, fewer
+// and longer items, for the matrix-core kernel whose waves own heads, 16-bit
+// and FP8 caches alike (an FP8 wave keeps two tiles in flight; measured on
+// MI355X, same GPU, three against two: GQA varlen 66.6 -> 62.3 us, paged GQA
+// 177.4 -> 172.6 us); three for an FP8 cache on the kernel whose waves share
+// a head (its occupancy).
 constexpr int32_t kTileTokens = 16;
 constexpr int32_t kBalancedMinTiles = 16;
 constexpr int32_t kBalancedWgPerCu16 = 2;
 constexpr int32_t kBalancedWgPerCuFp8 = 3;
 // The matrix-core kernel with waves owning heads and four column tiles (49 to
 // 64 query rows per KV head) does four times the matrix work per byte of a
-// single tile: it wants a third work-group per compute unit, whatever the
-// split mode (measured on MI355X, same GPU: paged GQA with 8 query tokens
-// 492.8 -> 429.5 us, 128K-token MHA with 64 query tokens 458.3 -> 425.2 us;
-// two column tiles lose with it: 121.6 -> 149.1 us, 348.5 -> 412.7 us).
-constexpr int32_t kWideMultiQueryWgPerCu = 3;
+// single tile and fits four work-groups per compute unit: it wants them all,
+// whatever the split mode (measured on MI355X, same GPU, three against four:
+// paged GQA with 8 query tokens 406.7 -> 388.8 us, 128K-token MHA with 64
+// query tokens 402.8 -> 382.1 us; two column tiles lose with more than two:
+// GQA varlen with 8 query tokens 121.3 -> 123.2 (three) and 128.2 us (four)).
+constexpr int32_t kWideMultiQueryWgPerCu = 4;
 constexpr int32_t kBalancedMaxBatch = 4096;
 // List positions a sequence takes before its tiles in the balanced list: the
 // cost of starting a share (the pipeline's first loads, the wave merge and the

@@ -58,7 +58,7 @@
 //   * the next tile's K and V loads are in flight while the current tile is
 //     computed: a 16-bit tile's registers go to LDS first and then receive the
 //     next tile's loads, so one tile's worth of registers suffices; FP8 tiles
-//     use a two-deep register ring;
+//     use a two-deep register ring, so two of them are in flight;
 //   * paged caches whose splits start on a page boundary look pages up once
 //     per 64 tiles: lane i of a wave holds the page of its i-th next tile and
 //     each tile reads its page with readlane, so no K/V load waits on a table
@@ -172,8 +172,12 @@ __device__ __forceinline__ uint32_t widen_fp8_pair(uint32_t w) {
 // share (two buffers per head, one barrier per tile) and each run their own
 // column tile from it, so a K/V byte is loaded and staged once per work-group
 // instead of once per column tile.
+// Register budget: at most 168 VGPRs (three waves per SIMD, so three
+// work-groups per compute unit can be resident), and 128 (four) for the
+// shared-tile forms, which the planner gives four work-groups per compute
+// unit; none spills.
 template <int NQ, int KT, int QT, int PAGE_MODE, bool KEEP, bool WH = false, int NTS = 1>
-__global__ __launch_bounds__(64 * kMW) void partial_mfma(const PartialArgs a) {
+__global__ __launch_bounds__(64 * kMW) __attribute__((amdgpu_waves_per_eu(NTS > 1 && PAGE_MODE != 1 ? 4 : 3))) void partial_mfma(const PartialArgs a) {
     using M = Mfma<QT>;
     constexpr bool PAGED = PAGE_MODE != 0;
     constexpr bool FP8 = KT == FD_FP8_E4M3;
@@ -234,6 +238,11 @@ __global__ __launch_bounds__(64 * kMW) void partial_mfma(const PartialArgs a) {
     }
     int phase = 0;  // shared tile buffers (NTS > 1): the one the next tile is staged into
 next_share:
+    // The unit is the same in every lane, but it leaves the lookups through
+    // branches the compiler takes for lane-divergent: restated as scalars, the
+    // tile loop's buffer descriptors and bounds stay in scalar registers.
+    uniform_unit(wu);
+    S_b = uniform(S_b);
     if (wu.s >= s_max) return;
     const int s = wu.s, b = wu.b, t0 = wu.t0, t1 = wu.t1;
     const int64_t row0 = wu.row0;
@@ -244,7 +253,11 @@ next_share:
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // The wave index is wave-uniform: taking it through a scalar register lets
+    // the compiler keep the per-wave K/V buffer descriptors in scalar
+    // registers (a vector-held descriptor turns every buffer load into a loop
+    // over its distinct values).
+    const int wave = uniform(tid >> 6);
     const int grp = lane >> 4;  // 0..3
     const int col = lane & 15;  // query row (scores, output) / token (K operand) / d-slice (V load)
     // This wave's KV head and column tile.
@@ -371,14 +384,16 @@ next_share:
                 hi[2 * w + 1] = widen_fp8_pair<QT, true>(x[w + 2]);
             }
             // Lane lcol's 32 bytes are chunks 2 lcol and 2 lcol + 1 of the row.
-            // Lanes 4..7 of each eight store their high chunk first, so each
+            // In dims 64..127 (lanes 4..7 of each eight) the two 8-dim halves
+            // of every 16 dims trade places (dim x sits at x ^ 8), so each
             // store instruction's eight-lane groups cover 128 distinct bytes
-            // modulo 128 (with low chunks first everywhere, every bank is hit
-            // twice: measured 0.37 conflict cycles per LDS-active cycle).
+            // modulo 128 with no per-lane data select (with the plain layout
+            // every bank is hit twice: measured 0.37 conflict cycles per
+            // LDS-active cycle); the tile readers apply the same swap.
             uint16_t* d = dst + (RPI * i + lrow) * kPitch + 16 * lcol;
-            const bool hi_first = (lcol >> 2) & 1;
-            *reinterpret_cast<u32x4*>(d + (hi_first ? 8 : 0)) = hi_first ? hi : lo;
-            *reinterpret_cast<u32x4*>(d + (hi_first ? 0 : 8)) = hi_first ? lo : hi;
+            const int sw = (lcol & 4) * 2;
+            *reinterpret_cast<u32x4*>(d + sw) = lo;
+            *reinterpret_cast<u32x4*>(d + (sw ^ 8)) = hi;
         } else {
             *reinterpret_cast<u32x4*>(dst + (RPI * i + lrow) * kPitch + 8 * lcol) = x;
         }
@@ -411,7 +426,9 @@ next_share:
         f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const u32x4 ka = *reinterpret_cast<const u32x4*>(my_sk + col * kPitch + 32 * j + 8 * grp);
+            // dims 64..127 of an FP8 tile: 8-dim halves swapped (stage_one)
+            const int hsw = (FP8 && j >= 2) ? 8 : 0;
+            const u32x4 ka = *reinterpret_cast<const u32x4*>(my_sk + col * kPitch + 32 * j + ((8 * grp) ^ hsw));
             sc = M::qk(ka, qb[j], sc);
         }
 
@@ -456,7 +473,10 @@ next_share:
         // V^T blocks of 16 dims: lane 16 g' + 4 e + j reads row 4 g' + e,
         // dims 16 jd + 4 j .. +4; the transposing read hands lane 16 g' + i
         // the dims-i column of rows 4 g' .. 4 g' + 3.
-        const uint16_t* rd = my_sv + (4 * grp + ((lane >> 2) & 3)) * kPitch + 4 * (lane & 3);
+        const uint16_t* rd_lo = my_sv + (4 * grp + ((lane >> 2) & 3)) * kPitch + 4 * (lane & 3);
+        // dims 64..127 of an FP8 tile: 8-dim halves swapped (stage_one)
+        const uint16_t* rd_hi = my_sv + (4 * grp + ((lane >> 2) & 3)) * kPitch + 4 * ((lane & 3) ^ (FP8 ? 2 : 0));
+        auto rd = [&](int jd) { return (jd < 4 ? rd_lo : rd_hi) + 16 * jd; };
         if constexpr (WH) {
             // Both parts in one double-rate product: the contraction runs over
             // the tile's 16 tokens twice, slots 8 g .. 8 g + 3 of lane group g
@@ -468,14 +488,14 @@ next_share:
             const u32x4 pb = {hw[0], hw[1], lw[0], lw[1]};
 #pragma unroll
             for (int jd = 0; jd < 8; ++jd) {
-                const u32x2_t vt = __builtin_bit_cast(u32x2_t, lds_read_transposed(rd + 16 * jd));
+                const u32x2_t vt = __builtin_bit_cast(u32x2_t, lds_read_transposed(rd(jd)));
                 acc[jd] = M::pv2(u32x4{vt[0], vt[1], vt[0], vt[1]}, pb, acc[jd]);
             }
         } else {
             // Two products (the other form's registers stay within 3 waves per SIMD).
 #pragma unroll
             for (int jd = 0; jd < 8; ++jd) {
-                const i16x4_t vt = lds_read_transposed(rd + 16 * jd);
+                const i16x4_t vt = lds_read_transposed(rd(jd));
                 acc[jd] = M::pv(vt, plo, M::pv(vt, phi, acc[jd]));
             }
         }
@@ -529,19 +549,21 @@ next_share:
             tile += TSTEP;
         }
     } else {
-        // FP8 tiles are half the registers but take longer to stage (the codes
-        // are widened on the way): a two-deep register ring keeps the next
-        // tile's loads ahead of that work (measured faster than the above).
+        // FP8 tiles are half the registers of 16-bit ones, so a two-deep
+        // register ring keeps two tiles in flight (the same bytes in flight
+        // per wave as one 16-bit tile): a tile's registers go to LDS and then
+        // take the loads of the tile two steps on.
         u32x4 ka[KL], va[KL], kb[KL], vb[KL];
         if (tile < ntiles) load(tile, ka, va);
+        if (tile + TSTEP < ntiles) load(tile + TSTEP, kb, vb);
         while (tile < ntiles) {
-            if (tile + TSTEP < ntiles) load(tile + TSTEP, kb, vb);
             stage(ka, va);
+            if (tile + 2 * TSTEP < ntiles) load(tile + 2 * TSTEP, ka, va);
             compute(tile);
             tile += TSTEP;
             if (tile >= ntiles) break;
-            if (tile + TSTEP < ntiles) load(tile + TSTEP, ka, va);
             stage(kb, vb);
+            if (tile + 2 * TSTEP < ntiles) load(tile + 2 * TSTEP, kb, vb);
             compute(tile);
             tile += TSTEP;
         }

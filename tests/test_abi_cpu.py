@@ -165,16 +165,25 @@ def test_balanced_plan(hq, hkv, lens, page):
     assert plan.workspace_bytes == workspace_bytes(len(lens), hq, hkv, plan.max_splits)
 
 
-def test_balanced_plan_fp8_aims_at_three_per_cu():
-    """An FP8 cache's items are sized for three work-groups per compute unit."""
+@pytest.mark.parametrize("hq,hkv,q_len,fp8,per_cu", [
+    (32, 8, 1, True, 2),    # FP8 on the kernel whose waves own heads: two per compute unit
+    (16, 2, 1, True, 3),    # FP8 on the kernel whose waves share a head (two KV heads): three
+    (64, 8, 8, False, 4),   # four column tiles: four
+    (32, 8, 4, False, 2),   # one column tile, 16-bit: two
+])
+def test_balanced_plan_work_groups_per_cu(hq, hkv, q_len, fp8, per_cu):
+    """The balanced list's items are sized for the work-groups per compute unit
+    each matrix-core form runs best with."""
     import torch
     lens = [2915, 4487, 5931, 8309, 8336, 8684, 8905, 10375] * 2
-    p = prob(batch=len(lens), num_q_heads=32, num_kv_heads=8, kv_dtype=torch.float8_e4m3fn, q_dtype=torch.bfloat16)
+    kw = dict(kv_dtype=torch.float8_e4m3fn if fp8 else torch.bfloat16)
+    p = prob(batch=len(lens), num_q_heads=hq, num_kv_heads=hkv, q_dtype=torch.bfloat16, q_len=q_len, **kw)
     plan = fd.fd_plan_splits(p, lens, num_cus=256)
-    assert plan.split_mode == 1 and plan.partial_kernel == 4
-    wg = mfma_work_groups(32, 8, 1, 4)  # two work-groups of four KV heads per item
+    kern = mfma_kernel(hq, hkv, q_len)
+    assert plan.split_mode == 1 and plan.partial_kernel == kern
+    wg = mfma_work_groups(hq, hkv, q_len, kern)
     P = plan.chunk_tokens // 16
-    assert 256 * 3 * (P - 1) / P - wg <= plan.total_splits * wg <= 256 * 3 + wg
+    assert 256 * per_cu * (P - 1) / P - wg <= plan.total_splits * wg <= 256 * per_cu + wg
 
 
 def test_balanced_plan_choice(monkeypatch):
