@@ -97,6 +97,45 @@ def test_append_matches_oracle(fd, case):
         assert_same_storage(q, rq, "q")
 
 
+LOOP_CASES = [
+    # a few hundred new tokens per sequence (chunks of a prompt), every token checked
+    (torch.bfloat16, torch.bfloat16, "half", 128, 8, 2, [300, 500, 177], 150),
+    (torch.float8_e4m3fn, torch.float16, "interleaved", 64, 4, 4, [700], 600),
+    (torch.float16, torch.float16, None, 128, 4, 2, [400, 301], 300),
+]
+
+
+@pytest.mark.parametrize("case", range(len(LOOP_CASES)))
+def test_append_many_new_tokens(fd, case):
+    """Hundreds of new tokens per sequence (a prompt chunk) against the
+    oracle: every token, rotated queries included."""
+    kvdt, qdt, style, d, hq, hkv, lens, n = LOOP_CASES[case]
+    wl, k_new, v_new = setup(LOOP_CASES[case], 990 + case)
+    announce(f"append chunk case {case}: cache {kvdt} rope {style} d={d} Hq={hq} Hkv={hkv} lens={lens} n={n}")
+    dev = torch.device("cuda", 0)
+    kc, vc, q = wl.k.to(dev), wl.v.to(dev), wl.q.to(dev).contiguous()
+    ks = wl.k_scale.to(dev) if wl.k_scale is not None else None
+    vs = wl.v_scale.to(dev) if wl.v_scale is not None else None
+    prob = fd.make_problem(batch=wl.batch, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, kv_dtype=kvdt,
+                           q_dtype=qdt, page_size=16, max_pages_per_seq=wl.max_pages_per_seq, q_len=n)
+    fd.fd_append_kv(prob, k_new.to(dev), v_new.to(dev), q, kc, vc, wl.block_table.to(dev), wl.seq_lens.to(dev),
+                    rope_style=style, rope_base=10000.0, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    rk, rv, rq = append_kv(wl.k, wl.v, wl.block_table, wl.seq_lens, k_new, v_new, wl.q, rope_style=style,
+                           rope_base=10000.0, k_scale=wl.k_scale, v_scale=wl.v_scale)
+    mask = np.zeros(tuple(wl.k.shape), dtype=bool)
+    for b, L in enumerate(wl.lens):
+        for j in range(n):
+            pos = L - n + j
+            mask[int(wl.block_table[b, pos // 16]), pos % 16] = True
+    assert_same_storage(kc, rk, "K cache", mask)
+    assert_same_storage(vc, rv, "V cache", mask)
+    if style is None:
+        assert torch.equal(q.cpu(), wl.q)
+    else:
+        assert_same_storage(q, rq, "q")
+
+
 def test_append_then_decode(fd):
     """The step a decoder runs: append with RoPE, then split-KV decode with the
     rotated queries, against the oracle doing the same two steps."""
