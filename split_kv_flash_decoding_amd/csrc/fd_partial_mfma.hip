@@ -422,6 +422,23 @@ next_share:
     auto compute = [&](int tile) {
         const int tt = t0 + tile * kTile;
 
+        // V^T blocks of 16 dims: lane 16 g' + 4 e + j reads row 4 g' + e,
+        // dims 16 jd + 4 j .. +4; the transposing read hands lane 16 g' + i
+        // the dims-i column of rows 4 g' .. 4 g' + 3. The eight reads go out
+        // first, so their latency passes under the scores and the softmax
+        // (the shared-tile forms, held to 128 registers, read each block just
+        // before its product instead).
+        const uint16_t* rd_lo = my_sv + (4 * grp + ((lane >> 2) & 3)) * kPitch + 4 * (lane & 3);
+        // dims 64..127 of an FP8 tile: 8-dim halves swapped (stage_one)
+        const uint16_t* rd_hi = my_sv + (4 * grp + ((lane >> 2) & 3)) * kPitch + 4 * ((lane & 3) ^ (FP8 ? 2 : 0));
+        constexpr bool kEarlyV = NTS == 1;
+        auto read_v = [&](int jd) { return lds_read_transposed((jd < 4 ? rd_lo : rd_hi) + 16 * jd); };
+        i16x4_t vt[8];
+        if constexpr (kEarlyV) {
+#pragma unroll
+            for (int jd = 0; jd < 8; ++jd) vt[jd] = read_v(jd);
+        }
+
         // A operand of d-block j: K row col, dims 32 j + 8 grp .. +8.
         f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -470,13 +487,6 @@ next_share:
         typename M::v4 phi, plo;
         M::split(p, phi, plo);
 
-        // V^T blocks of 16 dims: lane 16 g' + 4 e + j reads row 4 g' + e,
-        // dims 16 jd + 4 j .. +4; the transposing read hands lane 16 g' + i
-        // the dims-i column of rows 4 g' .. 4 g' + 3.
-        const uint16_t* rd_lo = my_sv + (4 * grp + ((lane >> 2) & 3)) * kPitch + 4 * (lane & 3);
-        // dims 64..127 of an FP8 tile: 8-dim halves swapped (stage_one)
-        const uint16_t* rd_hi = my_sv + (4 * grp + ((lane >> 2) & 3)) * kPitch + 4 * ((lane & 3) ^ (FP8 ? 2 : 0));
-        auto rd = [&](int jd) { return (jd < 4 ? rd_lo : rd_hi) + 16 * jd; };
         if constexpr (WH) {
             // Both parts in one double-rate product: the contraction runs over
             // the tile's 16 tokens twice, slots 8 g .. 8 g + 3 of lane group g
@@ -488,15 +498,15 @@ next_share:
             const u32x4 pb = {hw[0], hw[1], lw[0], lw[1]};
 #pragma unroll
             for (int jd = 0; jd < 8; ++jd) {
-                const u32x2_t vt = __builtin_bit_cast(u32x2_t, lds_read_transposed(rd(jd)));
-                acc[jd] = M::pv2(u32x4{vt[0], vt[1], vt[0], vt[1]}, pb, acc[jd]);
+                const u32x2_t v2 = __builtin_bit_cast(u32x2_t, kEarlyV ? vt[jd] : read_v(jd));
+                acc[jd] = M::pv2(u32x4{v2[0], v2[1], v2[0], v2[1]}, pb, acc[jd]);
             }
         } else {
             // Two products (the other form's registers stay within 3 waves per SIMD).
 #pragma unroll
             for (int jd = 0; jd < 8; ++jd) {
-                const i16x4_t vt = lds_read_transposed(rd(jd));
-                acc[jd] = M::pv(vt, plo, M::pv(vt, phi, acc[jd]));
+                const i16x4_t v4 = kEarlyV ? vt[jd] : read_v(jd);
+                acc[jd] = M::pv(v4, plo, M::pv(v4, phi, acc[jd]));
             }
         }
     };
