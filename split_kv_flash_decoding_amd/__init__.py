@@ -25,6 +25,7 @@ from ._capi import (  # noqa: F401
     FdError,
     FdPlan,
     FdProblem,
+    bind_decode_attention,
     decode_attention,
     FD_ROPE_HALF,
     FD_ROPE_INTERLEAVED,

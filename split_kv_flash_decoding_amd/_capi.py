@@ -342,6 +342,40 @@ def fd_decode_attention(problem: FdProblem, q, k, v, block_table, seq_lens_host,
         _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
+def bind_decode_attention(problem: FdProblem, q, k, v, block_table, seq_lens_host, seq_lens_dev, out, lse,
+                          workspace, stream=None, k_scale=None, v_scale=None):
+    """fd_decode_attention (or its _scaled form) with every argument checked
+    and converted once: returns a callable that makes the one C call (plan,
+    partial kernel, combine) on the same buffers each time it is called,
+    for loops that repeat a step on resident data. The lengths are copied
+    now; the tensors must stay alive and unchanged in shape."""
+    arr, vals = _lens_array(seq_lens_host)
+    _check_tensors(problem, q, k, v, block_table, seq_lens_dev, sum(vals))
+    _check_out(problem, out, lse)
+    problem = FdProblem.from_buffer_copy(_with_pool(problem, k))
+    lib = load_library()
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _stream(stream)
+    pp = ctypes.byref(problem)
+    if problem.kv_dtype == FD_FP8_E4M3 or k_scale is not None or v_scale is not None:
+        _check_scales(problem, k_scale, v_scale)
+        fn = lib.fd_decode_attention_scaled
+        args = (pp, _ptr(q), _ptr(k), _ptr(v), _ptr(k_scale), _ptr(v_scale), _ptr(block_table), arr,
+                _ptr(seq_lens_dev), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, st)
+    else:
+        fn = lib.fd_decode_attention
+        args = (pp, _ptr(q), _ptr(k), _ptr(v), _ptr(block_table), arr, _ptr(seq_lens_dev), _ptr(out), _ptr(lse),
+                _ptr(workspace), ws_bytes, st)
+
+    def run() -> None:
+        status = fn(*args)
+        if status:
+            _check(status)
+
+    run.keep = (problem, arr, q, k, v, block_table, seq_lens_dev, out, lse, workspace, k_scale, v_scale)
+    return run
+
+
 NOALLOC_WORKSPACE_BYTES = 64 << 20  # FD_NOALLOC_WORKSPACE_BYTES
 
 
