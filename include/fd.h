@@ -152,17 +152,20 @@ typedef struct fd_plan {
  * work-groups (sequence, KV head, split) for k = 1, 2, 3, 4, 6, 8, ... and
  * keeps the largest one whose full-size splits alone give every compute unit
  * two work-groups (three when shorter last splits exist; twice that for the
- * token-rows kernel on an FP8 cache) while at most an eighth of the tokens
- * fall in shorter last splits. Chunks are multiples of
+ * token-rows kernel on an FP8 cache; four work-groups per compute unit
+ * directly for the matrix-core kernel with four column tiles) while at most
+ * an eighth of the tokens fall in shorter last splits. Chunks are multiples of
  * 64 and at least 256 tokens (1024 for the kernel whose work-groups cover
  * several heads, 2048 when the cache is FP8; that kernel gives way to one
  * head per work-group when its work-groups would be fewer than the compute
  * units).
  * A batch of unequal lengths on the matrix-core kernel (at most 4096
  * sequences, no forced split count) gets split_mode 1 instead:
- * P = max(16, ceil(sum_b (n_b + 4) * Hkv / (num_cus * k))) positions per work item,
- * i.e. about k work-groups per compute unit, all of them the same size: k = 2
- * for a 16-bit cache, 3 (the kernel's occupancy) for FP8.
+ * P = max(16, ceil(sum_b (n_b + 4) * W / (num_cus * k))) positions per work
+ * item (n_b = ceil(L_b / 16) tiles, W the work-groups per item), i.e. about k
+ * work-groups per compute unit, all of them the same size: k = 4 for the
+ * kernel with each wave owning a head and four column tiles, 3 for an FP8
+ * cache on the kernel whose waves share a head, 2 otherwise.
  * `force_num_splits` > 0 instead sets C = ceil(max_b L_b / force) and accepts
  * any C >= 1 (split_mode 0). `num_cus` == 0 asks the current HIP device (the only HIP call
  * here; its count is cached per device). Validates the problem and every
@@ -170,7 +173,7 @@ typedef struct fd_plan {
  * seq_lens_host: B lengths in host memory. out: receives the plan.
  * The environment variables FD_NUM_SPLITS (forces splits when the argument
  * is 0), FD_MIN_CHUNK, FD_WG_PER_CU (fixes k, or the work-groups per compute
- * unit of split_mode 1), FD_PARTIAL_KERNEL (0, 1 or 2) and FD_SPLIT_MODE (0 or
+ * unit of split_mode 1), FD_PARTIAL_KERNEL (0 to 4) and FD_SPLIT_MODE (0 or
  * 1, where the balanced mode applies) override these choices for experiments.
  */
 fd_status fd_plan_splits(const fd_problem* problem, const int32_t* seq_lens_host,
