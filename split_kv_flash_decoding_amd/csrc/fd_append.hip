@@ -73,15 +73,19 @@ __device__ __forceinline__ uint32_t e4m3_encode(double x) {
 // bit set when v was not exact. fp32 keeps at least two more bits than fp16
 // and bf16, so rounding this to nearest-even in either gives what one
 // rounding of v itself gives (Boldo and Melquiond, "Emulation of FMA and
-// correctly rounded sums: proved algorithms using rounding to odd", 2008);
-// overflowed values stay infinite, as the direct rounding makes them.
+// correctly rounded sums: proved algorithms using rounding to odd", 2008).
+// No special cases are needed: an exact v (infinities included) comes back
+// unchanged; a v past fp32's range rounds to infinity, steps back to the
+// largest finite fp32 with its last bit already set, and that rounds to
+// infinity again in either 16-bit format, as v itself does; a NaN stays a
+// NaN.
 __device__ __forceinline__ float round_to_odd_f32(double v) {
     const float f = (float)v;  // nearest, ties to even
     const double back = (double)f;
-    if (back == v || __builtin_isinf(f) || !(v == v)) return f;
     uint32_t u = __builtin_bit_cast(uint32_t, f);
-    if (fabs(back) > fabs(v)) u -= 1;  // rounded away from zero: one step back
-    return __builtin_bit_cast(float, u | 1u);
+    u -= (fabs(back) > fabs(v)) ? 1u : 0u;  // rounded away from zero: one step back
+    u |= (back != v) ? 1u : 0u;             // inexact: the sticky bit
+    return __builtin_bit_cast(float, u);
 }
 
 // N (4 or 8) fp64 values rounded once to the storage format DT and stored as
@@ -98,15 +102,18 @@ __device__ __forceinline__ void store(void* base, int64_t elem, const double* x)
         else
             *reinterpret_cast<uint32_t*>(dst) = w[0];
     } else {
+        // Two values per conversion instruction (nearest even, element 2i in
+        // the low half).
+        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+        typedef float f32x2_t __attribute__((ext_vector_type(2)));
         uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int e = 0; e < N; ++e) {
-            uint32_t h;
+        for (int e = 0; e < N; e += 2) {
+            const f32x2_t f = {round_to_odd_f32(x[e]), round_to_odd_f32(x[e + 1])};
             if constexpr (DT == FD_F16)
-                h = __builtin_bit_cast(uint16_t, (_Float16)round_to_odd_f32(x[e]));
+                w[e / 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, half2_t));
             else
-                h = __builtin_bit_cast(uint16_t, (__bf16)round_to_odd_f32(x[e]));
-            w[e / 2] |= h << (16 * (e % 2));
+                w[e / 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
         }
         uint16_t* dst = static_cast<uint16_t*>(base) + elem;
         if constexpr (N == 8)
@@ -196,6 +203,7 @@ __global__ __launch_bounds__(256) void append_kv(const AppendArgs a) {
     // 16-byte piece), 4p .. 4p+3 and their partners 4p + d/2 .. +3 in the half
     // pairing (two 8-byte pieces); a V item is 8 elements.
     const int per_row = d / 8;
+    const int row_shift = d == 128 ? 4 : 3;  // log2(per_row); d is 64 or 128
     const int nq = (STYLE != FD_ROPE_NONE && a.q) ? a.hq * per_row : 0;
     const int nk = a.hkv * per_row;
     const int total = nq + nk + a.hkv * per_row;
@@ -208,7 +216,7 @@ __global__ __launch_bounds__(256) void append_kv(const AppendArgs a) {
         auto locate = [&](int idx, int& kind, int& h, int& p) {
             kind = idx < nq ? 0 : idx < nq + nk ? 1 : 2;
             const int k = idx - (kind == 0 ? 0 : kind == 1 ? nq : nq + nk);
-            h = k / per_row, p = k % per_row;
+            h = k >> row_shift, p = k & (per_row - 1);  // per_row is 8 or 16
         };
         auto src_of = [&](int kind, int h) -> const uint16_t* {
             const void* base_ptr = kind == 0 ? a.q : kind == 1 ? a.k_new : a.v_new;
@@ -238,10 +246,8 @@ __global__ __launch_bounds__(256) void append_kv(const AppendArgs a) {
             if (page >= a.num_pages) page = -1;
             if constexpr (STYLE != FD_ROPE_NONE) {
                 for (int i = threadIdx.x; i < half; i += blockDim.x) {
-                    // base^(-2i/d) as 2^(log2(base) * (-2i/d)): within a few ulps of the
-                    // rounded power (a relative angle error near 1e-15, far below what
-                    // moves a stored 16-bit result), and fewer registers than pow.
-                    const double angle = (double)pos * exp2(log2((double)a.rope_base) * (-2.0 * i / d));
+                    // inv_freq[i] = base^(-2i/d), computed once per call on the host.
+                    const double angle = (double)pos * a.inv_freq[i];
                     sincos_f64(angle, s_sin[i], s_cos[i]);
                 }
                 __syncthreads();

@@ -484,6 +484,7 @@ struct AppendArgs {
     const int32_t* lens;
     int n, hkv, hq, d, max_pages, num_pages, style;
     float rope_base;
+    double inv_freq[64];  // base^(-2i/d) for pair i < d/2 (RoPE)
 };
 
 // Launchers (each defined in the file that holds its kernel). They enqueue on
