@@ -205,8 +205,9 @@ def probe_patterns(fd, k, v, sink, row_bytes: int, chunks=None) -> dict:
     plain streaming read (K, then V), and the row pattern of the decode
     kernels (include/fd_probe.h) over rows of row_bytes: 1 KB column blocks
     with the waves splitting the rows (head rows), at chunks that give about
-    1, 2 and 4 work-groups per compute unit, and 8 KB blocks with the waves
-    across them (head columns) where the rows hold 8 KB."""
+    1, 2 and 4 work-groups per compute unit, plain and from rotated starts,
+    and 8 KB blocks with the waves across them (head columns) where the rows
+    hold 8 KB."""
     nbytes = 2 * k.numel() * k.element_size()
     out = {"stream": time_gbps(lambda: (fd.fd_probe_read(k, sink), fd.fd_probe_read(v, sink)), nbytes)}
     if row_bytes % 1024:
@@ -215,12 +216,14 @@ def probe_patterns(fd, k, v, sink, row_bytes: int, chunks=None) -> dict:
     for per_cu in (1, 2, 4):
         chunk = max(16, -(-rows * (row_bytes // 1024) // (256 * per_cu)))
         out[f"rows_1k_{per_cu}wg_per_cu"] = time_gbps(
-            lambda: fd.fd_probe_read_rows(k, v, row_bytes, chunk, False, sink), nbytes)
+            lambda: fd.fd_probe_read_rows(k, v, row_bytes, chunk, 0, sink), nbytes)
+        out[f"rows_1k_rot_{per_cu}wg_per_cu"] = time_gbps(
+            lambda: fd.fd_probe_read_rows(k, v, row_bytes, chunk, 2, sink), nbytes)
     if row_bytes % 8192 == 0:
         for per_cu in (1, 2):
             chunk = max(16, -(-rows * (row_bytes // 8192) // (256 * per_cu)))
             out[f"cols_8k_{per_cu}wg_per_cu"] = time_gbps(
-                lambda: fd.fd_probe_read_rows(k, v, row_bytes, chunk, True, sink), nbytes)
+                lambda: fd.fd_probe_read_rows(k, v, row_bytes, chunk, 1, sink), nbytes)
     return out
 
 

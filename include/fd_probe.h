@@ -39,7 +39,11 @@ fd_status fd_probe_read(const void* src, size_t bytes, float* sink, void* stream
  * per wave instruction, 4 rows of a and 4 of b per wave stage with the next
  * stage in flight. waves_across 0: block_bytes 1024, the eight waves split
  * the chunk's rows; waves_across 1: block_bytes 8192, wave w reads column w of
- * the block in every row. sink: device memory of FD_PROBE_SINK_FLOATS floats. */
+ * the block in every row; waves_across 2: as 0, but a chunk whose stages are a
+ * whole multiple of the eight waves starts at a rotated stage (chunk c at
+ * (7 c mod n) 8 of its n 8 stages, wrapping round), the traversal of the
+ * head-rows kernel on a 16-bit cache. Any other value: FD_ERR_INVALID_ARGUMENT.
+ * sink: device memory of FD_PROBE_SINK_FLOATS floats. */
 fd_status fd_probe_read_rows(const void* a, const void* b, int64_t rows, int32_t row_bytes, int32_t block_bytes,
                              int32_t chunk_rows, int32_t waves_across, float* sink, void* stream);
 

@@ -533,18 +533,20 @@ def fd_probe_read(src, sink, stream=None) -> None:
     _check(load_library().fd_probe_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(stream)))
 
 
-def fd_probe_read_rows(a, b, row_bytes: int, chunk_rows: int, waves_across: bool, sink, stream=None) -> None:
+def fd_probe_read_rows(a, b, row_bytes: int, chunk_rows: int, waves_across, sink, stream=None) -> None:
     """Read the CUDA tensors ``a`` and ``b`` (the same byte size, a whole
     number of ``row_bytes`` rows) in the decode kernels' row pattern
     (include/fd_probe.h): 1 KB column blocks with the eight waves splitting
-    the rows, or 8 KB blocks with wave w reading column w."""
+    the rows (``waves_across`` 0 or False; 2: each chunk from a rotated start,
+    as the head-rows kernel walks a 16-bit cache), or 8 KB blocks with wave w
+    reading column w (1 or True)."""
     nbytes = a.numel() * a.element_size()
     if not a.is_cuda or not b.is_cuda or b.numel() * b.element_size() != nbytes or nbytes % row_bytes:
         raise ValueError("a and b must be CUDA tensors of one size, a whole number of rows")
     if not sink.is_cuda or sink.numel() * sink.element_size() < PROBE_SINK_FLOATS * 4:
         raise ValueError("sink must be a CUDA tensor of PROBE_SINK_FLOATS floats")
     _check(load_library().fd_probe_read_rows(_ptr(a), _ptr(b), nbytes // row_bytes, row_bytes,
-                                             8192 if waves_across else 1024, chunk_rows, int(bool(waves_across)),
+                                             8192 if int(waves_across) == 1 else 1024, chunk_rows, int(waves_across),
                                              _ptr(sink), _stream(stream)))
 
 

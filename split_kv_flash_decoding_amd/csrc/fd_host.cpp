@@ -238,10 +238,11 @@ fd_status fd_plan_splits(const fd_problem* p, const int32_t* lens, int32_t num_c
         if (force_num_splits > 0) {
             c = ceil_div(lmax, force_num_splits);
         } else {
-            // Head-rows work-groups cover several heads and slow down below
+            // Head-rows work-groups cover several heads and run best from
             // ~1024 tokens (2 KB per head of a 16-bit cache) per split
-            // (measured: 32K tokens at 512-token chunks ran 23% slower than at
-            // 1024); an FP8 split needs twice the tokens for the same bytes
+            // (measured on a 32K-token cache: 512-token chunks 86.8 us against
+            // 85.3-85.9 at 1024 with the rotated traversal, 102.2 without it);
+            // an FP8 split needs twice the tokens for the same bytes
             // (128K-token FP8 cache: 2048-token splits 3% faster than 1024).
             const int32_t head_rows_min = kHeadRowsMinChunk * 2 / kv_elem_bytes(p);
             // Head columns: the same bytes per work-group as head rows.

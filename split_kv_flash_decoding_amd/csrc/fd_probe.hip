@@ -54,8 +54,11 @@ __global__ __launch_bounds__(kThreads) void read_kernel(const u32x4* __restrict_
 // stages w, w + 8, ... of the chunk in a 1 KB column block (the head-rows
 // kernel); ACROSS = true: wave w takes every stage of column w of an 8 KB
 // block (the head-columns kernel). Rows past the chunk re-read its last row.
+// ROTATE (head rows only): a full chunk c starts at stage (7 c mod n) 8 of its
+// n 8 stages and wraps round, the head-rows kernel's traversal of a 16-bit
+// cache.
 constexpr int kRowWaves = 8;
-template <bool ACROSS>
+template <bool ACROSS, bool ROTATE = false>
 __global__ __launch_bounds__(64 * kRowWaves) void read_rows_kernel(const uint8_t* __restrict__ a,
                                                                    const uint8_t* __restrict__ b, int64_t rows,
                                                                    int row_bytes, int block_bytes, int chunk_rows,
@@ -69,7 +72,10 @@ __global__ __launch_bounds__(64 * kRowWaves) void read_rows_kernel(const uint8_t
     const int64_t col = (int64_t)blk * block_bytes + (ACROSS ? wave * 1024 : 0) + lane * 16;
     const int nst = (int)((r1 - r0 + 3) / 4);
     const int step = ACROSS ? 1 : kRowWaves;
-    auto load = [&](int st, u32x4* x) {
+    int rot = 0;
+    if (ROTATE && nst % kRowWaves == 0) rot = (int)((blockIdx.x / nblk * 7) % (nst / kRowWaves)) * kRowWaves;
+    auto load = [&](int st_, u32x4* x) {
+        const int st = st_ + rot < nst ? st_ + rot : st_ + rot - nst;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             int64_t r = r0 + 4 * st + u;
@@ -132,7 +138,9 @@ fd_status fd_probe_read_rows(const void* a, const void* b, int64_t rows, int32_t
     if (rows < 1 || chunk_rows < 1 || row_bytes < 1024 || row_bytes % 1024)
         return fail(FD_ERR_INVALID_ARGUMENT, "probe_read_rows: rows %lld, chunk_rows %d, row_bytes %d (a multiple "
                     "of 1024)", (long long)rows, chunk_rows, row_bytes);
-    const int32_t want_block = waves_across ? 1024 * fdp::kRowWaves : 1024;
+    if (waves_across < 0 || waves_across > 2)
+        return fail(FD_ERR_INVALID_ARGUMENT, "probe_read_rows: waves_across %d is not 0, 1 or 2", waves_across);
+    const int32_t want_block = waves_across == 1 ? 1024 * fdp::kRowWaves : 1024;
     if (block_bytes != want_block || row_bytes % block_bytes)
         return fail(FD_ERR_INVALID_ARGUMENT, "probe_read_rows: block_bytes must be %d and divide row_bytes %d",
                     want_block, row_bytes);
@@ -141,9 +149,12 @@ fd_status fd_probe_read_rows(const void* a, const void* b, int64_t rows, int32_t
     const uint8_t* pa = static_cast<const uint8_t*>(a);
     const uint8_t* pb = static_cast<const uint8_t*>(b);
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    if (waves_across)
+    if (waves_across == 1)
         hipLaunchKernelGGL(fdp::read_rows_kernel<true>, dim3((uint32_t)wgs), dim3(64 * fdp::kRowWaves), 0, hs, pa,
                            pb, rows, row_bytes, block_bytes, chunk_rows, sink);
+    else if (waves_across == 2)
+        hipLaunchKernelGGL((fdp::read_rows_kernel<false, true>), dim3((uint32_t)wgs), dim3(64 * fdp::kRowWaves), 0,
+                           hs, pa, pb, rows, row_bytes, block_bytes, chunk_rows, sink);
     else
         hipLaunchKernelGGL(fdp::read_rows_kernel<false>, dim3((uint32_t)wgs), dim3(64 * fdp::kRowWaves), 0, hs, pa,
                            pb, rows, row_bytes, block_bytes, chunk_rows, sink);

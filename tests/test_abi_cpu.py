@@ -52,6 +52,10 @@ def test_probe_calls_validate_before_launching():
     assert rp(fake, fake, 16, 4096, 8192, 64, 1, fake, None) == fd.FD_ERR_INVALID_ARGUMENT   # block wider than row
     assert rp(fake, fake, 0, 8192, 1024, 64, 0, fake, None) == fd.FD_ERR_INVALID_ARGUMENT    # no rows
     assert rp(fake, ctypes.c_void_p(0x10008), 16, 8192, 1024, 64, 0, fake, None) == fd.FD_ERR_INVALID_ARGUMENT
+    # mode 2 (rotated head rows) takes 1 KB blocks; modes past 2 are refused
+    assert rp(fake, fake, 16, 8192, 8192, 64, 2, fake, None) == fd.FD_ERR_INVALID_ARGUMENT   # block size
+    assert rp(fake, fake, 16, 8192, 1024, 64, 3, fake, None) == fd.FD_ERR_INVALID_ARGUMENT   # unknown mode
+    assert rp(fake, fake, 16, 8192, 1024, 64, -1, fake, None) == fd.FD_ERR_INVALID_ARGUMENT  # unknown mode
 
 
 def test_status_strings():
