@@ -239,11 +239,13 @@ fd_status fd_plan_splits(const fd_problem* p, const int32_t* lens, int32_t num_c
             c = ceil_div(lmax, force_num_splits);
         } else {
             // Head-rows work-groups cover several heads and run best from
-            // ~1024 tokens (2 KB per head of a 16-bit cache) per split
-            // (measured on a 32K-token cache: 512-token chunks 86.8 us against
-            // 85.3-85.9 at 1024 with the rotated traversal, 102.2 without it);
-            // an FP8 split needs twice the tokens for the same bytes
-            // (128K-token FP8 cache: 2048-token splits 3% faster than 1024).
+            // ~1024 tokens (2 KB per head of a 16-bit cache) per split when
+            // the chip is full (measured on a 32K-token cache: 512-token
+            // chunks 86.8 us against 85.3-85.9 at 1024 with the rotated
+            // traversal, 102.2 without it); an FP8 split needs twice the
+            // tokens for the same bytes (128K-token FP8 cache: 2048-token
+            // splits 3% faster than 1024). Shorter contexts get shorter
+            // head-row splits below (down to kHeadRowsFloorChunk).
             const int32_t head_rows_min = kHeadRowsMinChunk * 2 / kv_elem_bytes(p);
             // Head columns: the same bytes per work-group as head rows.
             const int32_t head_cols_min =
@@ -299,11 +301,28 @@ fd_status fd_plan_splits(const fd_problem* p, const int32_t* lens, int32_t num_c
     };
     int64_t chunk = choose_chunk(kernel);
     if (kernel == kPartialHeadRows && forced != kPartialHeadRows) {
-        // Too few multi-head work-groups to occupy the chip (short or forced
-        // few splits): one KV head per work-group gives Hkv/4 to Hkv/8 times more.
-        int64_t nsplit = 0;
-        for (int32_t b = 0; b < p->batch; ++b) nsplit += ceil_div(lens[b], chunk);
-        if (nsplit * (p->num_kv_heads / heads_per_workgroup(p, kernel)) < num_cus) {
+        // Too few multi-head work-groups to occupy the chip: shorter head-row
+        // splits first, halving the chunk down to kHeadRowsFloorChunk tokens
+        // (or FD_MIN_CHUNK), until every CU has one; failing that (short or
+        // forced few splits), one KV head per work-group (token rows) gives
+        // Hkv/4 to Hkv/8 times more. Measured on MI355X (same GPU, one-shot
+        // step, batch 1, 32 heads, d = 128): 16-bit 16K tokens 48.2 us as
+        // token rows -> 45.8 us as 512-token head rows, 8K 26.2 -> 25.7 us
+        // (256); FP8 32K 51.8 -> 49.5 us (512), FP8 64K 101.5 -> 89.2 us
+        // (1024); FP8 16K unchanged (28.8 / 28.6 us) and FP8 8K stays on token
+        // rows (20.2 us; 256-token head rows 22.6 us).
+        const int64_t groups = p->num_kv_heads / heads_per_workgroup(p, kernel);
+        auto workgroups = [&](int64_t c) {
+            int64_t n = 0;
+            for (int32_t b = 0; b < p->batch; ++b) n += ceil_div(lens[b], c);
+            return n * groups;
+        };
+        if (force_num_splits == 0) {
+            const int64_t floor_chunk = std::max<int32_t>(kHeadRowsFloorChunk, env_int("FD_MIN_CHUNK", 0));
+            while (workgroups(chunk) < num_cus && chunk > floor_chunk)
+                chunk = std::max<int64_t>(floor_chunk, ceil_div(chunk / 2, kChunkGranule) * kChunkGranule);
+        }
+        if (workgroups(chunk) < num_cus) {
             kernel = kPartialTokenRows;
             chunk = choose_chunk(kernel);
         }

@@ -18,6 +18,9 @@ constexpr int32_t kMaxGridYZ = 65535;
 constexpr int32_t kChunkGranule = 64;
 constexpr int32_t kDefaultMinChunk = 256;
 constexpr int32_t kHeadRowsMinChunk = 1024;
+// The shortest head-rows split the planner takes to give every CU a
+// work-group before it falls back to token rows.
+constexpr int32_t kHeadRowsFloorChunk = 256;
 constexpr int32_t kPageSize = 16;
 // Balanced split mode (fd_plan.split_mode 1): tokens per tile of the list,
 // the smallest work item in tiles (256 tokens), the work-groups per compute

@@ -438,9 +438,22 @@ def test_fp8_problems(monkeypatch):
                              num_cus=256).partial_kernel == 2
     # FP8 head-rows splits hold at least 2048 tokens (the bytes of 1024 16-bit tokens)
     assert plan.chunk_tokens == 2048 and fd.fd_plan_splits(prob(), [131072], num_cus=256).chunk_tokens == 2048
-    # FP8 token rows: twice the work-groups a 16-bit cache would get (32K-token MHA: 32 heads x 32 splits)
-    p2 = fd.fd_plan_splits(prob(kv_dtype=f8), [32768], num_cus=256)
-    assert (p2.partial_kernel, p2.chunk_tokens) == (0, 1024)
+    # Shorter contexts: head-row splits are halved (not below 256 tokens) until every CU has a
+    # work-group (32 heads at 8 per FP8 load, 4 per 16-bit load), before token rows take over.
+    for kv, L, want in ((f8, 65536, (2, 1024)), (f8, 32768, (2, 512)), (f8, 16384, (2, 256)),
+                        (None, 16384, (2, 512)), (None, 8192, (2, 256)), (None, 32768, (2, 1024))):
+        pl = fd.fd_plan_splits(prob() if kv is None else prob(kv_dtype=kv), [L], num_cus=256)
+        assert (pl.partial_kernel, pl.chunk_tokens) == want, (kv, L)
+        groups = 4 if kv is f8 else 8
+        assert -(-L // pl.chunk_tokens) * groups >= 256
+    # too short for head rows even at 256 tokens: FP8 token rows, twice the work-groups a 16-bit
+    # cache would get (8K tokens: 32 heads x 32 splits)
+    p2 = fd.fd_plan_splits(prob(kv_dtype=f8), [8192], num_cus=256)
+    assert (p2.partial_kernel, p2.chunk_tokens) == (0, 256)
+    # FD_MIN_CHUNK bounds the halving too
+    monkeypatch.setenv("FD_MIN_CHUNK", "1024")
+    assert fd.fd_plan_splits(prob(kv_dtype=f8), [32768], num_cus=256).partial_kernel == 0
+    monkeypatch.delenv("FD_MIN_CHUNK")
     monkeypatch.setenv("FD_PARTIAL_KERNEL", "0")
     assert fd.fd_plan_splits(prob(), [32768], num_cus=256).chunk_tokens == 2048
     # the workspace does not depend on the cache type
