@@ -132,3 +132,24 @@ def test_fp8_multi_query(fd, case):
     assert res.plan.partial_kernel in (1, 4)
     ref_out, ref_lse = reference_fp8(wl)
     parity(res.out, res.lse, ref_out, ref_lse, what=f"fp8 multi-query {hq}/{hkv} q_len {ql}")
+
+
+@pytest.mark.parametrize("L,fp8,chunk", [(8192, False, 256), (16384, False, 512), (16384, True, 256),
+                                         (32768, True, 512)])
+def test_shortened_head_row_splits(fd, L, fp8, chunk):
+    """Batch 1, 32 heads: contexts too short for the head-rows kernel's usual
+    1024-token (FP8: 2048) splits to give every CU a work-group get halved
+    head-row splits from the planner, down to 256 tokens, instead of token
+    rows; every head against the oracle."""
+    wl = make_workload(name=f"mha{L}", batch=1, num_q_heads=32, num_kv_heads=32, head_dim=128, seq_lens=[L],
+                       dtype=torch.float16, seed=1500 + L // 1024)
+    if fp8:
+        wl = quantize_kv_fp8(wl)
+        res = run_fp8(fd, wl)
+        ref_out, ref_lse = reference_fp8(wl)
+    else:
+        from tests.test_parity_gpu import reference, run
+        res = run(fd, wl)
+        ref_out, ref_lse = reference(wl)
+    assert (res.plan.partial_kernel, res.plan.chunk_tokens) == (2, chunk), res.plan.as_dict()
+    parity(res.out, res.lse, ref_out, ref_lse, what=f"{L} tokens fp8={fp8} plan={res.plan.as_dict()}")
