@@ -351,8 +351,10 @@ fd_status fd_plan_splits(const fd_problem* p, const int32_t* lens, int32_t num_c
         }
         const int32_t per_cu = env_int("FD_WG_PER_CU", 0) > 0 ? env_int("FD_WG_PER_CU", 0)
                                : (kernel == kPartialMfmaHeads && mfma_column_tiles(p) == 4) ? kWideMultiQueryWgPerCu
-                               : (kernel == kPartialMfma && kv_elem_bytes(p) == 1)        ? kBalancedWgPerCuFp8
-                                                                                          : kBalancedWgPerCu16;
+                               : (kernel == kPartialMfmaHeads && mfma_column_tiles(p) == 1 && kv_elem_bytes(p) == 2)
+                                   ? kBalancedWgPerCuSingle16
+                               : (kernel == kPartialMfma && kv_elem_bytes(p) == 1) ? kBalancedWgPerCuFp8
+                                                                                   : kBalancedWgPerCu16;
         const int64_t target = std::max<int64_t>(1, (int64_t)num_cus * per_cu);
         const int64_t P = std::max<int64_t>(ceil_div(positions * workgroups_per_split(p, kernel), target),
                                             kBalancedMinTiles);

@@ -35,6 +35,15 @@ constexpr int32_t kTileTokens = 16;
 constexpr int32_t kBalancedMinTiles = 16;
 constexpr int32_t kBalancedWgPerCu16 = 2;
 constexpr int32_t kBalancedWgPerCuFp8 = 3;
+// One work-group per compute unit (one wave per SIMD) for that kernel with a
+// single column tile on a 16-bit cache: half as many, twice as long items,
+// so half the share starts and splits to merge (measured on MI355X, same GPU,
+// one against two: paged GQA 318.2 against 328.8 us per step, the same with 2
+// query tokens 330.3 against 343.2, GQA varlen 110.7 against 111.9, with 2 and
+// 4 query tokens 113.2 against 116.0 and 116.7 against 121.5-121.9). FP8
+// caches (GQA varlen with 2 query tokens 74.9 against 67.4 us) and two column
+// tiles (paged GQA with 4 query tokens 460.1 against 349.6 us) keep two.
+constexpr int32_t kBalancedWgPerCuSingle16 = 1;
 // The matrix-core kernel with waves owning heads and four column tiles (49 to
 // 64 query rows per KV head) does four times the matrix work per byte of a
 // single tile and fits four work-groups per compute unit: it wants them all,

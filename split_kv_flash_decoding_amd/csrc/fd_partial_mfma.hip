@@ -449,6 +449,13 @@ next_share:
             sc = M::qk(ka, qb[j], sc);
         }
 
+        // Shared-tile forms: the softmax (this wave's vector phase between its
+        // two matrix-core phases) issues at raised priority, so the waves of a
+        // SIMD tend to sit in different phases (measured on MI355X, same GPU,
+        // twice: paged GQA with 8 query tokens 387.0/387.9 -> 385.2/385.0 us
+        // per partial launch, 128K MHA with 64 query tokens 373.3/373.9 ->
+        // 370.8/370.6 us; the single-tile forms did not move).
+        if constexpr (NTS > 1) __builtin_amdgcn_s_setprio(1);
         float p[4];
         float mx = neg_inf();
         if (tt + kTile <= lim_lo) {
@@ -487,6 +494,7 @@ next_share:
         typename M::v4 phi, plo;
         M::split(p, phi, plo);
 
+        if constexpr (NTS > 1) __builtin_amdgcn_s_setprio(0);
         if constexpr (WH) {
             // Both parts in one double-rate product: the contraction runs over
             // the tile's 16 tokens twice, slots 8 g .. 8 g + 3 of lane group g

@@ -161,11 +161,13 @@ def test_balanced_plan(hq, hkv, lens, page):
             per_item[t // P] += 1
         U += SHARE_COST + n
     assert all(c == P for c in per_item[:-1]) and 0 < per_item[-1] <= P
-    # about two work-groups per compute unit for a 16-bit cache (one round):
-    # P = ceil(positions * wg / 512) tiles, so the items fall short of 512 / wg
-    # by at most the fraction 1 / P that the ceiling adds, plus one item
-    if positions * wg >= 256 * 2 * 16:
-        assert 256 * 2 * (P - 1) / P - wg <= plan.total_splits * wg <= 256 * 2 + wg
+    # one round of work-groups: one per compute unit on the kernel whose waves
+    # own heads (a single column tile, 16-bit cache), two on the other:
+    # P = ceil(positions * wg / (256 k)) tiles, so the items fall short of
+    # 256 k / wg by at most the fraction 1 / P that the ceiling adds, plus one item
+    k = 1 if plan.partial_kernel == 4 else 2
+    if positions * wg >= 256 * k * 16:
+        assert 256 * k * (P - 1) / P - wg <= plan.total_splits * wg <= 256 * k + wg
     assert plan.workspace_bytes == workspace_bytes(len(lens), hq, hkv, plan.max_splits)
 
 
@@ -173,7 +175,9 @@ def test_balanced_plan(hq, hkv, lens, page):
     (32, 8, 1, True, 2),    # FP8 on the kernel whose waves own heads: two per compute unit
     (16, 2, 1, True, 3),    # FP8 on the kernel whose waves share a head (two KV heads): three
     (64, 8, 8, False, 4),   # four column tiles: four
-    (32, 8, 4, False, 2),   # one column tile, 16-bit: two
+    (32, 8, 8, False, 2),   # two column tiles, 16-bit: two
+    (32, 8, 4, False, 1),   # one column tile, 16-bit: one
+    (32, 8, 1, False, 1),
 ])
 def test_balanced_plan_work_groups_per_cu(hq, hkv, q_len, fp8, per_cu):
     """The balanced list's items are sized for the work-groups per compute unit
