@@ -265,6 +265,14 @@ fd_status fd_plan_splits(const fd_problem* p, const int32_t* lens, int32_t num_c
             int32_t wg_per_cu = env_int("FD_WG_PER_CU", 0);
             if (wg_per_cu == 0 && kern == kPartialMfmaHeads && mfma_column_tiles(p) == 4)
                 wg_per_cu = kWideMultiQueryWgPerCu;
+            // One column tile on a 16-bit cache: one per CU, as on the balanced
+            // list (measured per step, same GPU: 128K-token MHA with 4 query
+            // tokens 325.5/326.1 -> 316.1/316.4 us, three per CU 332.8; equal
+            // lengths, 32/8 heads: 16 x 8K tokens 86.1 -> 82.4 us, 16 x 4K
+            // 48.2 -> 46.3, 4 x 32K 85.8 -> 82.4, 1 x 128K 89.1 -> 84.1; 64/8
+            // heads, 64 x 2K 88.3 -> 84.1).
+            if (wg_per_cu == 0 && kern == kPartialMfmaHeads && mfma_column_tiles(p) == 1 && kv_elem_bytes(p) == 2)
+                wg_per_cu = kBalancedWgPerCuSingle16;
             if (wg_per_cu > 0) {
                 c = chunk_for(wg_per_cu);
             } else {
