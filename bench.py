@@ -594,12 +594,10 @@ def main() -> int:
     # Steps without a pair make the one-shot C call (planner, partial kernel,
     # combine) with its arguments converted once: the same GPU work as the
     # three calls, less host time ahead of the first launch. A workload with a
-    # forced split count keeps the three calls (the one-shot call plans by
-    # itself).
-    if wl.force_num_splits:
-        one_shot = step
-    else:
-        one_shot = fd.bind_decode_attention(problem, q, k, v, bt, lens_host, lens_dev, out, lse, ws, None, ks, vs)
+    # forced split count makes the three C calls (planner with the forced
+    # count, partial kernel, combine) with their arguments converted once.
+    one_shot = fd.bind_decode_attention(problem, q, k, v, bt, lens_host, lens_dev, out, lse, ws, None, ks, vs,
+                                        num_splits=wl.force_num_splits)
     one_shot()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()

@@ -343,12 +343,16 @@ def fd_decode_attention(problem: FdProblem, q, k, v, block_table, seq_lens_host,
 
 
 def bind_decode_attention(problem: FdProblem, q, k, v, block_table, seq_lens_host, seq_lens_dev, out, lse,
-                          workspace, stream=None, k_scale=None, v_scale=None):
+                          workspace, stream=None, k_scale=None, v_scale=None, num_splits: int = 0):
     """fd_decode_attention (or its _scaled form) with every argument checked
     and converted once: returns a callable that makes the one C call (plan,
     partial kernel, combine) on the same buffers each time it is called,
     for loops that repeat a step on resident data. The lengths are copied
-    now; the tensors must stay alive and unchanged in shape."""
+    now; the tensors must stay alive and unchanged in shape. With
+    num_splits > 0 (a forced split count, which the one-shot call does not
+    take) the callable makes the three C calls fd_plan_splits,
+    fd_decode_partial[_scaled] and fd_combine instead, with the same
+    once-converted arguments."""
     arr, vals = _lens_array(seq_lens_host)
     _check_tensors(problem, q, k, v, block_table, seq_lens_dev, sum(vals))
     _check_out(problem, out, lse)
@@ -357,8 +361,33 @@ def bind_decode_attention(problem: FdProblem, q, k, v, block_table, seq_lens_hos
     ws_bytes = workspace.numel() * workspace.element_size()
     st = _stream(stream)
     pp = ctypes.byref(problem)
-    if problem.kv_dtype == FD_FP8_E4M3 or k_scale is not None or v_scale is not None:
+    scaled = problem.kv_dtype == FD_FP8_E4M3 or k_scale is not None or v_scale is not None
+    if scaled:
         _check_scales(problem, k_scale, v_scale)
+    if num_splits > 0:
+        plan = FdPlan()
+        pl = ctypes.byref(plan)
+        plan_args = (pp, arr, 0, int(num_splits), pl)
+        if scaled:
+            part_fn = lib.fd_decode_partial_scaled
+            part_args = (pp, pl, _ptr(q), _ptr(k), _ptr(v), _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
+                         _ptr(seq_lens_dev), _ptr(workspace), ws_bytes, st)
+        else:
+            part_fn = lib.fd_decode_partial
+            part_args = (pp, pl, _ptr(q), _ptr(k), _ptr(v), _ptr(block_table), _ptr(seq_lens_dev), _ptr(workspace),
+                         ws_bytes, st)
+        comb_args = (pp, pl, _ptr(seq_lens_dev), _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse), st)
+
+        def run_split() -> None:
+            for fn, args in ((lib.fd_plan_splits, plan_args), (part_fn, part_args), (lib.fd_combine, comb_args)):
+                status = fn(*args)
+                if status:
+                    _check(status)
+
+        run_split.keep = (problem, plan, arr, q, k, v, block_table, seq_lens_dev, out, lse, workspace, k_scale,
+                          v_scale)
+        return run_split
+    if scaled:
         fn = lib.fd_decode_attention_scaled
         args = (pp, _ptr(q), _ptr(k), _ptr(v), _ptr(k_scale), _ptr(v_scale), _ptr(block_table), arr,
                 _ptr(seq_lens_dev), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, st)

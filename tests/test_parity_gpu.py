@@ -446,10 +446,13 @@ def test_combine_forms_agree(fd, monkeypatch, case):
         assert diff <= 1e-5 + 2 * rnd * float(outs[0].out.double().abs().max()), (form, diff)
 
 
-def test_bound_one_shot_call_matches_the_three_calls(fd):
+@pytest.mark.parametrize("splits", [0, 5])
+def test_bound_one_shot_call_matches_the_three_calls(fd, splits):
     """bind_decode_attention's callable (the one-shot C call with its
-    arguments converted once) gives, bit for bit, what plan + partial +
-    combine give, on every call (16-bit and FP8, contiguous and paged)."""
+    arguments converted once; with a forced split count, the three C calls
+    with theirs) gives, bit for bit, what plan + partial + combine give
+    through the binding, on every call (16-bit and FP8, contiguous and
+    paged)."""
     from workloads import quantize_kv_fp8
     dev = torch.device("cuda", 0)
     for fp8, page in ((False, 0), (True, 16)):
@@ -466,14 +469,17 @@ def test_bound_one_shot_call_matches_the_three_calls(fd):
         prob = fd.make_problem(batch=3, num_q_heads=16, num_kv_heads=4, head_dim=128, kv_dtype=wl.kv_dtype,
                                q_dtype=torch.bfloat16, out_dtype=torch.float32, scale=wl.scale,
                                page_size=page, max_pages_per_seq=wl.max_pages_per_seq)
-        plan = fd.fd_plan_splits(prob, wl.lens)
+        plan = fd.fd_plan_splits(prob, wl.lens, 0, splits)
+        if splits:
+            assert plan.max_splits == splits
         ws = torch.empty(-(-plan.workspace_bytes // 4), dtype=torch.float32, device=dev)
         o1 = torch.empty(tuple(wl.q.shape), dtype=torch.float32, device=dev)
         l1 = torch.empty(tuple(wl.q.shape[:-1]), dtype=torch.float32, device=dev)
         fd.fd_decode_partial(prob, plan, q, k, v, bt, lens_dev, ws, None, ks, vs)
         fd.fd_combine(prob, plan, lens_dev, ws, o1, l1)
         o2, l2 = torch.full_like(o1, float("nan")), torch.full_like(l1, float("nan"))
-        run = fd.bind_decode_attention(prob, q, k, v, bt, wl.lens, lens_dev, o2, l2, ws, None, ks, vs)
+        run = fd.bind_decode_attention(prob, q, k, v, bt, wl.lens, lens_dev, o2, l2, ws, None, ks, vs,
+                                       num_splits=splits)
         for _ in range(3):
             o2.fill_(float("nan"))
             run()
