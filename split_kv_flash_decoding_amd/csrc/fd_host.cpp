@@ -110,11 +110,11 @@ bool head_rows_applicable(const fd_problem* p) {
 }
 
 bool head_cols_applicable(const fd_problem* p) {
-    return head_rows_applicable(p) && p->num_kv_heads % (rows_per_load(p) * head_rows_waves(p)) == 0;
+    return head_rows_applicable(p) && p->num_kv_heads % (rows_per_load(p) * head_cols_waves(p)) == 0;
 }
 
 int32_t heads_per_workgroup(const fd_problem* p, int32_t kernel) {
-    if (kernel == kPartialHeadCols) return rows_per_load(p) * head_rows_waves(p);
+    if (kernel == kPartialHeadCols) return rows_per_load(p) * head_cols_waves(p);
     if (kernel == kPartialMfmaHeads) return kMfmaWaves / mfma_column_tiles(p);
     return kernel == kPartialHeadRows ? rows_per_load(p) : 1;
 }
@@ -249,7 +249,7 @@ fd_status fd_plan_splits(const fd_problem* p, const int32_t* lens, int32_t num_c
             const int32_t head_rows_min = kHeadRowsMinChunk * 2 / kv_elem_bytes(p);
             // Head columns: the same bytes per work-group as head rows.
             const int32_t head_cols_min =
-                std::max<int32_t>(kChunkGranule, head_rows_min / head_rows_waves(p));
+                std::max<int32_t>(kChunkGranule, head_rows_min / head_cols_waves(p));
             const int64_t min_chunk = std::max<int32_t>(
                 1, env_int("FD_MIN_CHUNK", kern == kPartialHeadRows   ? head_rows_min
                                            : kern == kPartialHeadCols ? head_cols_min

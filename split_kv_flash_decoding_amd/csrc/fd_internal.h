@@ -124,9 +124,10 @@ inline int32_t q_dtype_of(const fd_problem* p) { return p->kv_dtype == FD_FP8_E4
 // d * bytes / 16 lanes per row.
 inline int32_t rows_per_load(const fd_problem* p) { return 64 / (p->head_dim * kv_elem_bytes(p) / 16); }
 
-// Waves per work-group of the head-rows kernels (fd_partial_valu.hip): eight
-// for 16-bit caches, four for FP8.
-inline int32_t head_rows_waves(const fd_problem* p) { return kv_elem_bytes(p) == 1 ? 4 : 8; }
+// Waves per work-group of the head-columns kernel (fd_partial_valu.hip):
+// eight for 16-bit caches, four for FP8. (Head rows always run eight; a
+// head-rows work-group covers rows_per_load heads whatever its waves.)
+inline int32_t head_cols_waves(const fd_problem* p) { return kv_elem_bytes(p) == 1 ? 4 : 8; }
 
 // Whether the matrix-core partial kernel covers this problem: d = 128 and
 // 2 <= q_len * Hq/Hkv <= kMaxQueryRows query rows per KV head.

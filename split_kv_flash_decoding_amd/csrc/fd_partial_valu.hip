@@ -241,11 +241,13 @@ __global__ __launch_bounds__(kThreads) void partial_valu(const PartialArgs a) {
 // Requires Hkv % RPW == 0. PAGE_MODE: 0 contiguous, 1 paged (a table lookup
 // per token), 2 paged with page-aligned splits and U dividing 16 (page
 // indices fetched 64 at a time and read with readlane).
-// Waves per head-rows work-group: eight for 16-bit caches, four for FP8.
-// Measured on MI355X (same GPU, 200 steps, twice): 32K-token MHA 87.9/88.2 ->
-// 86.2/86.0 us and 128K-token MHA 320.4/321.1 -> 319.1/318.6 us per partial
-// launch with eight; the FP8 128K cache is no faster with eight.
-constexpr int head_rows_waves(int kt) { return kt == FD_FP8_E4M3 ? 4 : 8; }
+// Waves per work-group: eight, except head columns (WH) on an FP8 cache,
+// four (a work-group then covers 32 heads, a whole 4 KB token row of a
+// 32-head cache with d = 128; eight would need 64 heads). Eight against four head-rows waves, measured on MI355X
+// (same GPU, 200 steps, twice, per partial launch): 16-bit 32K-token MHA
+// 87.9/88.2 -> 86.2/86.0 us, 128K-token MHA 320.4/321.1 -> 319.1/318.6 us;
+// FP8 32K 48.3/47.7 -> 47.7/47.2 us, 128K 168.2 -> 166.0 us.
+constexpr int head_rows_waves(int kt, bool wh) { return (wh && kt == FD_FP8_E4M3) ? 4 : 8; }
 
 // WH (head columns): the waves of a work-group take different heads of the
 // same tokens instead of different tokens of the same heads. Wave w owns KV
@@ -255,9 +257,9 @@ constexpr int head_rows_waves(int kt) { return kt == FD_FP8_E4M3 ? 4 : 8; }
 // share a head: each writes its own partial, with no merge through LDS and
 // no barrier. Requires Hkv % (NW * RPW) == 0.
 template <int D, int G, int KT, int QT, int PAGE_MODE, bool WH = false>
-__global__ __launch_bounds__(64 * head_rows_waves(KT)) void partial_valu_heads(const PartialArgs a) {
+__global__ __launch_bounds__(64 * head_rows_waves(KT, WH)) void partial_valu_heads(const PartialArgs a) {
     using KV = KvLoad<KT, QT>;
-    constexpr int NW = head_rows_waves(KT);  // waves per work-group
+    constexpr int NW = head_rows_waves(KT, WH);  // waves per work-group
     constexpr int EPL = KV::kElems;  // elements per 16-byte load
     constexpr int EB = 16 / EPL;     // bytes per element
     constexpr int LPR = D / EPL;     // lanes per head row
@@ -530,13 +532,13 @@ hipError_t launch_heads_g(bool paged, const PartialArgs& a, dim3 grid, hipStream
     const int mode = !paged ? 0 : ((a.chunk % 16 == 0) && (16 % kUnroll == 0)) ? 2 : 1;
     return with_types(a, [&]<int KT, int QT>() {
         if (mode == 0)
-            hipLaunchKernelGGL((partial_valu_heads<D, G, KT, QT, 0, WH>), grid, dim3(64 * head_rows_waves(KT)), 0, st,
+            hipLaunchKernelGGL((partial_valu_heads<D, G, KT, QT, 0, WH>), grid, dim3(64 * head_rows_waves(KT, WH)), 0, st,
                                a);
         else if (mode == 1)
-            hipLaunchKernelGGL((partial_valu_heads<D, G, KT, QT, 1, WH>), grid, dim3(64 * head_rows_waves(KT)), 0, st,
+            hipLaunchKernelGGL((partial_valu_heads<D, G, KT, QT, 1, WH>), grid, dim3(64 * head_rows_waves(KT, WH)), 0, st,
                                a);
         else
-            hipLaunchKernelGGL((partial_valu_heads<D, G, KT, QT, 2, WH>), grid, dim3(64 * head_rows_waves(KT)), 0, st,
+            hipLaunchKernelGGL((partial_valu_heads<D, G, KT, QT, 2, WH>), grid, dim3(64 * head_rows_waves(KT, WH)), 0, st,
                                a);
         return hipGetLastError();
     });
