@@ -156,16 +156,18 @@ typedef struct fd_plan {
  * directly for the matrix-core kernel with four column tiles) while at most
  * an eighth of the tokens fall in shorter last splits. Chunks are multiples of
  * 64 and at least 256 tokens (1024 for the kernel whose work-groups cover
- * several heads, 2048 when the cache is FP8; that kernel gives way to one
- * head per work-group when its work-groups would be fewer than the compute
- * units).
+ * several heads, 2048 when the cache is FP8; when that kernel's
+ * work-groups would be fewer than the compute units its chunk is halved, down
+ * to 256 tokens, and only if that still leaves too few does the plan fall back
+ * to one head per work-group).
  * A batch of unequal lengths on the matrix-core kernel (at most 4096
  * sequences, no forced split count) gets split_mode 1 instead:
  * P = max(16, ceil(sum_b (n_b + 4) * W / (num_cus * k))) positions per work
  * item (n_b = ceil(L_b / 16) tiles, W the work-groups per item), i.e. about k
  * work-groups per compute unit, all of them the same size: k = 4 for the
- * kernel with each wave owning a head and four column tiles, 3 for an FP8
- * cache on the kernel whose waves share a head, 2 otherwise.
+ * kernel with each wave owning a head and four column tiles, 1 for that
+ * kernel with one column tile on a 16-bit cache, 3 for an FP8 cache on the
+ * kernel whose waves share a head, 2 otherwise.
  * `force_num_splits` > 0 instead sets C = ceil(max_b L_b / force) and accepts
  * any C >= 1 (split_mode 0). `num_cus` == 0 asks the current HIP device (the only HIP call
  * here; its count is cached per device). Validates the problem and every
