@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "KV-read GB/s and µs/call, decode attention 128K ctx b=1 (fraction of HBM peak)"
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E peak
+LAUNCH_BOUND_BYTES = 32 << 20  # decode: K/V bytes below which a call is bound by launch and latency
 EVENT_EVERY = 8  # decode: steps per event-timed partial launch in the timed region (runs of 64+ steps)
 KERNEL_SOURCES = os.path.join(ROOT, "split_kv_flash_decoding_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -677,6 +678,9 @@ def main() -> int:
 
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (partial_mean * 1e-3) / 1e9
+    # Below LAUNCH_BOUND_BYTES of K/V a launch ends before streaming reaches
+    # its rate, for the probes too: their ratio then means nothing.
+    launch_bound = nbytes < LAUNCH_BOUND_BYTES
     workload = wl.name
     traffic = measured_traffic(workload)
     rec = {
@@ -721,7 +725,8 @@ def main() -> int:
             "cold_achieved": round(nbytes / (cold_mean * 1e-3) / 1e9, 1),
             "hbm_read_probe_gbps": round(probe_gbps, 1),
             "hbm_read_probe_pattern": probe_name,
-            "frac_of_probe": round(achieved / probe_gbps, 4),
+            "frac_of_probe": None if launch_bound else round(achieved / probe_gbps, 4),
+            "launch_bound": launch_bound,
         },
     }
     if not args.no_cpu_baseline:
